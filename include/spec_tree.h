@@ -1,0 +1,226 @@
+/*
+ * spec_tree.h - C ABI of libspectree, the MI355X (gfx950) verification hot path
+ * of EAGLE-2-style dynamic-tree speculative decoding.
+ *
+ * Pipeline per decoding step and layer:
+ *   spec_tree_build_step (x depth) -> spec_tree_build_finish      draft tree
+ *   spec_tree_attention                                            tree attention
+ *   spec_tree_verify                                               accepted path + bonus
+ *   spec_kv_compact                                                keep accepted KV
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers to caller-owned, contiguous,
+ *     row-major memory (shapes in brackets, outermost first). The library never
+ *     allocates, frees or synchronizes, and keeps no global state besides a
+ *     thread-local error string.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     on it and the call returns immediately.
+ *   - Return value: SPEC_OK or a negative SPEC_E_* code. Every code is decided
+ *     on the host before any launch (shape, range and workspace checks), so a
+ *     failing call enqueues nothing; spec_last_error() describes the failure.
+ *   - Problems in the DATA (which the host cannot see) never abort: they are
+ *     reported in per-sequence `status` words (SPEC_STATUS_* bits) and have
+ *     the defined fallbacks documented below.
+ *   - Workspaces: caller-allocated device memory of at least the size the
+ *     matching *_workspace_size() returns for the same arguments. A workspace
+ *     must be zero-filled before its FIRST use; every call leaves the parts
+ *     that must start at zero at zero again, so it can be reused without
+ *     clearing. Calls that share one workspace must not overlap in time.
+ *
+ * Notation: B sequences; node 0 of a tree is the root (the last emitted token,
+ * whose KV the target writes in the same forward pass) and nodes 1..N are
+ * drafts; T_b = N_b + 1 <= max_T <= 65; parents[i] < i; Hq query heads,
+ * Hkv KV heads, G = Hq / Hkv (query head h reads KV head h / G); d = head dim.
+ */
+#ifndef SPEC_TREE_H
+#define SPEC_TREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+
+/* return codes */
+#define SPEC_OK 0
+#define SPEC_E_INVAL (-1)       /* null pointer, bad shape or range */
+#define SPEC_E_UNSUPPORTED (-2) /* valid but not implemented (e.g. head dim 96) */
+#define SPEC_E_WORKSPACE (-3)   /* workspace too small */
+#define SPEC_E_DEVICE (-4)      /* HIP runtime error at launch */
+
+/* per-sequence status bits (data problems; OR-ed together) */
+#define SPEC_STATUS_INVALID_PARENT 1u  /* parents[i] outside [0, i): node treated as a child of the root */
+#define SPEC_STATUS_INVALID_TOKEN 2u   /* draft token outside [0, V): never accepted, never tested */
+#define SPEC_STATUS_NAN_INPUT 4u       /* NaN in a target row, or in the q row of a sampling node with children */
+#define SPEC_STATUS_ZERO_Q 8u          /* sampling node on the path with children but a missing / all-zero q row */
+#define SPEC_STATUS_ZERO_RESIDUAL 16u  /* sampling node on the path whose residual max(0, p - q) became zero */
+#define SPEC_STATUS_INVALID_PAGE 32u   /* page-table entry outside [0, num_pages): its keys are skipped */
+#define SPEC_STATUS_INVALID_LENGTH 64u /* prefix_lens[b] < 0 or prefix + T_b beyond the page table: clamped */
+
+/* verification modes (per sequence, int8) */
+#define SPEC_MODE_GREEDY 0
+#define SPEC_MODE_SAMPLE 1
+
+/* Library ABI version (SPEC_ABI_VERSION of the build). Pure host call. */
+int32_t spec_abi_version(void);
+
+/* Message of the last failing call on this thread ("" if none). Pure host call. */
+const char* spec_last_error(void);
+
+/* ----------------------------------------------------------------------------
+ * Draft-tree construction - EAGLE-2 expansion and reranking.
+ * Follows the SGLang "Speculative Decoding" page, sections "EAGLE Decoding"
+ * (speculative_num_steps = depth D, speculative_eagle_topk = k,
+ * speculative_num_draft_tokens = N) and "References" (tree-style expansion
+ * with topk branches per step, unlikely branches stop, final rerank to the
+ * top N), and lesty.tech "EAGLE-2 & Lookahead Decoding", section 4 "Dynamic
+ * Tree Construction Mechanics" (path confidence = product of conditional
+ * probabilities = sum of log-probs).
+ *
+ * Step 1 expands the root's row: its top-k tokens (by log-prob desc, token
+ * asc; NaN -> -inf, log-probs >= 0 clamp to 0) become pool entries with score
+ * = log-prob (fp64). Step d >= 2 expands each of the k frontier entries f
+ * (rank order) with row f of this step: its top-k tokens join the pool with
+ * score = parent score + log-prob, and the k best of these k*k candidates (by
+ * score desc, pool index asc) are the next frontier. Finish keeps the N best
+ * pool entries (same order), numbers them 1..N in pool order, and derives
+ * parents, depth, the ancestor bitmask and q_row.
+ *
+ * Draft rows: the caller's draft model produces, for step d, one log-prob row
+ * per frontier slot; rows for sequence b, slot f start at
+ * draft_logprobs + b * seq_stride + f * V (fp32). Step 1 reads slot 0 only.
+ * Per-sequence k, D, N are device int32 [B] arrays; values outside
+ * [1, max_topk], [1, max_depth], [1, min(pool, max_T - 1)] are clamped.
+ * ------------------------------------------------------------------------- */
+size_t spec_tree_build_workspace_size(int32_t B, int32_t max_topk, int32_t max_depth);
+
+/* step: 1..max_depth (sequences with depth[b] < step are left alone).
+ * frontier_tokens: int32 [B, max_topk] out - the new frontier's tokens in rank
+ * order (-1 past k_b), i.e. the tokens the draft model extends next.
+ * Requires 1 <= max_topk <= 8, 1 <= max_depth <= 16, max_topk <= V. */
+int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
+                             int64_t seq_stride, const int32_t* topk, const int32_t* depth, int32_t B,
+                             int32_t max_topk, int32_t max_depth, int32_t V, int32_t* frontier_tokens,
+                             void* stream);
+
+/* Outputs, all [B, max_T]: tokens (node 0 = root_tokens[b]), parents (-1 for
+ * the root), depth_out, anc_mask (uint64, bit j-1 set iff draft j is an
+ * ancestor of node i or i itself; 0 for the root), q_row (row of the per-
+ * sequence draft-row array holding node i's children distribution: 0 for the
+ * root, 1 + (d - 1) * max_topk + f for a node that was frontier slot f at
+ * depth d < D_b, -1 otherwise). Entries i >= N_b + 1 are -1 / 0. */
+int32_t spec_tree_build_finish(void* ws, size_t ws_bytes, const int32_t* root_tokens, const int32_t* topk,
+                               const int32_t* depth, const int32_t* num_draft, int32_t B, int32_t max_topk,
+                               int32_t max_depth, int32_t max_T, int32_t* tokens, int32_t* parents,
+                               int32_t* depth_out, uint64_t* anc_mask, int32_t* q_row, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Tree mask - tanhdev "Tech Radar: SGLang EAGLE-2", section 2 "Dynamic
+ * Tree-Attention Verification" (node i attends exactly to its ancestors and
+ * itself) and section 5 "FlashAttention-3 Tree Kernel Design" (one 64-bit
+ * word per node; ancestry is one AND).
+ * anc_mask[b, i] = anc_mask[b, parents[i]] | (1 << (i - 1)), anc_mask[b, 0] = 0;
+ * depth[b, i] = depth of node i. parents int32 [B, max_T]; T_b int32 [B] or
+ * NULL (= max_T); anc_mask uint64 [B, max_T]; depth int32 [B, max_T] or NULL;
+ * status uint32 [B] or NULL (INVALID_PARENT; such a node hangs off the root).
+ * ------------------------------------------------------------------------- */
+int32_t spec_tree_mask(const int32_t* parents, const int32_t* T_b, int32_t B, int32_t max_T,
+                       uint64_t* anc_mask, int32_t* depth, uint32_t* status, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Tree attention - every tree node attends to the whole paged prefix plus the
+ * root, its ancestors and itself (mask as above; the tree is flattened into
+ * the sequence as in n1n.ai "Speculative Decoding in Production: EAGLE-3
+ * Dynamic Trees", section "From Linear Sequences to Dynamic Draft Trees", and
+ * evaluated in one fused pass as in tanhdev section 5).
+ *
+ * q        bf16 [B, max_T, Hq, d]        query of node i, head h
+ * k_pages  bf16 [num_pages, page, Hkv, d] paged KV pool; token slot s of
+ * v_pages  bf16 [num_pages, page, Hkv, d] sequence b is in page
+ *                                         page_table[b, s / page], row s % page
+ * page_table int32 [B, max_pages]
+ * prefix_lens int32 [B]: L_b prefix tokens; tree node j's K/V is at slot L_b + j
+ * parents  int32 [B, max_T]; T_b int32 [B] or NULL (= max_T)
+ * out      bf16 [B, max_T, Hq, d]  (rows of nodes i >= T_b are not written)
+ * lse      fp32 [B, max_T, Hq] natural-log log-sum-exp of the scaled scores, or NULL
+ * status   uint32 [B] or NULL: INVALID_PARENT / INVALID_PAGE / INVALID_LENGTH (OR-ed in)
+ * sm_scale softmax scale (typically 1/sqrt(d)).
+ * Supported: d in {64, 128}; page a power of two in [1, 1024]; 1 <= max_T <= 65;
+ * Hq % Hkv == 0 and G <= 16. bf16 inputs, fp32 accumulation and softmax.
+ * ------------------------------------------------------------------------- */
+size_t spec_tree_attention_workspace_size(int32_t B, int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d,
+                                          int32_t page, int32_t max_pages);
+int32_t spec_tree_attention(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
+                            const int32_t* prefix_lens, const int32_t* parents, const int32_t* T_b, int32_t B,
+                            int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d, int32_t page, int32_t max_pages,
+                            int32_t num_pages, float sm_scale, void* out, float* lse, uint32_t* status, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Tree verification - greedy, or rejection sampling with residual resampling
+ * (n1n.ai page, section "Mathematical Proof of Lossless Speedup", steps 1-3;
+ * tanhdev section 5 "Speculative Rejection Sampling: Mathematical Invariance";
+ * lesty.tech "Tree Attention Masking and Target Verification": the longest
+ * valid path is accepted and one more token is emitted).
+ *
+ * target      fp32 [B, max_T, V]: node u's target row - logits for greedy
+ *             sequences, probabilities (temperature already applied) for
+ *             sampling sequences.
+ * draft_probs fp32 [B, R, V] draft probabilities, or NULL if no sequence samples;
+ *             q_row int32 [B, max_T] selects node u's children distribution.
+ * tokens, parents int32 [B, max_T]; T_b int32 [B] or NULL; mode int8 [B].
+ * Philox4x64-10 key (philox_key0, philox_key1); node i of sequence b uses
+ * counter (philox_offset, b, i, 0): m = (word0 >> 40) + 1 is its acceptance
+ * uniform r = m / 2^24, K = word1 >> 32 its resampling uniform K / 2^32.
+ *
+ * Greedy: a_u = argmax of row u (ties -> smallest index, NaN = -inf); node i
+ * is valid iff its parent is valid and tokens[i] == a_parent; the end node is
+ * the deepest valid node (ties -> smallest index); bonus = a_end.
+ * Sampling at node u, exact integer arithmetic on 2^-32 fixed point
+ * (fx(x) = 0 if NaN or x <= 0, 2^32-1 if x >= 1, else floor(x * 2^32)):
+ * P = fx(target row), Q = fx(q row), S_P = sum P, S_Q = sum Q; residual after
+ * j rejections N_j[v] = max(0, P[v] S_Q - G_j Q[v]), W_j = sum N_j, G_0 = 0,
+ * G_{j+1} = G_j + floor(W_j / S_Q). Children in index order: child c with
+ * token t is accepted iff N_j[t] > 0 and m_c Q[t] W_j <= 2^24 N_j[t] S_Q.
+ * If none is accepted: bonus = smallest v with 2^32 sum_{w<=v} N[w] > K_u W
+ * (argmax of P if W = 0); a leaf, or a node whose q row is missing or sums
+ * to 0, resamples from P.
+ *
+ * Outputs: accept_len int32 [B] (accepted drafts, root and bonus excluded);
+ * accept_nodes int32 [B, max_T] (root first, then the accepted nodes);
+ * out_tokens int32 [B, max_T] (the accepted drafts' tokens then the bonus:
+ * accept_len + 1 entries); status uint32 [B] (overwritten).
+ * Requires 1 <= max_T <= 65, 1 <= V < 2^24.
+ * ------------------------------------------------------------------------- */
+size_t spec_tree_verify_workspace_size(int32_t B, int32_t max_T, int32_t V);
+int32_t spec_tree_verify(const float* target, const float* draft_probs, const int32_t* q_row,
+                         const int32_t* tokens, const int32_t* parents, const int32_t* T_b, const int8_t* mode,
+                         uint64_t philox_key0, uint64_t philox_key1, uint64_t philox_offset, int32_t B,
+                         int32_t max_T, int32_t R, int32_t V, int32_t* accept_len, int32_t* accept_nodes,
+                         int32_t* out_tokens, uint32_t* status, void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Accepted-path KV compaction - tanhdev section 2 sequence diagram ("Retain
+ * Accepted Path KV & Discard Rejected Branches"); lesty.tech section 6
+ * ("Paged Tree KV-Cache Allocation").
+ * For every layer l (pools at k_pages + l * layer_stride_elems, same for v)
+ * and KV head, the k-th accepted node n_k (accept_nodes[b, k], k = 1..
+ * accept_len[b]) moves from slot L_b + n_k to slot L_b + k; the root stays
+ * at L_b. All sources are read before any destination is written.
+ * new_prefix_lens int32 [B] = L_b + 1 + accept_len[b]. k_pages / v_pages are
+ * modified in place; other inputs are read only. Invalid accept_len or
+ * accept_nodes (not increasing, >= max_T) leave that sequence's cache untouched.
+ * ------------------------------------------------------------------------- */
+int32_t spec_kv_compact(void* k_pages, void* v_pages, const int32_t* page_table, const int32_t* prefix_lens,
+                        const int32_t* accept_nodes, const int32_t* accept_len, int32_t B, int32_t max_T,
+                        int32_t Hkv, int32_t d, int32_t page, int32_t max_pages, int32_t num_pages,
+                        int32_t num_layers, int64_t layer_stride_elems, int32_t* new_prefix_lens, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_TREE_H */

@@ -1,0 +1,102 @@
+"""The C-ABI library loads, exports every function include/spec_tree.h declares,
+and rejects bad arguments on the host (before any launch, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_tree.h")
+
+SPEC_E_INVAL, SPEC_E_UNSUPPORTED, SPEC_E_WORKSPACE = -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tree_attention_verification_03_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from tree_attention_verification_03_amd.build import build
+
+        build(verbose=False)
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_pipeline():
+    names = declared_functions()
+    for n in ["spec_tree_build_step", "spec_tree_build_finish", "spec_tree_mask", "spec_tree_attention",
+              "spec_tree_verify", "spec_kv_compact", "spec_abi_version", "spec_last_error"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from tree_attention_verification_03_amd._lib import SIGNATURES
+
+    names = declared_functions()
+    for n in names:
+        assert hasattr(lib, n), f"{n} missing from libspectree.so"
+    assert set(names) == set(SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_version_and_error_string(lib):
+    assert lib.spec_abi_version() == 1
+    assert isinstance(lib.spec_last_error(), bytes)
+
+
+def test_workspace_sizes(lib):
+    assert lib.spec_tree_build_workspace_size(32, 8, 6) > 0
+    assert lib.spec_tree_attention_workspace_size(32, 33, 64, 8, 128, 16, 1029) > 0
+    assert lib.spec_tree_verify_workspace_size(32, 33, 128256) > 0
+    # unsupported shapes report 0
+    assert lib.spec_tree_attention_workspace_size(1, 9, 8, 2, 96, 16, 20) == 0
+    assert lib.spec_tree_build_workspace_size(1, 9, 3) == 0
+
+
+def _attn(lib, d=128, max_T=9, Hq=8, Hkv=2, page=16, ws_bytes=1 << 30, ptr=1 << 20, scale=0.1):
+    p = ctypes.c_void_p(ptr)
+    return lib.spec_tree_attention(p, p, p, p, p, p, None, 1, max_T, Hq, Hkv, d, page, 64, 64, scale, p, None, None, p,
+                                   ws_bytes, None)
+
+
+def test_attention_host_validation(lib):
+    assert _attn(lib, d=96) == SPEC_E_UNSUPPORTED
+    assert b"head dim" in lib.spec_last_error()
+    assert _attn(lib, max_T=66) == SPEC_E_UNSUPPORTED
+    assert _attn(lib, Hq=6, Hkv=4) == SPEC_E_INVAL
+    assert _attn(lib, page=12) == SPEC_E_UNSUPPORTED
+    assert _attn(lib, ws_bytes=16) == SPEC_E_WORKSPACE
+    assert _attn(lib, ptr=(1 << 20) + 2) == SPEC_E_INVAL  # misaligned
+    assert _attn(lib, scale=float("nan")) == SPEC_E_INVAL
+    assert lib.spec_tree_attention(None, None, None, None, None, None, None, 1, 9, 8, 2, 128, 16, 64, 64, 0.1, None,
+                                   None, None, None, 0, None) == SPEC_E_INVAL
+
+
+def test_verify_build_compact_mask_host_validation(lib):
+    p = ctypes.c_void_p(1 << 20)
+    v = lambda **kw: lib.spec_tree_verify(p, None, None, p, p, None, p, 1, 2, 0, kw.get("B", 1), kw.get("T", 9), 0,
+                                          kw.get("V", 1000), p, p, p, p, p, kw.get("ws", 1 << 20), None)
+    assert v(T=66) == SPEC_E_UNSUPPORTED
+    assert v(V=1 << 24) == SPEC_E_UNSUPPORTED
+    assert v(ws=8) == SPEC_E_WORKSPACE
+    assert lib.spec_tree_build_step(p, 1 << 20, 0, p, 1000, p, p, 1, 4, 3, 1000, p, None) == SPEC_E_INVAL
+    assert lib.spec_tree_build_step(p, 1 << 20, 1, p, 1000, p, p, 1, 9, 3, 1000, p, None) == SPEC_E_UNSUPPORTED
+    assert lib.spec_tree_build_step(p, 8, 1, p, 1000, p, p, 1, 4, 3, 1000, p, None) == SPEC_E_WORKSPACE
+    assert lib.spec_tree_build_finish(p, 1 << 20, p, p, p, p, 1, 4, 3, 70, p, p, p, p, p, None) == SPEC_E_UNSUPPORTED
+    assert lib.spec_kv_compact(p, p, p, p, p, p, 1, 9, 2, 80, 16, 4, 4, 1, 0, p, None) == SPEC_E_UNSUPPORTED
+    assert lib.spec_tree_mask(None, None, 1, 9, None, None, None, None) == SPEC_E_INVAL
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from tree_attention_verification_03_amd import _lib
+
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,108 @@
+"""GPU parity on the five workloads at full size, against the CPU oracle.
+
+Tree build, masks, accepted paths, tokens and status bit-exact; attention
+within max-abs 1e-2 and relative L2 5e-3 over every (sequence, head) pair, or
+for the largest workload over sampled pairs the oracle recomputes one by one
+(shortest and longest sequences and others, two heads of every KV group).
+Also the 64-node-tree workload with planted acceptance followed by KV
+compaction.
+"""
+import numpy as np
+import pytest
+
+from gpu_support import (ATTN_MAX_ABS, ATTN_REL_L2, LSE_ABS, check_build, check_verify, compare_attention, log,
+                         oracle_trees, parents_array, run_pipeline)
+from oracle.kvcompact import kv_compact as oracle_kv_compact
+from workloads import get_config
+from workloads.synth import from_spec
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+# ---------------------------------------------------------------- full-size workloads
+@pytest.fixture(scope="module", params=range(5), ids=lambda i: get_config(i).name)
+def full(request):
+    cfg = get_config(request.param)
+    log(f"[full] generating {cfg.name}")
+    w = from_spec(cfg)
+    log(f"[full] running HIP pipeline on {cfg.name}")
+    dw, step, host = run_pipeline(w, compact=False)
+    trees = oracle_trees(w)
+    yield dict(cfg=cfg, w=w, dw=dw, step=step, host=host, trees=trees)
+    del dw, step
+    torch.cuda.empty_cache()
+
+
+def test_full_tree_build(full):
+    check_build(full["w"], full["host"], full["trees"])
+
+
+def test_full_attention(full):
+    w, host = full["w"], full["host"]
+    parents = parents_array(w, full["trees"])
+    pairs = None
+    if w.B * w.Hq > 512:  # largest workload: sample sequences (shortest, longest, others) x heads of every KV group
+        order = np.argsort(w.prefix_lens)
+        seqs = sorted(set([int(order[0]), int(order[-1])] + [int(x) for x in order[:: max(1, w.B // 6)]]))
+        G = w.Hq // w.Hkv
+        heads = sorted(set([g * G for g in range(w.Hkv)] + [g * G + G - 1 for g in range(w.Hkv)]))
+        pairs = [(b, h) for b in seqs for h in heads]
+    log(f"[full] oracle attention on {w.name} ({'all' if pairs is None else len(pairs)} pairs)")
+    max_abs, rel, lse_err = compare_attention(w, host["attn_out"], host["lse"], parents, pairs)
+    log(f"[full] {w.name}: max_abs={max_abs:.3e} rel_l2={rel:.3e} lse_err={lse_err:.3e}")
+    assert max_abs <= ATTN_MAX_ABS and rel <= ATTN_REL_L2 and lse_err <= LSE_ABS
+    assert (host["attn_status"] == 0).all()
+
+
+def test_full_verify(full):
+    log(f"[full] oracle verify on {full['w'].name}")
+    check_verify(full["w"], full["host"], full["trees"])
+
+
+def test_full_attention_deterministic(full):
+    step = full["step"]
+    if full["w"].B * full["w"].Hq > 512:
+        pytest.skip("covered on the smaller workloads")
+    a = step.o.attn_out.clone()
+    for _ in range(3):
+        step.attention()
+        torch.cuda.synchronize()
+        assert torch.equal(step.o.attn_out.view(torch.int16), a.view(torch.int16))
+
+
+
+
+def _plant_greedy_path(rng, trees, target):
+    """Make a random root->leaf path the greedy choice (inputs only)."""
+    for b, t in enumerate(trees):
+        u = 0
+        while True:
+            kids = [i for i in range(1, len(t.tokens)) if t.parents[i] == u]
+            if not kids or rng.random() < 0.1:
+                break
+            c = kids[int(rng.integers(len(kids)))]
+            target[b, u, t.tokens[c]] = target[b, u].max() + 1.0
+            u = c
+
+
+def test_full_pipeline_with_planted_acceptance_and_compaction():
+    """Llama-3-70B-shaped workload (64-node tree): plant acceptance, verify, compact, check all of it."""
+    cfg = get_config(3)
+    w = from_spec(cfg)
+    trees = oracle_trees(w)
+    target = w.target.copy()
+    _plant_greedy_path(np.random.default_rng(1), trees, target)
+    w.target = target
+    log("[pipeline] planted greedy + compaction on the 64-node tree workload")
+    k_before, v_before = w.k_pages.copy(), w.v_pages.copy()
+    dw, step, host = run_pipeline(w, compact=True)
+    check_build(w, host, trees)
+    check_verify(w, host, trees)
+    assert host["accept_len"][0] > 0
+    k_ref, v_ref, l_ref = oracle_kv_compact(k_before[None], v_before[None], w.page_table, w.prefix_lens,
+                                            host["accept_nodes"], host["accept_len"], w.page)
+    assert np.array_equal(dw.k_pages.view(torch.int16).cpu().numpy().view(np.uint16), k_ref[0])
+    assert np.array_equal(dw.v_pages.view(torch.int16).cpu().numpy().view(np.uint16), v_ref[0])
+    assert host["new_prefix_lens"].tolist() == l_ref.tolist()

@@ -1,0 +1,140 @@
+// Device helpers shared by the libspectree kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spectree {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// round-to-nearest-even fp32 -> bf16 (NaN -> quiet NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// ---------------------------------------------------------------- ordering keys
+// Monotone map fp32 -> uint32 (larger float -> larger key) for finite values
+// and +-inf; callers canonicalise NaN and -0 first.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Same for fp64.
+__device__ __forceinline__ uint64_t f64_order_key(double f) {
+  uint64_t u = uint64_t(__double_as_longlong(f));
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------- Philox4x64-10
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
+// (SC'11): Philox-4x64 round function, 10 rounds, Weyl key schedule.
+struct U64x4 {
+  uint64_t w[4];
+};
+
+__device__ __forceinline__ U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                               uint64_t k1) {
+  constexpr uint64_t kMul0 = 0xD2E7470EE14C6C93ull;
+  constexpr uint64_t kMul1 = 0xCA5A826395121157ull;
+  constexpr uint64_t kWeyl0 = 0x9E3779B97F4A7C15ull;
+  constexpr uint64_t kWeyl1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kWeyl0;
+      k1 += kWeyl1;
+    }
+    const uint64_t lo0 = kMul0 * c0, hi0 = __umul64hi(kMul0, c0);
+    const uint64_t lo1 = kMul1 * c2, hi1 = __umul64hi(kMul1, c2);
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  U64x4 o;
+  o.w[0] = c0;
+  o.w[1] = c1;
+  o.w[2] = c2;
+  o.w[3] = c3;
+  return o;
+}
+
+// ---------------------------------------------------------------- wide unsigned integers
+typedef unsigned __int128 u128;
+
+struct U192 {
+  uint64_t lo, mid, hi;
+};
+
+__device__ __forceinline__ U192 mul_u128_u64(u128 a, uint64_t b) {
+  const uint64_t a0 = uint64_t(a), a1 = uint64_t(a >> 64);
+  const u128 p0 = u128(a0) * b;
+  const u128 p1 = u128(a1) * b + (p0 >> 64);
+  U192 r;
+  r.lo = uint64_t(p0);
+  r.mid = uint64_t(p1);
+  r.hi = uint64_t(p1 >> 64);
+  return r;
+}
+
+__device__ __forceinline__ U192 shl_u192(U192 a, int s) {  // 0 < s < 64
+  U192 r;
+  r.hi = (a.hi << s) | (a.mid >> (64 - s));
+  r.mid = (a.mid << s) | (a.lo >> (64 - s));
+  r.lo = a.lo << s;
+  return r;
+}
+
+__device__ __forceinline__ bool le_u192(U192 a, U192 b) {
+  if (a.hi != b.hi) return a.hi < b.hi;
+  if (a.mid != b.mid) return a.mid < b.mid;
+  return a.lo <= b.lo;
+}
+
+// floor(a / b) for b != 0 with a quotient known to fit in 64 bits (restoring division).
+__device__ __forceinline__ uint64_t div_u128_u64(u128 a, uint64_t b) {
+  if ((a >> 64) == 0) return uint64_t(a) / b;
+  u128 rem = 0;
+  uint64_t q = 0;
+  for (int i = 127; i >= 0; --i) {
+    rem = (rem << 1) | ((a >> i) & 1);
+    if (rem >= b) {
+      rem -= b;
+      if (i < 64) q |= (1ull << i);
+    }
+  }
+  return q;
+}
+
+}  // namespace spectree

@@ -1,0 +1,363 @@
+// EAGLE-2 draft-tree construction: top-k expansion per step, rerank to N nodes.
+//
+// SGLang "Speculative Decoding" page, sections "EAGLE Decoding" (num_steps,
+// eagle_topk, num_draft_tokens) and "References" (tree-style extension with
+// topk branches per step; unlikely branches stop; rerank keeps the top
+// num_draft_tokens); lesty.tech "EAGLE-2 & Lookahead Decoding", section 4
+// "Dynamic Tree Construction Mechanics" (confidence = product of conditional
+// probabilities, kept as an fp64 sum of log-probs).
+//
+// Kernels:
+//   build_root_kernel    step 1: one block per sequence, top-k of the root row.
+//   build_expand_kernel  step d >= 2: one block per (frontier slot, sequence),
+//                        top-k of that slot's row -> k candidates; the last block
+//                        of a sequence to finish (atomic ticket) ranks the k*k
+//                        candidates and writes the next frontier.
+//   build_finish_kernel  one block per sequence: rank the whole pool, keep the
+//                        N best, number them in pool order, emit parents /
+//                        depth / ancestry words / q_row.
+// Ranking keys are exact: vocabulary top-k uses the 64-bit key
+// (order(logprob) << 32) | (2^32 - 1 - token); pool ranking compares fp64
+// scores, ties broken by the smaller pool index.
+#include "api_common.h"
+#include "spec_common.h"
+
+namespace spectree {
+namespace {
+
+constexpr int kMaxTopk = 8;
+constexpr int kMaxDepth = 16;
+constexpr int kRowThreads = 512;
+constexpr int kFinishThreads = 256;
+
+struct BuildWs {
+  int32_t* tok;    // [B, P]
+  int32_t* par;    // [B, P] parent pool index, -1 = root
+  int32_t* depth;  // [B, P]
+  int32_t* fslot;  // [B, P] frontier slot held at its own step, -1 if never frontier
+  double* score;   // [B, P]
+  int32_t* frontier;  // [B, max_topk] pool indices, rank order
+  uint32_t* ticket;   // [B]
+};
+
+size_t pool_cap(int max_topk, int max_depth) {
+  return size_t(max_topk) + size_t(max_depth - 1) * max_topk * max_topk;
+}
+
+BuildWs carve(void* ws, int B, int max_topk, int max_depth, size_t* total) {
+  const size_t P = pool_cap(max_topk, max_depth);
+  char* c = static_cast<char*>(ws);
+  size_t off = 0;
+  BuildWs w;
+  auto take = [&](size_t bytes) {
+    char* r = c ? c + off : nullptr;
+    off = align_up(off + bytes, 256);
+    return r;
+  };
+  w.score = reinterpret_cast<double*>(take(sizeof(double) * B * P));
+  w.tok = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * P));
+  w.par = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * P));
+  w.depth = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * P));
+  w.fslot = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * P));
+  w.frontier = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * max_topk));
+  w.ticket = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B));
+  *total = off;
+  return w;
+}
+
+__device__ __forceinline__ int clamp_i(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// canonical log-prob -> 64-bit ranking key (value desc, token asc)
+__device__ __forceinline__ uint64_t lp_key(float x, int token) {
+  if (x != x) x = -INFINITY;  // NaN ranks as -inf
+  if (x >= 0.f) x = 0.f;      // log-probs are <= 0; also maps -0 to +0
+  return (uint64_t(f32_order_key(x)) << 32) | uint64_t(0xffffffffu - uint32_t(token));
+}
+
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t o = uint32_t(key >> 32);
+  const uint32_t bits = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(bits);
+}
+
+__device__ __forceinline__ int key_token(uint64_t key) { return int(0xffffffffu - uint32_t(key)); }
+
+// Block-wide top-k (k <= 8) of one fp32 row; results (rank order) in out_key[0..k).
+__device__ void block_row_topk(const float* row, int V, int k, uint64_t* out_key) {
+  __shared__ uint64_t red[kRowThreads / kWave];
+  __shared__ uint64_t win;
+  uint64_t best[kMaxTopk];
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j) best[j] = 0;
+  for (int v = threadIdx.x; v < V; v += blockDim.x) {
+    uint64_t key = lp_key(row[v], v);
+    if (key > best[kMaxTopk - 1]) {
+#pragma unroll
+      for (int j = 0; j < kMaxTopk; ++j) {
+        if (key > best[j]) {
+          const uint64_t t = best[j];
+          best[j] = key;
+          key = t;
+        }
+      }
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t m = wave_max_u64(best[0]);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint64_t x = red[0];
+      for (int w = 1; w < nw; ++w) x = red[w] > x ? red[w] : x;
+      win = x;
+      out_key[r] = x;
+    }
+    __syncthreads();
+    if (best[0] == win && win != 0) {  // keys are unique (distinct tokens): exactly one owner pops
+#pragma unroll
+      for (int j = 0; j < kMaxTopk - 1; ++j) best[j] = best[j + 1];
+      best[kMaxTopk - 1] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(kRowThreads) build_root_kernel(BuildWs w, int P, const float* draft, int64_t seq_stride,
+                                                                  const int32_t* topk, int max_topk, int V,
+                                                                  int32_t* frontier_tokens) {
+  __shared__ uint64_t keys[kMaxTopk];
+  const int b = blockIdx.x;
+  const int k = clamp_i(topk[b], 1, max_topk);
+  block_row_topk(draft + b * seq_stride, V, k, keys);
+  if (threadIdx.x < max_topk) {
+    const int f = threadIdx.x;
+    int tok = -1;
+    if (f < k) {
+      const size_t e = size_t(b) * P + f;
+      tok = key_token(keys[f]);
+      w.tok[e] = tok;
+      w.par[e] = -1;
+      w.depth[e] = 1;
+      w.fslot[e] = f;
+      w.score[e] = 0.0 + double(key_value(keys[f]));
+      w.frontier[b * max_topk + f] = f;
+    }
+    frontier_tokens[b * max_topk + f] = tok;
+  }
+}
+
+__global__ void __launch_bounds__(kRowThreads) build_expand_kernel(BuildWs w, int P, int step, const float* draft,
+                                                                    int64_t seq_stride, const int32_t* topk,
+                                                                    const int32_t* depth, int max_topk, int max_depth,
+                                                                    int V, int32_t* frontier_tokens) {
+  __shared__ uint64_t keys[kMaxTopk];
+  __shared__ int last;
+  const int f = blockIdx.x, b = blockIdx.y;
+  const int k = clamp_i(topk[b], 1, max_topk);
+  const int D = clamp_i(depth[b], 1, max_depth);
+  if (step > D || f >= k) return;
+  const int parent = w.frontier[b * max_topk + f];
+  const double pscore = w.score[size_t(b) * P + parent];
+  block_row_topk(draft + b * seq_stride + int64_t(f) * V, V, k, keys);
+  const int base = k + (step - 2) * k * k;
+  if (threadIdx.x < k) {
+    const int c = threadIdx.x;
+    const size_t e = size_t(b) * P + base + f * k + c;
+    w.tok[e] = key_token(keys[c]);
+    w.par[e] = parent;
+    w.depth[e] = step;
+    w.fslot[e] = -1;
+    w.score[e] = pscore + double(key_value(keys[c]));
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = (atomicAdd(w.ticket + b, 1u) == uint32_t(k - 1));
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  if (threadIdx.x == 0) atomicExch(w.ticket + b, 0u);
+  // rank the k*k candidates of this step: rank(c) = #candidates that beat c
+  const int n = k * k;
+  if (threadIdx.x < n) {
+    const int c = threadIdx.x;
+    const double sc = w.score[size_t(b) * P + base + c];
+    int rank = 0;
+    for (int o = 0; o < n; ++o) {
+      const double so = w.score[size_t(b) * P + base + o];
+      rank += (so > sc) || (so == sc && o < c);
+    }
+    if (rank < k) {
+      w.frontier[b * max_topk + rank] = base + c;
+      w.fslot[size_t(b) * P + base + c] = rank;
+      frontier_tokens[b * max_topk + rank] = w.tok[size_t(b) * P + base + c];
+    }
+  }
+  if (threadIdx.x >= k && threadIdx.x < max_topk) frontier_tokens[b * max_topk + threadIdx.x] = -1;
+}
+
+__global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w, int P, const int32_t* root_tokens,
+                                                                       const int32_t* topk, const int32_t* depth,
+                                                                       const int32_t* num_draft, int max_topk,
+                                                                       int max_depth, int max_T, int32_t* tokens,
+                                                                       int32_t* parents, int32_t* depth_out,
+                                                                       uint64_t* anc_mask, int32_t* q_row) {
+  __shared__ double sc[kMaxTopk + (kMaxDepth - 1) * kMaxTopk * kMaxTopk];
+  __shared__ int rank_s[kMaxTopk + (kMaxDepth - 1) * kMaxTopk * kMaxTopk];
+  __shared__ int pool_of[65];
+  __shared__ int node_par[65];
+  __shared__ uint64_t anc_s[65];
+  __shared__ int jump_s[65];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int k = clamp_i(topk[b], 1, max_topk);
+  const int D = clamp_i(depth[b], 1, max_depth);
+  const int pool = k + (D - 1) * k * k;
+  const int N = clamp_i(num_draft[b], 1, min(pool, max_T - 1));
+  const int T = N + 1;
+  const size_t row = size_t(b) * P;
+
+  for (int e = tid; e < pool; e += blockDim.x) sc[e] = w.score[row + e];
+  __syncthreads();
+  for (int e = tid; e < pool; e += blockDim.x) {
+    const double s = sc[e];
+    int r = 0;
+    for (int o = 0; o < pool; ++o) r += (sc[o] > s) || (sc[o] == s && o < e);
+    rank_s[e] = r;
+  }
+  __syncthreads();
+  // kept entries, numbered 1..N in pool order (wave 0 scans the pool 64 at a time)
+  if (tid < kWave) {
+    int base = 0;
+    for (int c0 = 0; c0 < pool; c0 += kWave) {
+      const int e = c0 + tid;
+      const bool kept = e < pool && rank_s[e] < N;
+      const uint64_t m = __ballot(kept);
+      if (kept) pool_of[1 + base + __popcll(m & ((1ull << tid) - 1))] = e;
+      base += __popcll(m);
+    }
+  }
+  __syncthreads();
+  // parents as node numbers: the parent entry of a kept entry is kept (scores never increase
+  // down a path and the parent has the smaller pool index), so it is among pool_of[1..n-1]
+  if (tid < T) {
+    const int n = tid;
+    int par_node = -1;
+    if (n > 0) {
+      const int pe = w.par[row + pool_of[n]];
+      par_node = 0;
+      if (pe >= 0)
+        for (int m2 = 1; m2 < n; ++m2)
+          if (pool_of[m2] == pe) par_node = m2;
+    }
+    node_par[n] = par_node;
+    jump_s[n] = n > 0 ? par_node : 0;
+    anc_s[n] = n > 0 ? (1ull << (n - 1)) : 0ull;
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int it = 0; it < 7; ++it) {
+    uint64_t na = 0;
+    int nj = 0;
+    if (tid < T) {
+      const int j = jump_s[tid];
+      na = anc_s[tid] | anc_s[j];
+      nj = jump_s[j];
+    }
+    __syncthreads();
+    if (tid < T) {
+      anc_s[tid] = na;
+      jump_s[tid] = nj;
+    }
+    __syncthreads();
+  }
+  for (int n = tid; n < max_T; n += blockDim.x) {
+    const size_t o = size_t(b) * max_T + n;
+    if (n == 0) {
+      tokens[o] = root_tokens[b];
+      parents[o] = -1;
+      depth_out[o] = 0;
+      anc_mask[o] = 0;
+      q_row[o] = 0;
+    } else if (n < T) {
+      const size_t e = row + pool_of[n];
+      const int d = w.depth[e];
+      const int fs = w.fslot[e];
+      tokens[o] = w.tok[e];
+      parents[o] = node_par[n];
+      depth_out[o] = d;
+      anc_mask[o] = anc_s[n];
+      q_row[o] = (fs >= 0 && d < D) ? 1 + (d - 1) * max_topk + fs : -1;
+    } else {
+      tokens[o] = -1;
+      parents[o] = -1;
+      depth_out[o] = 0;
+      anc_mask[o] = 0;
+      q_row[o] = -1;
+    }
+  }
+}
+
+int32_t check_build(const char* who, int32_t B, int32_t max_topk, int32_t max_depth) {
+  if (B < 1) return fail(SPEC_E_INVAL, "%s: B=%d", who, B);
+  if (max_topk < 1 || max_topk > kMaxTopk) return fail(SPEC_E_UNSUPPORTED, "%s: max_topk=%d not in [1, %d]", who, max_topk, kMaxTopk);
+  if (max_depth < 1 || max_depth > kMaxDepth)
+    return fail(SPEC_E_UNSUPPORTED, "%s: max_depth=%d not in [1, %d]", who, max_depth, kMaxDepth);
+  return SPEC_OK;
+}
+
+}  // namespace
+}  // namespace spectree
+
+using namespace spectree;
+
+extern "C" size_t spec_tree_build_workspace_size(int32_t B, int32_t max_topk, int32_t max_depth) {
+  if (check_build("spec_tree_build_workspace_size", B, max_topk, max_depth) != SPEC_OK) return 0;
+  size_t total = 0;
+  carve(nullptr, B, max_topk, max_depth, &total);
+  return total;
+}
+
+extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
+                                        int64_t seq_stride, const int32_t* topk, const int32_t* depth, int32_t B,
+                                        int32_t max_topk, int32_t max_depth, int32_t V, int32_t* frontier_tokens,
+                                        void* stream) {
+  int32_t rc = check_build("spec_tree_build_step", B, max_topk, max_depth);
+  if (rc != SPEC_OK) return rc;
+  if (step < 1 || step > max_depth) return fail(SPEC_E_INVAL, "spec_tree_build_step: step=%d not in [1, %d]", step, max_depth);
+  if (V < max_topk || V >= (1 << 30)) return fail(SPEC_E_INVAL, "spec_tree_build_step: V=%d must be in [max_topk, 2^30)", V);
+  if (!draft_logprobs || !topk || !depth || !frontier_tokens) return fail(SPEC_E_INVAL, "spec_tree_build_step: null pointer");
+  const int64_t min_stride = (step == 1 ? 1 : max_topk) * int64_t(V);
+  if (B > 1 && seq_stride < min_stride)
+    return fail(SPEC_E_INVAL, "spec_tree_build_step: seq_stride=%lld < %lld", (long long)seq_stride, (long long)min_stride);
+  size_t need = 0;
+  BuildWs w = carve(ws, B, max_topk, max_depth, &need);
+  if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_step: workspace %zu < %zu bytes", ws_bytes, need);
+  const int P = int(pool_cap(max_topk, max_depth));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (step == 1)
+    hipLaunchKernelGGL(build_root_kernel, dim3(B), dim3(kRowThreads), 0, st, w, P, draft_logprobs, seq_stride, topk,
+                       max_topk, V, frontier_tokens);
+  else
+    hipLaunchKernelGGL(build_expand_kernel, dim3(max_topk, B), dim3(kRowThreads), 0, st, w, P, step, draft_logprobs,
+                       seq_stride, topk, depth, max_topk, max_depth, V, frontier_tokens);
+  return check_launch("spec_tree_build_step");
+}
+
+extern "C" int32_t spec_tree_build_finish(void* ws, size_t ws_bytes, const int32_t* root_tokens, const int32_t* topk,
+                                          const int32_t* depth, const int32_t* num_draft, int32_t B, int32_t max_topk,
+                                          int32_t max_depth, int32_t max_T, int32_t* tokens, int32_t* parents,
+                                          int32_t* depth_out, uint64_t* anc_mask, int32_t* q_row, void* stream) {
+  int32_t rc = check_build("spec_tree_build_finish", B, max_topk, max_depth);
+  if (rc != SPEC_OK) return rc;
+  if (max_T < 2 || max_T > 65) return fail(SPEC_E_UNSUPPORTED, "spec_tree_build_finish: max_T=%d not in [2, 65]", max_T);
+  if (!root_tokens || !topk || !depth || !num_draft || !tokens || !parents || !depth_out || !anc_mask || !q_row)
+    return fail(SPEC_E_INVAL, "spec_tree_build_finish: null pointer");
+  size_t need = 0;
+  BuildWs w = carve(ws, B, max_topk, max_depth, &need);
+  if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_finish: workspace %zu < %zu bytes", ws_bytes, need);
+  const int P = int(pool_cap(max_topk, max_depth));
+  hipLaunchKernelGGL(build_finish_kernel, dim3(B), dim3(kFinishThreads), 0, static_cast<hipStream_t>(stream), w, P,
+                     root_tokens, topk, depth, num_draft, max_topk, max_depth, max_T, tokens, parents, depth_out,
+                     anc_mask, q_row);
+  return check_launch("spec_tree_build_finish");
+}

@@ -40,9 +40,22 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
     Inputs here are finite normal draws, so no NaN handling is needed.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = u >> np.uint32(16)
+    lsb &= np.uint32(1)
+    u += np.uint32(0x7FFF)  # finite inputs: no uint32 overflow
+    u += lsb
+    u >>= np.uint32(16)
+    return u.astype(np.uint16)
+
+
+def _bf16_normals(rng: np.random.Generator, shape, chunk: int = 1 << 22) -> np.ndarray:
+    """N(0, 1) fp32 draws rounded to bf16 bits, drawn in order chunk by chunk."""
+    out = np.empty(int(np.prod(shape)), dtype=np.uint16)
+    for lo in range(0, out.size, chunk):
+        hi = min(out.size, lo + chunk)
+        out[lo:hi] = f32_to_bf16_bits(rng.standard_normal(hi - lo, dtype=np.float32))
+    return out.reshape(shape)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -190,11 +203,11 @@ def make_workload(
         cursor += n
     r_kv = np.random.Generator(np.random.PCG64(s_kv))
     kv_shape = (num_pages, page, Hkv, d)
-    k_pages = f32_to_bf16_bits(r_kv.standard_normal(kv_shape, dtype=np.float32))
-    v_pages = f32_to_bf16_bits(r_kv.standard_normal(kv_shape, dtype=np.float32))
+    k_pages = _bf16_normals(r_kv, kv_shape)
+    v_pages = _bf16_normals(r_kv, kv_shape)
 
     r_q = np.random.Generator(np.random.PCG64(s_q))
-    q = f32_to_bf16_bits(r_q.standard_normal((B, max_T, Hq, d), dtype=np.float32))
+    q = _bf16_normals(r_q, (B, max_T, Hq, d))
 
     # ---- draft rows ----------------------------------------------------
     R = 1 + (max_depth - 1) * max_topk
