@@ -138,3 +138,32 @@ __device__ __forceinline__ uint64_t div_u128_u64(u128 a, uint64_t b) {
 }
 
 }  // namespace spectree
+
+namespace spectree {
+
+// ---------------------------------------------------------------- cross-block hand-off
+// Data one block publishes for another block of the same launch (split-K
+// partials, per-slice candidates) is written and read with relaxed atomics at
+// agent scope: on CDNA3/CDNA4 these carry the device-scope cache policy, so
+// stores write through the XCD's L2 and loads do not hit a stale L2 line of
+// another XCD. The writer waits for its stores to complete (vmcnt) before it
+// takes a ticket; the block that draws the last ticket reads after it.
+// This avoids agent-scope fences, whose L2 writeback serialises the blocks.
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until this thread's global stores are complete, and keep the compiler from moving memory ops across
+__device__ __forceinline__ void wait_global_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t ticket_add(uint32_t* t) {
+  return __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ticket_reset(uint32_t* t) {
+  __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace spectree

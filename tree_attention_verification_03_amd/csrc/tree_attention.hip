@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(kThreads) tree_attn_kernel(AttnParams p) {
   constexpr int ITEM = ROWS * D + 2 * ROWS;  // floats per partial: O[ROWS][D], m[ROWS], l[ROWS]
   constexpr int V_BYTES = 4 * kSubKeys * VROW * 2;
   constexpr int O_BYTES = ROWS * OROW * 4;
-  constexpr int W_BYTES = kMaxItems * ROWS * 4;
+  constexpr int W_BYTES = kMaxItems * ROWS * 4 * 3;  // merge weights + staged (m, l)
   constexpr int SMEM = V_BYTES > O_BYTES ? (V_BYTES > W_BYTES ? V_BYTES : W_BYTES)
                                          : (O_BYTES > W_BYTES ? O_BYTES : W_BYTES);
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
@@ -372,39 +372,44 @@ __global__ void __launch_bounds__(kThreads) tree_attn_kernel(AttnParams p) {
     return;
   }
 
-  // ---- publish this item's partial, then the last arrival merges all items
+  // ---- publish this item's partial (write-through stores), then the last arrival merges all items
   float* const grp = p.part + (size_t(bg) * p.n_rb + rb) * size_t(p.n_splits) * ITEM;
   float* const mine = grp + size_t(s) * ITEM;
-  for (int idx = tid; idx < nrows * D; idx += kThreads) {
-    const int row = idx / D, d = idx - row * D;
-    mine[row * D + d] = obuf[row * OROW + d];
+  constexpr int D2 = D / 2;
+  for (int idx = tid; idx < nrows * D2; idx += kThreads) {
+    const int row = idx / D2, c2 = idx - row * D2;
+    const float2 v2 = *reinterpret_cast<const float2*>(obuf + row * OROW + 2 * c2);
+    st_agent(reinterpret_cast<uint64_t*>(mine + row * D) + c2, __builtin_bit_cast(uint64_t, v2));
   }
   if (tid < nrows) {
-    mine[ROWS * D + tid] = row_m[tid];
-    mine[ROWS * D + ROWS + tid] = row_l[tid];
+    st_agent(mine + ROWS * D + tid, row_m[tid]);
+    st_agent(mine + ROWS * D + ROWS + tid, row_l[tid]);
   }
-  __threadfence();
+  wait_global_stores();
   __syncthreads();
   uint32_t* ticket = p.tickets + size_t(bg) * p.n_rb + rb;
-  if (tid == 0) flag_s = (atomicAdd(ticket, 1u) == uint32_t(n_items - 1));
+  if (tid == 0) flag_s = (ticket_add(ticket) == uint32_t(n_items - 1));
   __syncthreads();
   if (!flag_s) return;
-  __threadfence();
-  if (tid == 0) atomicExch(ticket, 0u);  // leave the workspace ready for the next call
+  if (tid == 0) ticket_reset(ticket);  // leave the workspace ready for the next call
 
-  float* wts = reinterpret_cast<float*>(smem);  // [item][row] normalised merge weights
+  // merge: stage every item's (m, l) in LDS with all threads, then weights, then O in float4 columns
+  float* wts = reinterpret_cast<float*>(smem);                // [item][ROWS] normalised weights
+  float* ml = wts + kMaxItems * ROWS;                         // [item][2][ROWS] raw (m, l)
+  for (int idx = tid; idx < n_items * 2 * ROWS; idx += kThreads) {
+    const int it = idx / (2 * ROWS), r2 = idx - it * 2 * ROWS;
+    const int si = it < nsp ? it : p.n_splits - 1;
+    ml[idx] = (r2 % ROWS) < nrows ? ld_agent(grp + size_t(si) * ITEM + ROWS * D + r2) : 0.f;
+  }
+  __syncthreads();
   if (tid < nrows) {
     float mx = -INFINITY;
-    for (int it = 0; it < n_items; ++it) {
-      const int si = it < nsp ? it : p.n_splits - 1;
-      mx = fmaxf(mx, grp[size_t(si) * ITEM + ROWS * D + tid]);
-    }
+    for (int it = 0; it < n_items; ++it) mx = fmaxf(mx, ml[it * 2 * ROWS + tid]);
     float ls = 0.f;
     for (int it = 0; it < n_items; ++it) {
-      const int si = it < nsp ? it : p.n_splits - 1;
-      const float m = grp[size_t(si) * ITEM + ROWS * D + tid];
+      const float m = ml[it * 2 * ROWS + tid];
       const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - mx);
-      ls += grp[size_t(si) * ITEM + ROWS * D + ROWS + tid] * f;
+      ls += ml[it * 2 * ROWS + ROWS + tid] * f;
       wts[it * ROWS + tid] = f;
     }
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
@@ -415,15 +420,46 @@ __global__ void __launch_bounds__(kThreads) tree_attn_kernel(AttnParams p) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < nrows * D; idx += kThreads) {
-    const int row = idx / D, d = idx - row * D;
-    float o = 0.f;
-    for (int it = 0; it < n_items; ++it) {
+  constexpr int D4 = D / 4;
+  for (int idx = tid; idx < nrows * D4; idx += kThreads) {
+    const int row = idx / D4, c4 = idx - row * D4;
+    const float* src = grp + row * D + 4 * c4;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    int it = 0;
+    for (; it + 4 <= n_items; it += 4) {  // four independent loads in flight per step
+      float4 a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int si = (it + u) < nsp ? (it + u) : p.n_splits - 1;
+        const uint64_t* q2 = reinterpret_cast<const uint64_t*>(src + size_t(si) * ITEM);
+        const float2 lo2 = __builtin_bit_cast(float2, ld_agent(q2)), hi2 = __builtin_bit_cast(float2, ld_agent(q2 + 1));
+        a[u] = make_float4(lo2.x, lo2.y, hi2.x, hi2.y);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wv = wts[(it + u) * ROWS + row];
+        o.x += a[u].x * wv;
+        o.y += a[u].y * wv;
+        o.z += a[u].z * wv;
+        o.w += a[u].w * wv;
+      }
+    }
+    for (; it < n_items; ++it) {
       const int si = it < nsp ? it : p.n_splits - 1;
-      o += grp[size_t(si) * ITEM + row * D + d] * wts[it * ROWS + row];
+      const uint64_t* q2 = reinterpret_cast<const uint64_t*>(src + size_t(si) * ITEM);
+      const float2 lo2 = __builtin_bit_cast(float2, ld_agent(q2)), hi2 = __builtin_bit_cast(float2, ld_agent(q2 + 1));
+      const float4 a = make_float4(lo2.x, lo2.y, hi2.x, hi2.y);
+      const float wv = wts[it * ROWS + row];
+      o.x += a.x * wv;
+      o.y += a.y * wv;
+      o.z += a.z * wv;
+      o.w += a.w * wv;
     }
     const int r = row0 + row, i = r / p.G, h = g * p.G + (r - i * p.G);
-    p.out[((size_t(b) * p.max_T + i) * p.Hq + h) * D + d] = f32_to_bf16(o);
+    uint16_t* dst = p.out + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 4 * c4;
+    const uint32_t lo = uint32_t(f32_to_bf16(o.x)) | (uint32_t(f32_to_bf16(o.y)) << 16);
+    const uint32_t hi = uint32_t(f32_to_bf16(o.z)) | (uint32_t(f32_to_bf16(o.w)) << 16);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
   }
 }
 

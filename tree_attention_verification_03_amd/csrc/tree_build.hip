@@ -8,11 +8,13 @@
 // probabilities, kept as an fp64 sum of log-probs).
 //
 // Kernels:
-//   build_root_kernel    step 1: one block per sequence, top-k of the root row.
-//   build_expand_kernel  step d >= 2: one block per (frontier slot, sequence),
-//                        top-k of that slot's row -> k candidates; the last block
-//                        of a sequence to finish (atomic ticket) ranks the k*k
-//                        candidates and writes the next frontier.
+//   build_step_kernel    one launch per step; block (slice, frontier slot f,
+//                        sequence) takes the top-k of a slice of row f; the last
+//                        slice of a row (atomic ticket) merges the slices; step 1
+//                        seeds the pool and frontier from the root row; at step
+//                        d >= 2 the row's k children join the pool and the last
+//                        row of a sequence (second ticket) ranks the k*k children
+//                        and writes the next frontier.
 //   build_finish_kernel  one block per sequence: rank the whole pool, keep the
 //                        N best, number them in pool order, emit parents /
 //                        depth / ancestry words / q_row.
@@ -27,7 +29,8 @@ namespace {
 
 constexpr int kMaxTopk = 8;
 constexpr int kMaxDepth = 16;
-constexpr int kRowThreads = 512;
+constexpr int kRowThreads = 256;
+constexpr int kMaxSlices = 32;  // blocks per draft row
 constexpr int kFinishThreads = 256;
 
 struct BuildWs {
@@ -37,7 +40,9 @@ struct BuildWs {
   int32_t* fslot;  // [B, P] frontier slot held at its own step, -1 if never frontier
   double* score;   // [B, P]
   int32_t* frontier;  // [B, max_topk] pool indices, rank order
-  uint32_t* ticket;   // [B]
+  uint32_t* ticket;   // [B] frontier-selection tickets
+  uint64_t* cand;     // [B, max_topk, kMaxSlices, kMaxTopk] per-slice top-k keys
+  uint32_t* row_ticket;  // [B, max_topk]
 };
 
 size_t pool_cap(int max_topk, int max_depth) {
@@ -61,6 +66,8 @@ BuildWs carve(void* ws, int B, int max_topk, int max_depth, size_t* total) {
   w.fslot = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * P));
   w.frontier = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * max_topk));
   w.ticket = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B));
+  w.cand = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * B * max_topk * kMaxSlices * kMaxTopk));
+  w.row_ticket = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B * max_topk));
   *total = off;
   return w;
 }
@@ -82,15 +89,15 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 
 __device__ __forceinline__ int key_token(uint64_t key) { return int(0xffffffffu - uint32_t(key)); }
 
-// Block-wide top-k (k <= 8) of one fp32 row; results (rank order) in out_key[0..k).
-__device__ void block_row_topk(const float* row, int V, int k, uint64_t* out_key) {
+// Block-wide top-k (k <= 8) of row[lo, hi); results (rank order, 0 = none) in out_key[0..k).
+template <bool VEC>
+__device__ void block_slice_topk(const float* row, int lo, int hi, int k, uint64_t* out_key) {
   __shared__ uint64_t red[kRowThreads / kWave];
   __shared__ uint64_t win;
   uint64_t best[kMaxTopk];
 #pragma unroll
   for (int j = 0; j < kMaxTopk; ++j) best[j] = 0;
-  for (int v = threadIdx.x; v < V; v += blockDim.x) {
-    uint64_t key = lp_key(row[v], v);
+  auto insert = [&](uint64_t key) {
     if (key > best[kMaxTopk - 1]) {
 #pragma unroll
       for (int j = 0; j < kMaxTopk; ++j) {
@@ -101,15 +108,28 @@ __device__ void block_row_topk(const float* row, int V, int k, uint64_t* out_key
         }
       }
     }
+  };
+  if (VEC) {
+#pragma unroll 4
+    for (int v = lo + 4 * threadIdx.x; v < hi; v += 4 * kRowThreads) {
+      const float4 x = *reinterpret_cast<const float4*>(row + v);
+      insert(lp_key(x.x, v));
+      insert(lp_key(x.y, v + 1));
+      insert(lp_key(x.z, v + 2));
+      insert(lp_key(x.w, v + 3));
+    }
+  } else {
+#pragma unroll 4
+    for (int v = lo + threadIdx.x; v < hi; v += kRowThreads) insert(lp_key(row[v], v));
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int r = 0; r < k; ++r) {
     const uint64_t m = wave_max_u64(best[0]);
     if (lane == 0) red[wave] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
       uint64_t x = red[0];
-      for (int w = 1; w < nw; ++w) x = red[w] > x ? red[w] : x;
+      for (int w2 = 1; w2 < kRowThreads / kWave; ++w2) x = red[w2] > x ? red[w2] : x;
       win = x;
       out_key[r] = x;
     }
@@ -123,74 +143,100 @@ __device__ void block_row_topk(const float* row, int V, int k, uint64_t* out_key
   }
 }
 
-__global__ void __launch_bounds__(kRowThreads) build_root_kernel(BuildWs w, int P, const float* draft, int64_t seq_stride,
-                                                                  const int32_t* topk, int max_topk, int V,
-                                                                  int32_t* frontier_tokens) {
-  __shared__ uint64_t keys[kMaxTopk];
-  const int b = blockIdx.x;
-  const int k = clamp_i(topk[b], 1, max_topk);
-  block_row_topk(draft + b * seq_stride, V, k, keys);
-  if (threadIdx.x < max_topk) {
-    const int f = threadIdx.x;
-    int tok = -1;
-    if (f < k) {
-      const size_t e = size_t(b) * P + f;
-      tok = key_token(keys[f]);
-      w.tok[e] = tok;
-      w.par[e] = -1;
-      w.depth[e] = 1;
-      w.fslot[e] = f;
-      w.score[e] = 0.0 + double(key_value(keys[f]));
-      w.frontier[b * max_topk + f] = f;
-    }
-    frontier_tokens[b * max_topk + f] = tok;
-  }
-}
-
-__global__ void __launch_bounds__(kRowThreads) build_expand_kernel(BuildWs w, int P, int step, const float* draft,
-                                                                    int64_t seq_stride, const int32_t* topk,
-                                                                    const int32_t* depth, int max_topk, int max_depth,
-                                                                    int V, int32_t* frontier_tokens) {
-  __shared__ uint64_t keys[kMaxTopk];
+// One kernel for every step. Block (slice x, frontier slot f, sequence b) reduces a slice of
+// step-`step` draft row f to its top-k keys; the last slice of a row to finish merges the
+// slices (row ticket); at step 1 that row is the root's and fills the pool and the frontier,
+// at step >= 2 the row's k children join the pool and the last row of the sequence to finish
+// (sequence ticket) ranks the k*k children and writes the next frontier.
+template <bool VEC>
+__global__ void __launch_bounds__(kRowThreads) build_step_kernel(BuildWs w, int P, int step, const float* draft,
+                                                                  int64_t seq_stride, const int32_t* topk,
+                                                                  const int32_t* depth, int max_topk, int max_depth,
+                                                                  int V, int slice, int32_t* frontier_tokens) {
+  __shared__ uint64_t keys[kMaxSlices * kMaxTopk];
+  __shared__ uint64_t top[kMaxTopk];
   __shared__ int last;
-  const int f = blockIdx.x, b = blockIdx.y;
+  const int x = blockIdx.x, f = blockIdx.y, b = blockIdx.z;
+  const int n_slices = gridDim.x;
   const int k = clamp_i(topk[b], 1, max_topk);
   const int D = clamp_i(depth[b], 1, max_depth);
-  if (step > D || f >= k) return;
+  if (step > D || f >= (step == 1 ? 1 : k)) return;
+  const float* row = draft + b * seq_stride + int64_t(f) * V;
+  const int lo = x * slice, hi = min(V, lo + slice);
+  uint64_t* cand = w.cand + ((size_t(b) * max_topk + f) * kMaxSlices + x) * kMaxTopk;
+  block_slice_topk<VEC>(row, lo, hi, k, keys);
+  if (threadIdx.x < k) st_agent(cand + threadIdx.x, keys[threadIdx.x]);
+  wait_global_stores();
+  __syncthreads();
+  uint32_t* rt = w.row_ticket + size_t(b) * max_topk + f;
+  if (threadIdx.x == 0) last = (ticket_add(rt) == uint32_t(n_slices - 1));
+  __syncthreads();
+  if (!last) return;
+  if (threadIdx.x == 0) ticket_reset(rt);
+  // merge the slices' candidates: rank = number of larger keys (keys are unique; 0 = empty)
+  const uint64_t* rowc = w.cand + (size_t(b) * max_topk + f) * kMaxSlices * kMaxTopk;
+  const int nc = n_slices * kMaxTopk;
+  for (int i = threadIdx.x; i < nc; i += kRowThreads) keys[i] = ((i % kMaxTopk) < k) ? ld_agent(rowc + i) : 0ull;
+  __syncthreads();
+  for (int i = threadIdx.x; i < nc; i += kRowThreads) {
+    const uint64_t ki = keys[i];
+    if (ki == 0) continue;
+    int r = 0;
+    for (int j = 0; j < nc; ++j) r += keys[j] > ki;
+    if (r < k) top[r] = ki;
+  }
+  __syncthreads();
+
+  if (step == 1) {
+    if (threadIdx.x < max_topk) {
+      const int c = threadIdx.x;
+      int tok = -1;
+      if (c < k) {
+        const size_t e = size_t(b) * P + c;
+        tok = key_token(top[c]);
+        w.tok[e] = tok;
+        w.par[e] = -1;
+        w.depth[e] = 1;
+        w.fslot[e] = c;
+        w.score[e] = 0.0 + double(key_value(top[c]));
+        w.frontier[b * max_topk + c] = c;
+      }
+      frontier_tokens[b * max_topk + c] = tok;
+    }
+    return;
+  }
+
   const int parent = w.frontier[b * max_topk + f];
-  const double pscore = w.score[size_t(b) * P + parent];
-  block_row_topk(draft + b * seq_stride + int64_t(f) * V, V, k, keys);
   const int base = k + (step - 2) * k * k;
   if (threadIdx.x < k) {
     const int c = threadIdx.x;
     const size_t e = size_t(b) * P + base + f * k + c;
-    w.tok[e] = key_token(keys[c]);
-    w.par[e] = parent;
-    w.depth[e] = step;
-    w.fslot[e] = -1;
-    w.score[e] = pscore + double(key_value(keys[c]));
+    st_agent(w.tok + e, key_token(top[c]));
+    st_agent(w.par + e, parent);
+    st_agent(w.depth + e, step);
+    st_agent(w.fslot + e, -1);
+    st_agent(w.score + e, w.score[size_t(b) * P + parent] + double(key_value(top[c])));
   }
-  __threadfence();
+  wait_global_stores();
   __syncthreads();
-  if (threadIdx.x == 0) last = (atomicAdd(w.ticket + b, 1u) == uint32_t(k - 1));
+  if (threadIdx.x == 0) last = (ticket_add(w.ticket + b) == uint32_t(k - 1));
   __syncthreads();
   if (!last) return;
-  __threadfence();
-  if (threadIdx.x == 0) atomicExch(w.ticket + b, 0u);
+  if (threadIdx.x == 0) ticket_reset(w.ticket + b);
   // rank the k*k candidates of this step: rank(c) = #candidates that beat c
   const int n = k * k;
   if (threadIdx.x < n) {
     const int c = threadIdx.x;
-    const double sc = w.score[size_t(b) * P + base + c];
+    const double sc = ld_agent(w.score + size_t(b) * P + base + c);
     int rank = 0;
     for (int o = 0; o < n; ++o) {
-      const double so = w.score[size_t(b) * P + base + o];
+      const double so = ld_agent(w.score + size_t(b) * P + base + o);
       rank += (so > sc) || (so == sc && o < c);
     }
     if (rank < k) {
       w.frontier[b * max_topk + rank] = base + c;
-      w.fslot[size_t(b) * P + base + c] = rank;
-      frontier_tokens[b * max_topk + rank] = w.tok[size_t(b) * P + base + c];
+      st_agent(w.fslot + size_t(b) * P + base + c, rank);
+      frontier_tokens[b * max_topk + rank] = ld_agent(w.tok + size_t(b) * P + base + c);
     }
   }
   if (threadIdx.x >= k && threadIdx.x < max_topk) frontier_tokens[b * max_topk + threadIdx.x] = -1;
@@ -334,12 +380,18 @@ extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step,
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_step: workspace %zu < %zu bytes", ws_bytes, need);
   const int P = int(pool_cap(max_topk, max_depth));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (step == 1)
-    hipLaunchKernelGGL(build_root_kernel, dim3(B), dim3(kRowThreads), 0, st, w, P, draft_logprobs, seq_stride, topk,
-                       max_topk, V, frontier_tokens);
+  // slices of >= 1024 elements, at most kMaxSlices per row
+  int slice = (V + kMaxSlices - 1) / kMaxSlices;
+  slice = (slice + 1023) / 1024 * 1024;
+  const int n_slices = (V + slice - 1) / slice;
+  const dim3 grid(n_slices, step == 1 ? 1 : max_topk, B);
+  const bool vec = (V % 4 == 0) && (seq_stride % 4 == 0) && ((reinterpret_cast<uintptr_t>(draft_logprobs) & 15) == 0);
+  if (vec)
+    hipLaunchKernelGGL(build_step_kernel<true>, grid, dim3(kRowThreads), 0, st, w, P, step, draft_logprobs, seq_stride,
+                       topk, depth, max_topk, max_depth, V, slice, frontier_tokens);
   else
-    hipLaunchKernelGGL(build_expand_kernel, dim3(max_topk, B), dim3(kRowThreads), 0, st, w, P, step, draft_logprobs,
-                       seq_stride, topk, depth, max_topk, max_depth, V, frontier_tokens);
+    hipLaunchKernelGGL(build_step_kernel<false>, grid, dim3(kRowThreads), 0, st, w, P, step, draft_logprobs, seq_stride,
+                       topk, depth, max_topk, max_depth, V, slice, frontier_tokens);
   return check_launch("spec_tree_build_step");
 }
 

@@ -70,7 +70,7 @@ class StepOutputs:
 
 
 class SpecTreeStep:
-    def __init__(self, dw: DeviceWorkload):
+    def __init__(self, dw: DeviceWorkload, attn_status: bool = True):
         w = dw.w
         self.dw = dw
         dev = dw.device
@@ -86,6 +86,8 @@ class SpecTreeStep:
             ops.spec_tree_attention_workspace_size(B, T, w.Hq, w.Hkv, w.d, w.page, w.max_pages), dev)
         self.ws_verify = ops.zeroed_workspace(ops.spec_tree_verify_workspace_size(B, T, w.V), dev)
         self.sampling = bool((w.modes == ops.MODE_SAMPLE).any())
+        # the attention status word is OR-ed into, so collecting it costs a fill per step
+        self.attn_status = attn_status
 
     # -- the four stages --------------------------------------------------
     def build(self):
@@ -99,9 +101,11 @@ class SpecTreeStep:
 
     def attention(self):
         w, dw, o = self.dw.w, self.dw, self.o
-        o.attn_status.zero_()
+        if self.attn_status:
+            o.attn_status.zero_()
         ops.spec_tree_attention(dw.q, dw.k_pages, dw.v_pages, dw.page_table, dw.prefix_lens, o.parents, dw.T_b,
-                                w.sm_scale, o.attn_out, o.lse, o.attn_status, self.ws_attn)
+                                w.sm_scale, o.attn_out, o.lse, o.attn_status if self.attn_status else None,
+                                self.ws_attn)
 
     def verify(self):
         w, dw, o = self.dw.w, self.dw, self.o
