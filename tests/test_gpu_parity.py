@@ -33,6 +33,9 @@ ATTN_CASES = [
     ("star_g8_t65", 1, 64, 8, 128, [513], [65], 16, "star", 256),
     ("chunk_edges", 3, 8, 8, 64, [128, 256, 129], [2, 3, 4], 16, "random", 128),
     ("g3_odd_rows", 2, 6, 2, 128, [77, 1030], [11, 23], 32, "random", 384),
+    ("item_cap", 2, 8, 2, 128, [5000, 4100], [9, 33], 16, "random", 128),  # 40 chunks asked, capped at 31
+    ("pipelined_g4", 3, 16, 4, 128, [1500, 700, 2100], [9, 17, 5], 16, "random", 512),
+    ("pipelined_d64", 2, 8, 2, 64, [999, 1536], [33, 65], 16, "chain", 1024),
 ]
 
 

@@ -8,6 +8,7 @@ GPU host) finds it without installation.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -53,8 +54,21 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_no_spills(src: str):
+    """The attention kernel's pipelined loop counts its own outstanding loads (s_waitcnt vmcnt(n));
+    scratch (spill) traffic would be counted too, so a spilling build is rejected."""
+    cmd = [_hipcc(), "-x", "hip", *COMMON, "--offload-device-only", "-c", os.path.join(CSRC, src), "-o", os.devnull,
+           "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    sizes = re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", r.stderr)
+    if r.returncode != 0 or not sizes or any(int(x) for x in sizes):
+        raise RuntimeError(f"{src}: kernels must not spill to scratch (per-kernel scratch bytes/lane: {sizes})\n"
+                           + r.stderr[-2000:])
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
+    _check_no_spills("tree_attention.hip")
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
