@@ -8,24 +8,29 @@
 // node, no K x K mask in HBM).
 //
 // Work decomposition (one launch):
-//   grid.z = (b, kv head g); grid.y = block of up to 48 packed rows; grid.x =
-//   prefix chunk s (keys [s*chunk, min((s+1)*chunk, L_b))) or, for the last x,
-//   the tree slots [L_b, L_b + T_b).
+//   The keys of sequence b are its L_b prefix slots followed by its T_b tree
+//   slots (stored in the same pages). grid.x = key chunk s, keys
+//   [s*chunk, min((s+1)*chunk, L_b + T_b)); grid.y = block of row tiles;
+//   grid.z = (b, kv head g).
 //   Rows r = i * G + h' pack the G query heads sharing KV head g with the tree
 //   nodes, so every K/V tile fetched from HBM serves all G*T rows of (b, g).
-//   Each of the 4 waves takes 32-key sub-tiles of the item's range:
-//     S^T = K Q^T  : bf16 MFMA 16x16x32, keys are the A operand (rows), so K
-//                    goes from HBM straight into the A registers (8 consecutive
-//                    head-dim elements per lane = one 16-byte load);
-//     online softmax on S^T columns (each lane owns one query row; row max
-//                    across the 4 lanes sharing it via two xor-shuffles);
-//     O^T += V^T P^T: P^T is the S^T accumulator re-packed to bf16 in place
-//                    (keys permuted identically in both operands), V^T is read
-//                    from a per-wave LDS copy of the V sub-tile.
-//   Waves merge (m, l, O) in LDS in fixed order; the item writes its partial
-//   to the workspace; the last item of (b, g, row block) to arrive (atomic
-//   ticket) merges all partials in fixed item order and writes out / lse.
-//   Run-to-run deterministic; no float atomics.
+//   Rows form 16-row tiles; wave w of a block owns tiles w, w + NW, ... of the
+//   block's range and keeps their Q operands in registers.
+//   All waves stream the chunk through an NS-stage LDS ring of 32-key tiles (K
+//   and V rows loaded straight from HBM into LDS); per tile each wave computes
+//   for its rows:
+//     S^T = K Q^T  : bf16 MFMA 16x16x32, keys are the A operand (read from LDS);
+//     online softmax on S^T columns (each lane owns one query row; the row max
+//                    over the 4 lanes sharing it via two xor-shuffles). The
+//                    reference max only moves when a score exceeds it by more
+//                    than 2^8, so the O rescale is rare; exponentials stay
+//                    below 2^8 and exact in the final normalisation;
+//     O^T += V^T P^T: P^T is the S^T accumulator re-packed to bf16 in place,
+//                    V^T comes from transposing LDS reads.
+//   Waves own distinct rows, so nothing is merged inside a block. An item
+//   whose sequence needs more than one item writes its partial (O, m, l) to
+//   the workspace; a second, small kernel combines the partials of each row
+//   in fixed item order and writes out / lse. Deterministic; no atomics.
 #include "api_common.h"
 #include "spec_common.h"
 
@@ -34,12 +39,16 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kThreads = 256;
-constexpr int kSubKeys = 32;  // keys per wave sub-tile
-constexpr int kMaxChunk = 2048;
-constexpr int kMergeItems = 32;  // items whose (m, l) the merge stages in LDS at a time
-constexpr int kMaxPageIds = kMaxChunk + 2;  // page ids of one chunk (page size 1) or of the tree slots
+constexpr int kTile = 32;         // keys per ring stage
+constexpr int kMaxChunk = 2048;   // keys per work item, at most
+constexpr float kTau = 8.f;       // log2 headroom of the lazily moved reference max
+constexpr int kTargetBlocks = 512;
 
 struct AttnParams {
   const uint16_t* q;
@@ -53,11 +62,10 @@ struct AttnParams {
   float* lse;
   uint32_t* status;
   float* part;
-  uint32_t* tickets;
-  const uint16_t* zeros;  // a zero-filled (token, head) row in the workspace: target of masked loads
+  const uint16_t* zeros;  // a zero-filled (token, head) row in the workspace: source of masked loads
   int max_T, Hq, Hkv, G;
   int page_shift, max_pages, num_pages;
-  int chunk, n_splits, n_rb;
+  int chunk, n_splits, n_rb, tpb, npg;
   float scale_log2;
 };
 
@@ -65,37 +73,12 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 
-__device__ __forceinline__ bf16x8 pack_bf16x8(const uint16_t (&e)[8]) {
-  uint4 u;
-  u.x = uint32_t(e[0]) | (uint32_t(e[1]) << 16);
-  u.y = uint32_t(e[2]) | (uint32_t(e[3]) << 16);
-  u.z = uint32_t(e[4]) | (uint32_t(e[5]) << 16);
-  u.w = uint32_t(e[6]) | (uint32_t(e[7]) << 16);
-  return __builtin_bit_cast(bf16x8, u);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // two fp32 -> packed bf16 pair, hardware round-to-nearest-even
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
-
-// LDS address space pointer for the direct global->LDS loads
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Chunk swizzle of a V row in LDS (16-byte chunks XOR 2 * (key & 3)): the transposed reads of four
-// consecutive keys then hit 128 distinct bytes of banks.
-template <int D>
-__device__ __forceinline__ int v_swz(int key) {
-  return 2 * (key & 3);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // gfx950 transposing LDS read: within each 16-lane group, lane i names a row of 4 consecutive
 // 16-bit elements and lane l receives element (l % 4) of rows l/4, l/4 + 4, l/4 + 8, l/4 + 12.
@@ -103,103 +86,134 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(addr));
 }
 
-// single-stage variants rely on two blocks per CU for latency hiding: ask for 2 waves per SIMD
-template <int D, int RT, bool PIPE>
-__global__ void __launch_bounds__(kThreads, 2) tree_attn_kernel(AttnParams p) {
-  constexpr int KK = D / 32;          // MFMA k-steps over the head dim
-  constexpr int DT = D / 16;          // 16-wide head-dim tiles of O^T
-  constexpr int ROWS = RT * 16;       // packed rows per block
-  constexpr int CPR = D / 8;          // 16-byte chunks per (token, head) row
-  constexpr int NL = D / 16;          // per-lane loads per sub-tile, for K and for V each
-  constexpr int VSUB = kSubKeys * D * 2;                  // bytes of one V sub-tile
-  constexpr int NSTAGE = PIPE ? 2 : 1;                    // V stages per wave (2 = prefetch one sub-tile ahead)
-  constexpr int V_BYTES = 4 * NSTAGE * VSUB;
-  constexpr int OREG = ROWS * D * 4;                      // one fp32 [ROWS][D] merge region
-  constexpr int SM_BYTES = V_BYTES > 2 * OREG ? V_BYTES : 2 * OREG;  // V staging, reused by the wave merge
-  constexpr int NREG = (4 * OREG <= SM_BYTES) ? 4 : 2;    // wave-merge regions (2 -> two rounds)
-  constexpr int ITEM = ROWS * D + 2 * ROWS;               // floats per partial: O[ROWS][D], m[ROWS], l[ROWS]
-  static_assert(kMergeItems * ROWS * 3 * 4 <= SM_BYTES, "merge staging must fit in the shared area");
-  __shared__ __attribute__((aligned(16))) unsigned char vsm[SM_BYTES];
-  __shared__ __attribute__((aligned(16))) uint16_t q_s[ROWS * D];
-  __shared__ float red_m[4][ROWS], red_l[4][ROWS];
-  __shared__ float row_m[ROWS], row_l[ROWS];
+// Direct global -> LDS load of 16 bytes per lane (lane l's bytes land at lds_dst + 16 l), written as
+// inline asm on purpose: the compiler then keeps these loads out of its wait-count bookkeeping, which
+// would otherwise wait for every outstanding direct load before each LDS read of the kernel. The ring
+// is synchronised explicitly instead (s_waitcnt vmcnt(n) + barrier), and no load the compiler issues
+// is in flight while the ring runs. M0 carries the LDS base (uniform by contract: read from lane 0);
+// nothing else in this file uses M0.
+__device__ __forceinline__ void load_to_lds16(const void* src, unsigned char* lds_dst) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_void*)lds_dst)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m) : "memory");
+}
+
+// max over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes holding one query row of an S^T tile), with
+// the gfx950 row swaps: swapping the odd 16-lane rows of one copy with the even rows of another puts
+// every lane's xor-16 partner in one of the two results (likewise for 32-lane halves)
+__device__ __forceinline__ float lanegroup_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// LDS layout of one ring stage: K rows then V rows, 2*D bytes per key, 16-byte chunks swizzled per key:
+//   K: chunk c of key j sits at c ^ (j & 7)      (A-operand reads of 8 keys hit 8 different chunks)
+//   V: chunk c of key j sits at c ^ 2 (j & 3)    (transposing reads of 4 keys hit 4 different 32-byte groups)
+__device__ __forceinline__ int k_swz(int key) { return key & 7; }
+__device__ __forceinline__ int v_swz(int key) { return 2 * (key & 3); }
+
+// occupancy target: two blocks per CU (the LDS ring allows two), i.e. 8 / NW * 2 ... waves per SIMD
+template <int D, int NW, int RW, int NS>
+__global__ void __launch_bounds__(64 * NW, NW / 2) tree_attn_kernel(AttnParams p) {
+  constexpr int KK = D / 32;               // MFMA k-steps over the head dim
+  constexpr int DT = D / 16;               // 16-wide head-dim tiles of O^T
+  constexpr int CPR = D / 8;               // 16-byte chunks per (token, head) row
+  constexpr int ROWB = 2 * D;              // bytes per (token, head) row
+  constexpr int TILE_B = kTile * ROWB;     // bytes of K (or V) per ring stage
+  constexpr int STAGE_B = 2 * TILE_B;
+  constexpr int RPI = 1024 / ROWB;         // key rows per direct-to-LDS instruction (64 lanes x 16 B)
+  constexpr int NLD = TILE_B / 1024;       // such instructions per stage and buffer
+  constexpr int PW = 2 * NLD / NW;         // ... per wave and stage
+  constexpr int NT = 64 * NW;
+  static_assert(PW >= 2 && PW * NW == 2 * NLD, "each wave loads whole K/V row pairs");
+  constexpr int PH = PW / 2;               // key rows (x 1 KB) per wave and stage, each loaded for K and for V
+  static_assert(NT >= 65, "the tree prologue uses one thread per node");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE_B];
   __shared__ uint64_t anc_s[65];
   __shared__ int par_s[65];
-  __shared__ int pg_s[kMaxPageIds];  // page-table entries covering this item's keys
-  __shared__ int flag_s;
+  extern __shared__ int pg_s[];  // page-table entries covering this item's keys (p.npg of them)
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform, so everything derived from it is scalar
   const int s = blockIdx.x, rb = blockIdx.y, bg = blockIdx.z;
   const int b = bg / p.Hkv, g = bg - b * p.Hkv;
-  const bool is_tree = (s == p.n_splits - 1);
   const int32_t* ptab = p.page_table + size_t(b) * p.max_pages;
-  const int row0 = rb * ROWS;
+  const int t0 = rb * p.tpb;  // first row tile of this block
+  const int l15 = lane & 15, g4 = 4 * (lane >> 4);
 
   // ---- round trip 1: everything that does not depend on the sequence's lengths
   const int T_raw = p.T_b ? p.T_b[b] : p.max_T;
   const int L_raw = p.prefix_lens[b];
-  const int pg0_spec = (s * p.chunk) >> p.page_shift;  // page ids of this prefix chunk (speculative)
-  if (!is_tree) {
-    const int npg = ((p.chunk - 1) >> p.page_shift) + 1;
-    for (int i = tid; i < npg; i += kThreads) {
-      const int pi = pg0_spec + i;
-      pg_s[i] = pi < p.max_pages ? ptab[pi] : -1;
-    }
-  }
-  // Q tile -> LDS, row-major [row][d] with 16-byte chunks swizzled by (row & 7); rows up to G * max_T
-  // are always inside q, rows past this tree's M are computed and ignored
-  for (int idx = tid; idx < ROWS * CPR; idx += kThreads) {
-    const int row = idx / CPR, c = idx - row * CPR;
-    const int r = row0 + row;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r < p.G * p.max_T) {
-      const int i = r / p.G, h = g * p.G + (r - i * p.G);
-      v = *reinterpret_cast<const uint4*>(p.q + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 8 * c);
-    }
-    *reinterpret_cast<uint4*>(q_s + row * D + 8 * (c ^ (row & 7))) = v;
+  const int pg0 = (s * p.chunk) >> p.page_shift;  // pg_s[i] holds page-table entry pg0 + i
+  for (int i = tid; i < p.npg; i += NT) {
+    const int pi = pg0 + i;
+    pg_s[i] = pi < p.max_pages ? ptab[pi] : -1;
   }
   int par_raw = 0;
-  if (is_tree && tid > 0 && tid < p.max_T) par_raw = p.parents[size_t(b) * p.max_T + tid];
+  if (tid > 0 && tid < p.max_T) par_raw = p.parents[size_t(b) * p.max_T + tid];
+  // Q operands of this wave's row tiles: lane = row (lane & 15), head-dim chunk (lane >> 4) + 4 kk.
+  // Rows up to G * max_T are inside q; rows past this tree's M are computed and ignored.
+  bf16x8 qop[RW][KK];
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw) {
+    const int lt = wave + NW * rw;
+    const int r = 16 * (t0 + lt) + l15;
+    const bool ok = lt < p.tpb && r < p.G * p.max_T;
+    const int rr = ok ? r : 0;
+    const int i = rr / p.G, h = g * p.G + (rr - i * p.G);
+    const uint16_t* src = p.q + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 v = load_bf16x8(src + 32 * kk);
+      qop[rw][kk] = ok ? v : bf16x8{};
+    }
+  }
   __syncthreads();
 
   int T = min(max(T_raw, 1), p.max_T);
   int L = L_raw;
   const int cap = p.max_pages << p.page_shift;
   if (L < 0 || L > cap - T) {
-    if (p.status && is_tree && rb == 0 && g == 0 && tid == 0) atomicOr(p.status + b, SPEC_STATUS_INVALID_LENGTH);
+    if (p.status && s == 0 && rb == 0 && g == 0 && tid == 0) atomicOr(p.status + b, SPEC_STATUS_INVALID_LENGTH);
     L = min(max(L, 0), cap - T);
   }
   const int M = p.G * T;
-  if (row0 >= M) return;
-  const int nrows = min(ROWS, M - row0);
-  const int nsp = (L + p.chunk - 1) / p.chunk;
-  if (!is_tree && s >= nsp) return;
-  const int n_items = nsp + 1;
-  const int key_lo = is_tree ? L : s * p.chunk;
-  const int key_hi = is_tree ? L + T : min(L, key_lo + p.chunk);
-  const int pg0 = key_lo >> p.page_shift;  // pg_s[i] holds page-table entry pg0 + i
+  const int ntM = (M + 15) >> 4;
+  if (t0 >= ntM) return;
+  const int n_items = (L + T + p.chunk - 1) / p.chunk;
+  if (s >= n_items) return;
+  const int key_lo = s * p.chunk;
+  const int key_hi = min(L + T, key_lo + p.chunk);
+  const bool has_tree = key_hi > L;
 
-  // ---- tree item: its page ids and the ancestry words (pointer doubling)
-  if (is_tree) {
-    const int npg = ((key_hi - 1) >> p.page_shift) - pg0 + 1;
-    for (int i = tid; i < npg; i += kThreads) pg_s[i] = ptab[pg0 + i];
-    if (tid < T) {
-      int par = 0;
-      uint64_t a = 0;
-      if (tid > 0) {
-        par = par_raw;
-        if (par < 0 || par >= tid) {
-          par = 0;
-          if (p.status && rb == 0 && g == 0) atomicOr(p.status + b, SPEC_STATUS_INVALID_PARENT);
-        }
-        a = 1ull << (tid - 1);
+  // ---- page-table entries of the chunk must name pages of the pool; tree ancestry words
+  bool bad = false;
+  {
+    const int npg_used = ((key_hi - 1) >> p.page_shift) - pg0 + 1;
+    for (int i = tid; i < npg_used; i += NT) bad |= unsigned(pg_s[i]) >= unsigned(p.num_pages);
+  }
+  if (has_tree && tid < T) {
+    int par = 0;
+    uint64_t a = 0;
+    if (tid > 0) {
+      par = par_raw;
+      if (par < 0 || par >= tid) {
+        par = 0;
+        if (p.status && rb == 0 && g == 0) atomicOr(p.status + b, SPEC_STATUS_INVALID_PARENT);
       }
-      par_s[tid] = par;
-      anc_s[tid] = a;
+      a = 1ull << (tid - 1);
     }
-    __syncthreads();
+    par_s[tid] = par;
+    anc_s[tid] = a;
+  }
+  const bool pages_ok = !__syncthreads_or(bad);
+  if (!pages_ok && p.status && tid == 0) atomicOr(p.status + b, SPEC_STATUS_INVALID_PAGE);
+  if (has_tree) {  // pointer doubling: after round k each word covers 2^k generations
 #pragma unroll 1
-    for (int it = 0; it < 7; ++it) {  // 2^7 > 64: every chain is covered
+    for (int it = 0; it < 7; ++it) {
       uint64_t na = 0;
       int np = 0;
       if (tid < T) {
@@ -215,428 +229,387 @@ __global__ void __launch_bounds__(kThreads, 2) tree_attn_kernel(AttnParams p) {
       __syncthreads();
     }
   }
-  uint64_t row_anc[RT];
+  uint64_t ranc[RW];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = row0 + rt * 16 + (lane & 15);
-    row_anc[rt] = (is_tree && r < M) ? anc_s[r / p.G] : 0ull;
+  for (int rw = 0; rw < RW; ++rw) {
+    const int r = 16 * (t0 + wave + NW * rw) + l15;
+    ranc[rw] = (has_tree && r < M) ? anc_s[r / p.G] : 0ull;
   }
+  // this wave owns at least one row tile of the block that holds rows of this tree
+  const bool active = wave < p.tpb && t0 + wave < ntM;
 
-  float m_run[RT], l_run[RT];
-  f32x4 acc[RT][DT];
+  // per row tile: reference max (log2 domain), O^T accumulator and the row sums of P (from an extra
+  // MFMA against an all-ones V^T tile: every lane gets its row's sum, no reduction needed)
+  float m_run[RW];
+  f32x4 acc[RW][DT], lacc[RW];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
+  for (int rw = 0; rw < RW; ++rw) {
+    m_run[rw] = -INFINITY;
+    lacc[rw] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt) acc[rw][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
   const int pmask = (1 << p.page_shift) - 1;
   const size_t tok_stride = size_t(p.Hkv) * D;
-  const size_t page_stride = tok_stride << p.page_shift;
   const uint16_t* kbase = p.k + size_t(g) * D;
   const uint16_t* vbase = p.v + size_t(g) * D;
-  const int g4 = 4 * (lane >> 4);
-  bool bad_page = false;
-  unsigned char* vwave = vsm + wave * NSTAGE * VSUB;
 
-  // address of the (slot, head g) row in the pool, or of the zero row if the slot is not usable
-  // (past the item's range, or an invalid page-table entry); branch-free
-  auto row_ptr = [&](const uint16_t* base, int slot, bool& ok) -> const uint16_t* {
-    const bool in = slot < key_hi;
-    const int phys = pg_s[in ? (slot >> p.page_shift) - pg0 : 0];
-    const bool pok = unsigned(phys) < unsigned(p.num_pages);
-    bad_page |= in && !pok;
-    ok = in && pok;
-    const size_t row = size_t(uint32_t(phys) << p.page_shift) + size_t(slot & pmask);
-    return ok ? base + row * tok_stride : p.zeros;
-  };
-  // issue sub-tile st: V straight into LDS stage `stg` (swizzled rows), K into registers
-  auto issue = [&](int st, int stg, bf16x8 (&kop)[2][KK], uint32_t (&kvalid)[2]) {
-    unsigned char* vdst = vwave + stg * VSUB;
+  // this wave's share of a stage: key rows sub_i * RPI + lane / CPR (sub_i = wave + NW i), one 16-byte chunk
+  // per lane, loaded once for K and once for V (swizzled on the global side: LDS gets lane-order bytes)
+  const size_t page_elems = tok_stride << p.page_shift;
+  int lkey[PH], koff[PH], voff[PH];
 #pragma unroll
-    for (int c = 0; c < NL; ++c) {  // 1 KB of LDS per instruction: lane l -> bytes [16 l, 16 l + 16)
-      const int key = c * (64 / CPR) + lane / CPR;
-      const int pos = lane % CPR;
-      bool ok;
-      const uint16_t* src = row_ptr(vbase, st + key, ok) + 8 * (pos ^ v_swz<D>(key));
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(vdst + c * 1024), 16, 0, 0);
+  for (int i = 0; i < PH; ++i) {
+    lkey[i] = (wave + NW * i) * RPI + lane / CPR;
+    const int pos = lane % CPR;
+    koff[i] = 8 * (pos ^ k_swz(lkey[i]));
+    voff[i] = 8 * (pos ^ v_swz(lkey[i]));
+  }
+  // issue the direct loads of this wave's share of key tile `tile` into ring stage `slot`; slots past
+  // the chunk and slots on invalid pages read the zero row (their keys are masked in compute)
+  auto issue = [&](int tile, int slot) {
+    const int st = key_lo + tile * kTile;
+    unsigned char* sb = ring + slot * STAGE_B;
+    const bool full = pages_ok && st + kTile <= key_hi;  // uniform
+#pragma unroll
+    for (int i = 0; i < PH; ++i) {
+      const int slot_k = st + lkey[i];
+      const uint16_t *ks, *vs;
+      if (full) {
+        const int phys = pg_s[(slot_k >> p.page_shift) - pg0];
+        const size_t off = size_t(uint32_t(phys)) * page_elems + size_t((slot_k & pmask) * tok_stride);
+        ks = kbase + off + koff[i];
+        vs = vbase + off + voff[i];
+      } else {
+        const bool in = slot_k < key_hi;
+        const int phys = pg_s[in ? (slot_k >> p.page_shift) - pg0 : 0];
+        const bool ok = in && unsigned(phys) < unsigned(p.num_pages);
+        const size_t off = size_t(uint32_t(phys)) * page_elems + size_t((slot_k & pmask) * tok_stride);
+        ks = ok ? kbase + off + koff[i] : p.zeros + koff[i];
+        vs = ok ? vbase + off + voff[i] : p.zeros + voff[i];
+      }
+      const int sub = wave + NW * i;
+      load_to_lds16(ks, sb + sub * 1024);
+      load_to_lds16(vs, sb + TILE_B + sub * 1024);
     }
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {  // A operand: lane = key (lane & 15), head-dim chunk (lane >> 4) + 4 kk
-      bool ok;
-      const uint16_t* src = row_ptr(kbase, st + 16 * kt + (lane & 15), ok) + 8 * (lane >> 4);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kop[kt][kk] = load_bf16x8(src + 32 * kk);
-      kvalid[kt] = uint32_t(__ballot(ok) & 0xffffull);
-    }
   };
-  // one sub-tile: S^T = K Q^T, online softmax, O^T += V^T P^T
-  auto compute = [&](int st, int stg, const bf16x8 (&kop)[2][KK], const uint32_t (&kvalid)[2]) {
-    const unsigned char* vsrc = vwave + stg * VSUB;
-    f32x4 sc[2][RT];
+
+  // one key tile for this wave's row tiles: S^T = K Q^T, online softmax, O^T += V^T P^T. Masked tiles
+  // (the chunk's end, tree slots, invalid pages) test every key; the others skip all masking.
+  auto compute = [&](int tile, int slot, bool masked) {
+    const unsigned char* kb = ring + slot * STAGE_B;
+    const unsigned char* vb = kb + TILE_B;
+    const int st = key_lo + tile * kTile;
+    f32x4 sc[RW][2];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int row = rt * 16 + (lane & 15);
-      bf16x8 qop[KK];
+    for (int kt = 0; kt < 2; ++kt) {
+      const unsigned char* kr = kb + (16 * kt + l15) * ROWB;
+      bf16x8 kop[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        qop[kk] = *reinterpret_cast<const bf16x8*>(q_s + row * D + 8 * ((4 * kk + (lane >> 4)) ^ (row & 7)));
+        kop[kk] = *reinterpret_cast<const bf16x8*>(kr + 16 * ((4 * kk + (lane >> 4)) ^ k_swz(l15)));
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int rw = 0; rw < RW; ++rw) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kt][kk], qop[kk], a, 0, 0, 0);
-        sc[kt][rt] = a;
+        for (int kk = 0; kk < KK; ++kk) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qop[rw][kk], a, 0, 0, 0);
+        sc[rw][kt] = a;
       }
     }
-    // visibility of the lane's 8 keys (bit kt*4 + j <-> key 16 kt + 4 (lane>>4) + j)
-    const uint32_t kbits = ((kvalid[0] >> g4) & 0xfu) | (((kvalid[1] >> g4) & 0xfu) << 4);
-    bf16x8 pop[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      uint32_t vis = kbits;
-      if (is_tree) {  // uniform: ancestor test per key (root always visible)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jn = st + 16 * (e >> 2) + g4 + (e & 3) - L;  // tree node index of this key
-          const uint64_t sh = row_anc[rt] >> (jn > 0 ? jn - 1 : 0);
-          const bool anc = (jn == 0) || (jn > 0 && (sh & 1ull));
-          vis &= anc ? 0xffu : ~(1u << e);
-        }
-      }
-      float sv[8];  // raw scores (masked -> -inf); the scale is folded into the exponent's fma
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sv[kt * 4 + j] = ((vis >> (kt * 4 + j)) & 1u) ? sc[kt][rt][j] : -INFINITY;
-      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mnew = fmaxf(m_run[rt], mx * p.scale_log2);  // running max in the scaled (log2) domain
-      const bool none = (mnew == -INFINITY);
-      const float alpha = none ? 1.f : fast_exp2(m_run[rt] - mnew);
-      float pe[8];
-      float psum = 0.f;
+    // usable keys among the lane's 8 (bit 4 kt + j <-> key st + 16 kt + g4 + j)
+    uint32_t kvis = 0xffu;
+    if (masked) {  // uniform
+      kvis = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pe[e] = none ? 0.f : fast_exp2(__builtin_fmaf(sv[e], p.scale_log2, -mnew));
-        psum += pe[e];
+        const int key = st + 16 * (e >> 2) + g4 + (e & 3);
+        const bool in = key < key_hi;
+        const int phys = pg_s[in ? (key >> p.page_shift) - pg0 : 0];
+        kvis |= (in && unsigned(phys) < unsigned(p.num_pages)) ? (1u << e) : 0u;
       }
-      l_run[rt] = l_run[rt] * alpha + psum;
-      m_run[rt] = mnew;
-      if (__any(alpha != 1.f)) {  // uniform: skip the rescale when no row's max moved
+    }
+    bf16x8 pop[RW];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+    for (int rw = 0; rw < RW; ++rw) {
+      float sv[8];  // raw scores, masked -> -inf; the scale is folded into the exponent's fma
+      if (masked) {  // uniform
+        uint32_t vis = kvis;
+        if (st + kTile > L) {  // uniform: tree slots in this tile; the root is every node's ancestor
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int jn = st + 16 * (e >> 2) + g4 + (e & 3) - L;  // tree node index of this key
+            const int sh = min(max(jn - 1, 0), 63);
+            const bool anc = jn == 0 || (jn > 0 && ((ranc[rw] >> sh) & 1ull));
+            vis &= anc || jn < 0 ? 0xffu : ~(1u << e);
+          }
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sv[kt * 4 + j] = ((vis >> (kt * 4 + j)) & 1u) ? sc[rw][kt][j] : -INFINITY;
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sv[kt * 4 + j] = sc[rw][kt][j];
       }
+      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mx = lanegroup_max(mx);
+      const float mxs = mx * p.scale_log2;  // tile max in the scaled (log2) domain
+      const bool move = mxs > m_run[rw] + kTau;
+      if (__any(move)) {  // uniform: some row's reference max moves (always on its first visible key)
+        const float mnew = move ? mxs : m_run[rw];
+        const float alpha = move ? fast_exp2(m_run[rw] - mnew) : 1.f;
+        lacc[rw] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[rw][dt] *= alpha;
+        m_run[rw] = mnew;
+      }
+      const float mref = m_run[rw] == -INFINITY ? 0.f : m_run[rw];  // no visible key yet: every p is 0
+      float pe[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sv[e], p.scale_log2, -mref));
       uint4 pk;
       pk.x = pack2_bf16(pe[0], pe[1]);
       pk.y = pack2_bf16(pe[2], pe[3]);
       pk.z = pack2_bf16(pe[4], pe[5]);
       pk.w = pack2_bf16(pe[6], pe[7]);
-      pop[rt] = __builtin_bit_cast(bf16x8, pk);
+      pop[rw] = __builtin_bit_cast(bf16x8, pk);
+      lacc[rw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop[rw], lacc[rw], 0, 0, 0);
     }
-    // V^T operand for head-dim column dt*16 + (lane & 15): keys 4(lane>>4) + {0..3} and 16 + 4(lane>>4) + {0..3}
-    // (the same keys, in the same order, as the lane's P^T column). Two transposing reads: lane i of
-    // group g points at key 16 h + 4 g + i/4, columns 16 dt + 4 (i % 4) .. +3.
-    const int ig = lane & 15;
-    const int q4 = ig >> 2;        // key & 3 of the row this lane points at
-    const int cl = (ig & 3) >> 1;  // which 16-byte chunk of the 32-byte column group
-    const int e4 = 4 * (ig & 1);   // element offset inside the chunk
+    // V^T operand for head-dim column dt*16 + (lane & 15): keys g4 + {0..3} and 16 + g4 + {0..3} (the same
+    // keys, in the same order, as the lane's P^T column). Two transposing reads: lane i of each 16-lane
+    // group points at key 16 h + g4 + i/4, columns 16 dt + 4 (i % 4) .. +3.
+    const int q4 = l15 >> 2;        // key & 3 of the row this lane points at
+    const int cl = (l15 & 3) >> 1;  // which 16-byte chunk of the 32-byte column group
+    const int e4 = 4 * (l15 & 1);   // element offset inside the chunk
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       s16x4 half[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int key = 16 * h + g4 + q4;
-        const int chunk = (2 * dt + cl) ^ v_swz<D>(key);
-        half[h] = lds_read_tr16(vsrc + key * (2 * D) + 16 * chunk + 2 * e4);
+        const int chunk = (2 * dt + cl) ^ v_swz(key);
+        half[h] = lds_read_tr16(vb + key * ROWB + 16 * chunk + 2 * e4);
       }
       const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rt], acc[rt][dt], 0, 0, 0);
+      for (int rw = 0; rw < RW; ++rw) acc[rw][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rw], acc[rw][dt], 0, 0, 0);
     }
   };
 
-  // ---- main loop: two register sets for K, two LDS stages for V, one sub-tile in flight ahead.
-  // The next sub-tile is always issued (past the end it reads the zero row), so the loop body is
-  // straight-line and exactly 2 * NL loads are outstanding at each wait.
-  const int first = key_lo + kSubKeys * wave;
-  const int nsub = first < key_hi ? (key_hi - first + 4 * kSubKeys - 1) / (4 * kSubKeys) : 0;
-  if constexpr (PIPE) {
-    bf16x8 kA[2][KK], kB[2][KK];
-    uint32_t vA[2], vB[2];
-    if (nsub > 0) {
-      issue(first, 0, kA, vA);
+  // ---- main loop over the chunk's key tiles. Stage t is loaded NS - 1 tiles ahead; every wave issues
+  // exactly PW loads per tile (past the end they read the zero row), so after the loads of tile t
+  // exactly PW * (NS - 2) of the wave's loads may still be in flight. One barrier per tile publishes
+  // the stage just landed and retires the stage about to be refilled (its LDS reads have returned).
+  const int ntile = (key_hi - key_lo + kTile - 1) / kTile;
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) issue(i, i);
 #pragma unroll 1
-      for (int j = 0; j < nsub; j += 2) {
-        const int st0 = first + j * 4 * kSubKeys, st1 = st0 + 4 * kSubKeys;
-        issue(st1, 1, kB, vB);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");  // sub-tile j landed; j+1 in flight
-        compute(st0, 0, kA, vA);
-        if (j + 1 >= nsub) break;
-        issue(st1 + 4 * kSubKeys, 0, kA, vA);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
-        compute(st1, 1, kB, vB);
-      }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the prefetch past the end
-    }
-  } else {  // one stage: other blocks on the SIMD hide the latency
-    bf16x8 kA[2][KK];
-    uint32_t vA[2];
-#pragma unroll 1
-    for (int j = 0; j < nsub; ++j) {
-      const int st = first + j * 4 * kSubKeys;
-      issue(st, 0, kA, vA);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      compute(st, 0, kA, vA);
+  for (int t = 0; t < ntile; ++t) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(PW * (NS - 2)) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const int nt = t + NS - 1;
+    issue(nt, nt % NS);
+    if (active) {
+      const int st = key_lo + t * kTile;
+      compute(t, t % NS, !pages_ok || st + kTile > min(key_hi, L));
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads issued past the end
 
-  if (bad_page && p.status) atomicOr(p.status + b, SPEC_STATUS_INVALID_PAGE);
-
+  float l_run[RW];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    l_run[rt] += __shfl_xor(l_run[rt], 16, kWave);
-    l_run[rt] += __shfl_xor(l_run[rt], 32, kWave);
-  }
-
-  // ---- merge the 4 waves (fixed order): NREG separate fp32 regions in the V area, summed when read
-  __syncthreads();
-  if (lane < 16) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      red_m[wave][rt * 16 + lane] = m_run[rt];
-      red_l[wave][rt * 16 + lane] = l_run[rt];
-    }
-  }
-  __syncthreads();
-  float fac[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = rt * 16 + (lane & 15);
-    float mx = red_m[0][row];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, red_m[w][row]);
-    float ls = 0.f, mine = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = (red_m[w][row] == -INFINITY) ? 0.f : fast_exp2(red_m[w][row] - mx);
-      ls += red_l[w][row] * f;
-      if (w == wave) mine = f;
-    }
-    fac[rt] = mine;
-    if (wave == 0 && lane < 16) {
-      row_m[row] = mx;
-      row_l[row] = ls;
-    }
-  }
-  float* oreg = reinterpret_cast<float*>(vsm);  // [NREG][ROWS][D]
-  auto put = [&](bool add) {
-    float* o = oreg + (wave % NREG) * (ROWS * D);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int row = rt * 16 + (lane & 15);
-        float4* dst = reinterpret_cast<float4*>(o + row * D + dt * 16 + g4);
-        const f32x4 v4 = acc[rt][dt] * fac[rt];
-        float4 t = make_float4(v4[0], v4[1], v4[2], v4[3]);
-        if (add) {
-          const float4 x = *dst;
-          t = make_float4(x.x + t.x, x.y + t.y, x.z + t.z, x.w + t.w);
-        }
-        *dst = t;
-      }
-  };
-  if (wave < NREG) put(false);
-  __syncthreads();
-  if (NREG == 2) {
-    if (wave >= 2) put(true);
-    __syncthreads();
-  }
-  auto merged = [&](int row, int d) {
-    float v = 0.f;
-#pragma unroll
-    for (int r = 0; r < NREG; ++r) v += oreg[r * (ROWS * D) + row * D + d];
-    return v;
-  };
+  for (int rw = 0; rw < RW; ++rw) l_run[rw] = lacc[rw][0];
 
   constexpr float kLn2 = 0.69314718055994530942f;
-  if (n_items == 1) {  // no prefix: this item is the whole answer
-    for (int idx = tid; idx < nrows * D; idx += kThreads) {
-      const int row = idx / D, d = idx - row * D;
-      const int r = row0 + row, i = r / p.G, h = g * p.G + (r - i * p.G);
-      const float ls = row_l[row];
-      const float o = ls > 0.f ? merged(row, d) / ls : 0.f;
-      p.out[((size_t(b) * p.max_T + i) * p.Hq + h) * D + d] = f32_to_bf16(o);
+  // out / lse of one row tile from (m, l, O^T accumulator); lanes hold row (lane & 15), columns dt*16 + g4 + {0..3}
+  auto finish = [&](int lt, float m, float ls, const f32x4 (&o)[DT]) {
+    const int r = 16 * (t0 + lt) + l15;
+    if (r >= M) return;
+    const int i = r / p.G, h = g * p.G + (r - i * p.G);
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    uint16_t* dst = p.out + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + g4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 v = o[dt] * inv;
+      *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
     }
-    if (p.lse && tid < nrows) {
-      const int r = row0 + tid, i = r / p.G, h = g * p.G + (r - i * p.G);
-      const float ls = row_l[tid];
-      p.lse[(size_t(b) * p.max_T + i) * p.Hq + h] = ls > 0.f ? (row_m[tid] + __log2f(ls)) * kLn2 : -INFINITY;
+    if (p.lse && lane < 16)
+      p.lse[(size_t(b) * p.max_T + i) * p.Hq + h] = ls > 0.f ? (m + __log2f(ls)) * kLn2 : -INFINITY;
+  };
+
+  if (n_items == 1) {  // the whole key range in one item: this is the answer
+    if (active) {
+#pragma unroll
+      for (int rw = 0; rw < RW; ++rw) {
+        const int lt = wave + NW * rw;
+        if (lt < p.tpb && t0 + lt < ntM) finish(lt, m_run[rw], l_run[rw], acc[rw]);
+      }
     }
     return;
   }
 
-  // ---- publish this item's partial (write-through stores), then the last arrival merges all items
-  float* const grp = p.part + (size_t(bg) * p.n_rb + rb) * size_t(p.n_splits) * ITEM;
-  float* const mine = grp + size_t(s) * ITEM;
-  constexpr int D2 = D / 2;
-  for (int idx = tid; idx < nrows * D2; idx += kThreads) {
-    const int row = idx / D2, c2 = idx - row * D2;
-    const float2 v2 = make_float2(merged(row, 2 * c2), merged(row, 2 * c2 + 1));
-    st_agent(reinterpret_cast<uint64_t*>(mine + row * D) + c2, __builtin_bit_cast(uint64_t, v2));
-  }
-  if (tid < nrows) {
-    st_agent(mine + ROWS * D + tid, row_m[tid]);
-    st_agent(mine + ROWS * D + ROWS + tid, row_l[tid]);
-  }
-  wait_global_stores();
-  __syncthreads();
-  uint32_t* ticket = p.tickets + size_t(bg) * p.n_rb + rb;
-  if (tid == 0) flag_s = (ticket_add(ticket) == uint32_t(n_items - 1));
-  __syncthreads();
-  if (!flag_s) return;
-  if (tid == 0) ticket_reset(ticket);  // leave the workspace ready for the next call
-
-  // merge in fixed item order. (1) every item's (m, l) -> LDS in one round trip; (2) per-row max,
-  // normaliser and item weights; (3) O: each thread owns KP float4 columns and loads them for IB items
-  // at a time, so the KP * IB loads of a batch are in flight together.
-  constexpr int D4 = D / 4;
-  constexpr int KP = (ROWS * D4 + kThreads - 1) / kThreads;  // float4 columns per thread
-  constexpr int IB = KP >= 6 ? 4 : (KP >= 4 ? 6 : 12);       // items per batch (bounded registers)
-  float* wts = reinterpret_cast<float*>(vsm);                   // [n_items][ROWS] weights
-  float* mls = wts + kMergeItems * ROWS;                        // [n_items][2][ROWS] raw (m, l)
-  constexpr float kLn2m = 0.69314718055994530942f;
-  // n_items <= kMergeItems by construction of the plan
-  for (int idx = tid; idx < n_items * 2 * ROWS; idx += kThreads) {
-    const int it = idx / (2 * ROWS), r2 = idx - it * 2 * ROWS;
-    mls[idx] = (r2 % ROWS) < nrows ? ld_agent(grp + size_t(it < nsp ? it : p.n_splits - 1) * ITEM + ROWS * D + r2) : 0.f;
-  }
-  __syncthreads();
-  if (tid < nrows) {
-    float mx = -INFINITY;
-    for (int it = 0; it < n_items; ++it) mx = fmaxf(mx, mls[it * 2 * ROWS + tid]);
-    float ls = 0.f;
-    for (int it = 0; it < n_items; ++it) {
-      const float m = mls[it * 2 * ROWS + tid];
-      const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - mx);
-      ls += mls[it * 2 * ROWS + ROWS + tid] * f;
-      wts[it * ROWS + tid] = f;
+  // ---- this item's partial (unnormalised O, reference max m, row sum l) for the combine kernel.
+  // Layout per (b, g, row block, item): O [tpb * 16][D], then m [tpb * 16], then l [tpb * 16].
+  if (!active) return;
+  const int TR = p.tpb * 16;
+  const size_t ITEM = size_t(TR) * (D + 2);
+  float* const mine = p.part + ((size_t(bg) * p.n_rb + rb) * size_t(p.n_splits) + s) * ITEM;
+#pragma unroll
+  for (int rw = 0; rw < RW; ++rw) {
+    const int lt = wave + NW * rw;
+    if (lt >= p.tpb || t0 + lt >= ntM) continue;
+    const int row = lt * 16 + l15;
+    float* o = mine + size_t(row) * D + g4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = acc[rw][dt];
+    if (lane < 16) {
+      mine[size_t(TR) * D + row] = m_run[rw];
+      mine[size_t(TR) * (D + 1) + row] = l_run[rw];
     }
-    row_m[tid] = mx;
-    row_l[tid] = ls;
-  }
-  __syncthreads();
-  {
-    float4 o[KP];
-#pragma unroll
-    for (int k = 0; k < KP; ++k) o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int ib = 0; ib < n_items; ib += IB) {
-      float4 av[IB][KP];
-#pragma unroll
-      for (int u = 0; u < IB; ++u)
-#pragma unroll
-        for (int k = 0; k < KP; ++k) {
-          const int idx = tid + k * kThreads;
-          const int it = ib + u;
-          av[u][k] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (it < n_items && idx < nrows * D4) {
-            const int row = idx / D4, c4 = idx - row * D4;
-            const uint64_t* q2 = reinterpret_cast<const uint64_t*>(
-                grp + size_t(it < nsp ? it : p.n_splits - 1) * ITEM + row * D + 4 * c4);
-            const float2 lo2 = __builtin_bit_cast(float2, ld_agent(q2));
-            const float2 hi2 = __builtin_bit_cast(float2, ld_agent(q2 + 1));
-            av[u][k] = make_float4(lo2.x, lo2.y, hi2.x, hi2.y);
-          }
-        }
-#pragma unroll
-      for (int u = 0; u < IB; ++u)
-#pragma unroll
-        for (int k = 0; k < KP; ++k) {
-          const int idx = tid + k * kThreads;
-          const int it = ib + u;
-          if (it < n_items && idx < nrows * D4) {
-            const float wv = wts[it * ROWS + idx / D4];
-            o[k].x += av[u][k].x * wv;
-            o[k].y += av[u][k].y * wv;
-            o[k].z += av[u][k].z * wv;
-            o[k].w += av[u][k].w * wv;
-          }
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      const int idx = tid + k * kThreads;
-      if (idx >= nrows * D4) continue;
-      const int row = idx / D4, c4 = idx - row * D4;
-      const float ls = row_l[row];
-      const float inv = ls > 0.f ? 1.f / ls : 0.f;
-      const int r = row0 + row, i = r / p.G, h = g * p.G + (r - i * p.G);
-      uint16_t* dst = p.out + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 4 * c4;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(pack2_bf16(o[k].x * inv, o[k].y * inv), pack2_bf16(o[k].z * inv, o[k].w * inv));
-    }
-  }
-  if (p.lse && tid < nrows) {
-    const int r = row0 + tid, i = r / p.G, h = g * p.G + (r - i * p.G);
-    const float ls = row_l[tid];
-    p.lse[(size_t(b) * p.max_T + i) * p.Hq + h] = ls > 0.f ? (row_m[tid] + __log2f(ls)) * kLn2m : -INFINITY;
   }
 }
 
+// Split-K combine (runs after the main kernel): one block per (b, g, row block, row tile of 16 rows); a
+// thread owns one row and 8 consecutive columns. Items are combined in fixed order, CB at a time (their
+// loads in flight together), online against the running maximum reference max: out = sum_i w_i O_i /
+// sum_i w_i l_i with w_i = 2^(m_i - max_j m_j). Sequences whose keys fit one item were written directly.
+template <int D>
+__global__ void __launch_bounds__(2 * D) tree_attn_combine(AttnParams p) {
+  constexpr int CH = D / 8;  // 8-column chunks per row
+  constexpr int CB = 8;      // items per batch
+  const int tid = threadIdx.x;
+  const int row16 = tid / CH, c = tid - row16 * CH;
+  const int lt = blockIdx.x, rbg = blockIdx.y;
+  const int bg = rbg / p.n_rb, rb = rbg - bg * p.n_rb;
+  const int b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int T = min(max(p.T_b ? p.T_b[b] : p.max_T, 1), p.max_T);
+  const int cap = p.max_pages << p.page_shift;
+  const int L = min(max(p.prefix_lens[b], 0), cap - T);  // the main kernel's clamp
+  const int n_items = (L + T + p.chunk - 1) / p.chunk;
+  const int M = p.G * T;
+  const int r = 16 * (rb * p.tpb + lt) + row16;
+  if (n_items == 1 || r >= M) return;
+  const int TR = p.tpb * 16;
+  const size_t ITEM = size_t(TR) * (D + 2);
+  const float* grp = p.part + size_t(rbg) * p.n_splits * ITEM;
+  const int row = lt * 16 + row16;
+  float mx = -INFINITY, ls = 0.f;
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int ib = 0; ib < n_items; ib += CB) {
+    float mi[CB], li[CB];
+    f32x4 a0[CB], a1[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const float* base = grp + size_t(min(ib + u, n_items - 1)) * ITEM;  // past the end: weight 0 below
+      mi[u] = base[size_t(TR) * D + row];
+      li[u] = base[size_t(TR) * (D + 1) + row];
+      const f32x4* src = reinterpret_cast<const f32x4*>(base + size_t(row) * D + 8 * c);
+      a0[u] = src[0];
+      a1[u] = src[1];
+    }
+    float mb = mx;
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      if (ib + u < n_items) mb = fmaxf(mb, mi[u]);
+    if (mb == -INFINITY) continue;  // nothing visible yet
+    const float sc = (mx == -INFINITY) ? 0.f : fast_exp2(mx - mb);
+    ls *= sc;
+    o0 *= sc;
+    o1 *= sc;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const float w = (ib + u < n_items && mi[u] != -INFINITY) ? fast_exp2(mi[u] - mb) : 0.f;
+      ls += w * li[u];
+      o0 += a0[u] * w;
+      o1 += a1[u] * w;
+    }
+    mx = mb;
+  }
+  const int i = r / p.G, h = g * p.G + (r - i * p.G);
+  const float inv = ls > 0.f ? 1.f / ls : 0.f;
+  o0 *= inv;
+  o1 *= inv;
+  *reinterpret_cast<uint4*>(p.out + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 8 * c) =
+      make_uint4(pack2_bf16(o0[0], o0[1]), pack2_bf16(o0[2], o0[3]), pack2_bf16(o1[0], o1[1]), pack2_bf16(o1[2], o1[3]));
+  constexpr float kLn2 = 0.69314718055994530942f;
+  if (p.lse && c == 0) p.lse[(size_t(b) * p.max_T + i) * p.Hq + h] = ls > 0.f ? (mx + __log2f(ls)) * kLn2 : -INFINITY;
+}
+
+struct AttnShape {
+  int NW, RW, NS;
+};
+
 struct AttnPlan {
-  int G, RT, rows, n_rb, chunk, n_splits;
-  size_t zero_bytes, part_bytes, ticket_bytes;
+  AttnShape sh;
+  int G, tiles, n_rb, tpb, chunk, n_splits, npg;
+  size_t zero_bytes, part_bytes, lds_dyn;
 };
 
 AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_pages) {
   AttnPlan pl;
   pl.G = Hq / Hkv;
-  const int M = pl.G * max_T;
-  pl.RT = (M + 15) / 16;
-  if (pl.RT > 3) pl.RT = 3;  // 48 rows: the largest tile whose pipelined loop fits the register file without spills
-  pl.rows = pl.RT * 16;
-  pl.n_rb = (M + pl.rows - 1) / pl.rows;
+  pl.tiles = (pl.G * max_T + 15) / 16;
+  // waves x row tiles per wave (one tile per wave; two only on 4-wave blocks, which have the registers)
+  pl.sh = pl.tiles <= 4 ? AttnShape{4, 1, 4} : AttnShape{8, 1, 4};
+  if (const char* env = getenv("SPEC_TREE_ATTN_SHAPE")) {
+    int nw = 0, rw = 0, ns = 0;
+    if (sscanf(env, "%d,%d,%d", &nw, &rw, &ns) == 3 && (nw == 4 || nw == 8) && (rw == 1 || (rw == 2 && nw == 4)) && (ns == 3 || ns == 4))
+      pl.sh = AttnShape{nw, rw, ns};
+  }
+  if (d == 64) pl.sh.NW = 4;
+  const int cap = pl.sh.NW * pl.sh.RW;
+  pl.n_rb = (pl.tiles + cap - 1) / cap;
+  pl.tpb = (pl.tiles + pl.n_rb - 1) / pl.n_rb;  // row tiles spread evenly over the row blocks
   const long long slots = (long long)max_pages * page;
   const long long groups = (long long)B * Hkv * pl.n_rb;
-  long long chunk = (slots * groups + 4095) / 4096;  // aim at ~4k work items
-  if (chunk < 4LL * pl.rows) chunk = 4LL * pl.rows;  // keep partials small next to the KV they summarise
-  if (chunk > kMaxChunk) chunk = kMaxChunk;
+  long long n = (kTargetBlocks + groups - 1) / groups;  // items per (b, g, row block)
+  long long chunk = (slots + n - 1) / n;
   if (const char* env = getenv("SPEC_TREE_ATTN_CHUNK")) {
     const long long c = atoll(env);
-    if (c >= 128) chunk = c;
+    if (c >= kTile) chunk = c;
   }
-  // at most kMergeItems - 1 prefix chunks, so the merge stages every item at once
-  const long long min_chunk = (slots + kMergeItems - 2) / (kMergeItems - 1);
-  if (chunk < min_chunk) chunk = min_chunk;
-  chunk = (chunk + 127) / 128 * 128;
-  pl.chunk = int(std::min<long long>(chunk, 1LL << 30));
-  pl.n_splits = int((slots + chunk - 1) / chunk) + 1;
-  const size_t item = size_t(pl.rows) * d + 2 * size_t(pl.rows);
+  chunk = std::max<long long>(chunk, 4 * kTile);
+  chunk = std::min<long long>(chunk, kMaxChunk);
+  chunk = (chunk + kTile - 1) / kTile * kTile;
+  pl.chunk = int(chunk);
+  pl.n_splits = int((slots + chunk - 1) / chunk);
+  pl.npg = int((chunk - 1) / page) + 2;  // a chunk may straddle one page more than it covers
+  const size_t item = size_t(pl.tpb) * 16 * (d + 2);
   pl.zero_bytes = 1024;  // never written: stays as zero-filled as the caller provided it
   pl.part_bytes = align_up(size_t(groups) * pl.n_splits * item * sizeof(float), 256);
-  pl.ticket_bytes = align_up(size_t(groups) * sizeof(uint32_t), 256);
+  pl.lds_dyn = size_t(pl.npg) * sizeof(int);
   return pl;
 }
 
-template <int D, bool PIPE>
-void launch_dp(const AttnPlan& pl, const AttnParams& prm, dim3 grid, hipStream_t st) {
-  switch (pl.RT) {
-    case 1: hipLaunchKernelGGL((tree_attn_kernel<D, 1, PIPE>), grid, dim3(kThreads), 0, st, prm); break;
-    case 2: hipLaunchKernelGGL((tree_attn_kernel<D, 2, PIPE>), grid, dim3(kThreads), 0, st, prm); break;
-    default: hipLaunchKernelGGL((tree_attn_kernel<D, 3, PIPE>), grid, dim3(kThreads), 0, st, prm); break;
-  }
+template <int D, int NW, int RW>
+void launch_ns(const AttnPlan& pl, const AttnParams& prm, dim3 grid, hipStream_t st) {
+  if (pl.sh.NS == 3)
+    hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 3>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+  else
+    hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 4>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
 }
 
-// the prefetching loop pays off only when a wave walks more than one sub-tile of its chunk
 template <int D>
 void launch_d(const AttnPlan& pl, const AttnParams& prm, dim3 grid, hipStream_t st) {
-  if (pl.chunk > 4 * kSubKeys)
-    launch_dp<D, true>(pl, prm, grid, st);
-  else
-    launch_dp<D, false>(pl, prm, grid, st);
+  if constexpr (D == 64) {  // a 32-key stage of d = 64 holds 4 K/V row pairs: at most 4 loading waves
+    if (pl.sh.RW == 1)
+      launch_ns<D, 4, 1>(pl, prm, grid, st);
+    else
+      launch_ns<D, 4, 2>(pl, prm, grid, st);
+  } else {
+    if (pl.sh.NW == 4 && pl.sh.RW == 1)
+      launch_ns<D, 4, 1>(pl, prm, grid, st);
+    else if (pl.sh.NW == 4)
+      launch_ns<D, 4, 2>(pl, prm, grid, st);
+    else
+      launch_ns<D, 8, 1>(pl, prm, grid, st);
+  }
 }
 
 int32_t check_shapes(int32_t B, int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d, int32_t page, int32_t max_pages) {
@@ -663,8 +636,7 @@ extern "C" size_t spec_tree_attention_workspace_size(int32_t B, int32_t max_T, i
                                                      int32_t page, int32_t max_pages) {
   if (check_shapes(B, max_T, Hq, Hkv, d, page, max_pages) != SPEC_OK) return 0;
   const AttnPlan pl = make_plan(B, max_T, Hq, Hkv, d, page, max_pages);
-  if (((pl.chunk - 1) >> ilog2(page)) + 1 > kMaxPageIds - 2) return 0;
-  return pl.zero_bytes + pl.part_bytes + pl.ticket_bytes;
+  return pl.zero_bytes + pl.part_bytes;
 }
 
 extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
@@ -679,10 +651,7 @@ extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const
   if (num_pages < 1) return fail(SPEC_E_INVAL, "spec_tree_attention: num_pages=%d", num_pages);
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SPEC_E_INVAL, "spec_tree_attention: sm_scale must be finite and > 0");
   const AttnPlan pl = make_plan(B, max_T, Hq, Hkv, d, page, max_pages);
-  if (((pl.chunk - 1) >> ilog2(page)) + 1 > kMaxPageIds - 2)
-    return fail(SPEC_E_UNSUPPORTED, "spec_tree_attention: prefix of %lld slots needs chunks of %d keys > %d pages",
-                (long long)max_pages * page, pl.chunk, kMaxPageIds - 2);
-  const size_t need = pl.zero_bytes + pl.part_bytes + pl.ticket_bytes;
+  const size_t need = pl.zero_bytes + pl.part_bytes;
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_attention: workspace %zu bytes < %zu", ws_bytes, need);
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages) |
        reinterpret_cast<uintptr_t>(ws)) & 15)
@@ -701,7 +670,6 @@ extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const
   prm.status = status;
   prm.zeros = static_cast<const uint16_t*>(ws);
   prm.part = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.zero_bytes);
-  prm.tickets = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + pl.zero_bytes + pl.part_bytes);
   prm.max_T = max_T;
   prm.Hq = Hq;
   prm.Hkv = Hkv;
@@ -712,12 +680,18 @@ extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const
   prm.chunk = pl.chunk;
   prm.n_splits = pl.n_splits;
   prm.n_rb = pl.n_rb;
+  prm.tpb = pl.tpb;
+  prm.npg = pl.npg;
   prm.scale_log2 = sm_scale * 1.4426950408889634f;
   const dim3 grid(pl.n_splits, pl.n_rb, B * Hkv);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (d == 64)
+  const dim3 cgrid(pl.tpb, pl.n_rb * B * Hkv);
+  if (d == 64) {
     launch_d<64>(pl, prm, grid, st);
-  else
+    if (pl.n_splits > 1) hipLaunchKernelGGL((tree_attn_combine<64>), cgrid, dim3(128), 0, st, prm);
+  } else {
     launch_d<128>(pl, prm, grid, st);
+    if (pl.n_splits > 1) hipLaunchKernelGGL((tree_attn_combine<128>), cgrid, dim3(256), 0, st, prm);
+  }
   return check_launch("spec_tree_attention");
 }
