@@ -475,43 +475,49 @@ __global__ void __launch_bounds__(64 * NW, NW / 2) tree_attn_kernel(AttnParams p
 }
 
 // Split-K combine (runs after the main kernel): one block per (b, g, row block, row tile of 16 rows); a
-// thread owns one row and 8 consecutive columns. Items are combined in fixed order, CB at a time (their
-// loads in flight together), online against the running maximum reference max: out = sum_i w_i O_i /
-// sum_i w_i l_i with w_i = 2^(m_i - max_j m_j). Sequences whose keys fit one item were written directly.
+// thread owns one row and 8 consecutive columns. The first CB items' partials are loaded in the same
+// round trip as the sequence's lengths (loads of items the sequence does not have read workspace
+// memory and are never used), so short sequences finish in one round trip. Items are combined in
+// fixed order, online against the running maximum reference max: out = sum_i w_i O_i / sum_i w_i l_i
+// with w_i = 2^(m_i - max_j m_j). Sequences whose keys fit one item were written directly.
 template <int D>
 __global__ void __launch_bounds__(2 * D) tree_attn_combine(AttnParams p) {
   constexpr int CH = D / 8;  // 8-column chunks per row
-  constexpr int CB = 8;      // items per batch
+  constexpr int CB = 16;     // items per batch
   const int tid = threadIdx.x;
   const int row16 = tid / CH, c = tid - row16 * CH;
   const int lt = blockIdx.x, rbg = blockIdx.y;
   const int bg = rbg / p.n_rb, rb = rbg - bg * p.n_rb;
   const int b = bg / p.Hkv, g = bg - b * p.Hkv;
-  const int T = min(max(p.T_b ? p.T_b[b] : p.max_T, 1), p.max_T);
-  const int cap = p.max_pages << p.page_shift;
-  const int L = min(max(p.prefix_lens[b], 0), cap - T);  // the main kernel's clamp
-  const int n_items = (L + T + p.chunk - 1) / p.chunk;
-  const int M = p.G * T;
-  const int r = 16 * (rb * p.tpb + lt) + row16;
-  if (n_items == 1 || r >= M) return;
+  const int T_raw = p.T_b ? p.T_b[b] : p.max_T;
+  const int L_raw = p.prefix_lens[b];
   const int TR = p.tpb * 16;
   const size_t ITEM = size_t(TR) * (D + 2);
   const float* grp = p.part + size_t(rbg) * p.n_splits * ITEM;
   const int row = lt * 16 + row16;
   float mx = -INFINITY, ls = 0.f;
   f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  int n_items = CB;  // known after the first batch's loads
 #pragma unroll 1
   for (int ib = 0; ib < n_items; ib += CB) {
     float mi[CB], li[CB];
     f32x4 a0[CB], a1[CB];
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      const float* base = grp + size_t(min(ib + u, n_items - 1)) * ITEM;  // past the end: weight 0 below
+      const float* base = grp + size_t(min(ib + u, p.n_splits - 1)) * ITEM;
       mi[u] = base[size_t(TR) * D + row];
       li[u] = base[size_t(TR) * (D + 1) + row];
       const f32x4* src = reinterpret_cast<const f32x4*>(base + size_t(row) * D + 8 * c);
       a0[u] = src[0];
       a1[u] = src[1];
+    }
+    if (ib == 0) {
+      const int T = min(max(T_raw, 1), p.max_T);
+      const int cap = p.max_pages << p.page_shift;
+      const int L = min(max(L_raw, 0), cap - T);  // the main kernel's clamp
+      n_items = (L + T + p.chunk - 1) / p.chunk;
+      const int r = 16 * (rb * p.tpb + lt) + row16;
+      if (n_items == 1 || r >= p.G * T) return;
     }
     float mb = mx;
 #pragma unroll
@@ -524,13 +530,16 @@ __global__ void __launch_bounds__(2 * D) tree_attn_combine(AttnParams p) {
     o1 *= sc;
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      const float w = (ib + u < n_items && mi[u] != -INFINITY) ? fast_exp2(mi[u] - mb) : 0.f;
-      ls += w * li[u];
-      o0 += a0[u] * w;
-      o1 += a1[u] * w;
+      if (ib + u < n_items && mi[u] != -INFINITY) {  // guarded, not weighted: unused loads may hold anything
+        const float w = fast_exp2(mi[u] - mb);
+        ls += w * li[u];
+        o0 += a0[u] * w;
+        o1 += a1[u] * w;
+      }
     }
     mx = mb;
   }
+  const int r = 16 * (rb * p.tpb + lt) + row16;
   const int i = r / p.G, h = g * p.G + (r - i * p.G);
   const float inv = ls > 0.f ? 1.f / ls : 0.f;
   o0 *= inv;

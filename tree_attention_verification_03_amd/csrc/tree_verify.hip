@@ -11,26 +11,26 @@
 // wins and one more token is emitted).
 //
 // Every node's outcome depends only on its own rows, its children's tokens and
-// the node's uniforms, so all nodes are evaluated in parallel:
-//   verify_greedy_scan   greedy rows: (row, slice) blocks reduce a packed
-//                        64-bit key (order(value) << 32 | ~index) and merge it
-//                        with a 64-bit atomicMax - order-free, bit-exact.
-//   verify_sample_node   sampling rows: one block per node runs the exact
-//                        integer state machine (2^-32 fixed point; sums are
-//                        integers, so reduction order cannot change them).
-//   verify_walk          one block per sequence: longest valid path (greedy) or
-//                        the chain of ACCEPT links (sampling), emits the path,
-//                        tokens, bonus and status, and re-zeroes the workspace.
+// the node's uniforms, so all nodes are evaluated in parallel, in one launch of
+// 1024-thread blocks, grid (n_slices + 1, B * max_T):
+//   x < n_slices   greedy rows: the block reduces a slice of the row to a packed
+//                  64-bit key (order(value) << 32 | ~index) and merges it with
+//                  a 64-bit atomicMax - order-free, bit-exact;
+//   x = n_slices   sampling rows: the block runs the node's exact integer state
+//                  machine (2^-32 fixed point; sums are integers, so reduction
+//                  order cannot change them).
+// Blocks of the other mode exit at once. Every block then takes a ticket of its
+// sequence; the last one walks the tree: longest valid path (greedy) or the
+// chain of ACCEPT links (sampling), emits the path, tokens, bonus and status,
+// and re-zeroes the workspace.
 #include "api_common.h"
 #include "spec_common.h"
 
 namespace spectree {
 namespace {
 
-constexpr int kScanThreads = 256;
-constexpr int kNodeThreads = 1024;
-constexpr int kNodeWaves = kNodeThreads / kWave;
-constexpr int kWalkThreads = 128;
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;
 
 struct VerifyWs {
   uint64_t* keys;      // [B*max_T] greedy argmax keys (0 = empty)
@@ -38,6 +38,7 @@ struct VerifyWs {
   int32_t* acc_child;  // [B*max_T] sampling: accepted child node or -1
   int32_t* bonus;      // [B*max_T] sampling: bonus token when the walk stops here
   uint32_t* nflag;     // [B*max_T] sampling node flags
+  uint32_t* tickets;   // [B] blocks of the sequence that have finished
 };
 
 VerifyWs carve(void* ws, int B, int max_T, size_t* total) {
@@ -55,9 +56,26 @@ VerifyWs carve(void* ws, int B, int max_T, size_t* total) {
   w.acc_child = reinterpret_cast<int32_t*>(take(4 * n));
   w.bonus = reinterpret_cast<int32_t*>(take(4 * n));
   w.nflag = reinterpret_cast<uint32_t*>(take(4 * n));
+  w.tickets = reinterpret_cast<uint32_t*>(take(4 * size_t(B)));
   *total = off;
   return w;
 }
+
+struct VerifyArgs {
+  const float* target;
+  const float* draft;
+  const int32_t* q_row;
+  const int32_t* tokens;
+  const int32_t* parents;
+  const int32_t* T_b;
+  const int8_t* mode;
+  uint64_t key0, key1, offset;
+  int max_T, R, V, n_slices, slice, seg;
+  int32_t* accept_len;
+  int32_t* accept_nodes;
+  int32_t* out_tokens;
+  uint32_t* status;
+};
 
 __device__ __forceinline__ int seq_T(const int32_t* T_b, int b, int max_T) {
   int T = T_b ? T_b[b] : max_T;
@@ -72,20 +90,17 @@ __device__ __forceinline__ uint64_t argmax_key(float x, int v) {
 
 // ------------------------------------------------------------------ greedy
 template <bool VEC>
-__global__ void __launch_bounds__(kScanThreads) verify_greedy_scan(VerifyWs w, const float* target, const int32_t* T_b,
-                                                                    const int8_t* mode, int max_T, int V, int slice) {
-  __shared__ uint64_t red[kScanThreads / kWave];
-  __shared__ uint32_t nanred[kScanThreads / kWave];
-  const int row = blockIdx.y;
-  const int b = row / max_T, u = row - b * max_T;
-  if (mode[b] == SPEC_MODE_SAMPLE || u >= seq_T(T_b, b, max_T)) return;
-  const int lo = blockIdx.x * slice;
-  const int hi = min(V, lo + slice);
-  const float* r = target + size_t(row) * V;
+__device__ void greedy_slice(const VerifyWs& w, const VerifyArgs& a, int row, int lo) {
+  __shared__ uint64_t red[kWaves];
+  __shared__ uint32_t nanred[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi = min(a.V, lo + a.slice);
+  const float* r = a.target + size_t(row) * a.V;
   uint64_t best = 0;
   bool nan = false;
   if (VEC) {
-    for (int v = lo + 4 * threadIdx.x; v < hi; v += 4 * kScanThreads) {
+#pragma unroll 2
+    for (int v = lo + 4 * tid; v < hi; v += 4 * kThreads) {
       const float4 x = *reinterpret_cast<const float4*>(r + v);
       nan |= (x.x != x.x) | (x.y != x.y) | (x.z != x.z) | (x.w != x.w);
       uint64_t k0 = argmax_key(x.x, v), k1 = argmax_key(x.y, v + 1), k2 = argmax_key(x.z, v + 2), k3 = argmax_key(x.w, v + 3);
@@ -95,7 +110,7 @@ __global__ void __launch_bounds__(kScanThreads) verify_greedy_scan(VerifyWs w, c
       best = k0 > best ? k0 : best;
     }
   } else {
-    for (int v = lo + threadIdx.x; v < hi; v += kScanThreads) {
+    for (int v = lo + tid; v < hi; v += kThreads) {
       const float x = r[v];
       nan |= (x != x);
       const uint64_t k = argmax_key(x, v);
@@ -104,16 +119,15 @@ __global__ void __launch_bounds__(kScanThreads) verify_greedy_scan(VerifyWs w, c
   }
   best = wave_max_u64(best);
   const uint32_t nw = wave_or_u32(nan ? 1u : 0u);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     red[wave] = best;
     nanred[wave] = nw;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     uint64_t m = red[0];
     uint32_t f = nanred[0];
-    for (int i = 1; i < kScanThreads / kWave; ++i) {
+    for (int i = 1; i < kWaves; ++i) {
       m = red[i] > m ? red[i] : m;
       f |= nanred[i];
     }
@@ -162,27 +176,68 @@ __device__ __forceinline__ u128 wave_sum_u128(u128 x) {
   return x;
 }
 
-__global__ void __launch_bounds__(kNodeThreads) verify_sample_node(VerifyWs w, const float* target, const float* draft,
-                                                                    const int32_t* q_row, const int32_t* tokens,
-                                                                    const int32_t* parents, const int32_t* T_b,
-                                                                    const int8_t* mode, uint64_t key0, uint64_t key1,
-                                                                    uint64_t offset, int max_T, int R, int V, int seg) {
+// f(v, p, q) over the wave's segment [lo, hi) of a row pair; q may be null (then 0)
+template <bool VEC, typename F>
+__device__ __forceinline__ void seg_for(const float* p, const float* q, int lo, int hi, int lane, F&& f) {
+  if (VEC) {
+    if (q) {
+#pragma unroll 2
+      for (int v = lo + 4 * lane; v < hi; v += 4 * kWave) {
+        const float4 x = *reinterpret_cast<const float4*>(p + v);
+        const float4 y = *reinterpret_cast<const float4*>(q + v);
+        f(v, x.x, y.x);
+        f(v + 1, x.y, y.y);
+        f(v + 2, x.z, y.z);
+        f(v + 3, x.w, y.w);
+      }
+    } else {
+#pragma unroll 2
+      for (int v = lo + 4 * lane; v < hi; v += 4 * kWave) {
+        const float4 x = *reinterpret_cast<const float4*>(p + v);
+        f(v, x.x, 0.f);
+        f(v + 1, x.y, 0.f);
+        f(v + 2, x.z, 0.f);
+        f(v + 3, x.w, 0.f);
+      }
+    }
+  } else {
+    for (int v = lo + lane; v < hi; v += kWave) f(v, p[v], q ? q[v] : 0.f);
+  }
+}
+
+// inclusive scan over the block's threads (u128); returns this thread's exclusive prefix
+__device__ u128 block_exclusive_scan_u128(u128 x, u128* wtot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  u128 incl = x;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const u128 t = shfl_up_u128(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) wtot[wave] = incl;
+  __syncthreads();
+  u128 before = 0;
+  for (int i = 0; i < wave; ++i) before += wtot[i];
+  return before + incl - x;
+}
+
+template <bool VEC>
+__device__ void sample_node(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
   __shared__ int kid_s[64];
   __shared__ int nkid_s;
-  __shared__ uint64_t sp_s[kNodeWaves], sq_s[kNodeWaves], am_s[kNodeWaves];
-  __shared__ uint32_t nanp_s[kNodeWaves], nanq_s[kNodeWaves];
-  __shared__ u128 segsum_s[kNodeWaves];
+  __shared__ uint64_t sp_s[kWaves], sq_s[kWaves], am_s[kWaves];
+  __shared__ uint32_t nan_s[kWaves];
+  __shared__ u128 segsum_s[kWaves];
+  __shared__ u128 wtot_s[kWaves];
   __shared__ u128 W_s;
   __shared__ uint64_t gamma_s;
-  __shared__ int decide_s;  // -1 keep testing, -2 stop (resample), >= 0 accepted child
+  __shared__ int decide_s;  // -1 keep testing, >= 0 accepted child
   __shared__ int wstar_s;
   __shared__ u128 excl_s;
   __shared__ int bonus_s;
 
-  const int node = blockIdx.x;
-  const int b = node / max_T, u = node - b * max_T;
-  const int T = seq_T(T_b, b, max_T);
-  if (mode[b] != SPEC_MODE_SAMPLE || u >= T) return;
+  const int max_T = a.max_T, V = a.V;
+  const int node = b * max_T + u;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // children of u in index order (a parent outside [0, c) counts as the root)
@@ -192,7 +247,7 @@ __global__ void __launch_bounds__(kNodeThreads) verify_sample_node(VerifyWs w, c
       const int c = c0 + lane;
       bool kid = false;
       if (c < T) {
-        int pc = parents[size_t(b) * max_T + c];
+        int pc = a.parents[size_t(b) * max_T + c];
         if (pc < 0 || pc >= c) pc = 0;
         kid = (pc == u);
       }
@@ -204,47 +259,41 @@ __global__ void __launch_bounds__(kNodeThreads) verify_sample_node(VerifyWs w, c
   }
   __syncthreads();
   const int nkid = nkid_s;
-  const int qr = q_row ? q_row[size_t(b) * max_T + u] : -1;
-  const bool has_q = nkid > 0 && draft != nullptr && qr >= 0 && qr < R;
-  const float* prow = target + size_t(node) * V;
-  const float* qrow = has_q ? draft + (size_t(b) * R + qr) * V : nullptr;
-  const int lo = wave * seg, hi = min(V, lo + seg);
+  const int qr = a.q_row ? a.q_row[size_t(b) * max_T + u] : -1;
+  const bool has_q = nkid > 0 && a.draft != nullptr && qr >= 0 && qr < a.R;
+  const float* prow = a.target + size_t(node) * V;
+  const float* qrow = has_q ? a.draft + (size_t(b) * a.R + qr) * V : nullptr;
+  const int lo = wave * a.seg, hi = min(V, lo + a.seg);
 
   // pass 0: S_P, S_Q, argmax of P, NaN checks, per-wave sums of P
   uint64_t sp = 0, sq = 0, am = 0;
-  bool nanp = false, nanq = false;
-  for (int v = lo + lane; v < hi; v += kWave) {
-    const float x = prow[v];
-    nanp |= (x != x);
+  bool nan = false;
+  seg_for<VEC>(prow, qrow, lo, hi, lane, [&](int v, float x, float y) {
+    nan |= (x != x) | (y != y);
     const uint32_t P = fx(x);
     sp += P;
     const uint64_t k = (uint64_t(P) << 32) | uint64_t(0xffffffffu - uint32_t(v));
     am = k > am ? k : am;
-    if (has_q) {
-      const float y = qrow[v];
-      nanq |= (y != y);
-      sq += fx(y);
-    }
-  }
+    sq += fx(y);
+  });
   sp = wave_sum_u64(sp);
   sq = wave_sum_u64(sq);
   am = wave_max_u64(am);
-  const uint32_t np = wave_or_u32(nanp), nq = wave_or_u32(nanq);
+  const uint32_t nw = wave_or_u32(nan ? 1u : 0u);
   if (lane == 0) {
     sp_s[wave] = sp;
     sq_s[wave] = sq;
     am_s[wave] = am;
-    nanp_s[wave] = np;
-    nanq_s[wave] = nq;
+    nan_s[wave] = nw;
   }
   __syncthreads();
   uint64_t S_P = 0, S_Q = 0, AM = 0;
   uint32_t flags = 0;
-  for (int i = 0; i < kNodeWaves; ++i) {
+  for (int i = 0; i < kWaves; ++i) {
     S_P += sp_s[i];
     S_Q += sq_s[i];
     AM = am_s[i] > AM ? am_s[i] : AM;
-    if (nanp_s[i] || nanq_s[i]) flags |= SPEC_STATUS_NAN_INPUT;
+    if (nan_s[i]) flags |= SPEC_STATUS_NAN_INPUT;
   }
   const bool test = nkid > 0 && has_q && S_Q > 0;
   if (nkid > 0 && !test) flags |= SPEC_STATUS_ZERO_Q;
@@ -258,18 +307,18 @@ __global__ void __launch_bounds__(kNodeThreads) verify_sample_node(VerifyWs w, c
   bool tested = false;
   for (int ki = 0; test && ki < nkid; ++ki) {
     const int c = kid_s[ki];
-    const int t = tokens[size_t(b) * max_T + c];
+    const int t = a.tokens[size_t(b) * max_T + c];
     if (t < 0 || t >= V) continue;  // invalid draft token: never tested
     tested = true;
     if (tid == 0) {
       const uint32_t Pt = fx(prow[t]), Qt = fx(qrow[t]);
       const u128 Nt = residual(Pt, Qt, S_Q, gamma_s, false);
-      const U64x4 r = philox4x64_10(offset, uint64_t(b), uint64_t(c), 0, key0, key1);
+      const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(c), 0, a.key0, a.key1);
       const uint64_t m = (r.w[0] >> 40) + 1;  // r = m / 2^24 in (0, 1]
       bool accept = false;
       if (Nt > 0) {
-        const U192 lhs = mul_u128_u64(W_s, m * uint64_t(Qt));          // m Q_t W
-        const U192 rhs = shl_u192(mul_u128_u64(Nt, S_Q), 24);           // 2^24 N_t S_Q
+        const U192 lhs = mul_u128_u64(W_s, m * uint64_t(Qt));  // m Q_t W
+        const U192 rhs = shl_u192(mul_u128_u64(Nt, S_Q), 24);   // 2^24 N_t S_Q
         accept = le_u192(lhs, rhs);
       }
       if (accept) {
@@ -280,16 +329,16 @@ __global__ void __launch_bounds__(kNodeThreads) verify_sample_node(VerifyWs w, c
     }
     __syncthreads();
     if (decide_s >= 0) break;
-    // recompute the residual mass W and per-wave sums under the new gamma
+    // the residual mass W and per-wave sums under the new gamma
     const uint64_t gamma = gamma_s;
     u128 acc = 0;
-    for (int v = lo + lane; v < hi; v += kWave) acc += residual(fx(prow[v]), fx(qrow[v]), S_Q, gamma, false);
+    seg_for<VEC>(prow, qrow, lo, hi, lane, [&](int, float x, float y) { acc += residual(fx(x), fx(y), S_Q, gamma, false); });
     acc = wave_sum_u128(acc);
     if (lane == 0) segsum_s[wave] = acc;
     __syncthreads();
     if (tid == 0) {
       u128 W = 0;
-      for (int i = 0; i < kNodeWaves; ++i) W += segsum_s[i];
+      for (int i = 0; i < kWaves; ++i) W += segsum_s[i];
       W_s = W;
     }
     __syncthreads();
@@ -298,9 +347,9 @@ __global__ void __launch_bounds__(kNodeThreads) verify_sample_node(VerifyWs w, c
 
   if (decide_s >= 0) {
     if (tid == 0) {
-      w.acc_child[node] = decide_s;
-      w.bonus[node] = -1;
-      w.nflag[node] = flags;
+      st_agent(w.acc_child + node, decide_s);
+      st_agent(w.bonus + node, -1);
+      st_agent(w.nflag + node, flags);
     }
     return;
   }
@@ -318,13 +367,13 @@ __global__ void __launch_bounds__(kNodeThreads) verify_sample_node(VerifyWs w, c
   } else {
     // threshold: smallest v with 2^32 * prefix(v) > K W  <=>  prefix(v) > floor(K W / 2^32)
     if (tid == 0) {
-      const U64x4 r = philox4x64_10(offset, uint64_t(b), uint64_t(u), 0, key0, key1);
+      const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(u), 0, a.key0, a.key1);
       const uint64_t K = r.w[1] >> 32;
       const U192 kw = mul_u128_u64(W, K);
       const u128 tau = (u128(kw.hi) << 96) | (u128(kw.mid) << 32) | u128(kw.lo >> 32);
       u128 run = 0;
-      int ws = kNodeWaves - 1;
-      for (int i = 0; i < kNodeWaves; ++i) {
+      int ws = kWaves - 1;
+      for (int i = 0; i < kWaves; ++i) {
         if (run + segsum_s[i] > tau) {
           ws = i;
           break;
@@ -336,29 +385,26 @@ __global__ void __launch_bounds__(kNodeThreads) verify_sample_node(VerifyWs w, c
       bonus_s = -1;
     }
     __syncthreads();
-    if (wave == wstar_s) {
-      const u128 rem = excl_s;  // find first v in this segment with prefix_in_segment(v) > rem
-      u128 run = 0;
-      const int wlo = wstar_s * seg, whi = min(V, wlo + seg);
-      for (int c0 = wlo; c0 < whi; c0 += kWave) {
-        const int v = c0 + lane;
-        const u128 n = v < whi ? residual(fx(prow[v]), has_q ? fx(qrow[v]) : 0u, S_Q, gamma, plain) : u128(0);
-        // inclusive wave scan
-        u128 incl = n;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const u128 t = shfl_up_u128(incl, o);
-          if (lane >= o) incl += t;
-        }
-        const bool hit = run + incl > rem;
-        const uint64_t hm = __ballot(hit);
-        if (hm) {
-          if (lane == __ffsll((long long)hm) - 1) bonus_s = v;
+    // the whole block searches the chosen segment: each thread sums a contiguous range, a block scan
+    // gives every range's prefix, and the one range holding the crossing is walked element by element
+    const int wlo = wstar_s * a.seg, whi = min(V, wlo + a.seg);
+    const int E = (whi - wlo + kThreads - 1) / kThreads;
+    const int e0 = min(whi, wlo + tid * E), e1 = min(whi, e0 + E);
+    auto resid = [&](int v) {
+      return residual(fx(prow[v]), has_q ? fx(qrow[v]) : 0u, S_Q, gamma, plain);
+    };
+    u128 tsum = 0;
+    for (int v = e0; v < e1; ++v) tsum += resid(v);
+    const u128 ex = block_exclusive_scan_u128(tsum, wtot_s);
+    const u128 rem = excl_s;
+    if (tsum > 0 && ex <= rem && rem < ex + tsum) {
+      u128 run = ex;
+      for (int v = e0; v < e1; ++v) {
+        run += resid(v);
+        if (run > rem) {
+          bonus_s = v;
           break;
         }
-        const uint64_t tot_lo = __shfl(uint64_t(incl), kWave - 1, kWave);
-        const uint64_t tot_hi = __shfl(uint64_t(incl >> 64), kWave - 1, kWave);
-        run += (u128(tot_hi) << 64) | tot_lo;  // this chunk's total (lane 63's inclusive sum)
       }
     }
   }
@@ -366,57 +412,57 @@ __global__ void __launch_bounds__(kNodeThreads) verify_sample_node(VerifyWs w, c
   if (tid == 0) {
     int bn = bonus_s;
     if (bn < 0) bn = int(0xffffffffu - uint32_t(AM));  // unreachable with exact sums; keeps the output defined
-    w.acc_child[node] = -1;
-    w.bonus[node] = bn;
-    w.nflag[node] = flags;
+    st_agent(w.acc_child + node, -1);
+    st_agent(w.bonus + node, bn);
+    st_agent(w.nflag + node, flags);
   }
 }
 
 // ------------------------------------------------------------------ walk
-__global__ void __launch_bounds__(kWalkThreads) verify_walk(VerifyWs w, const int32_t* tokens, const int32_t* parents,
-                                                             const int32_t* T_b, const int8_t* mode, int max_T, int V,
-                                                             int32_t* accept_len, int32_t* accept_nodes,
-                                                             int32_t* out_tokens, uint32_t* status) {
-  __shared__ int par_s[65], a_s[65], jmp_s[65], dep_s[65], ok_s[65];
-  __shared__ uint32_t flag_red[kWalkThreads / kWave];
-  __shared__ uint32_t best_red[kWalkThreads / kWave];
-  __shared__ int path_s[65];
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = seq_T(T_b, b, max_T);
-  const bool greedy = mode[b] != SPEC_MODE_SAMPLE;
+// Runs in the last block of sequence b to finish; reads the other blocks' results with agent-scope loads.
+__device__ void walk(const VerifyWs& w, const VerifyArgs& a, int b) {
+  __shared__ int par_s[65], a_s[65], jmp_s[65], dep_s[65], ok_s[65], path_s[65];
+  __shared__ uint32_t st_s, best_s;
+  __shared__ int n_s, bonus_s;
+  const int tid = threadIdx.x, max_T = a.max_T, V = a.V;
+  const int T = seq_T(a.T_b, b, max_T);
+  const bool greedy = a.mode[b] != SPEC_MODE_SAMPLE;
   const size_t base = size_t(b) * max_T;
-  uint32_t f = 0;
+  if (tid == 0) {
+    st_s = 0;
+    best_s = 0;
+  }
+  __syncthreads();
   if (tid < T) {
+    uint32_t f = 0;
     int par = -1;
     if (tid > 0) {
-      par = parents[base + tid];
+      par = a.parents[base + tid];
       if (par < 0 || par >= tid) {
         par = 0;
         f |= SPEC_STATUS_INVALID_PARENT;
       }
-      const int t = tokens[base + tid];
+      const int t = a.tokens[base + tid];
       if (t < 0 || t >= V) f |= SPEC_STATUS_INVALID_TOKEN;
     }
     par_s[tid] = par;
     if (greedy) {
-      const uint64_t k = w.keys[base + tid];
+      const uint64_t k = ld_agent(w.keys + base + tid);
       a_s[tid] = int(0xffffffffu - uint32_t(k));
-      if (w.rowflag[base + tid]) f |= SPEC_STATUS_NAN_INPUT;
-      w.keys[base + tid] = 0;  // leave the workspace zeroed
-      w.rowflag[base + tid] = 0;
+      if (ld_agent(w.rowflag + base + tid)) f |= SPEC_STATUS_NAN_INPUT;
+      st_agent(w.keys + base + tid, uint64_t(0));  // leave the workspace zeroed
+      st_agent(w.rowflag + base + tid, 0u);
     } else {
-      f |= w.nflag[base + tid] & SPEC_STATUS_NAN_INPUT;
+      f |= ld_agent(w.nflag + base + tid) & SPEC_STATUS_NAN_INPUT;
     }
+    if (f) atomicOr(&st_s, f);
   }
-  f = wave_or_u32(f);
-  if (lane == 0) flag_red[wave] = f;
   __syncthreads();
-  uint32_t st = flag_red[0] | flag_red[1];
 
   int e = 0;
   if (greedy) {
     if (tid < T) {
-      const int t = tid > 0 ? tokens[base + tid] : 0;
+      const int t = tid > 0 ? a.tokens[base + tid] : 0;
       const bool good = tid == 0 || (t >= 0 && t < V && t == a_s[par_s[tid]]);
       ok_s[tid] = good;
       jmp_s[tid] = tid > 0 ? par_s[tid] : 0;
@@ -440,30 +486,24 @@ __global__ void __launch_bounds__(kWalkThreads) verify_walk(VerifyWs w, const in
       __syncthreads();
     }
     // deepest valid node, ties -> smallest index
-    uint32_t key = 0;
-    if (tid < T && ok_s[tid]) key = (uint32_t(dep_s[tid] + 1) << 8) | uint32_t(255 - tid);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const uint32_t x = __shfl_xor(key, o, kWave);
-      key = x > key ? x : key;
-    }
-    if (lane == 0) best_red[wave] = key;
+    if (tid < T && ok_s[tid]) atomicMax(&best_s, (uint32_t(dep_s[tid] + 1) << 8) | uint32_t(255 - tid));
     __syncthreads();
-    const uint32_t kb = best_red[0] > best_red[1] ? best_red[0] : best_red[1];
-    e = 255 - int(kb & 255u);
+    e = 255 - int(best_s & 255u);
   } else {
     if (tid == 0) {
       int uu = 0, n = 0;
+      uint32_t sf = 0;
       path_s[0] = 0;
       while (true) {
-        st |= w.nflag[base + uu] & (SPEC_STATUS_ZERO_Q | SPEC_STATUS_ZERO_RESIDUAL);
-        const int c = w.acc_child[base + uu];
+        sf |= ld_agent(w.nflag + base + uu) & (SPEC_STATUS_ZERO_Q | SPEC_STATUS_ZERO_RESIDUAL);
+        const int c = ld_agent(w.acc_child + base + uu);
         if (c <= uu || c >= T || n >= 64) break;
         uu = c;
         path_s[++n] = uu;
       }
+      st_s |= sf;
       dep_s[0] = n;  // reuse as the path length
-      a_s[0] = w.bonus[base + uu];
+      a_s[0] = ld_agent(w.bonus + base + uu);
     }
     __syncthreads();
   }
@@ -482,13 +522,38 @@ __global__ void __launch_bounds__(kWalkThreads) verify_walk(VerifyWs w, const in
       n = dep_s[0];
       bonus = a_s[0];
     }
-    accept_len[b] = n;
-    status[b] = st;
-    for (int k = 0; k < max_T; ++k) {
-      accept_nodes[base + k] = k <= n ? path_s[k] : -1;
-      out_tokens[base + k] = k < n ? tokens[base + path_s[k + 1]] : (k == n ? bonus : -1);
-    }
+    a.accept_len[b] = n;
+    a.status[b] = st_s;
+    n_s = n;
+    bonus_s = bonus;
   }
+  __syncthreads();
+  const int n = n_s;
+  for (int k = tid; k < max_T; k += kThreads) {
+    a.accept_nodes[base + k] = k <= n ? path_s[k] : -1;
+    a.out_tokens[base + k] = k < n ? a.tokens[base + path_s[k + 1]] : (k == n ? bonus_s : -1);
+  }
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads) verify_kernel(VerifyWs w, VerifyArgs a) {
+  __shared__ int last_s;
+  const int unit = blockIdx.x, row = blockIdx.y;
+  const int b = row / a.max_T, u = row - b * a.max_T;
+  const int T = seq_T(a.T_b, b, a.max_T);
+  const bool greedy = a.mode[b] != SPEC_MODE_SAMPLE;
+  if (u < T) {
+    if (greedy && unit < a.n_slices) greedy_slice<VEC>(w, a, row, unit * a.slice);
+    if (!greedy && unit == a.n_slices) sample_node<VEC>(w, a, b, u, T);
+  }
+  // every block of the grid counts toward its sequence; the last one to arrive walks the tree
+  wait_global_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) last_s = ticket_add(w.tickets + b) == uint32_t((a.n_slices + 1) * a.max_T - 1);
+  __syncthreads();
+  if (!last_s) return;
+  if (threadIdx.x == 0) ticket_reset(w.tickets + b);  // leave the workspace ready for the next call
+  walk(w, a, b);
 }
 
 }  // namespace
@@ -515,28 +580,44 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
   if (draft_probs && (R < 1 || !q_row)) return fail(SPEC_E_INVAL, "spec_tree_verify: draft_probs needs R >= 1 and q_row");
   if (!target || !tokens || !parents || !mode || !accept_len || !accept_nodes || !out_tokens || !status)
     return fail(SPEC_E_INVAL, "spec_tree_verify: null pointer");
-  if ((long long)B * max_T > 65535LL * 64) return fail(SPEC_E_UNSUPPORTED, "spec_tree_verify: B*max_T too large");
+  if ((long long)B * max_T > 65535LL) return fail(SPEC_E_UNSUPPORTED, "spec_tree_verify: B*max_T=%lld > 65535",
+                                                  (long long)B * max_T);
   size_t need = 0;
   VerifyWs w = carve(ws, B, max_T, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_verify: workspace %zu < %zu bytes", ws_bytes, need);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   const int rows = B * max_T;
-  // greedy scan: slices sized so that the launch has >= ~1k blocks
-  long long sl = ((long long)V * rows + 1023) / 1024;
-  sl = (sl + 1023) / 1024 * 1024;
-  if (sl < 1024) sl = 1024;
-  if (sl > 16384) sl = 16384;
-  const int slice = int(sl);
-  const dim3 sgrid((V + slice - 1) / slice, rows);
-  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target) & 15) == 0);
+  // greedy slices: whole multiples of one block pass (4 K elements), about 512 slice blocks per launch
+  long long sl = ((long long)V * rows + 511) / 512;
+  sl = (sl + 4095) / 4096 * 4096;
+  if (sl > 65536) sl = 65536;
+  VerifyArgs a;
+  a.target = target;
+  a.draft = draft_probs;
+  a.q_row = q_row;
+  a.tokens = tokens;
+  a.parents = parents;
+  a.T_b = T_b;
+  a.mode = mode;
+  a.key0 = philox_key0;
+  a.key1 = philox_key1;
+  a.offset = philox_offset;
+  a.max_T = max_T;
+  a.R = draft_probs ? R : 0;
+  a.V = V;
+  a.slice = int(sl);
+  a.n_slices = int((V + sl - 1) / sl);
+  a.seg = (V + kWaves - 1) / kWaves;
+  a.seg = (a.seg + 3) / 4 * 4;  // segment bounds on 16-byte boundaries for the vector path
+  a.accept_len = accept_len;
+  a.accept_nodes = accept_nodes;
+  a.out_tokens = out_tokens;
+  a.status = status;
+  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target) | reinterpret_cast<uintptr_t>(draft_probs)) & 15) == 0;
+  const dim3 grid(a.n_slices + 1, rows);
+  hipStream_t st = static_cast<hipStream_t>(stream);
   if (vec)
-    hipLaunchKernelGGL(verify_greedy_scan<true>, sgrid, dim3(kScanThreads), 0, st, w, target, T_b, mode, max_T, V, slice);
+    hipLaunchKernelGGL(verify_kernel<true>, grid, dim3(kThreads), 0, st, w, a);
   else
-    hipLaunchKernelGGL(verify_greedy_scan<false>, sgrid, dim3(kScanThreads), 0, st, w, target, T_b, mode, max_T, V, slice);
-  const int seg = (V + kNodeWaves - 1) / kNodeWaves;
-  hipLaunchKernelGGL(verify_sample_node, dim3(rows), dim3(kNodeThreads), 0, st, w, target, draft_probs, q_row, tokens,
-                     parents, T_b, mode, philox_key0, philox_key1, philox_offset, max_T, draft_probs ? R : 0, V, seg);
-  hipLaunchKernelGGL(verify_walk, dim3(B), dim3(kWalkThreads), 0, st, w, tokens, parents, T_b, mode, max_T, V,
-                     accept_len, accept_nodes, out_tokens, status);
+    hipLaunchKernelGGL(verify_kernel<false>, grid, dim3(kThreads), 0, st, w, a);
   return check_launch("spec_tree_verify");
 }
