@@ -9,12 +9,12 @@
 //
 // Kernels:
 //   build_step_kernel    one launch per step; block (slice, frontier slot f,
-//                        sequence) takes the top-k of a slice of row f; the last
-//                        slice of a row (atomic ticket) merges the slices; step 1
+//                        sequence) takes the top-k of a slice of row f and
+//                        publishes it; the last block of the sequence's step
+//                        (atomic ticket) merges every row's slices in LDS; step 1
 //                        seeds the pool and frontier from the root row; at step
-//                        d >= 2 the row's k children join the pool and the last
-//                        row of a sequence (second ticket) ranks the k*k children
-//                        and writes the next frontier.
+//                        d >= 2 the k rows' children join the pool, the k*k
+//                        children are ranked and the next frontier is written.
 //   build_finish_kernel  one block per sequence: rank the whole pool, keep the
 //                        N best, number them in pool order, emit parents /
 //                        depth / ancestry words / q_row.
@@ -30,7 +30,7 @@ namespace {
 constexpr int kMaxTopk = 8;
 constexpr int kMaxDepth = 16;
 constexpr int kRowThreads = 256;
-constexpr int kMaxSlices = 32;  // blocks per draft row
+constexpr int kMaxSlices = 64;  // blocks per draft row (n_slices * max_topk <= 64 candidates per row)
 constexpr int kFinishThreads = 256;
 
 struct BuildWs {
@@ -40,9 +40,8 @@ struct BuildWs {
   int32_t* fslot;  // [B, P] frontier slot held at its own step, -1 if never frontier
   double* score;   // [B, P]
   int32_t* frontier;  // [B, max_topk] pool indices, rank order
-  uint32_t* ticket;   // [B] frontier-selection tickets
+  uint32_t* ticket;   // [B] blocks of the sequence's step that have finished
   uint64_t* cand;     // [B, max_topk, kMaxSlices, kMaxTopk] per-slice top-k keys
-  uint32_t* row_ticket;  // [B, max_topk]
 };
 
 size_t pool_cap(int max_topk, int max_depth) {
@@ -67,7 +66,6 @@ BuildWs carve(void* ws, int B, int max_topk, int max_depth, size_t* total) {
   w.frontier = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * max_topk));
   w.ticket = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B));
   w.cand = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * B * max_topk * kMaxSlices * kMaxTopk));
-  w.row_ticket = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B * max_topk));
   *total = off;
   return w;
 }
@@ -144,23 +142,28 @@ __device__ void block_slice_topk(const float* row, int lo, int hi, int k, uint64
 }
 
 // One kernel for every step. Block (slice x, frontier slot f, sequence b) reduces a slice of
-// step-`step` draft row f to its top-k keys; the last slice of a row to finish merges the
-// slices (row ticket); at step 1 that row is the root's and fills the pool and the frontier,
-// at step >= 2 the row's k children join the pool and the last row of the sequence to finish
-// (sequence ticket) ranks the k*k children and writes the next frontier.
+// step-`step` draft row f to its top-k keys and publishes them; the last block of the sequence's
+// step to finish (ticket) merges, in LDS, the slices of every row: at step 1 the root row fills the
+// pool and the frontier; at step >= 2 the k rows' k children join the pool (score = parent score +
+// log-prob, an fp64 left fold), the k*k children are ranked and the best k form the next frontier.
 template <bool VEC>
 __global__ void __launch_bounds__(kRowThreads) build_step_kernel(BuildWs w, int P, int step, const float* draft,
                                                                   int64_t seq_stride, const int32_t* topk,
                                                                   const int32_t* depth, int max_topk, int max_depth,
                                                                   int V, int slice, int32_t* frontier_tokens) {
+  constexpr int kCand = 64;  // candidates per row (n_slices * k)
   __shared__ uint64_t keys[kMaxSlices * kMaxTopk];
-  __shared__ uint64_t top[kMaxTopk];
+  __shared__ uint64_t ck[kMaxTopk * kCand];     // [row][slice * k + j]
+  __shared__ uint64_t top[kMaxTopk * kMaxTopk];  // [row][rank]
+  __shared__ double csc[kMaxTopk * kMaxTopk];    // child scores [row * k + c]
+  __shared__ int cpar[kMaxTopk];
   __shared__ int last;
   const int x = blockIdx.x, f = blockIdx.y, b = blockIdx.z;
   const int n_slices = gridDim.x;
   const int k = clamp_i(topk[b], 1, max_topk);
   const int D = clamp_i(depth[b], 1, max_depth);
-  if (step > D || f >= (step == 1 ? 1 : k)) return;
+  const int rows = step == 1 ? 1 : k;
+  if (step > D || f >= rows) return;
   const float* row = draft + b * seq_stride + int64_t(f) * V;
   const int lo = x * slice, hi = min(V, lo + slice);
   uint64_t* cand = w.cand + ((size_t(b) * max_topk + f) * kMaxSlices + x) * kMaxTopk;
@@ -168,23 +171,33 @@ __global__ void __launch_bounds__(kRowThreads) build_step_kernel(BuildWs w, int 
   if (threadIdx.x < k) st_agent(cand + threadIdx.x, keys[threadIdx.x]);
   wait_global_stores();
   __syncthreads();
-  uint32_t* rt = w.row_ticket + size_t(b) * max_topk + f;
-  if (threadIdx.x == 0) last = (ticket_add(rt) == uint32_t(n_slices - 1));
+  if (threadIdx.x == 0) last = (ticket_add(w.ticket + b) == uint32_t(n_slices * rows - 1));
   __syncthreads();
   if (!last) return;
-  if (threadIdx.x == 0) ticket_reset(rt);
-  // merge the slices' candidates: rank = number of larger keys (keys are unique; 0 = empty)
-  const uint64_t* rowc = w.cand + (size_t(b) * max_topk + f) * kMaxSlices * kMaxTopk;
-  const int nc = n_slices * kMaxTopk;
-  for (int i = threadIdx.x; i < nc; i += kRowThreads) keys[i] = ((i % kMaxTopk) < k) ? ld_agent(rowc + i) : 0ull;
-  __syncthreads();
-  for (int i = threadIdx.x; i < nc; i += kRowThreads) {
-    const uint64_t ki = keys[i];
-    if (ki == 0) continue;
-    int r = 0;
-    for (int j = 0; j < nc; ++j) r += keys[j] > ki;
-    if (r < k) top[r] = ki;
+  if (threadIdx.x == 0) ticket_reset(w.ticket + b);  // leave the workspace ready for the next step
+
+  // every row's candidates (0 = empty), and at step >= 2 the rows' parents and their scores
+  const int nc = n_slices * k;
+  for (int i = threadIdx.x; i < rows * nc; i += kRowThreads) {
+    const int r = i / nc, j = i - r * nc;
+    ck[r * kCand + j] = ld_agent(w.cand + ((size_t(b) * max_topk + r) * kMaxSlices + j / k) * kMaxTopk + j % k);
   }
+  const int base = k + (step - 2) * k * k;  // pool index of this step's first child (step >= 2)
+  double psc = 0.0;
+  if (step >= 2 && threadIdx.x < k) {
+    cpar[threadIdx.x] = w.frontier[b * max_topk + threadIdx.x];
+  }
+  __syncthreads();
+  // per row top-k: rank = number of larger keys (keys of one row are unique; 0 = empty)
+  for (int i = threadIdx.x; i < rows * nc; i += kRowThreads) {
+    const int r = i / nc;
+    const uint64_t ki = ck[r * kCand + (i - r * nc)];
+    if (ki == 0) continue;
+    int rank = 0;
+    for (int j = 0; j < nc; ++j) rank += ck[r * kCand + j] > ki;
+    if (rank < k) top[r * kMaxTopk + rank] = ki;
+  }
+  if (step >= 2 && threadIdx.x < k * k) psc = w.score[size_t(b) * P + cpar[threadIdx.x / k]];
   __syncthreads();
 
   if (step == 1) {
@@ -206,37 +219,30 @@ __global__ void __launch_bounds__(kRowThreads) build_step_kernel(BuildWs w, int 
     return;
   }
 
-  const int parent = w.frontier[b * max_topk + f];
-  const int base = k + (step - 2) * k * k;
-  if (threadIdx.x < k) {
-    const int c = threadIdx.x;
-    const size_t e = size_t(b) * P + base + f * k + c;
-    st_agent(w.tok + e, key_token(top[c]));
-    st_agent(w.par + e, parent);
-    st_agent(w.depth + e, step);
-    st_agent(w.fslot + e, -1);
-    st_agent(w.score + e, w.score[size_t(b) * P + parent] + double(key_value(top[c])));
-  }
-  wait_global_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) last = (ticket_add(w.ticket + b) == uint32_t(k - 1));
-  __syncthreads();
-  if (!last) return;
-  if (threadIdx.x == 0) ticket_reset(w.ticket + b);
-  // rank the k*k candidates of this step: rank(c) = #candidates that beat c
+  // children: row r's c-th best token becomes pool entry base + r * k + c
   const int n = k * k;
   if (threadIdx.x < n) {
+    const int r = threadIdx.x / k, c = threadIdx.x - r * k;
+    const uint64_t key = top[r * kMaxTopk + c];
+    const size_t e = size_t(b) * P + base + threadIdx.x;
+    const double sc = psc + double(key_value(key));
+    csc[threadIdx.x] = sc;
+    w.tok[e] = key_token(key);
+    w.par[e] = cpar[r];
+    w.depth[e] = step;
+    w.score[e] = sc;
+  }
+  __syncthreads();
+  // rank the k*k children: rank(c) = #children that beat c (higher score, ties -> smaller pool index)
+  if (threadIdx.x < n) {
     const int c = threadIdx.x;
-    const double sc = ld_agent(w.score + size_t(b) * P + base + c);
+    const double sc = csc[c];
     int rank = 0;
-    for (int o = 0; o < n; ++o) {
-      const double so = ld_agent(w.score + size_t(b) * P + base + o);
-      rank += (so > sc) || (so == sc && o < c);
-    }
+    for (int o = 0; o < n; ++o) rank += (csc[o] > sc) || (csc[o] == sc && o < c);
+    w.fslot[size_t(b) * P + base + c] = rank < k ? rank : -1;
     if (rank < k) {
       w.frontier[b * max_topk + rank] = base + c;
-      st_agent(w.fslot + size_t(b) * P + base + c, rank);
-      frontier_tokens[b * max_topk + rank] = ld_agent(w.tok + size_t(b) * P + base + c);
+      frontier_tokens[b * max_topk + rank] = key_token(top[(c / k) * kMaxTopk + c % k]);
     }
   }
   if (threadIdx.x >= k && threadIdx.x < max_topk) frontier_tokens[b * max_topk + threadIdx.x] = -1;
@@ -248,8 +254,10 @@ __global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w,
                                                                        int max_depth, int max_T, int32_t* tokens,
                                                                        int32_t* parents, int32_t* depth_out,
                                                                        uint64_t* anc_mask, int32_t* q_row) {
-  __shared__ double sc[kMaxTopk + (kMaxDepth - 1) * kMaxTopk * kMaxTopk];
-  __shared__ int rank_s[kMaxTopk + (kMaxDepth - 1) * kMaxTopk * kMaxTopk];
+  constexpr int kPool = kMaxTopk + (kMaxDepth - 1) * kMaxTopk * kMaxTopk;
+  __shared__ double sc[kPool];
+  __shared__ int rank_s[kPool];  // pool rank, then node number (0 = not kept)
+  __shared__ int par_e[kPool], dep_e[kPool], fs_e[kPool], tok_e[kPool];
   __shared__ int pool_of[65];
   __shared__ int node_par[65];
   __shared__ uint64_t anc_s[65];
@@ -262,7 +270,14 @@ __global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w,
   const int T = N + 1;
   const size_t row = size_t(b) * P;
 
-  for (int e = tid; e < pool; e += blockDim.x) sc[e] = w.score[row + e];
+  // one round trip: every field of the pool
+  for (int e = tid; e < pool; e += blockDim.x) {
+    sc[e] = w.score[row + e];
+    par_e[e] = w.par[row + e];
+    dep_e[e] = w.depth[row + e];
+    fs_e[e] = w.fslot[row + e];
+    tok_e[e] = w.tok[row + e];
+  }
   __syncthreads();
   for (int e = tid; e < pool; e += blockDim.x) {
     const double s = sc[e];
@@ -283,17 +298,17 @@ __global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w,
     }
   }
   __syncthreads();
+  if (tid >= 1 && tid < T) rank_s[pool_of[tid]] = -tid;  // kept entry -> -(node number)
+  __syncthreads();
   // parents as node numbers: the parent entry of a kept entry is kept (scores never increase
-  // down a path and the parent has the smaller pool index), so it is among pool_of[1..n-1]
+  // down a path and the parent has the smaller pool index), so it carries a node number
   if (tid < T) {
     const int n = tid;
     int par_node = -1;
     if (n > 0) {
-      const int pe = w.par[row + pool_of[n]];
+      const int pe = par_e[pool_of[n]];
       par_node = 0;
-      if (pe >= 0)
-        for (int m2 = 1; m2 < n; ++m2)
-          if (pool_of[m2] == pe) par_node = m2;
+      if (pe >= 0 && rank_s[pe] < 0) par_node = -rank_s[pe];
     }
     node_par[n] = par_node;
     jump_s[n] = n > 0 ? par_node : 0;
@@ -325,10 +340,10 @@ __global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w,
       anc_mask[o] = 0;
       q_row[o] = 0;
     } else if (n < T) {
-      const size_t e = row + pool_of[n];
-      const int d = w.depth[e];
-      const int fs = w.fslot[e];
-      tokens[o] = w.tok[e];
+      const int e = pool_of[n];
+      const int d = dep_e[e];
+      const int fs = fs_e[e];
+      tokens[o] = tok_e[e];
       parents[o] = node_par[n];
       depth_out[o] = d;
       anc_mask[o] = anc_s[n];
@@ -380,10 +395,12 @@ extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step,
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_step: workspace %zu < %zu bytes", ws_bytes, need);
   const int P = int(pool_cap(max_topk, max_depth));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // slices of >= 1024 elements, at most kMaxSlices per row
-  int slice = (V + kMaxSlices - 1) / kMaxSlices;
+  // slices of >= 1024 elements; at most 64 / max_topk slices per row, so a row has <= 64 candidates
+  const int max_sl = std::max(1, 64 / max_topk);
+  int n_slices = std::min((V + 1023) / 1024, max_sl);
+  int slice = (V + n_slices - 1) / n_slices;
   slice = (slice + 1023) / 1024 * 1024;
-  const int n_slices = (V + slice - 1) / slice;
+  n_slices = (V + slice - 1) / slice;
   const dim3 grid(n_slices, step == 1 ? 1 : max_topk, B);
   const bool vec = (V % 4 == 0) && (seq_stride % 4 == 0) && ((reinterpret_cast<uintptr_t>(draft_logprobs) & 15) == 0);
   if (vec)
