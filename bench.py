@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+PMC_COPY_BYTES = 256 << 20  # calibration copy of --profile-kernels
 BF16_DENSE_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
@@ -65,6 +66,31 @@ def algorithmic_work(w, host):
     build_rows = int(sum(1 + (int(w.depth[b]) - 1) * int(w.topk[b]) for b in range(B)))
     build_bytes = build_rows * V * 4
     return dict(attn_bytes=attn_bytes, attn_flops=attn_flops, verify_bytes=verify_bytes, build_bytes=build_bytes)
+
+
+def pmc_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 --pmc summary of this workload, or
+    None when there is none or the kernel source changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"tree_attn_kernel_{workload}_pmc.md")
+    src = os.path.join(ROOT, "tree_attention_verification_03_amd", "csrc", "tree_attention.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- `"):
+                k, _, v = line[3:].partition("`:")
+                fields[k.strip()] = v.strip().strip("`")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest:
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def time_graphs(graphs, n, torch):
@@ -143,6 +169,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--details", default=None, help="write per-stage details as JSON to this path")
+    ap.add_argument("--profile-kernels", type=int, default=0, metavar="N",
+                    help="profiling mode (run under rocprofv3): N eager attention calls over the replicas, then one "
+                         "256 MiB device-to-device copy whose counters calibrate FETCH_SIZE / WRITE_SIZE; no timing")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -181,6 +210,17 @@ def main():
         o, d = st.o, st.dw
         return lambda: ops.spec_tree_attention(d.q, d.k_pages, d.v_pages, d.page_table, d.prefix_lens, o.parents,
                                                d.T_b, d.w.sm_scale, o.attn_out, o.lse, None, st.ws_attn)
+
+    if args.profile_kernels:
+        for i in range(args.profile_kernels):
+            attn_only(steps[i % R])()
+        torch.cuda.synchronize()
+        src = torch.empty(PMC_COPY_BYTES, dtype=torch.uint8, device=dw0.device)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        eprint(f"[bench] profile mode: {args.profile_kernels} attention calls, one {PMC_COPY_BYTES >> 20} MiB copy")
+        return
 
     if args.eager:
         full_fns = [lambda st=st: st.run(compact=compact) for st in steps]
@@ -240,12 +280,16 @@ def main():
     t_mfma = work["attn_flops"] / (BF16_DENSE_TFLOPS * 1e12)
     if t_hbm >= t_mfma:
         roof = dict(bound="hbm", achieved=round(attn_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(attn_gbs / HBM_PEAK_GBS, 4), traffic=None)
+                    frac=round(attn_gbs / HBM_PEAK_GBS, 4), traffic=pmc_traffic(spec.name))
     else:
         roof = dict(bound="mfma", achieved=round(attn_tfs, 2), peak=BF16_DENSE_TFLOPS, unit="TFLOP/s",
-                    frac=round(attn_tfs / BF16_DENSE_TFLOPS, 4), traffic=None)
-    roof.update(kernel="tree_attn_kernel", bytes_per_launch=work["attn_bytes"], flops_per_launch=work["attn_flops"],
-                avg_launch_us=round(t_attn * 1e6, 3), timing="HIP events around a graph of back-to-back launches, one per replica")
+                    frac=round(attn_tfs / BF16_DENSE_TFLOPS, 4), traffic=pmc_traffic(spec.name))
+    roof.update(kernel="tree_attn_kernel (+ tree_attn_combine when the prefix is split)",
+                bytes_per_launch=work["attn_bytes"], flops_per_launch=work["attn_flops"],
+                avg_launch_us=round(t_attn * 1e6, 3),
+                timing="HIP events around a graph of back-to-back spec_tree_attention calls, one per replica; a "
+                       "call is the main kernel plus, for split prefixes, the combine kernel",
+                traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)")
 
     line = {
         "metric": "tree-attn+verify draft tokens/s per layer; achieved HBM GB/s vs MI355X peak",
