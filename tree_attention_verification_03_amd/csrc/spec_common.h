@@ -34,25 +34,73 @@ __device__ __forceinline__ uint64_t f64_order_key(double f) {
 }
 
 // ---------------------------------------------------------------- wave reductions
+// All-reduce butterflies on VALU data movement only (no LDS round trips): DPP quad permutes pair lanes
+// l ^ 1 and l ^ 2, row_half_mirror pairs the two quads of each 8 lanes, row_mirror the two halves of
+// each 16, and the gfx950 row swaps exchange 16-lane rows and 32-lane halves (every lane finds its
+// partner's value in one of the two swap results). Associative, commutative ops only.
+namespace dpp {
+constexpr int kXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141; // row_half_mirror
+constexpr int kMirror = 0x140;     // row_mirror
+}  // namespace dpp
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), CTRL, 0xf, 0xf, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return (uint64_t(dpp_u32<CTRL>(uint32_t(v >> 32))) << 32) | dpp_u32<CTRL>(uint32_t(v));
+}
+
+// op(value, partner value) over the xor-16 and xor-32 partners via the row swaps
+template <typename Op>
+__device__ __forceinline__ uint32_t swap_reduce_u32(uint32_t v, Op op) {
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(uint32_t(a[0]), uint32_t(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(uint32_t(c[0]), uint32_t(c[1]));
+}
+
+template <typename Op>
+__device__ __forceinline__ uint64_t swap_reduce_u64(uint64_t v, Op op) {
+  uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
+  const auto al = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto ah = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  v = op((uint64_t(uint32_t(ah[0])) << 32) | uint32_t(al[0]), (uint64_t(uint32_t(ah[1])) << 32) | uint32_t(al[1]));
+  lo = uint32_t(v);
+  hi = uint32_t(v >> 32);
+  const auto cl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto ch = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return op((uint64_t(uint32_t(ch[0])) << 32) | uint32_t(cl[0]), (uint64_t(uint32_t(ch[1])) << 32) | uint32_t(cl[1]));
+}
+
+template <typename Op>
+__device__ __forceinline__ uint64_t wave_reduce_u64(uint64_t v, Op op) {
+  v = op(v, dpp_u64<dpp::kXor1>(v));
+  v = op(v, dpp_u64<dpp::kXor2>(v));
+  v = op(v, dpp_u64<dpp::kHalfMirror>(v));
+  v = op(v, dpp_u64<dpp::kMirror>(v));
+  return swap_reduce_u64(v, op);
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
+  return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a > b ? a : b; });
 }
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce_u64(v, [](uint64_t a, uint64_t b) { return a + b; });
 }
 
 __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v |= __shfl_xor(v, o, kWave);
-  return v;
+  auto op = [](uint32_t a, uint32_t b) { return a | b; };
+  v = op(v, dpp_u32<dpp::kXor1>(v));
+  v = op(v, dpp_u32<dpp::kXor2>(v));
+  v = op(v, dpp_u32<dpp::kHalfMirror>(v));
+  v = op(v, dpp_u32<dpp::kMirror>(v));
+  return swap_reduce_u32(v, op);
 }
 
 // ---------------------------------------------------------------- Philox4x64-10

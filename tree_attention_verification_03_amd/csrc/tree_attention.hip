@@ -583,9 +583,10 @@ AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_p
     const long long c = atoll(env);
     if (c >= kTile) chunk = c;
   }
+  // any chunk length works (every lane looks up its own key's page); an unrounded chunk keeps a
+  // sequence's items equal, so no XCD is left with all the short tails
   chunk = std::max<long long>(chunk, 4 * kTile);
   chunk = std::min<long long>(chunk, kMaxChunk);
-  chunk = (chunk + kTile - 1) / kTile * kTile;
   pl.chunk = int(chunk);
   pl.n_splits = int((slots + chunk - 1) / chunk);
   pl.npg = int((chunk - 1) / page) + 2;  // a chunk may straddle one page more than it covers

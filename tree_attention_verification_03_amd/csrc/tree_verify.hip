@@ -170,10 +170,36 @@ __device__ __forceinline__ u128 shfl_up_u128(u128 x, int o) {
   return (u128(hi) << 64) | lo;
 }
 
-__device__ __forceinline__ u128 wave_sum_u128(u128 x) {
+template <int CTRL>
+__device__ __forceinline__ u128 dpp_u128(u128 v) {
+  return (u128(dpp_u64<CTRL>(uint64_t(v >> 64))) << 64) | dpp_u64<CTRL>(uint64_t(v));
+}
+
+// the two row-swap results of a u128 (every lane's partner value is in one of them)
+template <bool HALVES>
+__device__ __forceinline__ void swap_u128(u128 v, u128& r0, u128& r1) {
+  uint32_t a[4], b[4];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += shfl_xor_u128(x, o);
-  return x;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = uint32_t(v >> (32 * i));
+    const auto r = HALVES ? __builtin_amdgcn_permlane32_swap(x, x, false, false) : __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    a[i] = uint32_t(r[0]);
+    b[i] = uint32_t(r[1]);
+  }
+  r0 = (u128(a[3]) << 96) | (u128(a[2]) << 64) | (u128(a[1]) << 32) | a[0];
+  r1 = (u128(b[3]) << 96) | (u128(b[2]) << 64) | (u128(b[1]) << 32) | b[0];
+}
+
+__device__ __forceinline__ u128 wave_sum_u128(u128 x) {
+  x += dpp_u128<dpp::kXor1>(x);
+  x += dpp_u128<dpp::kXor2>(x);
+  x += dpp_u128<dpp::kHalfMirror>(x);
+  x += dpp_u128<dpp::kMirror>(x);
+  u128 r0, r1;
+  swap_u128<false>(x, r0, r1);
+  x = r0 + r1;
+  swap_u128<true>(x, r0, r1);
+  return r0 + r1;
 }
 
 // f(v, p, q) over the wave's segment [lo, hi) of a row pair; q may be null (then 0)
