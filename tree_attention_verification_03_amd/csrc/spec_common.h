@@ -171,17 +171,13 @@ __device__ __forceinline__ bool le_u192(U192 a, U192 b) {
 }
 
 // floor(a / b) for b != 0 with a quotient known to fit in 64 bits (restoring division).
+// floor(a / b) for a quotient below 2^52: an fp64 estimate (relative error ~2^-52, so off by at most
+// a few units), corrected to the exact quotient with 128-bit products
 __device__ __forceinline__ uint64_t div_u128_u64(u128 a, uint64_t b) {
-  if ((a >> 64) == 0) return uint64_t(a) / b;
-  u128 rem = 0;
-  uint64_t q = 0;
-  for (int i = 127; i >= 0; --i) {
-    rem = (rem << 1) | ((a >> i) & 1);
-    if (rem >= b) {
-      rem -= b;
-      if (i < 64) q |= (1ull << i);
-    }
-  }
+  const double ad = double(uint64_t(a >> 64)) * 18446744073709551616.0 + double(uint64_t(a));
+  uint64_t q = uint64_t(ad / double(b));
+  while (u128(q) * b > a) --q;
+  while (u128(q + 1) * b <= a) ++q;
   return q;
 }
 
@@ -209,6 +205,9 @@ __device__ __forceinline__ T ld_agent(const T* p) {
 __device__ __forceinline__ void wait_global_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ uint32_t ticket_add(uint32_t* t) {
   return __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ticket_add_n(uint32_t* t, uint32_t n) {
+  return __hip_atomic_fetch_add(t, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void ticket_reset(uint32_t* t) {
   __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -12,25 +12,48 @@
 //
 // Every node's outcome depends only on its own rows, its children's tokens and
 // the node's uniforms, so all nodes are evaluated in parallel, in one launch of
-// 1024-thread blocks, grid (n_slices + 1, B * max_T):
-//   x < n_slices   greedy rows: the block reduces a slice of the row to a packed
-//                  64-bit key (order(value) << 32 | ~index) and merges it with
-//                  a 64-bit atomicMax - order-free, bit-exact;
-//   x = n_slices   sampling rows: the block runs the node's exact integer state
-//                  machine (2^-32 fixed point; sums are integers, so reduction
-//                  order cannot change them).
-// Blocks of the other mode exit at once. Every block then takes a ticket of its
-// sequence; the last one walks the tree: longest valid path (greedy) or the
-// chain of ACCEPT links (sampling), emits the path, tokens, bonus and status,
-// and re-zeroes the workspace.
+// 256-thread blocks with two roles:
+//   greedy slice blocks  reduce a slice of a greedy row to a packed 64-bit key
+//                        (order(value) << 32 | ~index) merged with a 64-bit
+//                        atomicMax - order-free, bit-exact; the last slice block
+//                        of a greedy sequence (ticket) walks its tree;
+//   sampling workers     persistent blocks that pull (node, slice) items from a
+//                        device queue. Pass 0 of every sampling node (sums and
+//                        argmax of fx(p), sums of fx(q)) is a static item list;
+//                        the block finishing a node's pass (ticket) takes the
+//                        node's next decision - accept a child, or move gamma
+//                        and enqueue the residual pass, or resample - so one
+//                        node's passes spread over many CUs. Sums are exact
+//                        integers: per-slice 32-bit limb sums added with 64-bit
+//                        atomics. The block finishing a sequence's last node
+//                        walks its tree. A worker only ever waits for a queue
+//                        slot to be published or for every node to be done, and
+//                        an item is only published by a block that is running,
+//                        so the loop cannot deadlock whatever is resident.
+// The walk emits the longest valid path (greedy) or the chain of ACCEPT links
+// (sampling), the tokens, bonus and status, and re-zeroes the workspace.
 #include "api_common.h"
 #include "spec_common.h"
 
 namespace spectree {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kSampleSlice = 8192;  // row elements per sampling work item
+constexpr int kMaxWorkers = 512;
+
+struct NodeState {  // one sampling node; all zero between calls
+  uint64_t sp, sq, am;  // pass 0: sums of fx(p) and fx(q), argmax key of fx(p)
+  uint64_t wl[3];       // pass in flight: sums of the residual's 32-bit limbs
+  uint64_t gamma;       // gamma of the pass in flight
+  uint32_t nan;         // NaN seen in pass 0: bit 0 in p, bit 1 in q
+  uint32_t ticket;      // slices of the pass in flight that are done
+  uint32_t flags;       // status flags so far
+  int32_t kid;          // index (in the node's child list) of the next child to test
+  int32_t tested;       // some child was tested
+  int32_t pass;         // passes completed
+};
 
 struct VerifyWs {
   uint64_t* keys;      // [B*max_T] greedy argmax keys (0 = empty)
@@ -38,11 +61,18 @@ struct VerifyWs {
   int32_t* acc_child;  // [B*max_T] sampling: accepted child node or -1
   int32_t* bonus;      // [B*max_T] sampling: bonus token when the walk stops here
   uint32_t* nflag;     // [B*max_T] sampling node flags
-  uint32_t* tickets;   // [B] blocks of the sequence that have finished
+  uint32_t* tickets;   // [B] greedy: slice blocks done; sampling: nodes done
+  NodeState* node;     // [B*max_T]
+  uint64_t* ssum;      // [B*max_T][nsl][2] u128 slice sums of the node's last pass
+  uint32_t* queue;     // [B*max_T*nsl] published dynamic items (node * nsl + slice + 1), 0 = empty
+  uint32_t* qctl;      // [4] head, tail, nodes done, workers exited
 };
 
-VerifyWs carve(void* ws, int B, int max_T, size_t* total) {
+int sample_slices(int V) { return (V + kSampleSlice - 1) / kSampleSlice; }
+
+VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
   const size_t n = size_t(B) * max_T;
+  const size_t nsl = size_t(sample_slices(V));
   char* c = static_cast<char*>(ws);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -57,6 +87,10 @@ VerifyWs carve(void* ws, int B, int max_T, size_t* total) {
   w.bonus = reinterpret_cast<int32_t*>(take(4 * n));
   w.nflag = reinterpret_cast<uint32_t*>(take(4 * n));
   w.tickets = reinterpret_cast<uint32_t*>(take(4 * size_t(B)));
+  w.node = reinterpret_cast<NodeState*>(take(sizeof(NodeState) * n));
+  w.ssum = reinterpret_cast<uint64_t*>(take(16 * n * nsl));
+  w.queue = reinterpret_cast<uint32_t*>(take(4 * n * nsl));
+  w.qctl = reinterpret_cast<uint32_t*>(take(16));
   *total = off;
   return w;
 }
@@ -70,7 +104,7 @@ struct VerifyArgs {
   const int32_t* T_b;
   const int8_t* mode;
   uint64_t key0, key1, offset;
-  int max_T, R, V, n_slices, slice, seg;
+  int B, max_T, R, V, n_slices, slice, nsl, n_greedy_blocks, n_workers;
   int32_t* accept_len;
   int32_t* accept_nodes;
   int32_t* out_tokens;
@@ -90,7 +124,7 @@ __device__ __forceinline__ uint64_t argmax_key(float x, int v) {
 
 // ------------------------------------------------------------------ greedy
 template <bool VEC>
-__device__ void greedy_slice(const VerifyWs& w, const VerifyArgs& a, int row, int lo) {
+__device__ __forceinline__ void greedy_slice(const VerifyWs& w, const VerifyArgs& a, int row, int lo) {
   __shared__ uint64_t red[kWaves];
   __shared__ uint32_t nanred[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -232,7 +266,7 @@ __device__ __forceinline__ void seg_for(const float* p, const float* q, int lo, 
 }
 
 // inclusive scan over the block's threads (u128); returns this thread's exclusive prefix
-__device__ u128 block_exclusive_scan_u128(u128 x, u128* wtot) {
+__device__ __forceinline__ u128 block_exclusive_scan_u128(u128 x, u128* wtot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   u128 incl = x;
 #pragma unroll
@@ -247,33 +281,16 @@ __device__ u128 block_exclusive_scan_u128(u128 x, u128* wtot) {
   return before + incl - x;
 }
 
-template <bool VEC>
-__device__ void sample_node(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
-  __shared__ int kid_s[64];
-  __shared__ int nkid_s;
-  __shared__ uint64_t sp_s[kWaves], sq_s[kWaves], am_s[kWaves];
-  __shared__ uint32_t nan_s[kWaves];
-  __shared__ u128 segsum_s[kWaves];
-  __shared__ u128 wtot_s[kWaves];
-  __shared__ u128 W_s;
-  __shared__ uint64_t gamma_s;
-  __shared__ int decide_s;  // -1 keep testing, >= 0 accepted child
-  __shared__ int wstar_s;
-  __shared__ u128 excl_s;
-  __shared__ int bonus_s;
-
-  const int max_T = a.max_T, V = a.V;
-  const int node = b * max_T + u;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  // children of u in index order (a parent outside [0, c) counts as the root)
+// children of u in index order (a parent outside [0, c) counts as the root); returns their count
+__device__ __forceinline__ int node_children(const VerifyArgs& a, int b, int u, int T, int* kid_s, int* nkid_s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
     int n = 0;
     for (int c0 = 1; c0 < T; c0 += kWave) {
       const int c = c0 + lane;
       bool kid = false;
       if (c < T) {
-        int pc = a.parents[size_t(b) * max_T + c];
+        int pc = a.parents[size_t(b) * a.max_T + c];
         if (pc < 0 || pc >= c) pc = 0;
         kid = (pc == u);
       }
@@ -281,172 +298,357 @@ __device__ void sample_node(const VerifyWs& w, const VerifyArgs& a, int b, int u
       if (kid) kid_s[n + __popcll(m & ((1ull << lane) - 1))] = c;
       n += __popcll(m);
     }
-    if (lane == 0) nkid_s = n;
+    if (lane == 0) *nkid_s = n;
   }
   __syncthreads();
-  const int nkid = nkid_s;
-  const int qr = a.q_row ? a.q_row[size_t(b) * max_T + u] : -1;
-  const bool has_q = nkid > 0 && a.draft != nullptr && qr >= 0 && qr < a.R;
-  const float* prow = a.target + size_t(node) * V;
-  const float* qrow = has_q ? a.draft + (size_t(b) * a.R + qr) * V : nullptr;
-  const int lo = wave * a.seg, hi = min(V, lo + a.seg);
+  return *nkid_s;
+}
 
-  // pass 0: S_P, S_Q, argmax of P, NaN checks, per-wave sums of P
+// the node's q row, or null if it has none (no children, no draft tensor, or q_row out of range)
+__device__ __forceinline__ const float* node_qrow(const VerifyArgs& a, int b, int u, int nkid) {
+  const int qr = a.q_row ? a.q_row[size_t(b) * a.max_T + u] : -1;
+  const bool has_q = nkid > 0 && a.draft != nullptr && qr >= 0 && qr < a.R;
+  return has_q ? a.draft + (size_t(b) * a.R + qr) * a.V : nullptr;
+}
+
+// the q row named by q_row whether or not the node has children (pass 0 reads it before the children
+// are known; its sums only count for a node with children)
+__device__ __forceinline__ const float* node_qrow_any(const VerifyArgs& a, int b, int u) {
+  const int qr = a.q_row ? a.q_row[size_t(b) * a.max_T + u] : -1;
+  return (a.draft != nullptr && qr >= 0 && qr < a.R) ? a.draft + (size_t(b) * a.R + qr) * a.V : nullptr;
+}
+
+// f(v, p, q) over this thread's elements of [lo, hi) (q may be null: then 0); a slice is at most
+// kSampleSlice elements, so the vector path loads all of a thread's elements in one round trip
+template <bool VEC, typename F>
+__device__ __forceinline__ void slice_for(const float* p, const float* q, int lo, int hi, F&& f) {
+  const int tid = threadIdx.x;
+  if (VEC) {
+    constexpr int NV = kSampleSlice / (4 * kThreads);
+    float4 x[NV], y[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = lo + 4 * tid + 4 * kThreads * i;
+      x[i] = v < hi ? *reinterpret_cast<const float4*>(p + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+      y[i] = (q && v < hi) ? *reinterpret_cast<const float4*>(q + v) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = lo + 4 * tid + 4 * kThreads * i;
+      if (v < hi) {
+        f(v, x[i].x, y[i].x);
+        f(v + 1, x[i].y, y[i].y);
+        f(v + 2, x[i].z, y[i].z);
+        f(v + 3, x[i].w, y[i].w);
+      }
+    }
+  } else {
+    for (int v = lo + tid; v < hi; v += kThreads) f(v, p[v], q ? q[v] : 0.f);
+  }
+}
+
+// the block's sums of three u64 values; valid in thread 0
+__device__ __forceinline__ void block_sum3(uint64_t& x0, uint64_t& x1, uint64_t& x2, uint64_t (*red)[3]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x0 = wave_sum_u64(x0);
+  x1 = wave_sum_u64(x1);
+  x2 = wave_sum_u64(x2);
+  if (lane == 0) {
+    red[wave][0] = x0;
+    red[wave][1] = x1;
+    red[wave][2] = x2;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int i = 1; i < kWaves; ++i) {
+      x0 += red[i][0];
+      x1 += red[i][1];
+      x2 += red[i][2];
+    }
+}
+
+__device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArgs& a, int b, int u, int acc, int bonus, uint32_t flags,
+                              bool trivial);
+
+// after a slice of a pass: the block finishing the node's pass takes the node's next decision
+template <bool VEC>
+__device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T);
+
+template <bool VEC>
+__device__ __forceinline__ void pass_done(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
+  __shared__ int last_s;
+  NodeState* ns = w.node + (size_t(b) * a.max_T + u);
+  wait_global_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) last_s = ticket_add(&ns->ticket) == uint32_t(a.nsl - 1);
+  __syncthreads();
+  if (!last_s) return;
+  if (threadIdx.x == 0) ticket_reset(&ns->ticket);
+  sample_decide<VEC>(w, a, b, u, T);
+}
+
+// pass 0 over slice s: sums of fx(p) (and of fx(q) for a node with children and a q row), argmax key of
+// fx(p), NaN checks; the slice's p sum is kept for a resample from p
+template <bool VEC>
+__device__ __forceinline__ void sample_pass0(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T, int s) {
+  __shared__ uint64_t red[kWaves][3];
+  const size_t node = size_t(b) * a.max_T + u;
+  const float* prow = a.target + node * a.V;
+  const float* qrow = node_qrow_any(a, b, u);
+  const int lo = s * kSampleSlice, hi = min(a.V, lo + kSampleSlice);
   uint64_t sp = 0, sq = 0, am = 0;
-  bool nan = false;
-  seg_for<VEC>(prow, qrow, lo, hi, lane, [&](int v, float x, float y) {
-    nan |= (x != x) | (y != y);
+  uint32_t nan = 0;
+  slice_for<VEC>(prow, qrow, lo, hi, [&](int v, float x, float y) {
+    nan |= (x != x ? 1u : 0u) | (y != y ? 2u : 0u);
     const uint32_t P = fx(x);
     sp += P;
     const uint64_t k = (uint64_t(P) << 32) | uint64_t(0xffffffffu - uint32_t(v));
     am = k > am ? k : am;
     sq += fx(y);
   });
-  sp = wave_sum_u64(sp);
-  sq = wave_sum_u64(sq);
   am = wave_max_u64(am);
-  const uint32_t nw = wave_or_u32(nan ? 1u : 0u);
-  if (lane == 0) {
-    sp_s[wave] = sp;
-    sq_s[wave] = sq;
-    am_s[wave] = am;
-    nan_s[wave] = nw;
+  // NaN bits travel through the block sum as counts (lane 0 of each wave): p in bits 0-3, q in bits 4-7
+  const uint32_t nw = wave_or_u32(nan);
+  uint64_t nn = (threadIdx.x & 63) == 0 ? uint64_t(nw & 1u) + ((nw & 2u) ? 16u : 0u) : 0u;
+  {
+    __shared__ uint64_t amr[kWaves];
+    if ((threadIdx.x & 63) == 0) amr[threadIdx.x >> 6] = am;
+    block_sum3(sp, sq, nn, red);
+    if (threadIdx.x == 0) {
+      for (int i = 1; i < kWaves; ++i) am = amr[i] > am ? amr[i] : am;
+      NodeState* ns = w.node + node;
+      atomicAdd(reinterpret_cast<unsigned long long*>(&ns->sp), (unsigned long long)sp);
+      if (sq) atomicAdd(reinterpret_cast<unsigned long long*>(&ns->sq), (unsigned long long)sq);
+      atomicMax(reinterpret_cast<unsigned long long*>(&ns->am), (unsigned long long)am);
+      if (nn) atomicOr(&ns->nan, ((nn & 15u) ? 1u : 0u) | ((nn >> 4) ? 2u : 0u));
+      uint64_t* ss = w.ssum + (node * a.nsl + s) * 2;
+      st_agent(ss, sp);
+      st_agent(ss + 1, uint64_t(0));
+    }
   }
-  __syncthreads();
-  uint64_t S_P = 0, S_Q = 0, AM = 0;
-  uint32_t flags = 0;
-  for (int i = 0; i < kWaves; ++i) {
-    S_P += sp_s[i];
-    S_Q += sq_s[i];
-    AM = am_s[i] > AM ? am_s[i] : AM;
-    if (nan_s[i]) flags |= SPEC_STATUS_NAN_INPUT;
-  }
-  const bool test = nkid > 0 && has_q && S_Q > 0;
-  if (nkid > 0 && !test) flags |= SPEC_STATUS_ZERO_Q;
-  if (tid == 0) {
-    W_s = u128(S_P) * S_Q;
-    gamma_s = 0;
-    decide_s = -1;
-  }
-  __syncthreads();
+  pass_done<VEC>(w, a, b, u, T);
+}
 
-  bool tested = false;
-  for (int ki = 0; test && ki < nkid; ++ki) {
-    const int c = kid_s[ki];
-    const int t = a.tokens[size_t(b) * max_T + c];
-    if (t < 0 || t >= V) continue;  // invalid draft token: never tested
-    tested = true;
-    if (tid == 0) {
+// residual pass over slice s under the node's current gamma: the slice's sum of
+// N[v] = max(0, fx(p[v]) S_Q - gamma fx(q[v])) as 32-bit limb sums
+template <bool VEC>
+__device__ __forceinline__ void sample_passN(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T, int s) {
+  __shared__ uint64_t red[kWaves][3];
+  const size_t node = size_t(b) * a.max_T + u;
+  NodeState* ns = w.node + node;
+  const float* prow = a.target + node * a.V;
+  const float* qrow = node_qrow_any(a, b, u);  // present: only tested nodes have residual passes
+  const uint64_t S_Q = ld_agent(&ns->sq), gamma = ld_agent(&ns->gamma);
+  const int lo = s * kSampleSlice, hi = min(a.V, lo + kSampleSlice);
+  uint64_t l0 = 0, l1 = 0, l2 = 0;
+  slice_for<VEC>(prow, qrow, lo, hi, [&](int, float x, float y) {
+    const u128 n = residual(fx(x), fx(y), S_Q, gamma, false);
+    l0 += uint32_t(n);
+    l1 += uint32_t(n >> 32);
+    l2 += uint64_t(n >> 64);
+  });
+  block_sum3(l0, l1, l2, red);
+  if (threadIdx.x == 0) {
+    atomicAdd(reinterpret_cast<unsigned long long*>(&ns->wl[0]), (unsigned long long)l0);
+    atomicAdd(reinterpret_cast<unsigned long long*>(&ns->wl[1]), (unsigned long long)l1);
+    atomicAdd(reinterpret_cast<unsigned long long*>(&ns->wl[2]), (unsigned long long)l2);
+    const u128 v = u128(l0) + (u128(l1) << 32) + (u128(l2) << 64);
+    uint64_t* ss = w.ssum + (node * a.nsl + s) * 2;
+    st_agent(ss, uint64_t(v));
+    st_agent(ss + 1, uint64_t(v >> 64));
+  }
+  pass_done<VEC>(w, a, b, u, T);
+}
+
+template <bool VEC>
+__device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
+  __shared__ int kid_s[64], nkid_s;
+  __shared__ int act_s;  // accepted child, -1: residual pass enqueued, -2: resample
+  __shared__ u128 W_s, excl_s, wtot_s[kWaves];
+  __shared__ uint64_t SQ_s, gamma_s, AM_s;
+  __shared__ uint32_t flags_s;
+  __shared__ int plain_s, sstar_s, bonus_s;
+  __shared__ u128 ssl_s[kThreads];
+  __shared__ int found_s;
+  __shared__ u128 run_s, tau_s;
+  const int tid = threadIdx.x, max_T = a.max_T, V = a.V;
+  const int nkid = node_children(a, b, u, T, kid_s, &nkid_s);
+  const size_t node = size_t(b) * max_T + u;
+  NodeState* ns = w.node + node;
+  const float* prow = a.target + node * V;
+  const float* qrow = node_qrow(a, b, u, nkid);
+  if (tid == 0) {
+    const int pass = ld_agent(&ns->pass);
+    const uint64_t S_P = ld_agent(&ns->sp), S_Q = qrow ? ld_agent(&ns->sq) : 0;
+    const bool test = nkid > 0 && qrow != nullptr && S_Q > 0;
+    uint32_t flags;
+    uint64_t gamma;
+    int kid, tested;
+    u128 W;
+    if (pass == 0) {
+      const uint32_t nb = ld_agent(&ns->nan);
+      flags = ((nb & 1u) || ((nb & 2u) && qrow)) ? SPEC_STATUS_NAN_INPUT : 0u;
+      if (nkid > 0 && !test) flags |= SPEC_STATUS_ZERO_Q;
+      W = u128(S_P) * S_Q;
+      gamma = 0;
+      kid = 0;
+      tested = 0;
+    } else {
+      flags = ld_agent(&ns->flags);
+      gamma = ld_agent(&ns->gamma);
+      kid = ld_agent(&ns->kid);
+      tested = ld_agent(&ns->tested);
+      W = u128(ld_agent(&ns->wl[0])) + (u128(ld_agent(&ns->wl[1])) << 32) + (u128(ld_agent(&ns->wl[2])) << 64);
+      if (W == 0) flags |= SPEC_STATUS_ZERO_RESIDUAL;
+    }
+    int act = -2;
+    for (int ki = kid; test && ki < nkid; ++ki) {
+      const int c = kid_s[ki];
+      const int t = a.tokens[size_t(b) * max_T + c];
+      if (t < 0 || t >= V) continue;  // invalid draft token: never tested
+      tested = 1;
       const uint32_t Pt = fx(prow[t]), Qt = fx(qrow[t]);
-      const u128 Nt = residual(Pt, Qt, S_Q, gamma_s, false);
+      const u128 Nt = residual(Pt, Qt, S_Q, gamma, false);
       const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(c), 0, a.key0, a.key1);
       const uint64_t m = (r.w[0] >> 40) + 1;  // r = m / 2^24 in (0, 1]
       bool accept = false;
       if (Nt > 0) {
-        const U192 lhs = mul_u128_u64(W_s, m * uint64_t(Qt));  // m Q_t W
-        const U192 rhs = shl_u192(mul_u128_u64(Nt, S_Q), 24);   // 2^24 N_t S_Q
+        const U192 lhs = mul_u128_u64(W, m * uint64_t(Qt));  // m Q_t W
+        const U192 rhs = shl_u192(mul_u128_u64(Nt, S_Q), 24);  // 2^24 N_t S_Q
         accept = le_u192(lhs, rhs);
       }
       if (accept) {
-        decide_s = c;
-      } else {
-        gamma_s = gamma_s + div_u128_u64(W_s, S_Q);  // residual <- norm(max(0, residual - q))
+        act = c;
+        break;
       }
+      // rejected: residual <- norm(max(0, residual - q)); its mass needs a pass over the row
+      gamma = gamma + div_u128_u64(W, S_Q);
+      kid = ki + 1;
+      act = -1;
+      st_agent(&ns->gamma, gamma);
+      st_agent(&ns->kid, kid);
+      st_agent(&ns->tested, 1);
+      st_agent(&ns->flags, flags);
+      st_agent(&ns->pass, pass + 1);
+      st_agent(&ns->wl[0], uint64_t(0));
+      st_agent(&ns->wl[1], uint64_t(0));
+      st_agent(&ns->wl[2], uint64_t(0));
+      wait_global_stores();
+      const uint32_t pos = ticket_add_n(&w.qctl[1], uint32_t(a.nsl));
+      for (int sl = 0; sl < a.nsl; ++sl) st_agent(&w.queue[pos + sl], uint32_t(node * a.nsl + sl + 1));
+      break;
     }
-    __syncthreads();
-    if (decide_s >= 0) break;
-    // the residual mass W and per-wave sums under the new gamma
-    const uint64_t gamma = gamma_s;
-    u128 acc = 0;
-    seg_for<VEC>(prow, qrow, lo, hi, lane, [&](int, float x, float y) { acc += residual(fx(x), fx(y), S_Q, gamma, false); });
-    acc = wave_sum_u128(acc);
-    if (lane == 0) segsum_s[wave] = acc;
-    __syncthreads();
-    if (tid == 0) {
-      u128 W = 0;
-      for (int i = 0; i < kWaves; ++i) W += segsum_s[i];
-      W_s = W;
-    }
-    __syncthreads();
-    if (W_s == 0) flags |= SPEC_STATUS_ZERO_RESIDUAL;
-  }
-
-  if (decide_s >= 0) {
-    if (tid == 0) {
-      st_agent(w.acc_child + node, decide_s);
-      st_agent(w.bonus + node, -1);
-      st_agent(w.nflag + node, flags);
-    }
-    return;
-  }
-  // ---- no draft accepted: resample from the residual (or from P if nothing was tested)
-  if (!tested) {
-    if (lane == 0) segsum_s[wave] = u128(sp);
-    if (tid == 0) W_s = S_P;
+    act_s = act;
+    plain_s = !tested;
+    W_s = tested ? W : u128(S_P);
+    SQ_s = S_Q;
+    gamma_s = gamma;
+    AM_s = ld_agent(&ns->am);
+    flags_s = flags;
   }
   __syncthreads();
-  const bool plain = !tested;
-  const uint64_t gamma = gamma_s;
+  if (act_s == -1) return;
+  if (act_s >= 0) {
+    sample_finish(w, a, b, u, act_s, -1, flags_s, false);
+    return;
+  }
+  // ---- no draft accepted: resample from the residual (or from p if nothing was tested)
   const u128 W = W_s;
+  const bool plain = plain_s;
   if (W == 0) {
-    if (tid == 0) bonus_s = int(0xffffffffu - uint32_t(AM));  // smallest-index argmax of P
+    if (tid == 0) bonus_s = int(0xffffffffu - uint32_t(AM_s));  // smallest-index argmax of p
   } else {
+    // threshold: smallest v with 2^32 * prefix(v) > K W  <=>  prefix(v) > floor(K W / 2^32)
     // threshold: smallest v with 2^32 * prefix(v) > K W  <=>  prefix(v) > floor(K W / 2^32)
     if (tid == 0) {
       const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(u), 0, a.key0, a.key1);
       const uint64_t K = r.w[1] >> 32;
       const U192 kw = mul_u128_u64(W, K);
-      const u128 tau = (u128(kw.hi) << 96) | (u128(kw.mid) << 32) | u128(kw.lo >> 32);
-      u128 run = 0;
-      int ws = kWaves - 1;
-      for (int i = 0; i < kWaves; ++i) {
-        if (run + segsum_s[i] > tau) {
-          ws = i;
-          break;
-        }
-        run += segsum_s[i];
-      }
-      wstar_s = ws;
-      excl_s = tau - run;  // remaining threshold inside the chosen segment
+      tau_s = (u128(kw.hi) << 96) | (u128(kw.mid) << 32) | u128(kw.lo >> 32);
+      run_s = 0;
+      found_s = -1;
       bonus_s = -1;
     }
+    // the slice holding the threshold: slice sums kThreads at a time, one round trip per chunk
+    for (int c0 = 0; c0 < a.nsl; c0 += kThreads) {
+      __syncthreads();
+      if (found_s >= 0) break;
+      const int sl = c0 + tid;
+      if (sl < a.nsl) {
+        const uint64_t* q2 = w.ssum + (node * a.nsl + sl) * 2;
+        ssl_s[tid] = u128(ld_agent(q2)) | (u128(ld_agent(q2 + 1)) << 64);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        u128 run = run_s;
+        const int n = min(kThreads, a.nsl - c0);
+        for (int i = 0; i < n; ++i) {
+          if (run + ssl_s[i] > tau_s) {
+            found_s = c0 + i;
+            break;
+          }
+          run += ssl_s[i];
+        }
+        if (found_s < 0 && c0 + n >= a.nsl) found_s = a.nsl - 1;  // unreachable with exact sums
+        run_s = run;
+      }
+    }
     __syncthreads();
-    // the whole block searches the chosen segment: each thread sums a contiguous range, a block scan
-    // gives every range's prefix, and the one range holding the crossing is walked element by element
-    const int wlo = wstar_s * a.seg, whi = min(V, wlo + a.seg);
-    const int E = (whi - wlo + kThreads - 1) / kThreads;
-    const int e0 = min(whi, wlo + tid * E), e1 = min(whi, e0 + E);
-    auto resid = [&](int v) {
-      return residual(fx(prow[v]), has_q ? fx(qrow[v]) : 0u, S_Q, gamma, plain);
-    };
-    u128 tsum = 0;
-    for (int v = e0; v < e1; ++v) tsum += resid(v);
-    const u128 ex = block_exclusive_scan_u128(tsum, wtot_s);
-    const u128 rem = excl_s;
-    if (tsum > 0 && ex <= rem && rem < ex + tsum) {
-      u128 run = ex;
-      for (int v = e0; v < e1; ++v) {
-        run += resid(v);
-        if (run > rem) {
-          bonus_s = v;
-          break;
+    // the block searches the chosen slice in two halves; per half each thread sums a contiguous range
+    // of E elements (held in registers), a block scan gives every range's prefix, and the one range
+    // holding the crossing is walked element by element
+    const uint64_t S_Q = SQ_s, gamma = gamma_s;
+    constexpr int E = kSampleSlice / (2 * kThreads);
+    const int wlo = found_s * kSampleSlice, whi = min(V, wlo + kSampleSlice);
+    u128 rem = tau_s - run_s;  // remaining threshold inside the slice
+    for (int half = 0; half < 2; ++half) {
+      const int e0 = wlo + half * (kSampleSlice / 2) + tid * E;
+      uint32_t pv[E], qv[E];
+      if (VEC && e0 + E <= whi) {
+#pragma unroll
+        for (int i = 0; i < E; i += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(prow + e0 + i);
+          pv[i] = fx(x.x); pv[i + 1] = fx(x.y); pv[i + 2] = fx(x.z); pv[i + 3] = fx(x.w);
+          const float4 y = qrow ? *reinterpret_cast<const float4*>(qrow + e0 + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+          qv[i] = fx(y.x); qv[i + 1] = fx(y.y); qv[i + 2] = fx(y.z); qv[i + 3] = fx(y.w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const int v = e0 + i;
+          pv[i] = v < whi ? fx(prow[v]) : 0u;  // past the slice: adds nothing
+          qv[i] = (qrow && v < whi) ? fx(qrow[v]) : 0u;
         }
       }
+      u128 tsum = 0;
+#pragma unroll
+      for (int i = 0; i < E; ++i) tsum += residual(pv[i], qv[i], S_Q, gamma, plain);
+      const u128 ex = block_exclusive_scan_u128(tsum, wtot_s);
+      if (tsum > 0 && ex <= rem && rem < ex + tsum) {
+        u128 run = ex;
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          run += residual(pv[i], qv[i], S_Q, gamma, plain);
+          if (run > rem && bonus_s < 0) bonus_s = e0 + i;
+        }
+      }
+      // total of this half (last thread's inclusive prefix) for the second half's threshold
+      if (tid == kThreads - 1) excl_s = ex + tsum;
+      __syncthreads();
+      if (bonus_s >= 0) break;
+      rem -= excl_s;
+      __syncthreads();
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int bn = bonus_s;
-    if (bn < 0) bn = int(0xffffffffu - uint32_t(AM));  // unreachable with exact sums; keeps the output defined
-    st_agent(w.acc_child + node, -1);
-    st_agent(w.bonus + node, bn);
-    st_agent(w.nflag + node, flags);
-  }
+  int bn = bonus_s;
+  if (bn < 0) bn = int(0xffffffffu - uint32_t(AM_s));  // unreachable with exact sums; keeps the output defined
+  sample_finish(w, a, b, u, -1, bn, flags_s, false);
 }
 
 // ------------------------------------------------------------------ walk
 // Runs in the last block of sequence b to finish; reads the other blocks' results with agent-scope loads.
-__device__ void walk(const VerifyWs& w, const VerifyArgs& a, int b) {
+__device__ __forceinline__ void walk(const VerifyWs& w, const VerifyArgs& a, int b) {
   __shared__ int par_s[65], a_s[65], jmp_s[65], dep_s[65], ok_s[65], path_s[65];
   __shared__ uint32_t st_s, best_s;
   __shared__ int n_s, bonus_s;
@@ -561,21 +763,125 @@ __device__ void walk(const VerifyWs& w, const VerifyArgs& a, int b) {
   }
 }
 
-template <bool VEC>
-__global__ void __launch_bounds__(kThreads) verify_kernel(VerifyWs w, VerifyArgs a) {
+// a node's outcome is final: publish it, clear the node's state, count it for its sequence and for the
+// worker loop; the block finishing a sequence's last node walks the tree. Rows past T_b are finished
+// without outcome (trivial).
+__device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArgs& a, int b, int u, int acc, int bonus, uint32_t flags,
+                              bool trivial) {
   __shared__ int last_s;
-  const int unit = blockIdx.x, row = blockIdx.y;
-  const int b = row / a.max_T, u = row - b * a.max_T;
-  const int T = seq_T(a.T_b, b, a.max_T);
-  const bool greedy = a.mode[b] != SPEC_MODE_SAMPLE;
-  if (u < T) {
-    if (greedy && unit < a.n_slices) greedy_slice<VEC>(w, a, row, unit * a.slice);
-    if (!greedy && unit == a.n_slices) sample_node<VEC>(w, a, b, u, T);
+  const size_t node = size_t(b) * a.max_T + u;
+  if (threadIdx.x == 0) {
+    if (!trivial) {
+      st_agent(w.acc_child + node, acc);
+      st_agent(w.bonus + node, bonus);
+      st_agent(w.nflag + node, flags);
+      NodeState* ns = w.node + node;  // back to all-zero for the next call
+      st_agent(&ns->sp, uint64_t(0));
+      st_agent(&ns->sq, uint64_t(0));
+      st_agent(&ns->am, uint64_t(0));
+      st_agent(&ns->wl[0], uint64_t(0));
+      st_agent(&ns->wl[1], uint64_t(0));
+      st_agent(&ns->wl[2], uint64_t(0));
+      st_agent(&ns->gamma, uint64_t(0));
+      st_agent(&ns->nan, 0u);
+      st_agent(&ns->flags, 0u);
+      st_agent(&ns->kid, 0);
+      st_agent(&ns->tested, 0);
+      st_agent(&ns->pass, 0);
+    }
+    wait_global_stores();
+    ticket_add(&w.qctl[2]);
+    last_s = ticket_add(&w.tickets[b]) == uint32_t(a.max_T - 1);
   }
-  // every block of the grid counts toward its sequence; the last one to arrive walks the tree
+  __syncthreads();
+  if (!last_s) return;
+  if (threadIdx.x == 0) ticket_reset(&w.tickets[b]);
+  walk(w, a, b);
+}
+
+// persistent sampling worker: takes items until every sampling node is done
+template <bool VEC>
+__device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArgs& a) {
+  __shared__ int item_s;
+  const int tid = threadIdx.x, max_T = a.max_T;
+  int nseq = 0;
+  for (int b0 = 0; b0 < a.B; b0 += kThreads) {
+    const int b = b0 + tid;
+    nseq += __syncthreads_count(b < a.B && a.mode[b] == SPEC_MODE_SAMPLE);
+  }
+  if (nseq == 0) return;  // nothing to sample: the queue is never touched
+  const uint32_t total = uint32_t(nseq) * uint32_t(max_T);
+  const uint32_t rows = uint32_t(a.B) * uint32_t(max_T);
+  const uint32_t n_static = rows * uint32_t(a.nsl), cap = n_static;
+  for (;;) {
+    if (tid == 0) {
+      const uint32_t i = ticket_add(&w.qctl[0]);
+      uint32_t it = 0;  // 1 + static index, or 1 + n_static + node * nsl + slice, or 0 = stop
+      if (i < n_static) {
+        it = 1 + i;
+      } else {
+        const uint32_t j = i - n_static;
+        // wait for slot j to be published, or for every node to be done (bounded: never a hang)
+        int nap = 1;  // polls back off from ~0.05 us to ~1 us, which keeps the queue's lines quiet
+        for (uint32_t spin = 0; spin < (1u << 22); ++spin) {
+          if (j < cap) {
+            const uint32_t v = ld_agent(&w.queue[j]);
+            if (v) {
+              st_agent(&w.queue[j], 0u);  // leave the slot empty for the next call
+              it = 1 + n_static + (v - 1);
+              break;
+            }
+          }
+          if (ld_agent(&w.qctl[2]) >= total) break;
+          for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
+          nap = nap < 16 ? 2 * nap : 16;
+        }
+      }
+      item_s = int(it);
+    }
+    __syncthreads();
+    const uint32_t it = uint32_t(item_s);
+    __syncthreads();
+    if (it == 0) break;
+    const bool dynamic = it > n_static;
+    const uint32_t k = dynamic ? it - 1 - n_static : it - 1;
+    const int node = int(k / uint32_t(a.nsl)), sl = int(k % uint32_t(a.nsl));
+    const int b = node / max_T, u = node - b * max_T;
+    if (a.mode[b] != SPEC_MODE_SAMPLE) continue;  // a greedy row's static item
+    const int T = seq_T(a.T_b, b, max_T);
+    if (u >= T) {
+      if (sl == 0) sample_finish(w, a, b, u, -1, -1, 0u, true);
+      continue;
+    }
+    if (dynamic)
+      sample_passN<VEC>(w, a, b, u, T, sl);
+    else
+      sample_pass0<VEC>(w, a, b, u, T, sl);
+  }
+  // the last worker out leaves the queue counters at zero for the next call
+  if (tid == 0 && ticket_add(&w.qctl[3]) == uint32_t(a.n_workers - 1)) {
+    ticket_reset(&w.qctl[0]);
+    ticket_reset(&w.qctl[1]);
+    ticket_reset(&w.qctl[2]);
+    ticket_reset(&w.qctl[3]);
+  }
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kThreads, 2) verify_kernel(VerifyWs w, VerifyArgs a) {
+  __shared__ int last_s;
+  if (int(blockIdx.x) >= a.n_greedy_blocks) {
+    sample_worker<VEC>(w, a);
+    return;
+  }
+  const int x = blockIdx.x % a.n_slices, row = blockIdx.x / a.n_slices;
+  const int b = row / a.max_T, u = row - b * a.max_T;
+  if (a.mode[b] == SPEC_MODE_SAMPLE) return;
+  if (u < seq_T(a.T_b, b, a.max_T)) greedy_slice<VEC>(w, a, row, x * a.slice);
+  // every slice block of a greedy sequence counts; the last one to arrive walks the tree
   wait_global_stores();
   __syncthreads();
-  if (threadIdx.x == 0) last_s = ticket_add(w.tickets + b) == uint32_t((a.n_slices + 1) * a.max_T - 1);
+  if (threadIdx.x == 0) last_s = ticket_add(w.tickets + b) == uint32_t(a.n_slices * a.max_T - 1);
   __syncthreads();
   if (!last_s) return;
   if (threadIdx.x == 0) ticket_reset(w.tickets + b);  // leave the workspace ready for the next call
@@ -590,7 +896,7 @@ using namespace spectree;
 extern "C" size_t spec_tree_verify_workspace_size(int32_t B, int32_t max_T, int32_t V) {
   if (B < 1 || max_T < 1 || max_T > 65 || V < 1) return 0;
   size_t total = 0;
-  carve(nullptr, B, max_T, &total);
+  carve(nullptr, B, max_T, V, &total);
   return total;
 }
 
@@ -606,15 +912,15 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
   if (draft_probs && (R < 1 || !q_row)) return fail(SPEC_E_INVAL, "spec_tree_verify: draft_probs needs R >= 1 and q_row");
   if (!target || !tokens || !parents || !mode || !accept_len || !accept_nodes || !out_tokens || !status)
     return fail(SPEC_E_INVAL, "spec_tree_verify: null pointer");
-  if ((long long)B * max_T > 65535LL) return fail(SPEC_E_UNSUPPORTED, "spec_tree_verify: B*max_T=%lld > 65535",
-                                                  (long long)B * max_T);
+  const long long rows = (long long)B * max_T;
+  const long long nsl = sample_slices(V);
+  if (rows * nsl >= (1LL << 31)) return fail(SPEC_E_UNSUPPORTED, "spec_tree_verify: B*max_T*ceil(V/%d) too large", kSampleSlice);
   size_t need = 0;
-  VerifyWs w = carve(ws, B, max_T, &need);
+  VerifyWs w = carve(ws, B, max_T, V, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_verify: workspace %zu < %zu bytes", ws_bytes, need);
-  const int rows = B * max_T;
-  // greedy slices: whole multiples of one block pass (4 K elements), about 512 slice blocks per launch
+  // greedy slices: whole block passes (1 K elements), about 512 slice blocks per launch
   long long sl = ((long long)V * rows + 511) / 512;
-  sl = (sl + 4095) / 4096 * 4096;
+  sl = (sl + 1023) / 1024 * 1024;
   if (sl > 65536) sl = 65536;
   VerifyArgs a;
   a.target = target;
@@ -627,19 +933,23 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
   a.key0 = philox_key0;
   a.key1 = philox_key1;
   a.offset = philox_offset;
+  a.B = B;
   a.max_T = max_T;
   a.R = draft_probs ? R : 0;
   a.V = V;
   a.slice = int(sl);
   a.n_slices = int((V + sl - 1) / sl);
-  a.seg = (V + kWaves - 1) / kWaves;
-  a.seg = (a.seg + 3) / 4 * 4;  // segment bounds on 16-byte boundaries for the vector path
+  a.nsl = int(nsl);
+  a.n_greedy_blocks = int(rows) * a.n_slices;
+  a.n_workers = int(std::min<long long>(kMaxWorkers, rows * nsl));
   a.accept_len = accept_len;
   a.accept_nodes = accept_nodes;
   a.out_tokens = out_tokens;
   a.status = status;
+  if ((long long)a.n_greedy_blocks + a.n_workers >= (1LL << 31))
+    return fail(SPEC_E_UNSUPPORTED, "spec_tree_verify: grid too large");
   const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target) | reinterpret_cast<uintptr_t>(draft_probs)) & 15) == 0;
-  const dim3 grid(a.n_slices + 1, rows);
+  const dim3 grid(a.n_greedy_blocks + a.n_workers);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (vec)
     hipLaunchKernelGGL(verify_kernel<true>, grid, dim3(kThreads), 0, st, w, a);
