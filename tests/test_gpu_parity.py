@@ -231,6 +231,34 @@ def test_verify_root_only_trees():
     check_verify(w, host, trees, tokens=tok, parents=par, q_row=qr)
 
 
+def test_verify_sampling_star_tree_many_passes():
+    """A root with 40 children over a 3-slice vocabulary: every rejection costs one residual pass, so
+    the device queue chains up to 40 passes of one node; leaves resample from p."""
+    B, N, V = 3, 40, 20000
+    w = make_workload(name="verify", B=B, Hq=2, Hkv=1, d=64, prefix=16, topk=1, depth=1, num_draft=N, V=V,
+                      verify="sample", temperature=1.0, seed=23)
+    rng = np.random.default_rng(23)
+    T = N + 1
+    tok = np.full((B, w.max_T), -1, np.int32)
+    par = np.full((B, w.max_T), -1, np.int32)
+    qr = np.full((B, w.max_T), -1, np.int32)
+    tok[:, 0] = w.root_tokens
+    tok[:, 1:T] = rng.integers(0, V, size=(B, N))
+    tok[1, 7] = V + 3  # an invalid child in the middle of the chain: skipped, never tested
+    par[:, 1:T] = 0
+    qr[:, 0] = 0
+    target = w.target.copy()
+    # sequence 2: a target that favours its 30th child, so a late child is accepted
+    target[2, 0] *= 0.5
+    target[2, 0, tok[2, 30]] += 1.0
+    target[2, 0] /= target[2, 0].sum()
+    w.target = target
+    trees = [None] * B
+    log("[verify] sampling star tree, 40 children, V=20000")
+    host = _verify(w, tok, par, qr)
+    check_verify(w, host, trees, tokens=tok, parents=par, q_row=qr)
+
+
 # ---------------------------------------------------------------- KV compaction
 def test_kv_compact_multilayer():
     from tree_attention_verification_03_amd import ops
