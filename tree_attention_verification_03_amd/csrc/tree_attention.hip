@@ -109,11 +109,17 @@ __device__ __forceinline__ float lanegroup_max(float x) {
   return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-// LDS layout of one ring stage: K rows then V rows, 2*D bytes per key, 16-byte chunks swizzled per key:
-//   K: chunk c of key j sits at c ^ (j & 7)      (A-operand reads of 8 keys hit 8 different chunks)
-//   V: chunk c of key j sits at c ^ 2 (j & 3)    (transposing reads of 4 keys hit 4 different 32-byte groups)
-__device__ __forceinline__ int k_swz(int key) { return key & 7; }
-__device__ __forceinline__ int v_swz(int key) { return 2 * (key & 3); }
+// LDS layout of one ring stage: K rows then V rows, 2*D bytes per key, 16-byte chunks swizzled per key
+// (CPR = D / 8 chunks per row):
+//   K: chunk c of key j sits at c ^ (j & (CPR - 1)); the A-operand read of 16 keys at one chunk then
+//      touches 16 different chunks (d = 128: all 64 banks once);
+//   V: chunk c of key j sits at c ^ 2 (j & 3), and at d = 128 also ^ 8 for odd groups of 4 keys: a
+//      transposing read of 4 keys hits 4 different 32-byte groups, and the 16-lane groups reading
+//      keys 4g..4g+3 and 4(g+1)..4(g+1)+3 use opposite 128-byte halves of the bank row.
+template <int D>
+__device__ __forceinline__ int k_swz(int key) { return key & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int v_swz(int key) { return 2 * (key & 3) ^ (D == 128 ? 8 * ((key >> 2) & 1) : 0); }
 
 // occupancy target: two blocks per CU (the LDS ring allows two), i.e. 8 / NW * 2 ... waves per SIMD
 template <int D, int NW, int RW, int NS>
@@ -264,8 +270,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 2) tree_attn_kernel(AttnParams p
   for (int i = 0; i < PH; ++i) {
     lkey[i] = (wave + NW * i) * RPI + lane / CPR;
     const int pos = lane % CPR;
-    koff[i] = 8 * (pos ^ k_swz(lkey[i]));
-    voff[i] = 8 * (pos ^ v_swz(lkey[i]));
+    koff[i] = 8 * (pos ^ k_swz<D>(lkey[i]));
+    voff[i] = 8 * (pos ^ v_swz<D>(lkey[i]));
   }
   // issue the direct loads of this wave's share of key tile `tile` into ring stage `slot`; slots past
   // the chunk and slots on invalid pages read the zero row (their keys are masked in compute)
@@ -309,7 +315,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 2) tree_attn_kernel(AttnParams p
       bf16x8 kop[KK];
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        kop[kk] = *reinterpret_cast<const bf16x8*>(kr + 16 * ((4 * kk + (lane >> 4)) ^ k_swz(l15)));
+        kop[kk] = *reinterpret_cast<const bf16x8*>(kr + 16 * ((4 * kk + (lane >> 4)) ^ k_swz<D>(l15)));
 #pragma unroll
       for (int rw = 0; rw < RW; ++rw) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
@@ -391,7 +397,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 2) tree_attn_kernel(AttnParams p
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int key = 16 * h + g4 + q4;
-        const int chunk = (2 * dt + cl) ^ v_swz(key);
+        const int chunk = (2 * dt + cl) ^ v_swz<D>(key);
         half[h] = lds_read_tr16(vb + key * ROWB + 16 * chunk + 2 * e4);
       }
       const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
