@@ -33,7 +33,7 @@ ATTN_CASES = [
     ("star_g8_t65", 1, 64, 8, 128, [513], [65], 16, "star", 256),
     ("chunk_edges", 3, 8, 8, 64, [128, 256, 129], [2, 3, 4], 16, "random", 128),
     ("g3_odd_rows", 2, 6, 2, 128, [77, 1030], [11, 23], 32, "random", 384),
-    ("item_cap", 2, 8, 2, 128, [5000, 4100], [9, 33], 16, "random", 128),  # 40 chunks asked, capped at 31
+    ("many_items", 2, 8, 2, 128, [5000, 4100], [9, 33], 16, "random", 128),  # 40 items: several combine batches
     ("pipelined_g4", 3, 16, 4, 128, [1500, 700, 2100], [9, 17, 5], 16, "random", 512),
     ("pipelined_d64", 2, 8, 2, 64, [999, 1536], [33, 65], 16, "chain", 1024),
 ]
@@ -126,6 +126,24 @@ def test_tree_build_ragged(seed):
     torch.cuda.synchronize()
     host = {k: to_np(getattr(step.o, k)) for k in ("tokens", "parents", "depth", "anc", "q_row", "frontier")}
     check_build(w, host, oracle_trees(w))
+
+
+# every block shape the plan can pick (waves, row tiles per wave, ring stages, stages per softmax step),
+# on rows spanning several row blocks, with unaligned key chunks and tree slots straddling two items
+ATTN_SHAPES = ["4,1,3", "4,1,4", "4,2,3", "4,2,4", "8,1,3", "8,1,4", "4,1,4,2", "4,1,6,2", "8,1,4,2", "8,1,6,2"]
+
+
+@pytest.mark.parametrize("shape", ATTN_SHAPES)
+def test_attention_block_shapes(shape, monkeypatch):
+    monkeypatch.setenv("SPEC_TREE_ATTN_SHAPE", shape)
+    monkeypatch.setenv("SPEC_TREE_ATTN_CHUNK", "333")
+    w, parents = _attn_case(3, 32, 4, 128, [700, 0, 1201], [33, 17, 9], 16, "random", seed=77)
+    log(f"[attn] block shape {shape}")
+    out, lse, status = _run_attention(w, parents)
+    max_abs, rel, lse_err = compare_attention(w, out, lse, parents)
+    log(f"[attn] block shape {shape}: max_abs={max_abs:.3e} rel_l2={rel:.3e} lse_err={lse_err:.3e}")
+    assert max_abs <= ATTN_MAX_ABS and rel <= ATTN_REL_L2 and lse_err <= LSE_ABS
+    assert (status == 0).all()
 
 
 # ---------------------------------------------------------------- verify, small cases

@@ -48,7 +48,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kTile = 32;         // keys per ring stage
 constexpr int kMaxChunk = 2048;   // keys per work item, at most
 constexpr float kTau = 8.f;       // log2 headroom of the lazily moved reference max
-constexpr int kTargetBlocks = 512;
+constexpr int kTargetBlocks = 384;  // ~1.5 blocks per CU: fewer, longer items beat full occupancy (measured)
 
 struct AttnParams {
   const uint16_t* q;
@@ -121,9 +121,12 @@ __device__ __forceinline__ int k_swz(int key) { return key & (D / 8 - 1); }
 template <int D>
 __device__ __forceinline__ int v_swz(int key) { return 2 * (key & 3) ^ (D == 128 ? 8 * ((key >> 2) & 1) : 0); }
 
-// occupancy target: two blocks per CU (the LDS ring allows two), i.e. 8 / NW * 2 ... waves per SIMD
-template <int D, int NW, int RW, int NS>
-__global__ void __launch_bounds__(64 * NW, NW / 2) tree_attn_kernel(AttnParams p) {
+// blocks of this shape that fit one CU's 160 KB of LDS (the ring dominates): 2, or 1 for deep rings
+constexpr int blocks_per_cu(int D, int NS) { return NS * 128 * D + 4096 <= 160 * 1024 / 2 ? 2 : 1; }
+
+// SPS ring stages of 32 keys form one softmax step (one barrier, one running-max update per step)
+template <int D, int NW, int RW, int NS, int SPS>
+__global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_attn_kernel(AttnParams p) {
   constexpr int KK = D / 32;               // MFMA k-steps over the head dim
   constexpr int DT = D / 16;               // 16-wide head-dim tiles of O^T
   constexpr int CPR = D / 8;               // 16-byte chunks per (token, head) row
@@ -135,6 +138,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 2) tree_attn_kernel(AttnParams p
   constexpr int PW = 2 * NLD / NW;         // ... per wave and stage
   constexpr int NT = 64 * NW;
   static_assert(PW >= 2 && PW * NW == 2 * NLD, "each wave loads whole K/V row pairs");
+  static_assert(NS >= 2 * SPS && NS % SPS == 0, "a step's stages are consecutive ring slots");
   constexpr int PH = PW / 2;               // key rows (x 1 KB) per wave and stage, each loaded for K and for V
   static_assert(NT >= 65, "the tree prologue uses one thread per node");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE_B];
@@ -302,68 +306,72 @@ __global__ void __launch_bounds__(64 * NW, NW / 2) tree_attn_kernel(AttnParams p
     }
   };
 
-  // one key tile for this wave's row tiles: S^T = K Q^T, online softmax, O^T += V^T P^T. Masked tiles
-  // (the chunk's end, tree slots, invalid pages) test every key; the others skip all masking.
+  // one step = SPS consecutive key tiles (32 SPS keys) for this wave's row tiles: S^T = K Q^T, online
+  // softmax over the step's scores, O^T += V^T P^T. Masked steps (the chunk's end, tree slots, invalid
+  // pages) test every key; the others skip all masking.
+  constexpr int NE = 8 * SPS;  // scores per lane and row tile in one step
   auto compute = [&](int tile, int slot, bool masked) {
-    const unsigned char* kb = ring + slot * STAGE_B;
-    const unsigned char* vb = kb + TILE_B;
     const int st = key_lo + tile * kTile;
-    f32x4 sc[RW][2];
+    // lane score e <-> key st + 32 (e / 8) + 16 ((e / 4) % 2) + g4 + e % 4
+    auto key_of = [&](int e) { return st + 32 * (e >> 3) + 16 * ((e >> 2) & 1) + g4 + (e & 3); };
+    f32x4 sc[RW][2 * SPS];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const unsigned char* kr = kb + (16 * kt + l15) * ROWB;
-      bf16x8 kop[KK];
+    for (int ss = 0; ss < SPS; ++ss) {
+      const unsigned char* kb = ring + ((slot + ss) % NS) * STAGE_B;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        kop[kk] = *reinterpret_cast<const bf16x8*>(kr + 16 * ((4 * kk + (lane >> 4)) ^ k_swz<D>(l15)));
+      for (int kt = 0; kt < 2; ++kt) {
+        const unsigned char* kr = kb + (16 * kt + l15) * ROWB;
+        bf16x8 kop[KK];
 #pragma unroll
-      for (int rw = 0; rw < RW; ++rw) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < KK; ++kk)
+          kop[kk] = *reinterpret_cast<const bf16x8*>(kr + 16 * ((4 * kk + (lane >> 4)) ^ k_swz<D>(l15)));
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qop[rw][kk], a, 0, 0, 0);
-        sc[rw][kt] = a;
+        for (int rw = 0; rw < RW; ++rw) {
+          f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qop[rw][kk], a, 0, 0, 0);
+          sc[rw][2 * ss + kt] = a;
+        }
       }
     }
-    // usable keys among the lane's 8 (bit 4 kt + j <-> key st + 16 kt + g4 + j)
-    uint32_t kvis = 0xffu;
+    // usable keys among the lane's NE (bit e <-> key_of(e))
+    uint32_t kvis = (1u << NE) - 1u;
     if (masked) {  // uniform
       kvis = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = st + 16 * (e >> 2) + g4 + (e & 3);
+      for (int e = 0; e < NE; ++e) {
+        const int key = key_of(e);
         const bool in = key < key_hi;
         const int phys = pg_s[in ? (key >> p.page_shift) - pg0 : 0];
         kvis |= (in && unsigned(phys) < unsigned(p.num_pages)) ? (1u << e) : 0u;
       }
     }
-    bf16x8 pop[RW];
+    bf16x8 pop[RW][SPS];
 #pragma unroll
     for (int rw = 0; rw < RW; ++rw) {
-      float sv[8];  // raw scores, masked -> -inf; the scale is folded into the exponent's fma
+      float sv[NE];  // raw scores, masked -> -inf; the scale is folded into the exponent's fma
       if (masked) {  // uniform
         uint32_t vis = kvis;
-        if (st + kTile > L) {  // uniform: tree slots in this tile; the root is every node's ancestor
+        if (st + SPS * kTile > L) {  // uniform: tree slots in this step; the root is every node's ancestor
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int jn = st + 16 * (e >> 2) + g4 + (e & 3) - L;  // tree node index of this key
+          for (int e = 0; e < NE; ++e) {
+            const int jn = key_of(e) - L;  // tree node index of this key
             const int sh = min(max(jn - 1, 0), 63);
             const bool anc = jn == 0 || (jn > 0 && ((ranc[rw] >> sh) & 1ull));
-            vis &= anc || jn < 0 ? 0xffu : ~(1u << e);
+            vis &= anc || jn < 0 ? 0xffffffffu : ~(1u << e);
           }
         }
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sv[kt * 4 + j] = ((vis >> (kt * 4 + j)) & 1u) ? sc[rw][kt][j] : -INFINITY;
+        for (int e = 0; e < NE; ++e) sv[e] = ((vis >> e) & 1u) ? sc[rw][e >> 2][e & 3] : -INFINITY;
       } else {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sv[kt * 4 + j] = sc[rw][kt][j];
+        for (int e = 0; e < NE; ++e) sv[e] = sc[rw][e >> 2][e & 3];
       }
-      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < NE; ++e) mx = fmaxf(mx, sv[e]);
       mx = lanegroup_max(mx);
-      const float mxs = mx * p.scale_log2;  // tile max in the scaled (log2) domain
+      const float mxs = mx * p.scale_log2;  // step max in the scaled (log2) domain
       const bool move = mxs > m_run[rw] + kTau;
       if (__any(move)) {  // uniform: some row's reference max moves (always on its first visible key)
         const float mnew = move ? mxs : m_run[rw];
@@ -374,55 +382,67 @@ __global__ void __launch_bounds__(64 * NW, NW / 2) tree_attn_kernel(AttnParams p
         m_run[rw] = mnew;
       }
       const float mref = m_run[rw] == -INFINITY ? 0.f : m_run[rw];  // no visible key yet: every p is 0
-      float pe[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sv[e], p.scale_log2, -mref));
-      uint4 pk;
-      pk.x = pack2_bf16(pe[0], pe[1]);
-      pk.y = pack2_bf16(pe[2], pe[3]);
-      pk.z = pack2_bf16(pe[4], pe[5]);
-      pk.w = pack2_bf16(pe[6], pe[7]);
-      pop[rw] = __builtin_bit_cast(bf16x8, pk);
-      lacc[rw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop[rw], lacc[rw], 0, 0, 0);
+      for (int ss = 0; ss < SPS; ++ss) {
+        float pe[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pe[e] = fast_exp2(__builtin_fmaf(sv[8 * ss + e], p.scale_log2, -mref));
+        uint4 pk;
+        pk.x = pack2_bf16(pe[0], pe[1]);
+        pk.y = pack2_bf16(pe[2], pe[3]);
+        pk.z = pack2_bf16(pe[4], pe[5]);
+        pk.w = pack2_bf16(pe[6], pe[7]);
+        pop[rw][ss] = __builtin_bit_cast(bf16x8, pk);
+        lacc[rw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop[rw][ss], lacc[rw], 0, 0, 0);
+      }
     }
-    // V^T operand for head-dim column dt*16 + (lane & 15): keys g4 + {0..3} and 16 + g4 + {0..3} (the same
-    // keys, in the same order, as the lane's P^T column). Two transposing reads: lane i of each 16-lane
-    // group points at key 16 h + g4 + i/4, columns 16 dt + 4 (i % 4) .. +3.
+    // V^T operand for head-dim column dt*16 + (lane & 15): keys g4 + {0..3} and 16 + g4 + {0..3} of each
+    // stage (the same keys, in the same order, as the lane's P^T column). Two transposing reads: lane i
+    // of each 16-lane group points at key 16 h + g4 + i/4, columns 16 dt + 4 (i % 4) .. +3.
     const int q4 = l15 >> 2;        // key & 3 of the row this lane points at
     const int cl = (l15 & 3) >> 1;  // which 16-byte chunk of the 32-byte column group
     const int e4 = 4 * (l15 & 1);   // element offset inside the chunk
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      s16x4 half[2];
+    for (int ss = 0; ss < SPS; ++ss) {
+      const unsigned char* vb = ring + ((slot + ss) % NS) * STAGE_B + TILE_B;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int key = 16 * h + g4 + q4;
-        const int chunk = (2 * dt + cl) ^ v_swz<D>(key);
-        half[h] = lds_read_tr16(vb + key * ROWB + 16 * chunk + 2 * e4);
+      for (int dt = 0; dt < DT; ++dt) {
+        s16x4 half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int key = 16 * h + g4 + q4;
+          const int chunk = (2 * dt + cl) ^ v_swz<D>(key);
+          half[h] = lds_read_tr16(vb + key * ROWB + 16 * chunk + 2 * e4);
+        }
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rw = 0; rw < RW; ++rw)
+          acc[rw][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rw][ss], acc[rw][dt], 0, 0, 0);
       }
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int rw = 0; rw < RW; ++rw) acc[rw][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rw], acc[rw][dt], 0, 0, 0);
     }
   };
 
-  // ---- main loop over the chunk's key tiles. Stage t is loaded NS - 1 tiles ahead; every wave issues
-  // exactly PW loads per tile (past the end they read the zero row), so after the loads of tile t
-  // exactly PW * (NS - 2) of the wave's loads may still be in flight. One barrier per tile publishes
-  // the stage just landed and retires the stage about to be refilled (its LDS reads have returned).
+  // ---- main loop over the chunk's key tiles, SPS tiles per step. Tile t is requested NS - SPS tiles
+  // ahead; every wave issues exactly PW loads per tile (past the end they read the zero row), so once the
+  // step's tiles have landed exactly PW * (NS - 2 SPS) of the wave's loads may still be in flight. One
+  // barrier per step publishes the tiles just landed and retires the slots about to be refilled (the
+  // previous step's: their LDS reads have returned).
   const int ntile = (key_hi - key_lo + kTile - 1) / kTile;
 #pragma unroll
-  for (int i = 0; i < NS - 1; ++i) issue(i, i);
+  for (int i = 0; i < NS - SPS; ++i) issue(i, i);
 #pragma unroll 1
-  for (int t = 0; t < ntile; ++t) {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(PW * (NS - 2)) : "memory");
+  for (int t = 0; t < ntile; t += SPS) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(PW * (NS - 2 * SPS)) : "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const int nt = t + NS - 1;
-    issue(nt, nt % NS);
+#pragma unroll
+    for (int j = 0; j < SPS; ++j) {
+      const int nt = t + NS - SPS + j;
+      issue(nt, nt % NS);
+    }
     if (active) {
       const int st = key_lo + t * kTile;
-      compute(t, t % NS, !pages_ok || st + kTile > min(key_hi, L));
+      compute(t, t % NS, !pages_ok || st + SPS * kTile > min(key_hi, L));
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads issued past the end
@@ -557,7 +577,7 @@ __global__ void __launch_bounds__(2 * D) tree_attn_combine(AttnParams p) {
 }
 
 struct AttnShape {
-  int NW, RW, NS;
+  int NW, RW, NS, SPS;
 };
 
 struct AttnPlan {
@@ -571,11 +591,14 @@ AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_p
   pl.G = Hq / Hkv;
   pl.tiles = (pl.G * max_T + 15) / 16;
   // waves x row tiles per wave (one tile per wave; two only on 4-wave blocks, which have the registers)
-  pl.sh = pl.tiles <= 4 ? AttnShape{4, 1, 4} : AttnShape{8, 1, 4};
-  if (const char* env = getenv("SPEC_TREE_ATTN_SHAPE")) {
-    int nw = 0, rw = 0, ns = 0;
-    if (sscanf(env, "%d,%d,%d", &nw, &rw, &ns) == 3 && (nw == 4 || nw == 8) && (rw == 1 || (rw == 2 && nw == 4)) && (ns == 3 || ns == 4))
-      pl.sh = AttnShape{nw, rw, ns};
+  // two 32-key stages per softmax step at d = 128 (the d = 64 kernels take one)
+  pl.sh = pl.tiles <= 4 ? AttnShape{4, 1, 4, d == 128 ? 2 : 1} : AttnShape{8, 1, 4, d == 128 ? 2 : 1};
+  if (const char* env = getenv("SPEC_TREE_ATTN_SHAPE")) {  // "NW,RW,NS[,SPS]" for sweeps
+    int nw = 0, rw = 0, ns = 0, sps = 1;
+    const int n = sscanf(env, "%d,%d,%d,%d", &nw, &rw, &ns, &sps);
+    const bool single = (nw == 4 || nw == 8) && (rw == 1 || (rw == 2 && nw == 4)) && (ns == 3 || ns == 4) && sps == 1;
+    const bool pair = rw == 1 && (nw == 4 || nw == 8) && (ns == 4 || ns == 6) && sps == 2;
+    if (n >= 3 && (single || pair)) pl.sh = AttnShape{nw, rw, ns, sps};
   }
   if (d == 64) pl.sh.NW = 4;
   const int cap = pl.sh.NW * pl.sh.RW;
@@ -605,10 +628,19 @@ AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_p
 
 template <int D, int NW, int RW>
 void launch_ns(const AttnPlan& pl, const AttnParams& prm, dim3 grid, hipStream_t st) {
+  if constexpr (D == 128 && RW == 1) {  // two-stage steps
+    if (pl.sh.SPS == 2) {
+      if (pl.sh.NS == 6)
+        hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 6, 2>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+      else
+        hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 4, 2>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+      return;
+    }
+  }
   if (pl.sh.NS == 3)
-    hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 3>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+    hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 3, 1>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
   else
-    hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 4>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+    hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 4, 1>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
 }
 
 template <int D>
