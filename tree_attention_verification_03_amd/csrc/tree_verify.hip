@@ -132,10 +132,19 @@ __device__ __forceinline__ void greedy_slice(const VerifyWs& w, const VerifyArgs
   const float* r = a.target + size_t(row) * a.V;
   uint64_t best = 0;
   bool nan = false;
-  if (VEC) {
-#pragma unroll 2
-    for (int v = lo + 4 * tid; v < hi; v += 4 * kThreads) {
-      const float4 x = *reinterpret_cast<const float4*>(r + v);
+  if (VEC) {  // a slice is at most kSampleSlice elements: all of a thread's loads in one round trip
+    constexpr int NV = kSampleSlice / (4 * kThreads);
+    float4 xs[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = lo + 4 * tid + 4 * kThreads * i;
+      xs[i] = v < hi ? *reinterpret_cast<const float4*>(r + v) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = lo + 4 * tid + 4 * kThreads * i;
+      if (v >= hi) continue;
+      const float4 x = xs[i];
       nan |= (x.x != x.x) | (x.y != x.y) | (x.z != x.z) | (x.w != x.w);
       uint64_t k0 = argmax_key(x.x, v), k1 = argmax_key(x.y, v + 1), k2 = argmax_key(x.z, v + 2), k3 = argmax_key(x.w, v + 3);
       k0 = k0 > k1 ? k0 : k1;
@@ -918,10 +927,8 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
   size_t need = 0;
   VerifyWs w = carve(ws, B, max_T, V, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_verify: workspace %zu < %zu bytes", ws_bytes, need);
-  // greedy slices: whole block passes (1 K elements), about 512 slice blocks per launch
-  long long sl = ((long long)V * rows + 511) / 512;
-  sl = (sl + 1023) / 1024 * 1024;
-  if (sl > 65536) sl = 65536;
+  // greedy slices of kSampleSlice elements (one round trip per block; fewer blocks per sequence ticket)
+  const long long sl = kSampleSlice;
   VerifyArgs a;
   a.target = target;
   a.draft = draft_probs;
