@@ -30,7 +30,8 @@ namespace {
 constexpr int kMaxTopk = 8;
 constexpr int kMaxDepth = 16;
 constexpr int kRowThreads = 256;
-constexpr int kMaxSlices = 64;  // blocks per draft row (n_slices * max_topk <= 64 candidates per row)
+constexpr int kMaxSlices = 128;  // blocks per draft row (n_slices * max_topk <= 128 candidates per row)
+constexpr int kBatch = 8 * 4 * kRowThreads;  // row elements whose loads a block issues together (8 float4 per thread)
 constexpr int kFinishThreads = 256;
 
 struct BuildWs {
@@ -107,14 +108,23 @@ __device__ void block_slice_topk(const float* row, int lo, int hi, int k, uint64
       }
     }
   };
-  if (VEC) {
-#pragma unroll 4
-    for (int v = lo + 4 * threadIdx.x; v < hi; v += 4 * kRowThreads) {
-      const float4 x = *reinterpret_cast<const float4*>(row + v);
-      insert(lp_key(x.x, v));
-      insert(lp_key(x.y, v + 1));
-      insert(lp_key(x.z, v + 2));
-      insert(lp_key(x.w, v + 3));
+  if (VEC) {  // kBatch elements per round trip (a slice is normally one batch)
+    for (int base = lo; base < hi; base += kBatch) {
+      float4 xs[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int v = base + 4 * threadIdx.x + 4 * kRowThreads * i;
+        xs[i] = v < hi ? *reinterpret_cast<const float4*>(row + v) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int v = base + 4 * threadIdx.x + 4 * kRowThreads * i;
+        if (v >= hi) continue;
+        insert(lp_key(xs[i].x, v));
+        insert(lp_key(xs[i].y, v + 1));
+        insert(lp_key(xs[i].z, v + 2));
+        insert(lp_key(xs[i].w, v + 3));
+      }
     }
   } else {
 #pragma unroll 4
@@ -151,8 +161,8 @@ __global__ void __launch_bounds__(kRowThreads) build_step_kernel(BuildWs w, int 
                                                                   int64_t seq_stride, const int32_t* topk,
                                                                   const int32_t* depth, int max_topk, int max_depth,
                                                                   int V, int slice, int32_t* frontier_tokens) {
-  constexpr int kCand = 64;  // candidates per row (n_slices * k)
-  __shared__ uint64_t keys[kMaxSlices * kMaxTopk];
+  constexpr int kCand = 128;  // candidates per row (n_slices * k)
+  __shared__ uint64_t keys[kMaxTopk];
   __shared__ uint64_t ck[kMaxTopk * kCand];     // [row][slice * k + j]
   __shared__ uint64_t top[kMaxTopk * kMaxTopk];  // [row][rank]
   __shared__ double csc[kMaxTopk * kMaxTopk];    // child scores [row * k + c]
@@ -395,9 +405,12 @@ extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step,
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_step: workspace %zu < %zu bytes", ws_bytes, need);
   const int P = int(pool_cap(max_topk, max_depth));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // slices of >= 1024 elements; at most 64 / max_topk slices per row, so a row has <= 64 candidates
-  const int max_sl = std::max(1, 64 / max_topk);
-  int n_slices = std::min((V + 1023) / 1024, max_sl);
+  // about 64 blocks per sequence and step, and slices of at most one load batch (8 K elements) where
+  // possible; at most 128 / max_topk slices per row, so a row has <= 128 candidates; >= 1 K per slice
+  const int max_sl = std::max(1, 128 / max_topk);
+  const int rows = step == 1 ? 1 : max_topk;
+  int n_slices = std::max(64 / rows, (V + kBatch - 1) / kBatch);
+  n_slices = std::max(1, std::min(std::min(n_slices, max_sl), (V + 1023) / 1024));
   int slice = (V + n_slices - 1) / n_slices;
   slice = (slice + 1023) / 1024 * 1024;
   n_slices = (V + slice - 1) / slice;
