@@ -91,8 +91,7 @@ __device__ __forceinline__ int key_token(uint64_t key) { return int(0xffffffffu 
 // Block-wide top-k (k <= 8) of row[lo, hi); results (rank order, 0 = none) in out_key[0..k).
 template <bool VEC>
 __device__ void block_slice_topk(const float* row, int lo, int hi, int k, uint64_t* out_key) {
-  __shared__ uint64_t red[kRowThreads / kWave];
-  __shared__ uint64_t win;
+  __shared__ uint64_t wtop[(kRowThreads / kWave) * kMaxTopk];
   uint64_t best[kMaxTopk];
 #pragma unroll
   for (int j = 0; j < kMaxTopk; ++j) best[j] = 0;
@@ -130,25 +129,29 @@ __device__ void block_slice_topk(const float* row, int lo, int hi, int k, uint64
 #pragma unroll 4
     for (int v = lo + threadIdx.x; v < hi; v += kRowThreads) insert(lp_key(row[v], v));
   }
+  // each wave pops its own top k (wave maxima, no barriers; keys are unique, so exactly one lane owns
+  // each maximum), then the block ranks the waves' 4k candidates: rank = number of larger candidates
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int r = 0; r < k; ++r) {
     const uint64_t m = wave_max_u64(best[0]);
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint64_t x = red[0];
-      for (int w2 = 1; w2 < kRowThreads / kWave; ++w2) x = red[w2] > x ? red[w2] : x;
-      win = x;
-      out_key[r] = x;
-    }
-    __syncthreads();
-    if (best[0] == win && win != 0) {  // keys are unique (distinct tokens): exactly one owner pops
+    if (lane == 0) wtop[wave * kMaxTopk + r] = m;
+    if (best[0] == m && m != 0) {
 #pragma unroll
       for (int j = 0; j < kMaxTopk - 1; ++j) best[j] = best[j + 1];
       best[kMaxTopk - 1] = 0;
     }
-    __syncthreads();
   }
+  if (threadIdx.x < k) out_key[threadIdx.x] = 0;  // fewer than k keys in the slice: the rest stay empty
+  __syncthreads();
+  constexpr int NWV = kRowThreads / kWave;
+  if (threadIdx.x < NWV * k) {
+    const int wv = threadIdx.x / k, r = threadIdx.x - wv * k;
+    const uint64_t key = wtop[wv * kMaxTopk + r];
+    int rank = 0;
+    for (int o = 0; o < NWV * k; ++o) rank += wtop[(o / k) * kMaxTopk + o % k] > key;
+    if (key != 0 && rank < k) out_key[rank] = key;  // nonzero keys are unique
+  }
+  __syncthreads();
 }
 
 // One kernel for every step. Block (slice x, frontier slot f, sequence b) reduces a slice of
