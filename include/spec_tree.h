@@ -91,7 +91,10 @@ const char* spec_last_error(void);
  *
  * Draft rows: the caller's draft model produces, for step d, one log-prob row
  * per frontier slot; rows for sequence b, slot f start at
- * draft_logprobs + b * seq_stride + f * V (fp32). Step 1 reads slot 0 only.
+ * draft_logprobs + b * seq_stride + f * V (fp32). Step 1 reads slot 0 only;
+ * step d >= 2 reads slots f < max_topk of EVERY sequence (rows past k_b and
+ * rows of sequences with D_b < d are read and ignored), so the buffer holds
+ * (B - 1) * seq_stride + max_topk * V floats.
  * Per-sequence k, D, N are device int32 [B] arrays; values outside
  * [1, max_topk], [1, max_depth], [1, min(pool, max_T - 1)] are clamped.
  * ------------------------------------------------------------------------- */

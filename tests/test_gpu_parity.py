@@ -128,6 +128,51 @@ def test_tree_build_ragged(seed):
     check_build(w, host, oracle_trees(w))
 
 
+def _structured_row(pattern, V, rng):
+    """Draft rows whose best tokens crowd into few threads of a slice: descending / ascending values,
+    a constant row (ties broken by token), and a row whose best values sit on tokens 4 t + 1024 i + c
+    of one thread t, with a few NaN / +inf / -inf entries in the last one."""
+    if pattern == "descending":
+        return -np.arange(V, dtype=np.float32) / V
+    if pattern == "ascending":
+        return np.arange(V, dtype=np.float32) / V - 2.0
+    if pattern == "constant":
+        return np.full(V, -3.0, dtype=np.float32)
+    row = (-5.0 - rng.random(V)).astype(np.float32)
+    t = int(rng.integers(0, 256))
+    idx = np.array([4 * t + 1024 * i + c for i in range(8) for c in range(4)])
+    idx = idx[idx < V]
+    row[idx] = -np.linspace(0.01, 1.0, len(idx), dtype=np.float32)
+    row[int(rng.integers(0, V))] = np.nan
+    row[int(rng.integers(0, V))] = np.inf
+    row[int(rng.integers(0, V))] = -np.inf
+    return row
+
+
+# large vocabularies (slices of one or several load batches, up to four candidates per lane in the
+# row merge) with rows that make one thread hold several of a slice's best keys
+@pytest.mark.parametrize("V", [128256, 300000, 300001])
+def test_tree_build_structured_rows(V):
+    rng = np.random.default_rng(V)
+    B = 2
+    topk, depth, nd = [8, 5], [3, 3], [40, 12]
+    w = make_workload(name="build", B=B, Hq=2, Hkv=1, d=64, prefix=16, topk=topk, depth=depth, num_draft=nd, V=V,
+                      seed=5, max_topk=8, max_depth=3)
+    patterns = ["descending", "ascending", "constant", "crowded"]
+    for b in range(B):
+        for r in range(w.draft_logprobs.shape[1]):
+            w.draft_logprobs[b, r] = _structured_row(patterns[(b + r) % 4], V, rng)
+    log(f"[build] structured rows V={V} topk={topk} depth={depth} N={nd}")
+    from tree_attention_verification_03_amd.pipeline import DeviceWorkload, SpecTreeStep
+
+    dw = DeviceWorkload(w)
+    step = SpecTreeStep(dw)
+    step.build()
+    torch.cuda.synchronize()
+    host = {k: to_np(getattr(step.o, k)) for k in ("tokens", "parents", "depth", "anc", "q_row", "frontier")}
+    check_build(w, host, oracle_trees(w))
+
+
 # every block shape the plan can pick (waves, row tiles per wave, ring stages, stages per softmax step),
 # on rows spanning several row blocks, with unaligned key chunks and tree slots straddling two items
 ATTN_SHAPES = ["4,1,3", "4,1,4", "4,2,3", "4,2,4", "8,1,3", "8,1,4", "4,1,4,2", "4,1,6,2", "8,1,4,2", "8,1,6,2"]

@@ -30,8 +30,9 @@ namespace {
 constexpr int kMaxTopk = 8;
 constexpr int kMaxDepth = 16;
 constexpr int kRowThreads = 256;
-constexpr int kMaxSlices = 128;  // blocks per draft row (n_slices * max_topk <= 128 candidates per row)
-constexpr int kBatch = 8 * 4 * kRowThreads;  // row elements whose loads a block issues together (8 float4 per thread)
+constexpr int kCandPerLane = 4;
+constexpr int kCand = kCandPerLane * kWave;  // candidates per draft row (n_slices * k), four per lane of the merging wave
+constexpr int kMaxEpl = 32;                  // row elements per thread and load batch: 8, 16 or 32
 constexpr int kFinishThreads = 256;
 
 struct BuildWs {
@@ -41,8 +42,9 @@ struct BuildWs {
   int32_t* fslot;  // [B, P] frontier slot held at its own step, -1 if never frontier
   double* score;   // [B, P]
   int32_t* frontier;  // [B, max_topk] pool indices, rank order
+  double* fscore;     // [B, max_topk] their scores
   uint32_t* ticket;   // [B] blocks of the sequence's step that have finished
-  uint64_t* cand;     // [B, max_topk, kMaxSlices, kMaxTopk] per-slice top-k keys
+  uint64_t* cand;     // [B, max_topk, kCand] per-slice top-k keys, slice x at x * k
 };
 
 size_t pool_cap(int max_topk, int max_depth) {
@@ -65,8 +67,9 @@ BuildWs carve(void* ws, int B, int max_topk, int max_depth, size_t* total) {
   w.depth = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * P));
   w.fslot = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * P));
   w.frontier = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * max_topk));
+  w.fscore = reinterpret_cast<double*>(take(sizeof(double) * B * max_topk));
   w.ticket = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B));
-  w.cand = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * B * max_topk * kMaxSlices * kMaxTopk));
+  w.cand = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * B * max_topk * kCand));
   *total = off;
   return w;
 }
@@ -88,177 +91,322 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 
 __device__ __forceinline__ int key_token(uint64_t key) { return int(0xffffffffu - uint32_t(key)); }
 
-// Block-wide top-k (k <= 8) of row[lo, hi); results (rank order, 0 = none) in out_key[0..k).
+// Element j of a thread in the batch that starts at `base`: VEC -> base + 4 * tid + 4 * kRowThreads *
+// (j / 4) + j % 4, scalar -> base + tid + kRowThreads * j (both visit a thread's tokens in increasing
+// order).
 template <bool VEC>
-__device__ void block_slice_topk(const float* row, int lo, int hi, int k, uint64_t* out_key) {
-  __shared__ uint64_t wtop[(kRowThreads / kWave) * kMaxTopk];
-  uint64_t best[kMaxTopk];
+__device__ __forceinline__ int batch_token(int base, int j) {
+  return VEC ? base + 4 * int(threadIdx.x) + 4 * kRowThreads * (j >> 2) + (j & 3)
+             : base + int(threadIdx.x) + kRowThreads * j;
+}
+
+// Loads one batch of EPL elements per thread without branches: addresses past `hi` are clamped into
+// the slice (those elements are masked out later), so every load of the batch is in flight at once.
+template <bool VEC, int EPL>
+__device__ __forceinline__ void load_batch(const float* row, int base, int hi, float* xs) {
+  if (VEC) {
 #pragma unroll
-  for (int j = 0; j < kMaxTopk; ++j) best[j] = 0;
-  auto insert = [&](uint64_t key) {
-    if (key > best[kMaxTopk - 1]) {
+    for (int i = 0; i < EPL / 4; ++i) {
+      const int v = min(batch_token<VEC>(base, 4 * i), hi - 4);
+      const float4 q = *reinterpret_cast<const float4*>(row + v);
+      xs[4 * i] = q.x;
+      xs[4 * i + 1] = q.y;
+      xs[4 * i + 2] = q.z;
+      xs[4 * i + 3] = q.w;
+    }
+  } else {
 #pragma unroll
-      for (int j = 0; j < kMaxTopk; ++j) {
-        if (key > best[j]) {
-          const uint64_t t = best[j];
-          best[j] = key;
-          key = t;
+    for (int j = 0; j < EPL; ++j) xs[j] = row[min(batch_token<VEC>(base, j), hi - 1)];
+  }
+}
+
+// Top-2 lists (t0 > t1, 0 = none) merged: the larger head, then the larger of the winner's second
+// and the loser's head.
+__device__ __forceinline__ void top2_merge(uint64_t a0, uint64_t a1, uint64_t b0, uint64_t b1, uint64_t& t0,
+                                           uint64_t& t1) {
+  const bool c = a0 > b0;
+  const uint64_t x = c ? a1 : b1, y = c ? b0 : a0;
+  t0 = c ? a0 : b0;
+  t1 = x > y ? x : y;
+}
+
+// Two largest keys of this thread's elements of one batch (those below `below` if BOUNDED), folded
+// into the sorted cache c[0..2) by a balanced tree of merges, so the compare chains are independent.
+template <bool VEC, int EPL, bool BOUNDED>
+__device__ __forceinline__ void lane_top2(const float* xs, int base, int hi, uint64_t below, uint64_t* c) {
+  const bool full = base + EPL * kRowThreads <= hi;
+  uint64_t t0[EPL / 2], t1[EPL / 2];
+#pragma unroll
+  for (int i = 0; i < EPL / 2; ++i) {
+    uint64_t k2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = 2 * i + h, v = batch_token<VEC>(base, j);
+      uint64_t key = (full || v < hi) ? lp_key(xs[j], v) : 0ull;
+      if (BOUNDED) key = key < below ? key : 0ull;
+      k2[h] = key;
+    }
+    const bool g = k2[0] > k2[1];
+    t0[i] = g ? k2[0] : k2[1];
+    t1[i] = g ? k2[1] : k2[0];
+  }
+#pragma unroll
+  for (int w = 1; w < EPL / 2; w *= 2) {
+#pragma unroll
+    for (int i = 0; i + w < EPL / 2; i += 2 * w) top2_merge(t0[i], t1[i], t0[i + w], t1[i + w], t0[i], t1[i]);
+  }
+  top2_merge(c[0], c[1], t0[0], t1[0], c[0], c[1]);
+}
+
+// ------------------------------------------------------------------ wave-wide selection
+// Wave maximum of a u32, uniform: DPP steps within each 16-lane row (fused into the max), the row
+// broadcasts carry rows 0-1 into 1 and 2-3 into 3, then 0-1 into 2-3, so lane 63 holds the maximum.
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_max_rows(uint32_t v) {
+  return max(v, uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, ROWS, 0xf, false)));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_rows<dpp::kXor1, 0xf>(v);
+  v = dpp_max_rows<dpp::kXor2, 0xf>(v);
+  v = dpp_max_rows<dpp::kHalfMirror, 0xf>(v);
+  v = dpp_max_rows<dpp::kMirror, 0xf>(v);
+  v = dpp_max_rows<kRowBcast15, 0xa>(v);
+  v = dpp_max_rows<kRowBcast31, 0xc>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+struct Popped {
+  uint64_t key;  // the wave's largest head key (0 = none left)
+  int lane;      // the lowest lane holding it
+};
+
+// Takes the largest of the lanes' heads c[0] (every lane of the wave active; caches sorted, 0 =
+// none): the high words are reduced first, the low words only if several lanes share the largest
+// high word; the lowest lane holding the maximum gives it up (shifts its cache), so equal keys
+// leave in lane order.
+template <int N>
+__device__ __forceinline__ Popped wave_pop(uint64_t* c) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t hi = uint32_t(c[0] >> 32), lo = uint32_t(c[0]);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint64_t tied = __ballot(hi == mh);
+  uint32_t ml;
+  if (__popcll(tied) == 1)
+    ml = __builtin_amdgcn_readlane(lo, __ffsll(static_cast<unsigned long long>(tied)) - 1);
+  else
+    ml = wave_max_u32(hi == mh ? lo : 0u);
+  Popped p;
+  p.key = (uint64_t(mh) << 32) | ml;
+  p.lane = __ffsll(static_cast<unsigned long long>(__ballot(c[0] == p.key))) - 1;
+  if (lane == p.lane && p.key != 0) {
+#pragma unroll
+    for (int i = 0; i + 1 < N; ++i) c[i] = c[i + 1];
+    c[N - 1] = 0;
+  }
+  return p;
+}
+
+// Block-wide top-k (k <= 8) of row[lo, hi) in rank order (0 = none) in out_key[0..k).
+// xs holds the first batch (load_batch(row, lo, hi, xs)). Every lane keeps the two largest keys of
+// its own elements; each wave pops its k largest (a lane that gives up both refills them with its
+// largest keys below the last one taken, so the pops are exact), and wave 0 pops the k best of the
+// waves' lists.
+template <bool VEC, int EPL>
+__device__ __forceinline__ void block_slice_topk(const float* row, int lo, int hi, int k, float* xs,
+                                                 uint64_t* out_key) {
+  constexpr int NWV = kRowThreads / kWave;
+  constexpr int kBatch = EPL * kRowThreads;
+  __shared__ uint64_t wk[NWV * kMaxTopk];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  uint64_t c[2] = {0, 0};
+  for (int base = lo; base < hi; base += kBatch) {
+    if (base != lo) load_batch<VEC, EPL>(row, base, hi, xs);
+    lane_top2<VEC, EPL, false>(xs, base, hi, 0, c);
+  }
+  const bool one_batch = hi - lo <= kBatch;
+  uint64_t mine = 0;
+  for (int r = 0; r < k; ++r) {
+    const Popped p = wave_pop<2>(c);
+    if (lane == r) mine = p.key;
+    if (lane == p.lane && p.key != 0 && c[0] == 0 && r + 1 < k) {
+      // this lane gave both cached keys: refill with its two largest below the one just taken
+      if (one_batch) {
+        lane_top2<VEC, EPL, true>(xs, lo, hi, p.key, c);
+      } else {
+        for (int base = lo; base < hi; base += kBatch) {
+          load_batch<VEC, EPL>(row, base, hi, xs);
+          lane_top2<VEC, EPL, true>(xs, base, hi, p.key, c);
         }
       }
     }
-  };
-  if (VEC) {  // kBatch elements per round trip (a slice is normally one batch)
-    for (int base = lo; base < hi; base += kBatch) {
-      float4 xs[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int v = base + 4 * threadIdx.x + 4 * kRowThreads * i;
-        xs[i] = v < hi ? *reinterpret_cast<const float4*>(row + v) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int v = base + 4 * threadIdx.x + 4 * kRowThreads * i;
-        if (v >= hi) continue;
-        insert(lp_key(xs[i].x, v));
-        insert(lp_key(xs[i].y, v + 1));
-        insert(lp_key(xs[i].z, v + 2));
-        insert(lp_key(xs[i].w, v + 3));
-      }
-    }
-  } else {
-#pragma unroll 4
-    for (int v = lo + threadIdx.x; v < hi; v += kRowThreads) insert(lp_key(row[v], v));
   }
-  // each wave pops its own top k (wave maxima, no barriers; keys are unique, so exactly one lane owns
-  // each maximum), then the block ranks the waves' 4k candidates: rank = number of larger candidates
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = 0; r < k; ++r) {
-    const uint64_t m = wave_max_u64(best[0]);
-    if (lane == 0) wtop[wave * kMaxTopk + r] = m;
-    if (best[0] == m && m != 0) {
-#pragma unroll
-      for (int j = 0; j < kMaxTopk - 1; ++j) best[j] = best[j + 1];
-      best[kMaxTopk - 1] = 0;
-    }
-  }
-  if (threadIdx.x < k) out_key[threadIdx.x] = 0;  // fewer than k keys in the slice: the rest stay empty
+  if (lane < k) wk[wave * k + lane] = mine;
   __syncthreads();
-  constexpr int NWV = kRowThreads / kWave;
-  if (threadIdx.x < NWV * k) {
-    const int wv = threadIdx.x / k, r = threadIdx.x - wv * k;
-    const uint64_t key = wtop[wv * kMaxTopk + r];
-    int rank = 0;
-    for (int o = 0; o < NWV * k; ++o) rank += wtop[(o / k) * kMaxTopk + o % k] > key;
-    if (key != 0 && rank < k) out_key[rank] = key;  // nonzero keys are unique
+  if (wave == 0) {
+    uint64_t v = lane < NWV * k ? wk[lane] : 0ull, best = 0;
+    for (int r = 0; r < k; ++r) {
+      const Popped p = wave_pop<1>(&v);
+      if (lane == r) best = p.key;
+    }
+    if (lane < k) out_key[lane] = best;
   }
   __syncthreads();
 }
 
 // One kernel for every step. Block (slice x, frontier slot f, sequence b) reduces a slice of
 // step-`step` draft row f to its top-k keys and publishes them; the last block of the sequence's
-// step to finish (ticket) merges, in LDS, the slices of every row: at step 1 the root row fills the
-// pool and the frontier; at step >= 2 the k rows' k children join the pool (score = parent score +
-// log-prob, an fp64 left fold), the k*k children are ranked and the best k form the next frontier.
-template <bool VEC>
+// step to finish (ticket) merges the slices of every row: at step 1 the root row fills the pool and
+// the frontier; at step >= 2 the k rows' k children join the pool (score = parent score + log-prob,
+// an fp64 left fold), the k*k children are ranked and the best k form the next frontier.
+// Every block reads its row slice before it knows k_b and D_b (rows f < gridDim.y must exist), and
+// the frontier with its scores, so that those latencies overlap.
+template <bool VEC, int EPL>
 __global__ void __launch_bounds__(kRowThreads) build_step_kernel(BuildWs w, int P, int step, const float* draft,
                                                                   int64_t seq_stride, const int32_t* topk,
                                                                   const int32_t* depth, int max_topk, int max_depth,
                                                                   int V, int slice, int32_t* frontier_tokens) {
-  constexpr int kCand = 128;  // candidates per row (n_slices * k)
+  constexpr int NWV = kRowThreads / kWave;
   __shared__ uint64_t keys[kMaxTopk];
-  __shared__ uint64_t ck[kMaxTopk * kCand];     // [row][slice * k + j]
   __shared__ uint64_t top[kMaxTopk * kMaxTopk];  // [row][rank]
-  __shared__ double csc[kMaxTopk * kMaxTopk];    // child scores [row * k + c]
+  __shared__ double fsc_s[kMaxTopk];
   __shared__ int cpar[kMaxTopk];
   __shared__ int last;
-  const int x = blockIdx.x, f = blockIdx.y, b = blockIdx.z;
+  const int x = blockIdx.x, f = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
   const int n_slices = gridDim.x;
-  const int k = clamp_i(topk[b], 1, max_topk);
-  const int D = clamp_i(depth[b], 1, max_depth);
-  const int rows = step == 1 ? 1 : k;
-  if (step > D || f >= rows) return;
   const float* row = draft + b * seq_stride + int64_t(f) * V;
   const int lo = x * slice, hi = min(V, lo + slice);
-  uint64_t* cand = w.cand + ((size_t(b) * max_topk + f) * kMaxSlices + x) * kMaxTopk;
-  block_slice_topk<VEC>(row, lo, hi, k, keys);
-  if (threadIdx.x < k) st_agent(cand + threadIdx.x, keys[threadIdx.x]);
+  float xs[EPL];
+  load_batch<VEC, EPL>(row, lo, hi, xs);
+  const int k_in = topk[b], d_in = depth[b];
+  int fpar = 0;
+  double fsc = 0.0;
+  if (step >= 2 && tid < max_topk) {
+    fpar = w.frontier[b * max_topk + tid];
+    fsc = w.fscore[b * max_topk + tid];
+  }
+  const int k = clamp_i(k_in, 1, max_topk);
+  block_slice_topk<VEC, EPL>(row, lo, hi, k, xs, keys);
+  const int D = clamp_i(d_in, 1, max_depth);
+  const int rows = step == 1 ? 1 : k;
+  if (step > D || f >= rows) return;
+  uint64_t* cand = w.cand + (size_t(b) * max_topk + f) * kCand + x * k;
+  if (tid < k) st_agent(cand + tid, keys[tid]);
   wait_global_stores();
   __syncthreads();
-  if (threadIdx.x == 0) last = (ticket_add(w.ticket + b) == uint32_t(n_slices * rows - 1));
+  if (tid == 0) last = (ticket_add(w.ticket + b) == uint32_t(n_slices * rows - 1));
   __syncthreads();
   if (!last) return;
-  if (threadIdx.x == 0) ticket_reset(w.ticket + b);  // leave the workspace ready for the next step
+  if (tid == 0) ticket_reset(w.ticket + b);  // leave the workspace ready for the next step
 
-  // every row's candidates (0 = empty), and at step >= 2 the rows' parents and their scores
+  // every row's n_slices * k <= kCand candidates (0 = empty); wave w merges rows w and w + NWV,
+  // each lane holding up to four candidates of a row
   const int nc = n_slices * k;
-  for (int i = threadIdx.x; i < rows * nc; i += kRowThreads) {
-    const int r = i / nc, j = i - r * nc;
-    ck[r * kCand + j] = ld_agent(w.cand + ((size_t(b) * max_topk + r) * kMaxSlices + j / k) * kMaxTopk + j % k);
+  uint64_t cv[2][kCandPerLane];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+#pragma unroll
+    for (int h = 0; h < kCandPerLane; ++h) {
+      const int r = wave + it * NWV, j = lane + h * kWave;
+      cv[it][h] = (r < rows && j < nc) ? ld_agent(w.cand + (size_t(b) * max_topk + r) * kCand + j) : 0ull;
+    }
+  }
+  if (tid < k) {
+    cpar[tid] = fpar;
+    fsc_s[tid] = fsc;
   }
   const int base = k + (step - 2) * k * k;  // pool index of this step's first child (step >= 2)
-  double psc = 0.0;
-  if (step >= 2 && threadIdx.x < k) {
-    cpar[threadIdx.x] = w.frontier[b * max_topk + threadIdx.x];
+  // row r's k best in rank order: k pops (a lane holds all of its candidates); a wave with two rows
+  // runs both in the same rounds, so the two chains overlap
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    uint64_t* q = cv[it];
+    auto cs = [](uint64_t& x, uint64_t& y) {
+      const bool g = y > x;
+      const uint64_t t = g ? y : x;
+      y = g ? x : y;
+      x = t;
+    };
+    cs(q[0], q[1]);
+    cs(q[2], q[3]);
+    cs(q[0], q[2]);
+    cs(q[1], q[3]);
+    cs(q[1], q[2]);
   }
-  __syncthreads();
-  // per row top-k: rank = number of larger keys (keys of one row are unique; 0 = empty)
-  for (int i = threadIdx.x; i < rows * nc; i += kRowThreads) {
-    const int r = i / nc;
-    const uint64_t ki = ck[r * kCand + (i - r * nc)];
-    if (ki == 0) continue;
-    int rank = 0;
-    for (int j = 0; j < nc; ++j) rank += ck[r * kCand + j] > ki;
-    if (rank < k) top[r * kMaxTopk + rank] = ki;
+  if (wave < rows) {
+    const bool two = wave + NWV < rows;
+    uint64_t r0 = 0, r1 = 0;
+    for (int r = 0; r < k; ++r) {
+      const Popped p0 = wave_pop<kCandPerLane>(cv[0]);
+      if (lane == r) r0 = p0.key;
+      if (two) {
+        const Popped p1 = wave_pop<kCandPerLane>(cv[1]);
+        if (lane == r) r1 = p1.key;
+      }
+    }
+    if (lane < k) {
+      top[wave * kMaxTopk + lane] = r0;
+      if (two) top[(wave + NWV) * kMaxTopk + lane] = r1;
+    }
   }
-  if (step >= 2 && threadIdx.x < k * k) psc = w.score[size_t(b) * P + cpar[threadIdx.x / k]];
   __syncthreads();
 
   if (step == 1) {
-    if (threadIdx.x < max_topk) {
-      const int c = threadIdx.x;
+    if (tid < max_topk) {
+      const int c = tid;
       int tok = -1;
       if (c < k) {
         const size_t e = size_t(b) * P + c;
+        const double sc = 0.0 + double(key_value(top[c]));
         tok = key_token(top[c]);
         w.tok[e] = tok;
         w.par[e] = -1;
         w.depth[e] = 1;
         w.fslot[e] = c;
-        w.score[e] = 0.0 + double(key_value(top[c]));
+        w.score[e] = sc;
         w.frontier[b * max_topk + c] = c;
+        w.fscore[b * max_topk + c] = sc;
       }
       frontier_tokens[b * max_topk + c] = tok;
     }
     return;
   }
 
-  // children: row r's c-th best token becomes pool entry base + r * k + c
-  const int n = k * k;
-  if (threadIdx.x < n) {
-    const int r = threadIdx.x / k, c = threadIdx.x - r * k;
-    const uint64_t key = top[r * kMaxTopk + c];
-    const size_t e = size_t(b) * P + base + threadIdx.x;
-    const double sc = psc + double(key_value(key));
-    csc[threadIdx.x] = sc;
-    w.tok[e] = key_token(key);
-    w.par[e] = cpar[r];
-    w.depth[e] = step;
-    w.score[e] = sc;
-  }
-  __syncthreads();
-  // rank the k*k children: rank(c) = #children that beat c (higher score, ties -> smaller pool index)
-  if (threadIdx.x < n) {
-    const int c = threadIdx.x;
-    const double sc = csc[c];
-    int rank = 0;
-    for (int o = 0; o < n; ++o) rank += (csc[o] > sc) || (csc[o] == sc && o < c);
-    w.fslot[size_t(b) * P + base + c] = rank < k ? rank : -1;
-    if (rank < k) {
-      w.frontier[b * max_topk + rank] = base + c;
-      frontier_tokens[b * max_topk + rank] = key_token(top[(c / k) * kMaxTopk + c % k]);
+  // children (wave 0, one per lane): row r's c-th best token becomes pool entry base + r * k + c;
+  // the next frontier is the k best by score (ties -> smaller pool index): k pops of their scores'
+  // order keys, where the lowest lane wins ties
+  if (wave == 0) {
+    const int n = k * k;
+    const int r = lane / k, c = lane - r * k;
+    double sc = 0.0;
+    uint64_t key = 0, sk = 0;
+    if (lane < n) {
+      key = top[r * kMaxTopk + c];
+      sc = fsc_s[r] + double(key_value(key));
+      sk = f64_order_key(sc + 0.0);  // no NaN; +0.0 folds -0 into +0
+      const size_t e = size_t(b) * P + base + lane;
+      w.tok[e] = key_token(key);
+      w.par[e] = cpar[r];
+      w.depth[e] = step;
+      w.score[e] = sc;
+    }
+    int rank = -1;
+    for (int q = 0; q < k; ++q) {
+      const Popped p = wave_pop<1>(&sk);
+      if (lane == p.lane) rank = q;
+    }
+    if (lane < n) {
+      w.fslot[size_t(b) * P + base + lane] = rank;
+      if (rank >= 0) {
+        w.frontier[b * max_topk + rank] = base + lane;
+        w.fscore[b * max_topk + rank] = sc;
+        frontier_tokens[b * max_topk + rank] = key_token(key);
+      }
     }
   }
-  if (threadIdx.x >= k && threadIdx.x < max_topk) frontier_tokens[b * max_topk + threadIdx.x] = -1;
+  if (tid >= k && tid < max_topk) frontier_tokens[b * max_topk + tid] = -1;
 }
 
 __global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w, int P, const int32_t* root_tokens,
@@ -408,23 +556,37 @@ extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step,
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_step: workspace %zu < %zu bytes", ws_bytes, need);
   const int P = int(pool_cap(max_topk, max_depth));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // about 64 blocks per sequence and step, and slices of at most one load batch (8 K elements) where
-  // possible; at most 128 / max_topk slices per row, so a row has <= 128 candidates; >= 1 K per slice
-  const int max_sl = std::max(1, 128 / max_topk);
-  const int rows = step == 1 ? 1 : max_topk;
-  int n_slices = std::max(64 / rows, (V + kBatch - 1) / kBatch);
-  n_slices = std::max(1, std::min(std::min(n_slices, max_sl), (V + 1023) / 1024));
-  int slice = (V + n_slices - 1) / n_slices;
-  slice = (slice + 1023) / 1024 * 1024;
+  // about 512 blocks per launch, within: slices of at least 8 and at most 32 elements per thread
+  // (one load batch), and at most kCand / max_topk slices per row (a row's candidates fit the merging
+  // wave). EPL is the smallest of 8, 16, 32 that covers a slice in one batch; longer slices (large V)
+  // loop over batches of 32 per thread.
+  const int rows_grid = step == 1 ? 1 : max_topk;
+  const int max_sl = std::max(1, kCand / max_topk);
+  const int want = std::max(1, (512 + B * rows_grid - 1) / (B * rows_grid));
+  int n_slices = std::min(want, (V + 8 * kRowThreads - 1) / (8 * kRowThreads));
+  n_slices = std::max(n_slices, (V + kMaxEpl * kRowThreads - 1) / (kMaxEpl * kRowThreads));
+  n_slices = std::max(1, std::min(n_slices, max_sl));
+  const int per = (V + n_slices - 1) / n_slices;
+  int epl = 8;
+  while (epl < kMaxEpl && epl * kRowThreads < per) epl *= 2;
+  const int batch = epl * kRowThreads;
+  const int slice = (per + batch - 1) / batch * batch;
   n_slices = (V + slice - 1) / slice;
-  const dim3 grid(n_slices, step == 1 ? 1 : max_topk, B);
+  const dim3 grid(n_slices, rows_grid, B);
   const bool vec = (V % 4 == 0) && (seq_stride % 4 == 0) && ((reinterpret_cast<uintptr_t>(draft_logprobs) & 15) == 0);
-  if (vec)
-    hipLaunchKernelGGL(build_step_kernel<true>, grid, dim3(kRowThreads), 0, st, w, P, step, draft_logprobs, seq_stride,
-                       topk, depth, max_topk, max_depth, V, slice, frontier_tokens);
-  else
-    hipLaunchKernelGGL(build_step_kernel<false>, grid, dim3(kRowThreads), 0, st, w, P, step, draft_logprobs, seq_stride,
-                       topk, depth, max_topk, max_depth, V, slice, frontier_tokens);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kRowThreads), 0, st, w, P, step, draft_logprobs, seq_stride, topk, depth,
+                       max_topk, max_depth, V, slice, frontier_tokens);
+  };
+  if (vec) {
+    if (epl == 8) go(build_step_kernel<true, 8>);
+    else if (epl == 16) go(build_step_kernel<true, 16>);
+    else go(build_step_kernel<true, 32>);
+  } else {
+    if (epl == 8) go(build_step_kernel<false, 8>);
+    else if (epl == 16) go(build_step_kernel<false, 16>);
+    else go(build_step_kernel<false, 32>);
+  }
   return check_launch("spec_tree_build_step");
 }
 
