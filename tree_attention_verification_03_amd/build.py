@@ -55,8 +55,9 @@ def _compile(src: str) -> str:
 
 
 def _check_no_spills(src: str):
-    """The attention kernel's pipelined loop counts its own outstanding loads (s_waitcnt vmcnt(n));
-    scratch (spill) traffic would be counted too, so a spilling build is rejected."""
+    """The attention kernel's pipelined loop counts its own outstanding loads (s_waitcnt vmcnt(n)), so
+    scratch (spill) traffic would break its waits; the tree-build kernels are sized to stay resident
+    (registers for several blocks per CU). A spilling build of either is rejected."""
     cmd = [_hipcc(), "-x", "hip", *COMMON, "--offload-device-only", "-c", os.path.join(CSRC, src), "-o", os.devnull,
            "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -68,7 +69,8 @@ def _check_no_spills(src: str):
 
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    _check_no_spills("tree_attention.hip")
+    for src in ("tree_attention.hip", "tree_build.hip"):
+        _check_no_spills(src)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"

@@ -21,6 +21,8 @@
 // Ranking keys are exact: vocabulary top-k uses the 64-bit key
 // (order(logprob) << 32) | (2^32 - 1 - token); pool ranking compares fp64
 // scores, ties broken by the smaller pool index.
+#include <cstdlib>
+
 #include "api_common.h"
 #include "spec_common.h"
 
@@ -32,7 +34,8 @@ constexpr int kMaxDepth = 16;
 constexpr int kRowThreads = 256;
 constexpr int kCandPerLane = 4;
 constexpr int kCand = kCandPerLane * kWave;  // candidates per draft row (n_slices * k), four per lane of the merging wave
-constexpr int kMaxEpl = 32;                  // row elements per thread and load batch: 8, 16 or 32
+constexpr int kMaxEpl = 16;                  // row elements per thread and load batch: 8 or 16
+constexpr int kMaxBatches = 2;               // load batches per slice the block-count target may ask for
 constexpr int kFinishThreads = 256;
 
 struct BuildWs {
@@ -131,31 +134,36 @@ __device__ __forceinline__ void top2_merge(uint64_t a0, uint64_t a1, uint64_t b0
 }
 
 // Two largest keys of this thread's elements of one batch (those below `below` if BOUNDED), folded
-// into the sorted cache c[0..2) by a balanced tree of merges, so the compare chains are independent.
+// into the sorted cache c[0..2): groups of 8 elements reduce by a balanced tree of merges (independent
+// compare chains) and fold into the cache one group at a time, which bounds the live registers.
 template <bool VEC, int EPL, bool BOUNDED>
 __device__ __forceinline__ void lane_top2(const float* xs, int base, int hi, uint64_t below, uint64_t* c) {
+  constexpr int G = 8;
   const bool full = base + EPL * kRowThreads <= hi;
-  uint64_t t0[EPL / 2], t1[EPL / 2];
 #pragma unroll
-  for (int i = 0; i < EPL / 2; ++i) {
-    uint64_t k2[2];
+  for (int g0 = 0; g0 < EPL; g0 += G) {
+    uint64_t t0[G / 2], t1[G / 2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int j = 2 * i + h, v = batch_token<VEC>(base, j);
-      uint64_t key = (full || v < hi) ? lp_key(xs[j], v) : 0ull;
-      if (BOUNDED) key = key < below ? key : 0ull;
-      k2[h] = key;
+    for (int i = 0; i < G / 2; ++i) {
+      uint64_t k2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = g0 + 2 * i + h, v = batch_token<VEC>(base, j);
+        uint64_t key = (full || v < hi) ? lp_key(xs[j], v) : 0ull;
+        if (BOUNDED) key = key < below ? key : 0ull;
+        k2[h] = key;
+      }
+      const bool g = k2[0] > k2[1];
+      t0[i] = g ? k2[0] : k2[1];
+      t1[i] = g ? k2[1] : k2[0];
     }
-    const bool g = k2[0] > k2[1];
-    t0[i] = g ? k2[0] : k2[1];
-    t1[i] = g ? k2[1] : k2[0];
-  }
 #pragma unroll
-  for (int w = 1; w < EPL / 2; w *= 2) {
+    for (int w = 1; w < G / 2; w *= 2) {
 #pragma unroll
-    for (int i = 0; i + w < EPL / 2; i += 2 * w) top2_merge(t0[i], t1[i], t0[i + w], t1[i + w], t0[i], t1[i]);
+      for (int i = 0; i + w < G / 2; i += 2 * w) top2_merge(t0[i], t1[i], t0[i + w], t1[i + w], t0[i], t1[i]);
+    }
+    top2_merge(c[0], c[1], t0[0], t1[0], c[0], c[1]);
   }
-  top2_merge(c[0], c[1], t0[0], t1[0], c[0], c[1]);
 }
 
 // ------------------------------------------------------------------ wave-wide selection
@@ -212,7 +220,7 @@ __device__ __forceinline__ Popped wave_pop(uint64_t* c) {
 // xs holds the first batch (load_batch(row, lo, hi, xs)). Every lane keeps the two largest keys of
 // its own elements; each wave pops its k largest (a lane that gives up both refills them with its
 // largest keys below the last one taken, so the pops are exact), and wave 0 pops the k best of the
-// waves' lists.
+// waves' lists. xs is consumed (free after the lane pass).
 template <bool VEC, int EPL>
 __device__ __forceinline__ void block_slice_topk(const float* row, int lo, int hi, int k, float* xs,
                                                  uint64_t* out_key) {
@@ -222,23 +230,26 @@ __device__ __forceinline__ void block_slice_topk(const float* row, int lo, int h
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   uint64_t c[2] = {0, 0};
   for (int base = lo; base < hi; base += kBatch) {
-    if (base != lo) load_batch<VEC, EPL>(row, base, hi, xs);
+    float nxt[EPL];  // the next batch's loads are in flight while this one is reduced
+    const bool more = base + kBatch < hi;
+    if (more) load_batch<VEC, EPL>(row, base + kBatch, hi, nxt);
     lane_top2<VEC, EPL, false>(xs, base, hi, 0, c);
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) xs[j] = nxt[j];
+    }
   }
-  const bool one_batch = hi - lo <= kBatch;
   uint64_t mine = 0;
   for (int r = 0; r < k; ++r) {
     const Popped p = wave_pop<2>(c);
     if (lane == r) mine = p.key;
     if (lane == p.lane && p.key != 0 && c[0] == 0 && r + 1 < k) {
       // this lane gave both cached keys: refill with its two largest below the one just taken
-      if (one_batch) {
-        lane_top2<VEC, EPL, true>(xs, lo, hi, p.key, c);
-      } else {
-        for (int base = lo; base < hi; base += kBatch) {
-          load_batch<VEC, EPL>(row, base, hi, xs);
-          lane_top2<VEC, EPL, true>(xs, base, hi, p.key, c);
-        }
+      // (re-read from memory, so the batch's registers are free during the pops)
+      for (int base = lo; base < hi; base += kBatch) {
+        float ys[EPL];
+        load_batch<VEC, EPL>(row, base, hi, ys);
+        lane_top2<VEC, EPL, true>(ys, base, hi, p.key, c);
       }
     }
   }
@@ -263,7 +274,7 @@ __device__ __forceinline__ void block_slice_topk(const float* row, int lo, int h
 // Every block reads its row slice before it knows k_b and D_b (rows f < gridDim.y must exist), and
 // the frontier with its scores, so that those latencies overlap.
 template <bool VEC, int EPL>
-__global__ void __launch_bounds__(kRowThreads) build_step_kernel(BuildWs w, int P, int step, const float* draft,
+__global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, int P, int step, const float* draft,
                                                                   int64_t seq_stride, const int32_t* topk,
                                                                   const int32_t* depth, int max_topk, int max_depth,
                                                                   int V, int slice, int32_t* frontier_tokens) {
@@ -556,15 +567,26 @@ extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step,
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_step: workspace %zu < %zu bytes", ws_bytes, need);
   const int P = int(pool_cap(max_topk, max_depth));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // about 512 blocks per launch, within: slices of at least 8 and at most 32 elements per thread
-  // (one load batch), and at most kCand / max_topk slices per row (a row's candidates fit the merging
-  // wave). EPL is the smallest of 8, 16, 32 that covers a slice in one batch; longer slices (large V)
-  // loop over batches of 32 per thread.
+  // about 256 blocks per launch, within: slices of at least 8 elements per thread and of at most
+  // kMaxBatches load batches of 16 per thread, and at most kCand / max_topk slices per row (a row's
+  // candidates fit the merging wave). EPL is the smaller of 8, 16 that covers a slice in one batch,
+  // else 16 with several batches (each prefetched while the previous one is reduced). Registers stay
+  // within 5 waves per SIMD.
   const int rows_grid = step == 1 ? 1 : max_topk;
   const int max_sl = std::max(1, kCand / max_topk);
-  const int want = std::max(1, (512 + B * rows_grid - 1) / (B * rows_grid));
+  static const int target = [] {
+    const char* e = std::getenv("SPEC_TREE_BUILD_BLOCKS");  // blocks per launch (tuning override)
+    const int v = e ? std::atoi(e) : 0;
+    return v > 0 ? v : 256;
+  }();
+  static const int max_batches = [] {
+    const char* e = std::getenv("SPEC_TREE_BUILD_BATCHES");  // load batches per slice (tuning override)
+    const int v = e ? std::atoi(e) : 0;
+    return v > 0 ? std::min(v, kMaxBatches) : kMaxBatches;
+  }();
+  const int want = std::max(1, (target + B * rows_grid - 1) / (B * rows_grid));
   int n_slices = std::min(want, (V + 8 * kRowThreads - 1) / (8 * kRowThreads));
-  n_slices = std::max(n_slices, (V + kMaxEpl * kRowThreads - 1) / (kMaxEpl * kRowThreads));
+  n_slices = std::max(n_slices, (V + max_batches * kMaxEpl * kRowThreads - 1) / (max_batches * kMaxEpl * kRowThreads));
   n_slices = std::max(1, std::min(n_slices, max_sl));
   const int per = (V + n_slices - 1) / n_slices;
   int epl = 8;
@@ -580,12 +602,10 @@ extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step,
   };
   if (vec) {
     if (epl == 8) go(build_step_kernel<true, 8>);
-    else if (epl == 16) go(build_step_kernel<true, 16>);
-    else go(build_step_kernel<true, 32>);
+    else go(build_step_kernel<true, 16>);
   } else {
     if (epl == 8) go(build_step_kernel<false, 8>);
-    else if (epl == 16) go(build_step_kernel<false, 16>);
-    else go(build_step_kernel<false, 32>);
+    else go(build_step_kernel<false, 16>);
   }
   return check_launch("spec_tree_build_step");
 }
