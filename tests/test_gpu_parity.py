@@ -149,6 +149,27 @@ def _structured_row(pattern, V, rng):
     return row
 
 
+# deep trees: pools up to 8 + 15 * 64 = 968 entries (every slot width of the final selection), with
+# num_draft at the 64-node cap, a shallow sequence beside them, and ties in the pool scores
+@pytest.mark.parametrize("V", [1000, 4099])
+def test_tree_build_deep(V):
+    B = 4
+    topk, depth, nd = [8, 8, 3, 8], [16, 9, 16, 2], [64, 64, 40, 5]
+    w = make_workload(name="build", B=B, Hq=2, Hkv=1, d=64, prefix=16, topk=topk, depth=depth, num_draft=nd, V=V,
+                      seed=9, max_topk=8, max_depth=16)
+    # quantised log-probs make equal path scores common, so the pool-index tie-break decides
+    w.draft_logprobs[:] = np.round(w.draft_logprobs * 2.0) / 2.0
+    log(f"[build] deep trees V={V} topk={topk} depth={depth} N={nd}")
+    from tree_attention_verification_03_amd.pipeline import DeviceWorkload, SpecTreeStep
+
+    dw = DeviceWorkload(w)
+    step = SpecTreeStep(dw)
+    step.build()
+    torch.cuda.synchronize()
+    host = {k: to_np(getattr(step.o, k)) for k in ("tokens", "parents", "depth", "anc", "q_row", "frontier")}
+    check_build(w, host, oracle_trees(w))
+
+
 # large vocabularies (slices of one or several load batches, up to four candidates per lane in the
 # row merge) with rows that make one thread hold several of a slice's best keys
 @pytest.mark.parametrize("V", [128256, 300000, 300001])

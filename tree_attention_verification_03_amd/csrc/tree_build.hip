@@ -420,6 +420,68 @@ __global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, i
   if (tid >= k && tid < max_topk) frontier_tokens[b * max_topk + tid] = -1;
 }
 
+// Finish, selection (wave 0): the N best pool entries by (score desc, pool index asc). Entry e sits
+// in lane e % 64, slot e / 64 (PL slots per lane). A bitwise search on ballot counts finds the N-th
+// largest score key t (high words, then low words where the high word ties); the kept entries are
+// those above t and, in pool order, the first N - #(above t) equal to t. pool_of[1..N] receives them
+// in pool order, node_of[e] their node numbers.
+template <int PL>
+__device__ __forceinline__ void finish_select(const double* sc, int pool, int N, int* pool_of, int* node_of) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t below = (1ull << lane) - 1;
+  uint64_t key[PL];
+  uint32_t hi[PL];
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int e = lane + kWave * j;
+    key[j] = e < pool ? f64_order_key(sc[e] + 0.0) : 0ull;  // scores: no NaN; +0.0 folds -0 into +0
+    hi[j] = uint32_t(key[j] >> 32);
+  }
+  auto count = [&](auto pred) {
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < PL; ++j) n += __popcll(__ballot(pred(j)));
+    return n;
+  };
+  uint32_t th = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = th | (1u << bit);
+    if (count([&](int j) { return hi[j] >= cand; }) >= N) th = cand;
+  }
+  uint64_t t = uint64_t(th) << 32;
+  const int g_hi = count([&](int j) { return hi[j] > th; });
+  const int e_hi = count([&](int j) { return hi[j] == th; });
+  if (g_hi + e_hi > N) {  // the boundary falls inside one high word: search its low words
+    uint32_t tl = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tl | (1u << bit);
+      if (count([&](int j) { return hi[j] == th && uint32_t(key[j]) >= cand; }) >= N - g_hi) tl = cand;
+    }
+    t |= tl;
+  }
+  const int need = N - count([&](int j) { return key[j] > t; });
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const bool eq = key[j] == t && key[j] != 0;
+    const uint64_t me = __ballot(eq);
+    const bool kept = key[j] > t || (eq && eq_seen + __popcll(me & below) < need);
+    const uint64_t mk = __ballot(kept);
+    if (kept) {
+      const int n = 1 + base + __popcll(mk & below), e = lane + kWave * j;
+      pool_of[n] = e;
+      node_of[e] = n;
+    }
+    base += __popcll(mk);
+    eq_seen += __popcll(me);
+  }
+}
+
+// One block per sequence: keep the N best pool entries, number them 1..N in pool order and emit
+// parents (node numbers), depth, ancestry words and q_row. Wave 0 does everything after the loads:
+// the kept set is closed under parents (scores never increase down a path and a parent has the
+// smaller pool index), and node n's ancestry is found by pointer doubling over lanes (node n in lane
+// n - 1; depth <= 16, so four rounds).
 __global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w, int P, const int32_t* root_tokens,
                                                                        const int32_t* topk, const int32_t* depth,
                                                                        const int32_t* num_draft, int max_topk,
@@ -427,13 +489,10 @@ __global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w,
                                                                        int32_t* parents, int32_t* depth_out,
                                                                        uint64_t* anc_mask, int32_t* q_row) {
   constexpr int kPool = kMaxTopk + (kMaxDepth - 1) * kMaxTopk * kMaxTopk;
+  static_assert(kPool <= 16 * kWave, "pool fits 16 slots per lane");
   __shared__ double sc[kPool];
-  __shared__ int rank_s[kPool];  // pool rank, then node number (0 = not kept)
-  __shared__ int par_e[kPool], dep_e[kPool], fs_e[kPool], tok_e[kPool];
-  __shared__ int pool_of[65];
-  __shared__ int node_par[65];
-  __shared__ uint64_t anc_s[65];
-  __shared__ int jump_s[65];
+  __shared__ int par_e[kPool], dep_e[kPool], fs_e[kPool], tok_e[kPool], node_of[kPool];
+  __shared__ int pool_of[kWave + 1];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int k = clamp_i(topk[b], 1, max_topk);
   const int D = clamp_i(depth[b], 1, max_depth);
@@ -441,7 +500,6 @@ __global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w,
   const int N = clamp_i(num_draft[b], 1, min(pool, max_T - 1));
   const int T = N + 1;
   const size_t row = size_t(b) * P;
-
   // one round trip: every field of the pool
   for (int e = tid; e < pool; e += blockDim.x) {
     sc[e] = w.score[row + e];
@@ -451,82 +509,52 @@ __global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w,
     tok_e[e] = w.tok[row + e];
   }
   __syncthreads();
-  for (int e = tid; e < pool; e += blockDim.x) {
-    const double s = sc[e];
-    int r = 0;
-    for (int o = 0; o < pool; ++o) r += (sc[o] > s) || (sc[o] == s && o < e);
-    rank_s[e] = r;
+  if (tid >= kWave) return;
+  const int lane = tid;
+  if (pool <= kWave) finish_select<1>(sc, pool, N, pool_of, node_of);
+  else if (pool <= 2 * kWave) finish_select<2>(sc, pool, N, pool_of, node_of);
+  else if (pool <= 4 * kWave) finish_select<4>(sc, pool, N, pool_of, node_of);
+  else if (pool <= 8 * kWave) finish_select<8>(sc, pool, N, pool_of, node_of);
+  else finish_select<16>(sc, pool, N, pool_of, node_of);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // node n = lane + 1 (n <= N): its entry, parent node (0 = root) and ancestry by pointer doubling
+  const int n = lane + 1;
+  const bool real = n <= N;
+  const int e = real ? pool_of[n] : 0;
+  int par_node = 0;
+  if (real) {
+    const int pe = par_e[e];
+    par_node = pe >= 0 ? node_of[pe] : 0;
   }
-  __syncthreads();
-  // kept entries, numbered 1..N in pool order (wave 0 scans the pool 64 at a time)
-  if (tid < kWave) {
-    int base = 0;
-    for (int c0 = 0; c0 < pool; c0 += kWave) {
-      const int e = c0 + tid;
-      const bool kept = e < pool && rank_s[e] < N;
-      const uint64_t m = __ballot(kept);
-      if (kept) pool_of[1 + base + __popcll(m & ((1ull << tid) - 1))] = e;
-      base += __popcll(m);
+  uint64_t anc = real ? (1ull << lane) : 0ull;
+  int jump = par_node;  // 0 = reached the root
+  while (__ballot(jump != 0)) {
+    const int src = jump > 0 ? jump - 1 : lane;
+    const uint64_t pa = (uint64_t(uint32_t(__shfl(int(anc >> 32), src))) << 32) | uint32_t(__shfl(int(anc), src));
+    const int pj = __shfl(jump, src);
+    if (jump != 0) {
+      anc |= pa;
+      jump = pj;
     }
   }
-  __syncthreads();
-  if (tid >= 1 && tid < T) rank_s[pool_of[tid]] = -tid;  // kept entry -> -(node number)
-  __syncthreads();
-  // parents as node numbers: the parent entry of a kept entry is kept (scores never increase
-  // down a path and the parent has the smaller pool index), so it carries a node number
-  if (tid < T) {
-    const int n = tid;
-    int par_node = -1;
-    if (n > 0) {
-      const int pe = par_e[pool_of[n]];
-      par_node = 0;
-      if (pe >= 0 && rank_s[pe] < 0) par_node = -rank_s[pe];
-    }
-    node_par[n] = par_node;
-    jump_s[n] = n > 0 ? par_node : 0;
-    anc_s[n] = n > 0 ? (1ull << (n - 1)) : 0ull;
+  const size_t o = size_t(b) * max_T;
+  if (lane == 0) {  // the root
+    tokens[o] = root_tokens[b];
+    parents[o] = -1;
+    depth_out[o] = 0;
+    anc_mask[o] = 0;
+    q_row[o] = 0;
   }
-  __syncthreads();
-#pragma unroll 1
-  for (int it = 0; it < 7; ++it) {
-    uint64_t na = 0;
-    int nj = 0;
-    if (tid < T) {
-      const int j = jump_s[tid];
-      na = anc_s[tid] | anc_s[j];
-      nj = jump_s[j];
-    }
-    __syncthreads();
-    if (tid < T) {
-      anc_s[tid] = na;
-      jump_s[tid] = nj;
-    }
-    __syncthreads();
-  }
-  for (int n = tid; n < max_T; n += blockDim.x) {
-    const size_t o = size_t(b) * max_T + n;
-    if (n == 0) {
-      tokens[o] = root_tokens[b];
-      parents[o] = -1;
-      depth_out[o] = 0;
-      anc_mask[o] = 0;
-      q_row[o] = 0;
-    } else if (n < T) {
-      const int e = pool_of[n];
-      const int d = dep_e[e];
-      const int fs = fs_e[e];
-      tokens[o] = tok_e[e];
-      parents[o] = node_par[n];
-      depth_out[o] = d;
-      anc_mask[o] = anc_s[n];
-      q_row[o] = (fs >= 0 && d < D) ? 1 + (d - 1) * max_topk + fs : -1;
-    } else {
-      tokens[o] = -1;
-      parents[o] = -1;
-      depth_out[o] = 0;
-      anc_mask[o] = 0;
-      q_row[o] = -1;
-    }
+  if (n < max_T) {  // output row n: node n if n <= N, else padding
+    const int d = real ? dep_e[e] : 0;
+    const int fs = real ? fs_e[e] : -1;
+    tokens[o + n] = real ? tok_e[e] : -1;
+    parents[o + n] = real ? par_node : -1;
+    depth_out[o + n] = d;
+    anc_mask[o + n] = anc;
+    q_row[o + n] = (real && fs >= 0 && d < D) ? 1 + (d - 1) * max_topk + fs : -1;
   }
 }
 
