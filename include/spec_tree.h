@@ -4,6 +4,7 @@
  *
  * Pipeline per decoding step and layer:
  *   spec_tree_build_step (x depth) -> spec_tree_build_finish      draft tree
+ *     (or spec_tree_build_step_finish x depth, the same in fewer launches)
  *   spec_tree_attention                                            tree attention
  *   spec_tree_verify                                               accepted path + bonus
  *   spec_kv_compact                                                keep accepted KV
@@ -119,6 +120,21 @@ int32_t spec_tree_build_finish(void* ws, size_t ws_bytes, const int32_t* root_to
                                const int32_t* depth, const int32_t* num_draft, int32_t B, int32_t max_topk,
                                int32_t max_depth, int32_t max_T, int32_t* tokens, int32_t* parents,
                                int32_t* depth_out, uint64_t* anc_mask, int32_t* q_row, void* stream);
+
+/* Step `step` and, in the same launch, the finish of every sequence whose depth
+ * D_b equals `step` (its pool is complete once its last step has run): the
+ * outputs are exactly those of spec_tree_build_step followed, after the last
+ * step, by spec_tree_build_finish with the same arguments. Calling it for steps
+ * 1..max_depth replaces the step calls plus the finish call and saves a launch
+ * (the rerank follows the last expansion directly, as on the SGLang page,
+ * section "References": the top num_draft_tokens are kept after the last
+ * step). Requirements and errors: those of both calls. */
+int32_t spec_tree_build_step_finish(void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
+                                    int64_t seq_stride, const int32_t* topk, const int32_t* depth, int32_t B,
+                                    int32_t max_topk, int32_t max_depth, int32_t V, int32_t* frontier_tokens,
+                                    const int32_t* root_tokens, const int32_t* num_draft, int32_t max_T,
+                                    int32_t* tokens, int32_t* parents, int32_t* depth_out, uint64_t* anc_mask,
+                                    int32_t* q_row, void* stream);
 
 /* ----------------------------------------------------------------------------
  * Tree mask - tanhdev "Tech Radar: SGLang EAGLE-2", section 2 "Dynamic

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_pipeline():
     names = declared_functions()
-    for n in ["spec_tree_build_step", "spec_tree_build_finish", "spec_tree_mask", "spec_tree_attention",
+    for n in ["spec_tree_build_step", "spec_tree_build_step_finish", "spec_tree_build_finish", "spec_tree_mask", "spec_tree_attention",
               "spec_tree_verify", "spec_kv_compact", "spec_abi_version", "spec_last_error"]:
         assert n in names
 
@@ -89,6 +89,12 @@ def test_verify_build_compact_mask_host_validation(lib):
     assert lib.spec_tree_build_step(p, 1 << 20, 1, p, 1000, p, p, 1, 9, 3, 1000, p, None) == SPEC_E_UNSUPPORTED
     assert lib.spec_tree_build_step(p, 8, 1, p, 1000, p, p, 1, 4, 3, 1000, p, None) == SPEC_E_WORKSPACE
     assert lib.spec_tree_build_finish(p, 1 << 20, p, p, p, p, 1, 4, 3, 70, p, p, p, p, p, None) == SPEC_E_UNSUPPORTED
+    # the fused step + finish checks both calls' arguments before any launch
+    fused = lib.spec_tree_build_step_finish
+    assert fused(p, 1 << 20, 1, p, 1000, p, p, 1, 4, 3, 1000, p, p, p, 70, p, p, p, p, p, None) == SPEC_E_UNSUPPORTED
+    assert fused(p, 1 << 20, 1, p, 1000, p, p, 1, 4, 3, 1000, p, None, p, 17, p, p, p, p, p, None) == SPEC_E_INVAL
+    assert fused(p, 1 << 20, 0, p, 1000, p, p, 1, 4, 3, 1000, p, p, p, 17, p, p, p, p, p, None) == SPEC_E_INVAL
+    assert fused(p, 8, 1, p, 1000, p, p, 1, 4, 3, 1000, p, p, p, 17, p, p, p, p, p, None) == SPEC_E_WORKSPACE
     assert lib.spec_kv_compact(p, p, p, p, p, p, 1, 9, 2, 80, 16, 4, 4, 1, 0, p, None) == SPEC_E_UNSUPPORTED
     assert lib.spec_tree_mask(None, None, 1, 9, None, None, None, None) == SPEC_E_INVAL
 

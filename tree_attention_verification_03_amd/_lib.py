@@ -20,6 +20,8 @@ SIGNATURES = {
     "spec_last_error": (ctypes.c_char_p, []),
     "spec_tree_build_workspace_size": (c_sz, [c_i32, c_i32, c_i32]),
     "spec_tree_build_step": (c_i32, [c_vp, c_sz, c_i32, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "spec_tree_build_step_finish": (c_i32, [c_vp, c_sz, c_i32, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                            c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "spec_tree_build_finish": (c_i32, [c_vp, c_sz, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
                                        c_vp, c_vp, c_vp, c_vp]),
     "spec_tree_mask": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),

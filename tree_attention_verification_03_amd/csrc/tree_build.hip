@@ -266,6 +266,193 @@ __device__ __forceinline__ void block_slice_topk(const float* row, int lo, int h
   __syncthreads();
 }
 
+// Finish, selection (wave 0): the N best pool entries by (score desc, pool index asc). Entry e sits
+// in lane e % 64, slot e / 64 (PL slots per lane). A bitwise search on ballot counts finds the N-th
+// largest score key t (high words, then low words where the high word ties); the kept entries are
+// those above t and, in pool order, the first N - #(above t) equal to t. pool_of[1..N] receives them
+// in pool order, node_of[e] their node numbers.
+template <int PL>
+__device__ __forceinline__ void finish_select(const double* sc, int pool, int N, int* pool_of, int* node_of) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t below = (1ull << lane) - 1;
+  uint64_t key[PL];
+  uint32_t hi[PL];
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int e = lane + kWave * j;
+    key[j] = e < pool ? f64_order_key(sc[e] + 0.0) : 0ull;  // scores: no NaN; +0.0 folds -0 into +0
+    hi[j] = uint32_t(key[j] >> 32);
+  }
+  auto count = [&](auto pred) {
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < PL; ++j) n += __popcll(__ballot(pred(j)));
+    return n;
+  };
+  uint32_t th = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = th | (1u << bit);
+    if (count([&](int j) { return hi[j] >= cand; }) >= N) th = cand;
+  }
+  uint64_t t = uint64_t(th) << 32;
+  const int g_hi = count([&](int j) { return hi[j] > th; });
+  const int e_hi = count([&](int j) { return hi[j] == th; });
+  if (g_hi + e_hi > N) {  // the boundary falls inside one high word: search its low words
+    uint32_t tl = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = tl | (1u << bit);
+      if (count([&](int j) { return hi[j] == th && uint32_t(key[j]) >= cand; }) >= N - g_hi) tl = cand;
+    }
+    t |= tl;
+  }
+  const int need = N - count([&](int j) { return key[j] > t; });
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const bool eq = key[j] == t && key[j] != 0;
+    const uint64_t me = __ballot(eq);
+    const bool kept = key[j] > t || (eq && eq_seen + __popcll(me & below) < need);
+    const uint64_t mk = __ballot(kept);
+    if (kept) {
+      const int n = 1 + base + __popcll(mk & below), e = lane + kWave * j;
+      pool_of[n] = e;
+      node_of[e] = n;
+    }
+    base += __popcll(mk);
+    eq_seen += __popcll(me);
+  }
+}
+
+// Outputs of the finish (the caller's arrays, [B, max_T]).
+struct FinishArgs {
+  const int32_t* root_tokens;
+  const int32_t* num_draft;
+  int max_T;
+  int32_t* tokens;
+  int32_t* parents;
+  int32_t* depth_out;
+  uint64_t* anc_mask;
+  int32_t* q_row;
+};
+
+// Finish of sequence b by one block of kFinishThreads: keep the N best pool entries, number them
+// 1..N in pool order and emit parents (node numbers), depth, ancestry words and q_row. Wave 0 does
+// everything after the loads: the kept set is closed under parents (scores never increase down a path
+// and a parent has the smaller pool index), and node n's ancestry is found by pointer doubling over
+// lanes (node n in lane n - 1; depth <= 16, so four rounds). COHERENT loads read the pool at device
+// scope (entries this kernel wrote).
+template <bool COHERENT>
+__device__ __forceinline__ void finish_sequence(const BuildWs& w, int P, int b, int k, int D, int max_topk,
+                                                const FinishArgs& fa) {
+  constexpr int kPool = kMaxTopk + (kMaxDepth - 1) * kMaxTopk * kMaxTopk;
+  static_assert(kPool <= 16 * kWave, "pool fits 16 slots per lane");
+  __shared__ double sc[kPool];
+  __shared__ int par_e[kPool], dep_e[kPool], fs_e[kPool], tok_e[kPool], node_of[kPool];
+  __shared__ int pool_of[kWave + 1];
+  const int tid = threadIdx.x;
+  const int max_T = fa.max_T;
+  const int pool = k + (D - 1) * k * k;
+  const int N = clamp_i(fa.num_draft[b], 1, min(pool, max_T - 1));
+  const int T = N + 1;
+  const size_t row = size_t(b) * P;
+  auto ld = [](const auto* q) { return COHERENT ? ld_agent(q) : *q; };
+  // one round trip: every field of the pool
+  for (int e = tid; e < pool; e += kFinishThreads) {
+    sc[e] = ld(w.score + row + e);
+    par_e[e] = ld(w.par + row + e);
+    dep_e[e] = ld(w.depth + row + e);
+    fs_e[e] = ld(w.fslot + row + e);
+    tok_e[e] = ld(w.tok + row + e);
+  }
+  __syncthreads();
+  if (tid >= kWave) return;
+  const int lane = tid;
+  if (pool <= kWave) finish_select<1>(sc, pool, N, pool_of, node_of);
+  else if (pool <= 2 * kWave) finish_select<2>(sc, pool, N, pool_of, node_of);
+  else if (pool <= 4 * kWave) finish_select<4>(sc, pool, N, pool_of, node_of);
+  else if (pool <= 8 * kWave) finish_select<8>(sc, pool, N, pool_of, node_of);
+  else finish_select<16>(sc, pool, N, pool_of, node_of);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // node n = lane + 1 (n <= N): its entry, parent node (0 = root) and ancestry by pointer doubling
+  const int n = lane + 1;
+  const bool real = n <= N;
+  const int e = real ? pool_of[n] : 0;
+  int par_node = 0;
+  if (real) {
+    const int pe = par_e[e];
+    par_node = pe >= 0 ? node_of[pe] : 0;
+  }
+  uint64_t anc = real ? (1ull << lane) : 0ull;
+  int jump = par_node;  // 0 = reached the root
+  while (__ballot(jump != 0)) {
+    const int src = jump > 0 ? jump - 1 : lane;
+    const uint64_t pa = (uint64_t(uint32_t(__shfl(int(anc >> 32), src))) << 32) | uint32_t(__shfl(int(anc), src));
+    const int pj = __shfl(jump, src);
+    if (jump != 0) {
+      anc |= pa;
+      jump = pj;
+    }
+  }
+  const size_t o = size_t(b) * max_T;
+  if (lane == 0) {  // the root
+    fa.tokens[o] = fa.root_tokens[b];
+    fa.parents[o] = -1;
+    fa.depth_out[o] = 0;
+    fa.anc_mask[o] = 0;
+    fa.q_row[o] = 0;
+  }
+  if (n < max_T) {  // output row n: node n if n <= N, else padding
+    const int d = real ? dep_e[e] : 0;
+    const int fs = real ? fs_e[e] : -1;
+    fa.tokens[o + n] = real ? tok_e[e] : -1;
+    fa.parents[o + n] = real ? par_node : -1;
+    fa.depth_out[o + n] = d;
+    fa.anc_mask[o + n] = anc;
+    fa.q_row[o + n] = (real && fs >= 0 && d < D) ? 1 + (d - 1) * max_topk + fs : -1;
+  }
+}
+
+// Step >= 2, wave 0 of the merging block (one child per lane): row r's c-th best token becomes pool
+// entry base + r * k + c; the next frontier is the k best by score (ties -> smaller pool index): k
+// pops of their scores' order keys, where the lowest lane wins ties.
+__device__ __forceinline__ void step_children(const BuildWs& w, int P, int b, int step, int k, int base,
+                                              int max_topk, const uint64_t* top, const double* fsc_s,
+                                              const int* cpar, int32_t* frontier_tokens) {
+  const int lane = threadIdx.x & (kWave - 1);
+  {
+    const int n = k * k;
+    const int r = lane / k, c = lane - r * k;
+    double sc = 0.0;
+    uint64_t key = 0, sk = 0;
+    if (lane < n) {
+      key = top[r * kMaxTopk + c];
+      sc = fsc_s[r] + double(key_value(key));
+      sk = f64_order_key(sc + 0.0);  // no NaN; +0.0 folds -0 into +0
+      const size_t e = size_t(b) * P + base + lane;
+      w.tok[e] = key_token(key);
+      w.par[e] = cpar[r];
+      w.depth[e] = step;
+      w.score[e] = sc;
+    }
+    int rank = -1;
+    for (int q = 0; q < k; ++q) {
+      const Popped p = wave_pop<1>(&sk);
+      if (lane == p.lane) rank = q;
+    }
+    if (lane < n) {
+      w.fslot[size_t(b) * P + base + lane] = rank;
+      if (rank >= 0) {
+        w.frontier[b * max_topk + rank] = base + lane;
+        w.fscore[b * max_topk + rank] = sc;
+        frontier_tokens[b * max_topk + rank] = key_token(key);
+      }
+    }
+  }
+  if (lane >= k && lane < max_topk) frontier_tokens[b * max_topk + lane] = -1;
+}
+
 // One kernel for every step. Block (slice x, frontier slot f, sequence b) reduces a slice of
 // step-`step` draft row f to its top-k keys and publishes them; the last block of the sequence's
 // step to finish (ticket) merges the slices of every row: at step 1 the root row fills the pool and
@@ -277,7 +464,8 @@ template <bool VEC, int EPL>
 __global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, int P, int step, const float* draft,
                                                                   int64_t seq_stride, const int32_t* topk,
                                                                   const int32_t* depth, int max_topk, int max_depth,
-                                                                  int V, int slice, int32_t* frontier_tokens) {
+                                                                  int V, int slice, int32_t* frontier_tokens,
+                                                                  FinishArgs fa) {
   constexpr int NWV = kRowThreads / kWave;
   __shared__ uint64_t keys[kMaxTopk];
   __shared__ uint64_t top[kMaxTopk * kMaxTopk];  // [row][rank]
@@ -382,180 +570,22 @@ __global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, i
       }
       frontier_tokens[b * max_topk + c] = tok;
     }
-    return;
+  } else if (wave == 0) {
+    step_children(w, P, b, step, k, base, max_topk, top, fsc_s, cpar, frontier_tokens);
   }
-
-  // children (wave 0, one per lane): row r's c-th best token becomes pool entry base + r * k + c;
-  // the next frontier is the k best by score (ties -> smaller pool index): k pops of their scores'
-  // order keys, where the lowest lane wins ties
-  if (wave == 0) {
-    const int n = k * k;
-    const int r = lane / k, c = lane - r * k;
-    double sc = 0.0;
-    uint64_t key = 0, sk = 0;
-    if (lane < n) {
-      key = top[r * kMaxTopk + c];
-      sc = fsc_s[r] + double(key_value(key));
-      sk = f64_order_key(sc + 0.0);  // no NaN; +0.0 folds -0 into +0
-      const size_t e = size_t(b) * P + base + lane;
-      w.tok[e] = key_token(key);
-      w.par[e] = cpar[r];
-      w.depth[e] = step;
-      w.score[e] = sc;
-    }
-    int rank = -1;
-    for (int q = 0; q < k; ++q) {
-      const Popped p = wave_pop<1>(&sk);
-      if (lane == p.lane) rank = q;
-    }
-    if (lane < n) {
-      w.fslot[size_t(b) * P + base + lane] = rank;
-      if (rank >= 0) {
-        w.frontier[b * max_topk + rank] = base + lane;
-        w.fscore[b * max_topk + rank] = sc;
-        frontier_tokens[b * max_topk + rank] = key_token(key);
-      }
-    }
-  }
-  if (tid >= k && tid < max_topk) frontier_tokens[b * max_topk + tid] = -1;
-}
-
-// Finish, selection (wave 0): the N best pool entries by (score desc, pool index asc). Entry e sits
-// in lane e % 64, slot e / 64 (PL slots per lane). A bitwise search on ballot counts finds the N-th
-// largest score key t (high words, then low words where the high word ties); the kept entries are
-// those above t and, in pool order, the first N - #(above t) equal to t. pool_of[1..N] receives them
-// in pool order, node_of[e] their node numbers.
-template <int PL>
-__device__ __forceinline__ void finish_select(const double* sc, int pool, int N, int* pool_of, int* node_of) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const uint64_t below = (1ull << lane) - 1;
-  uint64_t key[PL];
-  uint32_t hi[PL];
-#pragma unroll
-  for (int j = 0; j < PL; ++j) {
-    const int e = lane + kWave * j;
-    key[j] = e < pool ? f64_order_key(sc[e] + 0.0) : 0ull;  // scores: no NaN; +0.0 folds -0 into +0
-    hi[j] = uint32_t(key[j] >> 32);
-  }
-  auto count = [&](auto pred) {
-    int n = 0;
-#pragma unroll
-    for (int j = 0; j < PL; ++j) n += __popcll(__ballot(pred(j)));
-    return n;
-  };
-  uint32_t th = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = th | (1u << bit);
-    if (count([&](int j) { return hi[j] >= cand; }) >= N) th = cand;
-  }
-  uint64_t t = uint64_t(th) << 32;
-  const int g_hi = count([&](int j) { return hi[j] > th; });
-  const int e_hi = count([&](int j) { return hi[j] == th; });
-  if (g_hi + e_hi > N) {  // the boundary falls inside one high word: search its low words
-    uint32_t tl = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = tl | (1u << bit);
-      if (count([&](int j) { return hi[j] == th && uint32_t(key[j]) >= cand; }) >= N - g_hi) tl = cand;
-    }
-    t |= tl;
-  }
-  const int need = N - count([&](int j) { return key[j] > t; });
-  int base = 0, eq_seen = 0;
-#pragma unroll
-  for (int j = 0; j < PL; ++j) {
-    const bool eq = key[j] == t && key[j] != 0;
-    const uint64_t me = __ballot(eq);
-    const bool kept = key[j] > t || (eq && eq_seen + __popcll(me & below) < need);
-    const uint64_t mk = __ballot(kept);
-    if (kept) {
-      const int n = 1 + base + __popcll(mk & below), e = lane + kWave * j;
-      pool_of[n] = e;
-      node_of[e] = n;
-    }
-    base += __popcll(mk);
-    eq_seen += __popcll(me);
+  if (fa.tokens && step == D) {  // the sequence's last step: rerank now (its pool is complete)
+    wait_global_stores();
+    __syncthreads();
+    finish_sequence<true>(w, P, b, k, D, max_topk, fa);
   }
 }
 
-// One block per sequence: keep the N best pool entries, number them 1..N in pool order and emit
-// parents (node numbers), depth, ancestry words and q_row. Wave 0 does everything after the loads:
-// the kept set is closed under parents (scores never increase down a path and a parent has the
-// smaller pool index), and node n's ancestry is found by pointer doubling over lanes (node n in lane
-// n - 1; depth <= 16, so four rounds).
-__global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w, int P, const int32_t* root_tokens,
-                                                                       const int32_t* topk, const int32_t* depth,
-                                                                       const int32_t* num_draft, int max_topk,
-                                                                       int max_depth, int max_T, int32_t* tokens,
-                                                                       int32_t* parents, int32_t* depth_out,
-                                                                       uint64_t* anc_mask, int32_t* q_row) {
-  constexpr int kPool = kMaxTopk + (kMaxDepth - 1) * kMaxTopk * kMaxTopk;
-  static_assert(kPool <= 16 * kWave, "pool fits 16 slots per lane");
-  __shared__ double sc[kPool];
-  __shared__ int par_e[kPool], dep_e[kPool], fs_e[kPool], tok_e[kPool], node_of[kPool];
-  __shared__ int pool_of[kWave + 1];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int k = clamp_i(topk[b], 1, max_topk);
-  const int D = clamp_i(depth[b], 1, max_depth);
-  const int pool = k + (D - 1) * k * k;
-  const int N = clamp_i(num_draft[b], 1, min(pool, max_T - 1));
-  const int T = N + 1;
-  const size_t row = size_t(b) * P;
-  // one round trip: every field of the pool
-  for (int e = tid; e < pool; e += blockDim.x) {
-    sc[e] = w.score[row + e];
-    par_e[e] = w.par[row + e];
-    dep_e[e] = w.depth[row + e];
-    fs_e[e] = w.fslot[row + e];
-    tok_e[e] = w.tok[row + e];
-  }
-  __syncthreads();
-  if (tid >= kWave) return;
-  const int lane = tid;
-  if (pool <= kWave) finish_select<1>(sc, pool, N, pool_of, node_of);
-  else if (pool <= 2 * kWave) finish_select<2>(sc, pool, N, pool_of, node_of);
-  else if (pool <= 4 * kWave) finish_select<4>(sc, pool, N, pool_of, node_of);
-  else if (pool <= 8 * kWave) finish_select<8>(sc, pool, N, pool_of, node_of);
-  else finish_select<16>(sc, pool, N, pool_of, node_of);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // node n = lane + 1 (n <= N): its entry, parent node (0 = root) and ancestry by pointer doubling
-  const int n = lane + 1;
-  const bool real = n <= N;
-  const int e = real ? pool_of[n] : 0;
-  int par_node = 0;
-  if (real) {
-    const int pe = par_e[e];
-    par_node = pe >= 0 ? node_of[pe] : 0;
-  }
-  uint64_t anc = real ? (1ull << lane) : 0ull;
-  int jump = par_node;  // 0 = reached the root
-  while (__ballot(jump != 0)) {
-    const int src = jump > 0 ? jump - 1 : lane;
-    const uint64_t pa = (uint64_t(uint32_t(__shfl(int(anc >> 32), src))) << 32) | uint32_t(__shfl(int(anc), src));
-    const int pj = __shfl(jump, src);
-    if (jump != 0) {
-      anc |= pa;
-      jump = pj;
-    }
-  }
-  const size_t o = size_t(b) * max_T;
-  if (lane == 0) {  // the root
-    tokens[o] = root_tokens[b];
-    parents[o] = -1;
-    depth_out[o] = 0;
-    anc_mask[o] = 0;
-    q_row[o] = 0;
-  }
-  if (n < max_T) {  // output row n: node n if n <= N, else padding
-    const int d = real ? dep_e[e] : 0;
-    const int fs = real ? fs_e[e] : -1;
-    tokens[o + n] = real ? tok_e[e] : -1;
-    parents[o + n] = real ? par_node : -1;
-    depth_out[o + n] = d;
-    anc_mask[o + n] = anc;
-    q_row[o + n] = (real && fs >= 0 && d < D) ? 1 + (d - 1) * max_topk + fs : -1;
-  }
+
+__global__ void __launch_bounds__(kFinishThreads) build_finish_kernel(BuildWs w, int P, const int32_t* topk,
+                                                                       const int32_t* depth, int max_topk,
+                                                                       int max_depth, FinishArgs fa) {
+  const int b = blockIdx.x;
+  finish_sequence<false>(w, P, b, clamp_i(topk[b], 1, max_topk), clamp_i(depth[b], 1, max_depth), max_topk, fa);
 }
 
 int32_t check_build(const char* who, int32_t B, int32_t max_topk, int32_t max_depth) {
@@ -578,21 +608,23 @@ extern "C" size_t spec_tree_build_workspace_size(int32_t B, int32_t max_topk, in
   return total;
 }
 
-extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
-                                        int64_t seq_stride, const int32_t* topk, const int32_t* depth, int32_t B,
-                                        int32_t max_topk, int32_t max_depth, int32_t V, int32_t* frontier_tokens,
-                                        void* stream) {
-  int32_t rc = check_build("spec_tree_build_step", B, max_topk, max_depth);
+namespace spectree {
+namespace {
+
+int32_t launch_step(const char* who, void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
+                    int64_t seq_stride, const int32_t* topk, const int32_t* depth, int32_t B, int32_t max_topk,
+                    int32_t max_depth, int32_t V, int32_t* frontier_tokens, const FinishArgs& fa, void* stream) {
+  int32_t rc = check_build(who, B, max_topk, max_depth);
   if (rc != SPEC_OK) return rc;
-  if (step < 1 || step > max_depth) return fail(SPEC_E_INVAL, "spec_tree_build_step: step=%d not in [1, %d]", step, max_depth);
-  if (V < max_topk || V >= (1 << 30)) return fail(SPEC_E_INVAL, "spec_tree_build_step: V=%d must be in [max_topk, 2^30)", V);
-  if (!draft_logprobs || !topk || !depth || !frontier_tokens) return fail(SPEC_E_INVAL, "spec_tree_build_step: null pointer");
+  if (step < 1 || step > max_depth) return fail(SPEC_E_INVAL, "%s: step=%d not in [1, %d]", who, step, max_depth);
+  if (V < max_topk || V >= (1 << 30)) return fail(SPEC_E_INVAL, "%s: V=%d must be in [max_topk, 2^30)", who, V);
+  if (!draft_logprobs || !topk || !depth || !frontier_tokens) return fail(SPEC_E_INVAL, "%s: null pointer", who);
   const int64_t min_stride = (step == 1 ? 1 : max_topk) * int64_t(V);
   if (B > 1 && seq_stride < min_stride)
-    return fail(SPEC_E_INVAL, "spec_tree_build_step: seq_stride=%lld < %lld", (long long)seq_stride, (long long)min_stride);
+    return fail(SPEC_E_INVAL, "%s: seq_stride=%lld < %lld", who, (long long)seq_stride, (long long)min_stride);
   size_t need = 0;
   BuildWs w = carve(ws, B, max_topk, max_depth, &need);
-  if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_step: workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
   const int P = int(pool_cap(max_topk, max_depth));
   hipStream_t st = static_cast<hipStream_t>(stream);
   // about 256 blocks per launch, within: slices of at least 8 elements per thread and of at most
@@ -626,7 +658,7 @@ extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step,
   const bool vec = (V % 4 == 0) && (seq_stride % 4 == 0) && ((reinterpret_cast<uintptr_t>(draft_logprobs) & 15) == 0);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kRowThreads), 0, st, w, P, step, draft_logprobs, seq_stride, topk, depth,
-                       max_topk, max_depth, V, slice, frontier_tokens);
+                       max_topk, max_depth, V, slice, frontier_tokens, fa);
   };
   if (vec) {
     if (epl == 8) go(build_step_kernel<true, 8>);
@@ -635,7 +667,37 @@ extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step,
     if (epl == 8) go(build_step_kernel<false, 8>);
     else go(build_step_kernel<false, 16>);
   }
-  return check_launch("spec_tree_build_step");
+  return check_launch(who);
+}
+
+}  // namespace
+}  // namespace spectree
+
+
+
+extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
+                                        int64_t seq_stride, const int32_t* topk, const int32_t* depth, int32_t B,
+                                        int32_t max_topk, int32_t max_depth, int32_t V, int32_t* frontier_tokens,
+                                        void* stream) {
+  const FinishArgs none{};
+  return launch_step("spec_tree_build_step", ws, ws_bytes, step, draft_logprobs, seq_stride, topk, depth, B, max_topk,
+                     max_depth, V, frontier_tokens, none, stream);
+}
+
+extern "C" int32_t spec_tree_build_step_finish(void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
+                                               int64_t seq_stride, const int32_t* topk, const int32_t* depth,
+                                               int32_t B, int32_t max_topk, int32_t max_depth, int32_t V,
+                                               int32_t* frontier_tokens, const int32_t* root_tokens,
+                                               const int32_t* num_draft, int32_t max_T, int32_t* tokens,
+                                               int32_t* parents, int32_t* depth_out, uint64_t* anc_mask,
+                                               int32_t* q_row, void* stream) {
+  const char* who = "spec_tree_build_step_finish";
+  if (max_T < 2 || max_T > 65) return fail(SPEC_E_UNSUPPORTED, "%s: max_T=%d not in [2, 65]", who, max_T);
+  if (!root_tokens || !num_draft || !tokens || !parents || !depth_out || !anc_mask || !q_row)
+    return fail(SPEC_E_INVAL, "%s: null pointer", who);
+  const FinishArgs fa{root_tokens, num_draft, max_T, tokens, parents, depth_out, anc_mask, q_row};
+  return launch_step(who, ws, ws_bytes, step, draft_logprobs, seq_stride, topk, depth, B, max_topk, max_depth, V,
+                     frontier_tokens, fa, stream);
 }
 
 extern "C" int32_t spec_tree_build_finish(void* ws, size_t ws_bytes, const int32_t* root_tokens, const int32_t* topk,
@@ -651,8 +713,8 @@ extern "C" int32_t spec_tree_build_finish(void* ws, size_t ws_bytes, const int32
   BuildWs w = carve(ws, B, max_topk, max_depth, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_finish: workspace %zu < %zu bytes", ws_bytes, need);
   const int P = int(pool_cap(max_topk, max_depth));
+  const FinishArgs fa{root_tokens, num_draft, max_T, tokens, parents, depth_out, anc_mask, q_row};
   hipLaunchKernelGGL(build_finish_kernel, dim3(B), dim3(kFinishThreads), 0, static_cast<hipStream_t>(stream), w, P,
-                     root_tokens, topk, depth, num_draft, max_topk, max_depth, max_T, tokens, parents, depth_out,
-                     anc_mask, q_row);
+                     topk, depth, max_topk, max_depth, fa);
   return check_launch("spec_tree_build_finish");
 }

@@ -89,6 +89,29 @@ def spec_tree_build_step(ws: torch.Tensor, step: int, draft_logprobs: torch.Tens
     check(rc, "spec_tree_build_step")
 
 
+def spec_tree_build_step_finish(ws: torch.Tensor, step: int, draft_logprobs: torch.Tensor, topk: torch.Tensor,
+                                depth: torch.Tensor, max_topk: int, max_depth: int, frontier_tokens: torch.Tensor,
+                                root_tokens, num_draft, max_T, tokens, parents, depth_out, anc_mask, q_row):
+    """Step ``step`` plus the finish of the sequences whose depth is ``step`` (one launch)."""
+    _dev(draft_logprobs, torch.float32, "draft_logprobs", contiguous=False)
+    B, F, V = draft_logprobs.shape
+    if draft_logprobs.stride(2) != 1 or (F > 1 and draft_logprobs.stride(1) != V):
+        raise ValueError("draft_logprobs rows must be contiguous [.., F, V]")
+    if F < (1 if step == 1 else max_topk):
+        raise ValueError(f"step {step} needs {1 if step == 1 else max_topk} draft rows per sequence, got {F}")
+    for n, t in (("topk", topk), ("depth", depth), ("frontier_tokens", frontier_tokens), ("root_tokens", root_tokens),
+                 ("num_draft", num_draft), ("tokens", tokens), ("parents", parents), ("depth_out", depth_out),
+                 ("q_row", q_row)):
+        _dev(t, torch.int32, n)
+    _dev(anc_mask, torch.int64, "anc_mask")  # uint64 bit patterns
+    _dev(ws, torch.uint8, "ws")
+    rc = load().spec_tree_build_step_finish(
+        _ptr(ws), ws.numel(), step, _ptr(draft_logprobs), draft_logprobs.stride(0), _ptr(topk), _ptr(depth), B,
+        max_topk, max_depth, V, _ptr(frontier_tokens), _ptr(root_tokens), _ptr(num_draft), max_T, _ptr(tokens),
+        _ptr(parents), _ptr(depth_out), _ptr(anc_mask), _ptr(q_row), _stream(ws))
+    check(rc, "spec_tree_build_step_finish")
+
+
 def spec_tree_build_finish(ws, root_tokens, topk, depth, num_draft, max_topk, max_depth, max_T, tokens, parents,
                            depth_out, anc_mask, q_row):
     for n, t in (("root_tokens", root_tokens), ("topk", topk), ("depth", depth), ("num_draft", num_draft),

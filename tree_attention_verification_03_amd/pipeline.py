@@ -70,9 +70,10 @@ class StepOutputs:
 
 
 class SpecTreeStep:
-    def __init__(self, dw: DeviceWorkload, attn_status: bool = True):
+    def __init__(self, dw: DeviceWorkload, attn_status: bool = True, fused_finish: bool = True):
         w = dw.w
         self.dw = dw
+        self.fused_finish = fused_finish
         dev = dw.device
         B, T = w.B, w.max_T
         z = lambda *s, dt=torch.int32: torch.zeros(*s, dtype=dt, device=dev)
@@ -91,13 +92,22 @@ class SpecTreeStep:
 
     # -- the four stages --------------------------------------------------
     def build(self):
+        """Every step; a sequence is reranked at its own last step (fused launches), or, with
+        ``fused_finish=False``, by a separate finish launch after the last step."""
         w, dw, o = self.dw.w, self.dw, self.o
         for step in range(1, w.max_depth + 1):
             lo, hi = step_row_range(step, w.max_topk)
-            ops.spec_tree_build_step(self.ws_build, step, dw.draft_logprobs[:, lo:hi, :], dw.topk, dw.depth,
-                                     w.max_topk, w.max_depth, o.frontier)
-        ops.spec_tree_build_finish(self.ws_build, dw.root_tokens, dw.topk, dw.depth, dw.num_draft, w.max_topk,
-                                   w.max_depth, w.max_T, o.tokens, o.parents, o.depth, o.anc, o.q_row)
+            rows = dw.draft_logprobs[:, lo:hi, :]
+            if self.fused_finish:
+                ops.spec_tree_build_step_finish(self.ws_build, step, rows, dw.topk, dw.depth, w.max_topk,
+                                                w.max_depth, o.frontier, dw.root_tokens, dw.num_draft, w.max_T,
+                                                o.tokens, o.parents, o.depth, o.anc, o.q_row)
+            else:
+                ops.spec_tree_build_step(self.ws_build, step, rows, dw.topk, dw.depth, w.max_topk, w.max_depth,
+                                         o.frontier)
+        if not self.fused_finish:
+            ops.spec_tree_build_finish(self.ws_build, dw.root_tokens, dw.topk, dw.depth, dw.num_draft, w.max_topk,
+                                       w.max_depth, w.max_T, o.tokens, o.parents, o.depth, o.anc, o.q_row)
 
     def attention(self):
         w, dw, o = self.dw.w, self.dw, self.o
