@@ -125,6 +125,49 @@ __device__ __forceinline__ int v_swz(int key) { return 2 * (key & 3) ^ (D == 128
 constexpr int blocks_per_cu(int D, int NS) { return NS * 128 * D + 4096 <= 160 * 1024 / 2 ? 2 : 1; }
 
 // SPS ring stages of 32 keys form one softmax step (one barrier, one running-max update per step)
+// Split-K merge of one output row, item by item in fixed order against the running maximum
+// reference max: out = sum_i w_i O_i / sum_i w_i l_i with w_i = 2^(m_i - max_j m_j). A thread owns
+// 8 columns (o0, o1) of the row.
+struct RowMerge {
+  float mx = -INFINITY, ls = 0.f;
+  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  // fold the first `navail` of a batch of CB items (the rest are unused loads and may hold anything)
+  template <int CB>
+  __device__ __forceinline__ void fold(const float (&mi)[CB], const float (&li)[CB], const f32x4 (&a0)[CB],
+                                       const f32x4 (&a1)[CB], int navail) {
+    float mb = mx;
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      if (u < navail) mb = fmaxf(mb, mi[u]);
+    if (mb == -INFINITY) return;  // nothing visible yet
+    const float sc = (mx == -INFINITY) ? 0.f : fast_exp2(mx - mb);
+    ls *= sc;
+    o0 *= sc;
+    o1 *= sc;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (u < navail && mi[u] != -INFINITY) {  // guarded, not weighted
+        const float w = fast_exp2(mi[u] - mb);
+        ls += w * li[u];
+        o0 += a0[u] * w;
+        o1 += a1[u] * w;
+      }
+    }
+    mx = mb;
+  }
+  // out / lse of packed row r (node r / G, head g G + r % G) of sequence b, KV head g; columns 8c..8c+7
+  template <int D>
+  __device__ __forceinline__ void write(const AttnParams& p, int b, int g, int r, int c) const {
+    const int i = r / p.G, h = g * p.G + (r - i * p.G);
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    const f32x4 v0 = o0 * inv, v1 = o1 * inv;
+    *reinterpret_cast<uint4*>(p.out + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 8 * c) =
+        make_uint4(pack2_bf16(v0[0], v0[1]), pack2_bf16(v0[2], v0[3]), pack2_bf16(v1[0], v1[1]), pack2_bf16(v1[2], v1[3]));
+    constexpr float kLn2 = 0.69314718055994530942f;
+    if (p.lse && c == 0) p.lse[(size_t(b) * p.max_T + i) * p.Hq + h] = ls > 0.f ? (mx + __log2f(ls)) * kLn2 : -INFINITY;
+  }
+};
+
 template <int D, int NW, int RW, int NS, int SPS>
 __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_attn_kernel(AttnParams p) {
   constexpr int KK = D / 32;               // MFMA k-steps over the head dim
@@ -143,7 +186,6 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
   static_assert(NT >= 65, "the tree prologue uses one thread per node");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE_B];
   __shared__ uint64_t anc_s[65];
-  __shared__ int par_s[65];
   extern __shared__ int pg_s[];  // page-table entries covering this item's keys (p.npg of them)
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -162,8 +204,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
     const int pi = pg0 + i;
     pg_s[i] = pi < p.max_pages ? ptab[pi] : -1;
   }
-  int par_raw = 0;
-  if (tid > 0 && tid < p.max_T) par_raw = p.parents[size_t(b) * p.max_T + tid];
+  int par_raw = 0;  // wave 0, lane l: the parent of node l + 1
+  if (tid < kWave && tid + 1 < p.max_T) par_raw = p.parents[size_t(b) * p.max_T + tid + 1];
   // Q operands of this wave's row tiles: lane = row (lane & 15), head-dim chunk (lane >> 4) + 4 kk.
   // Rows up to G * max_T are inside q; rows past this tree's M are computed and ignored.
   bf16x8 qop[RW][KK];
@@ -205,40 +247,35 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
     const int npg_used = ((key_hi - 1) >> p.page_shift) - pg0 + 1;
     for (int i = tid; i < npg_used; i += NT) bad |= unsigned(pg_s[i]) >= unsigned(p.num_pages);
   }
-  if (has_tree && tid < T) {
+  // ancestry words of the tree (wave 0; node n in lane n - 1): pointer doubling over lanes, each round
+  // doubling the generations covered, then one barrier publishes them
+  if (has_tree && tid < kWave) {
+    const int n = tid + 1;
+    const bool real = n < T;
     int par = 0;
-    uint64_t a = 0;
-    if (tid > 0) {
+    if (real) {
       par = par_raw;
-      if (par < 0 || par >= tid) {
+      if (par < 0 || par >= n) {
         par = 0;
         if (p.status && rb == 0 && g == 0) atomicOr(p.status + b, SPEC_STATUS_INVALID_PARENT);
       }
-      a = 1ull << (tid - 1);
     }
-    par_s[tid] = par;
-    anc_s[tid] = a;
+    uint64_t a = real ? (1ull << tid) : 0ull;
+    int jump = par;  // 0 = the root: nothing above
+    while (__ballot(jump != 0)) {
+      const int src = jump > 0 ? jump - 1 : tid;
+      const uint64_t pa = (uint64_t(uint32_t(__shfl(int(a >> 32), src))) << 32) | uint32_t(__shfl(int(a), src));
+      const int pj = __shfl(jump, src);
+      if (jump != 0) {
+        a |= pa;
+        jump = pj;
+      }
+    }
+    if (real) anc_s[n] = a;
+    if (tid == 0) anc_s[0] = 0;
   }
   const bool pages_ok = !__syncthreads_or(bad);
   if (!pages_ok && p.status && tid == 0) atomicOr(p.status + b, SPEC_STATUS_INVALID_PAGE);
-  if (has_tree) {  // pointer doubling: after round k each word covers 2^k generations
-#pragma unroll 1
-    for (int it = 0; it < 7; ++it) {
-      uint64_t na = 0;
-      int np = 0;
-      if (tid < T) {
-        const int pp = par_s[tid];
-        na = anc_s[tid] | anc_s[pp];
-        np = par_s[pp];
-      }
-      __syncthreads();
-      if (tid < T) {
-        anc_s[tid] = na;
-        par_s[tid] = np;
-      }
-      __syncthreads();
-    }
-  }
   uint64_t ranc[RW];
 #pragma unroll
   for (int rw = 0; rw < RW; ++rw) {
@@ -521,8 +558,7 @@ __global__ void __launch_bounds__(2 * D) tree_attn_combine(AttnParams p) {
   const size_t ITEM = size_t(TR) * (D + 2);
   const float* grp = p.part + size_t(rbg) * p.n_splits * ITEM;
   const int row = lt * 16 + row16;
-  float mx = -INFINITY, ls = 0.f;
-  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  RowMerge mr;
   int n_items = CB;  // known after the first batch's loads
 #pragma unroll 1
   for (int ib = 0; ib < n_items; ib += CB) {
@@ -545,35 +581,9 @@ __global__ void __launch_bounds__(2 * D) tree_attn_combine(AttnParams p) {
       const int r = 16 * (rb * p.tpb + lt) + row16;
       if (n_items == 1 || r >= p.G * T) return;
     }
-    float mb = mx;
-#pragma unroll
-    for (int u = 0; u < CB; ++u)
-      if (ib + u < n_items) mb = fmaxf(mb, mi[u]);
-    if (mb == -INFINITY) continue;  // nothing visible yet
-    const float sc = (mx == -INFINITY) ? 0.f : fast_exp2(mx - mb);
-    ls *= sc;
-    o0 *= sc;
-    o1 *= sc;
-#pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      if (ib + u < n_items && mi[u] != -INFINITY) {  // guarded, not weighted: unused loads may hold anything
-        const float w = fast_exp2(mi[u] - mb);
-        ls += w * li[u];
-        o0 += a0[u] * w;
-        o1 += a1[u] * w;
-      }
-    }
-    mx = mb;
+    mr.fold<CB>(mi, li, a0, a1, n_items - ib);
   }
-  const int r = 16 * (rb * p.tpb + lt) + row16;
-  const int i = r / p.G, h = g * p.G + (r - i * p.G);
-  const float inv = ls > 0.f ? 1.f / ls : 0.f;
-  o0 *= inv;
-  o1 *= inv;
-  *reinterpret_cast<uint4*>(p.out + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 8 * c) =
-      make_uint4(pack2_bf16(o0[0], o0[1]), pack2_bf16(o0[2], o0[3]), pack2_bf16(o1[0], o1[1]), pack2_bf16(o1[2], o1[3]));
-  constexpr float kLn2 = 0.69314718055994530942f;
-  if (p.lse && c == 0) p.lse[(size_t(b) * p.max_T + i) * p.Hq + h] = ls > 0.f ? (mx + __log2f(ls)) * kLn2 : -INFINITY;
+  mr.write<D>(p, b, g, 16 * (rb * p.tpb + lt) + row16, c);
 }
 
 struct AttnShape {
