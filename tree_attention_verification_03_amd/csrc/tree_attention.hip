@@ -37,6 +37,8 @@
 namespace spectree {
 namespace {
 
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, each with its own L2
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -66,6 +68,7 @@ struct AttnParams {
   int max_T, Hq, Hkv, G;
   int page_shift, max_pages, num_pages;
   int chunk, n_splits, n_rb, tpb, npg;
+  int n_groups;  // B * Hkv * n_splits
   float scale_log2;
 };
 
@@ -190,7 +193,25 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform, so everything derived from it is scalar
-  const int s = blockIdx.x, rb = blockIdx.y, bg = blockIdx.z;
+  // Workgroups are dealt to the 8 XCDs round-robin by flattened id. 8-wave blocks (the only plans
+  // with several row blocks per (sequence, KV head, item) group, which stream the same keys) run on
+  // a 1-D grid whose ids are re-mapped so a group's row blocks get one residue mod 8 and consecutive
+  // slots: they share that XCD's L2, and groups stay balanced over the XCDs (ids past the last group
+  // exit). 4-wave blocks have one row block and use the 3-D grid as it is (no division on the way to
+  // the first loads).
+  int s, rb, bg;
+  if constexpr (NW == 8) {
+    const int xcd = blockIdx.x & (kXcds - 1), slot = blockIdx.x / kXcds;
+    const int grp = (slot / p.n_rb) * kXcds + xcd;
+    if (grp >= p.n_groups) return;
+    rb = slot - (slot / p.n_rb) * p.n_rb;
+    bg = grp / p.n_splits;
+    s = grp - bg * p.n_splits;
+  } else {
+    s = blockIdx.x;
+    rb = blockIdx.y;
+    bg = blockIdx.z;
+  }
   const int b = bg / p.Hkv, g = bg - b * p.Hkv;
   const int32_t* ptab = p.page_table + size_t(b) * p.max_pages;
   const int t0 = rb * p.tpb;  // first row tile of this block
@@ -741,7 +762,9 @@ extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const
   prm.tpb = pl.tpb;
   prm.npg = pl.npg;
   prm.scale_log2 = sm_scale * 1.4426950408889634f;
-  const dim3 grid(pl.n_splits, pl.n_rb, B * Hkv);
+  prm.n_groups = B * Hkv * pl.n_splits;
+  const dim3 grid = pl.sh.NW == 8 ? dim3(unsigned((prm.n_groups + kXcds - 1) / kXcds * kXcds * pl.n_rb))
+                                  : dim3(pl.n_splits, pl.n_rb, B * Hkv);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 cgrid(pl.tpb, pl.n_rb * B * Hkv);
   if (d == 64) {
