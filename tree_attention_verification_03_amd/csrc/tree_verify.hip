@@ -656,119 +656,120 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
 }
 
 // ------------------------------------------------------------------ walk
-// Runs in the last block of sequence b to finish; reads the other blocks' results with agent-scope loads.
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  return (uint64_t(uint32_t(__shfl(int(v >> 32), src))) << 32) | uint32_t(__shfl(int(v), src));
+}
+
+// Runs in wave 0 of the last block of sequence b to finish (node n in lane n - 1; the root's values are
+// read by every lane); reads the other blocks' results with agent-scope loads, one round trip.
+// Greedy: a node is accepted when its token is its parent's argmax and so is every node above it;
+// validity (AND) and depth (sum) along the path come from pointer doubling over lanes, the deepest
+// valid node (ties -> smaller index) from a wave maximum, and the path from its ancestry bits.
+// Sampling: the accepted child chain from the root, chased in registers.
 __device__ __forceinline__ void walk(const VerifyWs& w, const VerifyArgs& a, int b) {
-  __shared__ int par_s[65], a_s[65], jmp_s[65], dep_s[65], ok_s[65], path_s[65];
-  __shared__ uint32_t st_s, best_s;
-  __shared__ int n_s, bonus_s;
-  const int tid = threadIdx.x, max_T = a.max_T, V = a.V;
+  __shared__ int path_s[65], tok_s[65];
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x, max_T = a.max_T, V = a.V;
   const int T = seq_T(a.T_b, b, max_T);
   const bool greedy = a.mode[b] != SPEC_MODE_SAMPLE;
   const size_t base = size_t(b) * max_T;
-  if (tid == 0) {
-    st_s = 0;
-    best_s = 0;
-  }
-  __syncthreads();
-  if (tid < T) {
-    uint32_t f = 0;
-    int par = -1;
-    if (tid > 0) {
-      par = a.parents[base + tid];
-      if (par < 0 || par >= tid) {
-        par = 0;
-        f |= SPEC_STATUS_INVALID_PARENT;
-      }
-      const int t = a.tokens[base + tid];
-      if (t < 0 || t >= V) f |= SPEC_STATUS_INVALID_TOKEN;
+  const int n = lane + 1;
+  const bool real = n < T;
+  uint32_t f = 0;
+  int par = 0, tok = 0;
+  if (real) {
+    par = a.parents[base + n];
+    if (par < 0 || par >= n) {
+      par = 0;
+      f |= SPEC_STATUS_INVALID_PARENT;
     }
-    par_s[tid] = par;
-    if (greedy) {
-      const uint64_t k = ld_agent(w.keys + base + tid);
-      a_s[tid] = int(0xffffffffu - uint32_t(k));
-      if (ld_agent(w.rowflag + base + tid)) f |= SPEC_STATUS_NAN_INPUT;
-      st_agent(w.keys + base + tid, uint64_t(0));  // leave the workspace zeroed
-      st_agent(w.rowflag + base + tid, 0u);
-    } else {
-      f |= ld_agent(w.nflag + base + tid) & SPEC_STATUS_NAN_INPUT;
-    }
-    if (f) atomicOr(&st_s, f);
+    tok = a.tokens[base + n];
+    if (tok < 0 || tok >= V) f |= SPEC_STATUS_INVALID_TOKEN;
+    tok_s[n] = tok;
   }
-  __syncthreads();
-
-  int e = 0;
+  if (lane == 0) path_s[0] = 0;
+  int nacc, bonus;
+  uint32_t rootf;
   if (greedy) {
-    if (tid < T) {
-      const int t = tid > 0 ? a.tokens[base + tid] : 0;
-      const bool good = tid == 0 || (t >= 0 && t < V && t == a_s[par_s[tid]]);
-      ok_s[tid] = good;
-      jmp_s[tid] = tid > 0 ? par_s[tid] : 0;
-      dep_s[tid] = tid > 0;
+    const uint64_t k0 = ld_agent(w.keys + base);
+    const uint32_t rf0 = ld_agent(w.rowflag + base);
+    uint64_t k = 0;
+    uint32_t rf = 0;
+    if (real) {
+      k = ld_agent(w.keys + base + n);
+      rf = ld_agent(w.rowflag + base + n);
     }
-    __syncthreads();
-    for (int it = 0; it < 7; ++it) {  // pointer doubling: validity = AND, depth = sum along the path
-      int no = 0, nd = 0, nj = 0;
-      if (tid < T) {
-        const int j = jmp_s[tid];
-        no = ok_s[tid] & ok_s[j];
-        nd = dep_s[tid] + dep_s[j];
-        nj = jmp_s[j];
-      }
-      __syncthreads();
-      if (tid < T) {
-        ok_s[tid] = no;
-        dep_s[tid] = nd;
-        jmp_s[tid] = nj;
-      }
-      __syncthreads();
+    const int am0 = int(0xffffffffu - uint32_t(k0)), am = int(0xffffffffu - uint32_t(k));
+    if (rf) f |= SPEC_STATUS_NAN_INPUT;
+    rootf = rf0 ? SPEC_STATUS_NAN_INPUT : 0u;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every lane has read the root before it is cleared
+    if (real) {  // leave the workspace zeroed
+      st_agent(w.keys + base + n, uint64_t(0));
+      st_agent(w.rowflag + base + n, 0u);
     }
-    // deepest valid node, ties -> smallest index
-    if (tid < T && ok_s[tid]) atomicMax(&best_s, (uint32_t(dep_s[tid] + 1) << 8) | uint32_t(255 - tid));
-    __syncthreads();
-    e = 255 - int(best_s & 255u);
+    if (lane == 0) {
+      st_agent(w.keys + base, uint64_t(0));
+      st_agent(w.rowflag + base, 0u);
+    }
+    const int par_am = __shfl(am, par > 0 ? par - 1 : lane);
+    int ok = real && tok >= 0 && tok < V && tok == (par > 0 ? par_am : am0);
+    int dep = 1, jump = real ? par : 0;  // 0 = reached the root
+    uint64_t anc = real ? (1ull << lane) : 0ull;
+    while (__ballot(jump != 0)) {
+      const int src = jump > 0 ? jump - 1 : lane;
+      const int oj = __shfl(ok, src), dj = __shfl(dep, src), jj = __shfl(jump, src);
+      const uint64_t aj = shfl_u64(anc, src);
+      if (jump != 0) {
+        ok &= oj;
+        dep += dj;
+        anc |= aj;
+        jump = jj;
+      }
+    }
+    // deepest valid node, ties -> smaller index; the root (depth 0, index 0) always qualifies
+    const uint32_t key = (real && ok) ? (uint32_t(dep + 1) << 8) | uint32_t(255 - n) : 0u;
+    const uint32_t best = max(uint32_t(wave_max_u64(key)), (1u << 8) | 255u);
+    const int e = 255 - int(best & 255u);
+    nacc = int(best >> 8) - 1;
+    const uint64_t anc_e = shfl_u64(anc, e > 0 ? e - 1 : 0);
+    if (e > 0 && real && ((anc_e >> lane) & 1)) path_s[dep] = n;
+    bonus = e > 0 ? __shfl(am, e - 1) : am0;
   } else {
-    if (tid == 0) {
-      int uu = 0, n = 0;
-      uint32_t sf = 0;
-      path_s[0] = 0;
-      while (true) {
-        sf |= ld_agent(w.nflag + base + uu) & (SPEC_STATUS_ZERO_Q | SPEC_STATUS_ZERO_RESIDUAL);
-        const int c = ld_agent(w.acc_child + base + uu);
-        if (c <= uu || c >= T || n >= 64) break;
-        uu = c;
-        path_s[++n] = uu;
-      }
-      st_s |= sf;
-      dep_s[0] = n;  // reuse as the path length
-      a_s[0] = ld_agent(w.bonus + base + uu);
+    const uint32_t nf0 = ld_agent(w.nflag + base);
+    const int ch0 = ld_agent(w.acc_child + base), bo0 = ld_agent(w.bonus + base);
+    uint32_t nf = 0;
+    int ch = -1, bo = 0;
+    if (real) {
+      nf = ld_agent(w.nflag + base + n);
+      ch = ld_agent(w.acc_child + base + n);
+      bo = ld_agent(w.bonus + base + n);
     }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    int n;
-    int bonus;
-    if (greedy) {
-      n = dep_s[e];
-      int x = e;
-      for (int k = n; k >= 0; --k) {
-        path_s[k] = x;
-        x = par_s[x] < 0 ? 0 : par_s[x];
-      }
-      bonus = a_s[e];
-    } else {
-      n = dep_s[0];
-      bonus = a_s[0];
+    f |= nf & SPEC_STATUS_NAN_INPUT;
+    constexpr uint32_t kPathFlags = SPEC_STATUS_ZERO_Q | SPEC_STATUS_ZERO_RESIDUAL;
+    rootf = nf0 & (SPEC_STATUS_NAN_INPUT | kPathFlags);
+    int u = 0, c = ch0, cnt = 0;
+    bonus = bo0;
+    while (c > u && c < T && cnt < kWave) {  // uniform: every value comes from a readlane
+      u = c;
+      ++cnt;
+      if (lane == 0) path_s[cnt] = u;
+      rootf |= __builtin_amdgcn_readlane(nf, u - 1) & kPathFlags;
+      bonus = __builtin_amdgcn_readlane(bo, u - 1);
+      c = __builtin_amdgcn_readlane(ch, u - 1);
     }
-    a.accept_len[b] = n;
-    a.status[b] = st_s;
-    n_s = n;
-    bonus_s = bonus;
+    nacc = cnt;
   }
-  __syncthreads();
-  const int n = n_s;
-  for (int k = tid; k < max_T; k += kThreads) {
-    a.accept_nodes[base + k] = k <= n ? path_s[k] : -1;
-    a.out_tokens[base + k] = k < n ? a.tokens[base + path_s[k + 1]] : (k == n ? bonus_s : -1);
+  const uint32_t st = wave_or_u32(f) | rootf;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // path_s / tok_s written by other lanes
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane == 0) {
+    a.accept_len[b] = nacc;
+    a.status[b] = st;
+  }
+  for (int k = lane; k < max_T; k += kWave) {
+    a.accept_nodes[base + k] = k <= nacc ? path_s[k] : -1;
+    a.out_tokens[base + k] = k < nacc ? tok_s[path_s[k + 1]] : (k == nacc ? bonus : -1);
   }
 }
 
