@@ -41,19 +41,20 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kSampleSlice = 8192;  // row elements per sampling work item
-constexpr int kMaxWorkers = 512;
+constexpr int kGreedySlice = 8192;  // row elements per greedy block (one round trip of loads)
+constexpr int kMaxWorkers = 512;  // persistent sampling blocks (2 per CU are resident)
 
-struct NodeState {  // one sampling node; all zero between calls
-  uint64_t sp, sq, am;  // pass 0: sums of fx(p) and fx(q), argmax key of fx(p)
-  uint64_t wl[3];       // pass in flight: sums of the residual's 32-bit limbs
+struct NodeState {  // one sampling node; all zero between calls (written by its decision blocks only)
+  uint64_t sp, sq, am;  // from pass 0: sums of fx(p) and fx(q), argmax key of fx(p)
   uint64_t gamma;       // gamma of the pass in flight
-  uint32_t nan;         // NaN seen in pass 0: bit 0 in p, bit 1 in q
   uint32_t ticket;      // slices of the pass in flight that are done
   uint32_t flags;       // status flags so far
   int32_t kid;          // index (in the node's child list) of the next child to test
   int32_t tested;       // some child was tested
   int32_t pass;         // passes completed
 };
+
+constexpr int kMaxKids = 64;  // children of one node (T <= 65)
 
 struct VerifyWs {
   uint64_t* keys;      // [B*max_T] greedy argmax keys (0 = empty)
@@ -63,7 +64,9 @@ struct VerifyWs {
   uint32_t* nflag;     // [B*max_T] sampling node flags
   uint32_t* tickets;   // [B] greedy: slice blocks done; sampling: nodes done
   NodeState* node;     // [B*max_T]
-  uint64_t* ssum;      // [B*max_T][nsl][2] u128 slice sums of the node's last pass
+  uint64_t* ssum;      // [B*max_T][nsl][2] u128 slice sums of the node's last pass (pass 0: of fx(p))
+  uint64_t* psum;      // [B*max_T][nsl][3] pass 0 per slice: sum of fx(q), argmax key of fx(p), NaN bits
+  uint64_t* kidpq;     // [B*max_T][kMaxKids] children: (fx(p[t]) << 32) | fx(q[t]), ~0 = invalid token
   uint32_t* queue;     // [B*max_T*nsl] published dynamic items (node * nsl + slice + 1), 0 = empty
   uint32_t* qctl;      // [4] head, tail, nodes done, workers exited
 };
@@ -89,6 +92,8 @@ VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
   w.tickets = reinterpret_cast<uint32_t*>(take(4 * size_t(B)));
   w.node = reinterpret_cast<NodeState*>(take(sizeof(NodeState) * n));
   w.ssum = reinterpret_cast<uint64_t*>(take(16 * n * nsl));
+  w.psum = reinterpret_cast<uint64_t*>(take(24 * n * nsl));
+  w.kidpq = reinterpret_cast<uint64_t*>(take(8 * n * kMaxKids));
   w.queue = reinterpret_cast<uint32_t*>(take(4 * n * nsl));
   w.qctl = reinterpret_cast<uint32_t*>(take(16));
   *total = off;
@@ -132,8 +137,8 @@ __device__ __forceinline__ void greedy_slice(const VerifyWs& w, const VerifyArgs
   const float* r = a.target + size_t(row) * a.V;
   uint64_t best = 0;
   bool nan = false;
-  if (VEC) {  // a slice is at most kSampleSlice elements: all of a thread's loads in one round trip
-    constexpr int NV = kSampleSlice / (4 * kThreads);
+  if (VEC) {  // a slice is at most kGreedySlice elements: all of a thread's loads in one round trip
+    constexpr int NV = kGreedySlice / (4 * kThreads);
     float4 xs[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -290,36 +295,6 @@ __device__ __forceinline__ u128 block_exclusive_scan_u128(u128 x, u128* wtot) {
   return before + incl - x;
 }
 
-// children of u in index order (a parent outside [0, c) counts as the root); returns their count
-__device__ __forceinline__ int node_children(const VerifyArgs& a, int b, int u, int T, int* kid_s, int* nkid_s) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave == 0) {
-    int n = 0;
-    for (int c0 = 1; c0 < T; c0 += kWave) {
-      const int c = c0 + lane;
-      bool kid = false;
-      if (c < T) {
-        int pc = a.parents[size_t(b) * a.max_T + c];
-        if (pc < 0 || pc >= c) pc = 0;
-        kid = (pc == u);
-      }
-      const uint64_t m = __ballot(kid);
-      if (kid) kid_s[n + __popcll(m & ((1ull << lane) - 1))] = c;
-      n += __popcll(m);
-    }
-    if (lane == 0) *nkid_s = n;
-  }
-  __syncthreads();
-  return *nkid_s;
-}
-
-// the node's q row, or null if it has none (no children, no draft tensor, or q_row out of range)
-__device__ __forceinline__ const float* node_qrow(const VerifyArgs& a, int b, int u, int nkid) {
-  const int qr = a.q_row ? a.q_row[size_t(b) * a.max_T + u] : -1;
-  const bool has_q = nkid > 0 && a.draft != nullptr && qr >= 0 && qr < a.R;
-  return has_q ? a.draft + (size_t(b) * a.R + qr) * a.V : nullptr;
-}
-
 // the q row named by q_row whether or not the node has children (pass 0 reads it before the children
 // are known; its sums only count for a node with children)
 __device__ __forceinline__ const float* node_qrow_any(const VerifyArgs& a, int b, int u) {
@@ -396,8 +371,8 @@ __device__ __forceinline__ void pass_done(const VerifyWs& w, const VerifyArgs& a
   sample_decide<VEC>(w, a, b, u, T);
 }
 
-// pass 0 over slice s: sums of fx(p) (and of fx(q) for a node with children and a q row), argmax key of
-// fx(p), NaN checks; the slice's p sum is kept for a resample from p
+// pass 0 over slice s: sums of fx(p) and fx(q), argmax key of fx(p), NaN bits, published per slice
+// (the node's decision block reduces them)
 template <bool VEC>
 __device__ __forceinline__ void sample_pass0(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T, int s) {
   __shared__ uint64_t red[kWaves][3];
@@ -425,21 +400,20 @@ __device__ __forceinline__ void sample_pass0(const VerifyWs& w, const VerifyArgs
     block_sum3(sp, sq, nn, red);
     if (threadIdx.x == 0) {
       for (int i = 1; i < kWaves; ++i) am = amr[i] > am ? amr[i] : am;
-      NodeState* ns = w.node + node;
-      atomicAdd(reinterpret_cast<unsigned long long*>(&ns->sp), (unsigned long long)sp);
-      if (sq) atomicAdd(reinterpret_cast<unsigned long long*>(&ns->sq), (unsigned long long)sq);
-      atomicMax(reinterpret_cast<unsigned long long*>(&ns->am), (unsigned long long)am);
-      if (nn) atomicOr(&ns->nan, ((nn & 15u) ? 1u : 0u) | ((nn >> 4) ? 2u : 0u));
       uint64_t* ss = w.ssum + (node * a.nsl + s) * 2;
+      uint64_t* ps = w.psum + (node * a.nsl + s) * 3;
       st_agent(ss, sp);
       st_agent(ss + 1, uint64_t(0));
+      st_agent(ps, sq);
+      st_agent(ps + 1, am);
+      st_agent(ps + 2, uint64_t(((nn & 15u) ? 1u : 0u) | ((nn >> 4) ? 2u : 0u)));
     }
   }
   pass_done<VEC>(w, a, b, u, T);
 }
 
 // residual pass over slice s under the node's current gamma: the slice's sum of
-// N[v] = max(0, fx(p[v]) S_Q - gamma fx(q[v])) as 32-bit limb sums
+// N[v] = max(0, fx(p[v]) S_Q - gamma fx(q[v])) (32-bit limb sums), published per slice
 template <bool VEC>
 __device__ __forceinline__ void sample_passN(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T, int s) {
   __shared__ uint64_t red[kWaves][3];
@@ -458,9 +432,6 @@ __device__ __forceinline__ void sample_passN(const VerifyWs& w, const VerifyArgs
   });
   block_sum3(l0, l1, l2, red);
   if (threadIdx.x == 0) {
-    atomicAdd(reinterpret_cast<unsigned long long*>(&ns->wl[0]), (unsigned long long)l0);
-    atomicAdd(reinterpret_cast<unsigned long long*>(&ns->wl[1]), (unsigned long long)l1);
-    atomicAdd(reinterpret_cast<unsigned long long*>(&ns->wl[2]), (unsigned long long)l2);
     const u128 v = u128(l0) + (u128(l1) << 32) + (u128(l2) << 64);
     uint64_t* ss = w.ssum + (node * a.nsl + s) * 2;
     st_agent(ss, uint64_t(v));
@@ -471,52 +442,132 @@ __device__ __forceinline__ void sample_passN(const VerifyWs& w, const VerifyArgs
 
 template <bool VEC>
 __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
-  __shared__ int kid_s[64], nkid_s;
+  __shared__ int kid_s[kMaxKids], nkid_s;
+  __shared__ uint64_t kpq_s[kMaxKids];  // children: (fx(p[t]) << 32) | fx(q[t]), ~0 = invalid token
   __shared__ int act_s;  // accepted child, -1: residual pass enqueued, -2: resample
   __shared__ u128 W_s, excl_s, wtot_s[kWaves];
   __shared__ uint64_t SQ_s, gamma_s, AM_s;
   __shared__ uint32_t flags_s;
-  __shared__ int plain_s, sstar_s, bonus_s;
-  __shared__ u128 ssl_s[kThreads];
+  __shared__ int plain_s, bonus_s, pass_s;
+  __shared__ u128 ssl_s[kThreads];  // the pass's slice sums (the first kThreads slices)
+  __shared__ u128 wred_s[kWaves];
+  __shared__ uint64_t red_s[kWaves][3];
   __shared__ int found_s;
   __shared__ u128 run_s, tau_s;
-  const int tid = threadIdx.x, max_T = a.max_T, V = a.V;
-  const int nkid = node_children(a, b, u, T, kid_s, &nkid_s);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, max_T = a.max_T, V = a.V;
   const size_t node = size_t(b) * max_T + u;
   NodeState* ns = w.node + node;
   const float* prow = a.target + node * V;
-  const float* qrow = node_qrow(a, b, u, nkid);
+  // a decision is one serial chain that every later pass of the node waits for, while the blocks
+  // around it run throughput work: its waves take issue priority until it is done
+  __builtin_amdgcn_s_setprio(3);
+  struct PrioRestore {
+    __device__ ~PrioRestore() { __builtin_amdgcn_s_setprio(0); }
+  } prio_restore;
+
+  // ---- one round trip: the node's state, every slice's results, its children and their cache
+  int pass = 0, kid = 0, tested = 0;
+  uint32_t flags = 0;
+  uint64_t gamma = 0, SPc = 0, SQc = 0, AMc = 0;
+  const int qr = a.q_row ? a.q_row[node] : -1;
   if (tid == 0) {
-    const int pass = ld_agent(&ns->pass);
-    const uint64_t S_P = ld_agent(&ns->sp), S_Q = qrow ? ld_agent(&ns->sq) : 0;
+    pass = ld_agent(&ns->pass);
+    kid = ld_agent(&ns->kid);
+    tested = ld_agent(&ns->tested);
+    flags = ld_agent(&ns->flags);
+    gamma = ld_agent(&ns->gamma);
+    SPc = ld_agent(&ns->sp);
+    SQc = ld_agent(&ns->sq);
+    AMc = ld_agent(&ns->am);
+  }
+  u128 wsum = 0;  // sum of the pass's slice sums (pass 0: of fx(p))
+  uint64_t sq = 0, am = 0, nanb = 0;
+  for (int sl = tid; sl < a.nsl; sl += kThreads) {
+    const uint64_t* s2 = w.ssum + (node * a.nsl + sl) * 2;
+    const uint64_t* p3 = w.psum + (node * a.nsl + sl) * 3;
+    const u128 v = u128(ld_agent(s2)) | (u128(ld_agent(s2 + 1)) << 64);
+    const uint64_t q = ld_agent(p3), m = ld_agent(p3 + 1), f = ld_agent(p3 + 2);
+    if (sl < kThreads) ssl_s[sl] = v;
+    wsum += v;
+    sq += q;
+    am = m > am ? m : am;
+    nanb |= f;
+  }
+  int c_kid = 0, c_tok = -1;  // wave 0, lane l: the tree's node l + 1 if it is a child of u, its token
+  uint64_t cached = 0;
+  if (wave == 0) {
+    const int c = lane + 1;
+    if (c < T) {
+      int pc = a.parents[size_t(b) * max_T + c];
+      if (pc < 0 || pc >= c) pc = 0;
+      c_kid = pc == u;
+      c_tok = a.tokens[size_t(b) * max_T + c];
+    }
+    cached = ld_agent(w.kidpq + node * kMaxKids + lane);
+  }
+  // ---- reductions (u128 sum, sum, max, or) and the child list in index order
+  wsum = wave_sum_u128(wsum);
+  sq = wave_sum_u64(sq);
+  am = wave_max_u64(am);
+  nanb = wave_or_u32(uint32_t(nanb));
+  if (lane == 0) {
+    wred_s[wave] = wsum;
+    red_s[wave][0] = sq;
+    red_s[wave][1] = am;
+    red_s[wave][2] = nanb;
+  }
+  int kslot = -1;  // this lane's position in the child list
+  if (wave == 0) {
+    const uint64_t m = __ballot(c_kid);
+    if (c_kid) {
+      kslot = __popcll(m & ((1ull << lane) - 1));
+      kid_s[kslot] = lane + 1;
+    }
+    if (lane == 0) nkid_s = __popcll(m);
+  }
+  if (tid == 0) pass_s = pass;
+  __syncthreads();
+  const int nkid = nkid_s;
+  // the node's q row, or null if it has none (no children, no draft tensor, or q_row out of range)
+  const float* qrow = (nkid > 0 && a.draft != nullptr && qr >= 0 && qr < a.R) ? a.draft + (size_t(b) * a.R + qr) * V : nullptr;
+  if (pass_s == 0) {  // first decision: the children's p and q at their tokens (cached for later passes)
+    if (wave == 0 && kslot >= 0) {
+      uint64_t pq = ~0ull;
+      if (c_tok >= 0 && c_tok < V) pq = (uint64_t(fx(prow[c_tok])) << 32) | (qrow ? fx(qrow[c_tok]) : 0u);
+      kpq_s[kslot] = pq;
+      st_agent(w.kidpq + node * kMaxKids + kslot, pq);
+    }
+  } else if (wave == 0) {
+    kpq_s[lane] = cached;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int i = 1; i < kWaves; ++i) {
+      wsum += wred_s[i];
+      sq += red_s[i][0];
+      am = red_s[i][1] > am ? red_s[i][1] : am;
+      nanb |= red_s[i][2];
+    }
+    const uint64_t S_P = pass == 0 ? uint64_t(wsum) : SPc;  // S_P < V 2^32 < 2^56
+    const uint64_t S_Q = pass == 0 ? (qrow ? sq : 0) : SQc;
+    const uint64_t AM = pass == 0 ? am : AMc;
     const bool test = nkid > 0 && qrow != nullptr && S_Q > 0;
-    uint32_t flags;
-    uint64_t gamma;
-    int kid, tested;
     u128 W;
     if (pass == 0) {
-      const uint32_t nb = ld_agent(&ns->nan);
-      flags = ((nb & 1u) || ((nb & 2u) && qrow)) ? SPEC_STATUS_NAN_INPUT : 0u;
+      flags = ((nanb & 1u) || ((nanb & 2u) && qrow)) ? SPEC_STATUS_NAN_INPUT : 0u;
       if (nkid > 0 && !test) flags |= SPEC_STATUS_ZERO_Q;
       W = u128(S_P) * S_Q;
-      gamma = 0;
-      kid = 0;
-      tested = 0;
     } else {
-      flags = ld_agent(&ns->flags);
-      gamma = ld_agent(&ns->gamma);
-      kid = ld_agent(&ns->kid);
-      tested = ld_agent(&ns->tested);
-      W = u128(ld_agent(&ns->wl[0])) + (u128(ld_agent(&ns->wl[1])) << 32) + (u128(ld_agent(&ns->wl[2])) << 64);
+      W = wsum;
       if (W == 0) flags |= SPEC_STATUS_ZERO_RESIDUAL;
     }
     int act = -2;
     for (int ki = kid; test && ki < nkid; ++ki) {
       const int c = kid_s[ki];
-      const int t = a.tokens[size_t(b) * max_T + c];
-      if (t < 0 || t >= V) continue;  // invalid draft token: never tested
+      const uint64_t pq = kpq_s[ki];
+      if (pq == ~0ull) continue;  // invalid draft token: never tested
       tested = 1;
-      const uint32_t Pt = fx(prow[t]), Qt = fx(qrow[t]);
+      const uint32_t Pt = uint32_t(pq >> 32), Qt = uint32_t(pq);
       const u128 Nt = residual(Pt, Qt, S_Q, gamma, false);
       const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(c), 0, a.key0, a.key1);
       const uint64_t m = (r.w[0] >> 40) + 1;  // r = m / 2^24 in (0, 1]
@@ -530,20 +581,22 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
         act = c;
         break;
       }
-      // rejected: residual <- norm(max(0, residual - q)); its mass needs a pass over the row
+      // rejected: residual <- norm(max(0, residual - q)); its mass needs a pass over the row. The
+      // state and the queue reservation go out together; the items are published once both are done.
       gamma = gamma + div_u128_u64(W, S_Q);
-      kid = ki + 1;
       act = -1;
       st_agent(&ns->gamma, gamma);
-      st_agent(&ns->kid, kid);
+      st_agent(&ns->kid, ki + 1);
       st_agent(&ns->tested, 1);
       st_agent(&ns->flags, flags);
       st_agent(&ns->pass, pass + 1);
-      st_agent(&ns->wl[0], uint64_t(0));
-      st_agent(&ns->wl[1], uint64_t(0));
-      st_agent(&ns->wl[2], uint64_t(0));
-      wait_global_stores();
+      if (pass == 0) {
+        st_agent(&ns->sp, S_P);
+        st_agent(&ns->sq, S_Q);
+        st_agent(&ns->am, AM);
+      }
       const uint32_t pos = ticket_add_n(&w.qctl[1], uint32_t(a.nsl));
+      wait_global_stores();  // this wave's state and children-cache stores are complete
       for (int sl = 0; sl < a.nsl; ++sl) st_agent(&w.queue[pos + sl], uint32_t(node * a.nsl + sl + 1));
       break;
     }
@@ -552,7 +605,7 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
     W_s = tested ? W : u128(S_P);
     SQ_s = S_Q;
     gamma_s = gamma;
-    AM_s = ld_agent(&ns->am);
+    AM_s = AM;
     flags_s = flags;
   }
   __syncthreads();
@@ -578,12 +631,13 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
       found_s = -1;
       bonus_s = -1;
     }
-    // the slice holding the threshold: slice sums kThreads at a time, one round trip per chunk
+    // the slice holding the threshold: slice sums kThreads at a time (the first chunk is in LDS
+    // already), one round trip per further chunk
     for (int c0 = 0; c0 < a.nsl; c0 += kThreads) {
       __syncthreads();
       if (found_s >= 0) break;
       const int sl = c0 + tid;
-      if (sl < a.nsl) {
+      if (c0 > 0 && sl < a.nsl) {
         const uint64_t* q2 = w.ssum + (node * a.nsl + sl) * 2;
         ssl_s[tid] = u128(ld_agent(q2)) | (u128(ld_agent(q2 + 1)) << 64);
       }
@@ -789,11 +843,7 @@ __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArg
       st_agent(&ns->sp, uint64_t(0));
       st_agent(&ns->sq, uint64_t(0));
       st_agent(&ns->am, uint64_t(0));
-      st_agent(&ns->wl[0], uint64_t(0));
-      st_agent(&ns->wl[1], uint64_t(0));
-      st_agent(&ns->wl[2], uint64_t(0));
       st_agent(&ns->gamma, uint64_t(0));
-      st_agent(&ns->nan, 0u);
       st_agent(&ns->flags, 0u);
       st_agent(&ns->kid, 0);
       st_agent(&ns->tested, 0);
@@ -832,7 +882,7 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
       } else {
         const uint32_t j = i - n_static;
         // wait for slot j to be published, or for every node to be done (bounded: never a hang)
-        int nap = 1;  // polls back off from ~0.05 us to ~1 us, which keeps the queue's lines quiet
+        int nap = 1;  // polls back off from ~0.05 us to ~0.2 us
         for (uint32_t spin = 0; spin < (1u << 22); ++spin) {
           if (j < cap) {
             const uint32_t v = ld_agent(&w.queue[j]);
@@ -844,7 +894,7 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
           }
           if (ld_agent(&w.qctl[2]) >= total) break;
           for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
-          nap = nap < 16 ? 2 * nap : 16;
+          nap = nap < 4 ? 2 * nap : 4;
         }
       }
       item_s = int(it);
@@ -855,7 +905,17 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
     if (it == 0) break;
     const bool dynamic = it > n_static;
     const uint32_t k = dynamic ? it - 1 - n_static : it - 1;
-    const int node = int(k / uint32_t(a.nsl)), sl = int(k % uint32_t(a.nsl));
+    int node, sl;
+    if (dynamic) {  // node * nsl + slice
+      node = int(k / uint32_t(a.nsl));
+      sl = int(k % uint32_t(a.nsl));
+    } else {  // pass 0 items by tree position first (every sequence's root, then node 1, ...): the
+              // nodes near the root, whose passes form the longest chains, start first
+      const uint32_t per_u = uint32_t(a.B) * uint32_t(a.nsl);
+      const uint32_t uu = k / per_u, rem = k - uu * per_u;
+      node = int(rem / uint32_t(a.nsl)) * max_T + int(uu);
+      sl = int(rem % uint32_t(a.nsl));
+    }
     const int b = node / max_T, u = node - b * max_T;
     if (a.mode[b] != SPEC_MODE_SAMPLE) continue;  // a greedy row's static item
     const int T = seq_T(a.T_b, b, max_T);
@@ -928,8 +988,8 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
   size_t need = 0;
   VerifyWs w = carve(ws, B, max_T, V, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_verify: workspace %zu < %zu bytes", ws_bytes, need);
-  // greedy slices of kSampleSlice elements (one round trip per block; fewer blocks per sequence ticket)
-  const long long sl = kSampleSlice;
+  // greedy slices of kGreedySlice elements (one round trip per block; fewer blocks per sequence ticket)
+  const long long sl = kGreedySlice;
   VerifyArgs a;
   a.target = target;
   a.draft = draft_probs;
