@@ -216,14 +216,15 @@ __device__ __forceinline__ Popped wave_pop(uint64_t* c) {
   return p;
 }
 
-// Block-wide top-k (k <= 8) of row[lo, hi) in rank order (0 = none) in out_key[0..k).
+// Block-wide top-k (k <= 8) of row[lo, hi) in rank order (0 = none) in out_key[0..k); with per_wave
+// each wave's own top k are returned instead (lane r holds the wave's r-th key) and out_key is unused.
 // xs holds the first batch (load_batch(row, lo, hi, xs)). Every lane keeps the two largest keys of
 // its own elements; each wave pops its k largest (a lane that gives up both refills them with its
 // largest keys below the last one taken, so the pops are exact), and wave 0 pops the k best of the
 // waves' lists. xs is consumed (free after the lane pass).
 template <bool VEC, int EPL>
-__device__ __forceinline__ void block_slice_topk(const float* row, int lo, int hi, int k, float* xs,
-                                                 uint64_t* out_key) {
+__device__ __forceinline__ uint64_t block_slice_topk(const float* row, int lo, int hi, int k, bool per_wave,
+                                                     float* xs, uint64_t* out_key) {
   constexpr int NWV = kRowThreads / kWave;
   constexpr int kBatch = EPL * kRowThreads;
   __shared__ uint64_t wk[NWV * kMaxTopk];
@@ -253,6 +254,7 @@ __device__ __forceinline__ void block_slice_topk(const float* row, int lo, int h
       }
     }
   }
+  if (per_wave) return mine;  // every wave publishes its own list (lane r: its r-th key)
   if (lane < k) wk[wave * k + lane] = mine;
   __syncthreads();
   if (wave == 0) {
@@ -264,6 +266,7 @@ __device__ __forceinline__ void block_slice_topk(const float* row, int lo, int h
     if (lane < k) out_key[lane] = best;
   }
   __syncthreads();
+  return 0;
 }
 
 // Finish, selection (wave 0): the N best pool entries by (score desc, pool index asc). Entry e sits
@@ -464,8 +467,8 @@ template <bool VEC, int EPL>
 __global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, int P, int step, const float* draft,
                                                                   int64_t seq_stride, const int32_t* topk,
                                                                   const int32_t* depth, int max_topk, int max_depth,
-                                                                  int V, int slice, int32_t* frontier_tokens,
-                                                                  FinishArgs fa) {
+                                                                  int V, int slice, int per_wave,
+                                                                  int32_t* frontier_tokens, FinishArgs fa) {
   constexpr int NWV = kRowThreads / kWave;
   __shared__ uint64_t keys[kMaxTopk];
   __shared__ uint64_t top[kMaxTopk * kMaxTopk];  // [row][rank]
@@ -487,12 +490,16 @@ __global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, i
     fsc = w.fscore[b * max_topk + tid];
   }
   const int k = clamp_i(k_in, 1, max_topk);
-  block_slice_topk<VEC, EPL>(row, lo, hi, k, xs, keys);
+  const uint64_t wave_key = block_slice_topk<VEC, EPL>(row, lo, hi, k, per_wave, xs, keys);
   const int D = clamp_i(d_in, 1, max_depth);
   const int rows = step == 1 ? 1 : k;
   if (step > D || f >= rows) return;
-  uint64_t* cand = w.cand + (size_t(b) * max_topk + f) * kCand + x * k;
-  if (tid < k) st_agent(cand + tid, keys[tid]);
+  uint64_t* cand = w.cand + (size_t(b) * max_topk + f) * kCand;
+  if (per_wave) {  // the wave lists of slice x are lists x NWV .. x NWV + NWV - 1 of the row
+    if (lane < k) st_agent(cand + (x * NWV + wave) * k + lane, wave_key);
+  } else if (tid < k) {
+    st_agent(cand + x * k + tid, keys[tid]);
+  }
   wait_global_stores();
   __syncthreads();
   if (tid == 0) last = (ticket_add(w.ticket + b) == uint32_t(n_slices * rows - 1));
@@ -502,7 +509,7 @@ __global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, i
 
   // every row's n_slices * k <= kCand candidates (0 = empty); wave w merges rows w and w + NWV,
   // each lane holding up to four candidates of a row
-  const int nc = n_slices * k;
+  const int nc = n_slices * (per_wave ? NWV : 1) * k;
   uint64_t cv[2][kCandPerLane];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
@@ -655,10 +662,13 @@ int32_t launch_step(const char* who, void* ws, size_t ws_bytes, int32_t step, co
   const int slice = (per + batch - 1) / batch * batch;
   n_slices = (V + slice - 1) / slice;
   const dim3 grid(n_slices, rows_grid, B);
+  // each wave publishes its own list when every row's wave lists fit the merging wave (saves the
+  // block's cross-wave selection: a barrier and k pops)
+  const int per_wave = n_slices * (kRowThreads / kWave) * max_topk <= kCand ? 1 : 0;
   const bool vec = (V % 4 == 0) && (seq_stride % 4 == 0) && ((reinterpret_cast<uintptr_t>(draft_logprobs) & 15) == 0);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kRowThreads), 0, st, w, P, step, draft_logprobs, seq_stride, topk, depth,
-                       max_topk, max_depth, V, slice, frontier_tokens, fa);
+                       max_topk, max_depth, V, slice, per_wave, frontier_tokens, fa);
   };
   if (vec) {
     if (epl == 8) go(build_step_kernel<true, 8>);
