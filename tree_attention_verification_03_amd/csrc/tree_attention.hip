@@ -128,16 +128,16 @@ __device__ __forceinline__ int v_swz(int key) { return 2 * (key & 3) ^ (D == 128
 constexpr int blocks_per_cu(int D, int NS) { return NS * 128 * D + 4096 <= 160 * 1024 / 2 ? 2 : 1; }
 
 // SPS ring stages of 32 keys form one softmax step (one barrier, one running-max update per step)
+
 // Split-K merge of one output row, item by item in fixed order against the running maximum
 // reference max: out = sum_i w_i O_i / sum_i w_i l_i with w_i = 2^(m_i - max_j m_j). A thread owns
-// 8 columns (o0, o1) of the row.
+// 4 columns (o) of the row.
 struct RowMerge {
   float mx = -INFINITY, ls = 0.f;
-  f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
   // fold the first `navail` of a batch of CB items (the rest are unused loads and may hold anything)
   template <int CB>
-  __device__ __forceinline__ void fold(const float (&mi)[CB], const float (&li)[CB], const f32x4 (&a0)[CB],
-                                       const f32x4 (&a1)[CB], int navail) {
+  __device__ __forceinline__ void fold(const float (&mi)[CB], const float (&li)[CB], const f32x4 (&ai)[CB], int navail) {
     float mb = mx;
 #pragma unroll
     for (int u = 0; u < CB; ++u)
@@ -145,27 +145,25 @@ struct RowMerge {
     if (mb == -INFINITY) return;  // nothing visible yet
     const float sc = (mx == -INFINITY) ? 0.f : fast_exp2(mx - mb);
     ls *= sc;
-    o0 *= sc;
-    o1 *= sc;
+    o *= sc;
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
       if (u < navail && mi[u] != -INFINITY) {  // guarded, not weighted
         const float w = fast_exp2(mi[u] - mb);
         ls += w * li[u];
-        o0 += a0[u] * w;
-        o1 += a1[u] * w;
+        o += ai[u] * w;
       }
     }
     mx = mb;
   }
-  // out / lse of packed row r (node r / G, head g G + r % G) of sequence b, KV head g; columns 8c..8c+7
+  // out / lse of packed row r (node r / G, head g G + r % G) of sequence b, KV head g; columns 4c..4c+3
   template <int D>
   __device__ __forceinline__ void write(const AttnParams& p, int b, int g, int r, int c) const {
     const int i = r / p.G, h = g * p.G + (r - i * p.G);
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
-    const f32x4 v0 = o0 * inv, v1 = o1 * inv;
-    *reinterpret_cast<uint4*>(p.out + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 8 * c) =
-        make_uint4(pack2_bf16(v0[0], v0[1]), pack2_bf16(v0[2], v0[3]), pack2_bf16(v1[0], v1[1]), pack2_bf16(v1[2], v1[3]));
+    const f32x4 v = o * inv;
+    *reinterpret_cast<uint2*>(p.out + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 4 * c) =
+        make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
     constexpr float kLn2 = 0.69314718055994530942f;
     if (p.lse && c == 0) p.lse[(size_t(b) * p.max_T + i) * p.Hq + h] = ls > 0.f ? (mx + __log2f(ls)) * kLn2 : -INFINITY;
   }
@@ -548,6 +546,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
     const int lt = wave + NW * rw;
     if (lt >= p.tpb || t0 + lt >= ntM) continue;
     const int row = lt * 16 + l15;
+    if (16 * (t0 + lt) + l15 >= M) continue;  // rows past this tree: never read
     float* o = mine + size_t(row) * D + g4;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = acc[rw][dt];
@@ -558,53 +557,55 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
   }
 }
 
-// Split-K combine (runs after the main kernel): one block per (b, g, row block, row tile of 16 rows); a
-// thread owns one row and 8 consecutive columns. The first CB items' partials are loaded in the same
-// round trip as the sequence's lengths (loads of items the sequence does not have read workspace
-// memory and are never used), so short sequences finish in one round trip. Items are combined in
-// fixed order, online against the running maximum reference max: out = sum_i w_i O_i / sum_i w_i l_i
-// with w_i = 2^(m_i - max_j m_j). Sequences whose keys fit one item were written directly.
+// Split-K combine (runs after the main kernel): one wave per block, D / 4 threads per row (4 columns
+// each), so a block holds 64 / (D / 4) rows and the grid spreads the partials over many CUs. Rows that
+// no tree of the batch can have (r >= G * max_T) exit before any load. The first CB items' partials
+// are loaded in the same round trip as the sequence's lengths (loads of items the sequence does not
+// have read workspace memory and are never used), so short sequences finish in one round trip. Items
+// are combined in fixed order, online against the running maximum reference max:
+// out = sum_i w_i O_i / sum_i w_i l_i with w_i = 2^(m_i - max_j m_j). Sequences whose keys fit one
+// item were written directly by the main kernel.
 template <int D>
-__global__ void __launch_bounds__(2 * D) tree_attn_combine(AttnParams p) {
-  constexpr int CH = D / 8;  // 8-column chunks per row
-  constexpr int CB = 16;     // items per batch
+__global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
+  constexpr int TPR = D / 4;     // threads per row
+  constexpr int RPB = 64 / TPR;  // rows per block
+  constexpr int CB = 16;         // items per batch
   const int tid = threadIdx.x;
-  const int row16 = tid / CH, c = tid - row16 * CH;
-  const int lt = blockIdx.x, rbg = blockIdx.y;
+  const int rsub = tid / TPR, c = tid - rsub * TPR;
+  const int rbg = blockIdx.y;
   const int bg = rbg / p.n_rb, rb = rbg - bg * p.n_rb;
   const int b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int TR = p.tpb * 16;
+  const int row = blockIdx.x * RPB + rsub;  // row of this row block's partials
+  const int r = rb * TR + row;               // packed row (node r / G, head g G + r % G)
+  if (row >= TR || r >= p.G * p.max_T) return;
   const int T_raw = p.T_b ? p.T_b[b] : p.max_T;
   const int L_raw = p.prefix_lens[b];
-  const int TR = p.tpb * 16;
   const size_t ITEM = size_t(TR) * (D + 2);
   const float* grp = p.part + size_t(rbg) * p.n_splits * ITEM;
-  const int row = lt * 16 + row16;
   RowMerge mr;
   int n_items = CB;  // known after the first batch's loads
 #pragma unroll 1
   for (int ib = 0; ib < n_items; ib += CB) {
     float mi[CB], li[CB];
-    f32x4 a0[CB], a1[CB];
+    f32x4 ai[CB];
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
       const float* base = grp + size_t(min(ib + u, p.n_splits - 1)) * ITEM;
       mi[u] = base[size_t(TR) * D + row];
       li[u] = base[size_t(TR) * (D + 1) + row];
-      const f32x4* src = reinterpret_cast<const f32x4*>(base + size_t(row) * D + 8 * c);
-      a0[u] = src[0];
-      a1[u] = src[1];
+      ai[u] = *reinterpret_cast<const f32x4*>(base + size_t(row) * D + 4 * c);
     }
     if (ib == 0) {
       const int T = min(max(T_raw, 1), p.max_T);
       const int cap = p.max_pages << p.page_shift;
       const int L = min(max(L_raw, 0), cap - T);  // the main kernel's clamp
       n_items = (L + T + p.chunk - 1) / p.chunk;
-      const int r = 16 * (rb * p.tpb + lt) + row16;
       if (n_items == 1 || r >= p.G * T) return;
     }
-    mr.fold<CB>(mi, li, a0, a1, n_items - ib);
+    mr.fold<CB>(mi, li, ai, n_items - ib);
   }
-  mr.write<D>(p, b, g, 16 * (rb * p.tpb + lt) + row16, c);
+  mr.write<D>(p, b, g, r, c);
 }
 
 struct AttnShape {
@@ -628,7 +629,7 @@ AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_p
     int nw = 0, rw = 0, ns = 0, sps = 1;
     const int n = sscanf(env, "%d,%d,%d,%d", &nw, &rw, &ns, &sps);
     const bool single = (nw == 4 || nw == 8) && (rw == 1 || (rw == 2 && nw == 4)) && (ns == 3 || ns == 4) && sps == 1;
-    const bool pair = rw == 1 && (nw == 4 || nw == 8) && (ns == 4 || ns == 6) && sps == 2;
+    const bool pair = rw == 1 && (nw == 4 || nw == 8) && (ns == 4 || ns == 6 || ns == 8) && sps == 2;
     if (n >= 3 && (single || pair)) pl.sh = AttnShape{nw, rw, ns, sps};
   }
   if (d == 64) pl.sh.NW = 4;
@@ -661,7 +662,9 @@ template <int D, int NW, int RW>
 void launch_ns(const AttnPlan& pl, const AttnParams& prm, dim3 grid, hipStream_t st) {
   if constexpr (D == 128 && RW == 1) {  // two-stage steps
     if (pl.sh.SPS == 2) {
-      if (pl.sh.NS == 6)
+      if (pl.sh.NS == 8)
+        hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 8, 2>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+      else if (pl.sh.NS == 6)
         hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 6, 2>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
       else
         hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 4, 2>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
@@ -766,13 +769,15 @@ extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const
   const dim3 grid = pl.sh.NW == 8 ? dim3(unsigned((prm.n_groups + kXcds - 1) / kXcds * kXcds * pl.n_rb))
                                   : dim3(pl.n_splits, pl.n_rb, B * Hkv);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 cgrid(pl.tpb, pl.n_rb * B * Hkv);
+  const int rows_used = std::min(pl.tpb * 16, pl.G * max_T);  // rows of a row block any tree can have
   if (d == 64) {
     launch_d<64>(pl, prm, grid, st);
-    if (pl.n_splits > 1) hipLaunchKernelGGL((tree_attn_combine<64>), cgrid, dim3(128), 0, st, prm);
+    const dim3 cgrid(unsigned((rows_used + 3) / 4), unsigned(pl.n_rb * B * Hkv));
+    if (pl.n_splits > 1) hipLaunchKernelGGL((tree_attn_combine<64>), cgrid, dim3(64), 0, st, prm);
   } else {
     launch_d<128>(pl, prm, grid, st);
-    if (pl.n_splits > 1) hipLaunchKernelGGL((tree_attn_combine<128>), cgrid, dim3(256), 0, st, prm);
+    const dim3 cgrid(unsigned((rows_used + 1) / 2), unsigned(pl.n_rb * B * Hkv));
+    if (pl.n_splits > 1) hipLaunchKernelGGL((tree_attn_combine<128>), cgrid, dim3(64), 0, st, prm);
   }
   return check_launch("spec_tree_attention");
 }
