@@ -198,8 +198,8 @@ def test_tree_build_structured_rows(V):
 
 # every block shape the plan can pick (waves, row tiles per wave, ring stages, stages per softmax step),
 # on rows spanning several row blocks, with unaligned key chunks and tree slots straddling two items
-ATTN_SHAPES = ["4,1,3", "4,1,4", "4,2,3", "4,2,4", "8,1,3", "8,1,4", "4,1,4,2", "4,1,6,2", "4,1,8,2", "8,1,4,2", "8,1,6,2",
-               "8,1,8,2"]
+ATTN_SHAPES = ["4,1,3", "4,1,4", "4,2,3", "4,2,4", "8,1,3", "8,1,4", "4,1,4,2", "4,1,6,2", "4,1,8,2", "4,2,4,2", "8,1,4,2",
+               "8,1,6,2", "8,1,8,2", "8,2,6,2", "8,2,8,2"]
 
 
 @pytest.mark.parametrize("shape", ATTN_SHAPES)

@@ -184,6 +184,8 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
   static_assert(PW >= 2 && PW * NW == 2 * NLD, "each wave loads whole K/V row pairs");
   static_assert(NS >= 2 * SPS && NS % SPS == 0, "a step's stages are consecutive ring slots");
   constexpr int PH = PW / 2;               // key rows (x 1 KB) per wave and stage, each loaded for K and for V
+  // 256-register kernels (at most two waves per SIMD) hold a stage's V operands across the softmax
+  constexpr bool kPrefetchV = NW / 4 * blocks_per_cu(D, NS) <= 2;
   static_assert(NT >= 65, "the tree prologue uses one thread per node");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE_B];
   __shared__ uint64_t anc_s[65];
@@ -371,24 +373,50 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
     // lane score e <-> key st + 32 (e / 8) + 16 ((e / 4) % 2) + g4 + e % 4
     auto key_of = [&](int e) { return st + 32 * (e >> 3) + 16 * ((e >> 2) & 1) + g4 + (e & 3); };
     f32x4 sc[RW][2 * SPS];
+    // K fragments of the step's 2 SPS units of 16 keys (A operand: key l15, head-dim chunk 4 kk + lane / 16),
+    // each unit's LDS reads issued before the MFMAs of the unit before it
+    auto read_k = [&](int u, bf16x8 (&kop)[KK]) {
+      const unsigned char* kr = ring + ((slot + u / 2) % NS) * STAGE_B + (16 * (u & 1) + l15) * ROWB;
 #pragma unroll
-    for (int ss = 0; ss < SPS; ++ss) {
-      const unsigned char* kb = ring + ((slot + ss) % NS) * STAGE_B;
+      for (int kk = 0; kk < KK; ++kk)
+        kop[kk] = *reinterpret_cast<const bf16x8*>(kr + 16 * ((4 * kk + (lane >> 4)) ^ k_swz<D>(l15)));
+    };
+    bf16x8 kbuf[2][KK];
+    read_k(0, kbuf[0]);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const unsigned char* kr = kb + (16 * kt + l15) * ROWB;
-        bf16x8 kop[KK];
+    for (int u = 0; u < 2 * SPS; ++u) {
+      if (u + 1 < 2 * SPS) read_k(u + 1, kbuf[(u + 1) & 1]);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          kop[kk] = *reinterpret_cast<const bf16x8*>(kr + 16 * ((4 * kk + (lane >> 4)) ^ k_swz<D>(l15)));
+      for (int rw = 0; rw < RW; ++rw) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rw = 0; rw < RW; ++rw) {
-          f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qop[rw][kk], a, 0, 0, 0);
-          sc[rw][2 * ss + kt] = a;
-        }
+        for (int kk = 0; kk < KK; ++kk) a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbuf[u & 1][kk], qop[rw][kk], a, 0, 0, 0);
+        sc[rw][u] = a;
       }
+    }
+    // V^T operand for head-dim column dt*16 + (lane & 15): keys g4 + {0..3} and 16 + g4 + {0..3} of each
+    // stage (the same keys, in the same order, as the lane's P^T column). Two transposing reads: lane i
+    // of each 16-lane group points at key 16 h + g4 + i/4, columns 16 dt + 4 (i % 4) .. +3.
+    const int q4 = l15 >> 2;        // key & 3 of the row this lane points at
+    const int cl = (l15 & 3) >> 1;  // which 16-byte chunk of the 32-byte column group
+    const int e4 = 4 * (l15 & 1);   // element offset inside the chunk
+    auto read_v = [&](int ss, int dt) {
+      const unsigned char* vb = ring + ((slot + ss) % NS) * STAGE_B + TILE_B;
+      s16x4 half[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int key = 16 * h + g4 + q4;
+        const int chunk = (2 * dt + cl) ^ v_swz<D>(key);
+        half[h] = lds_read_tr16(vb + key * ROWB + 16 * chunk + 2 * e4);
+      }
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // kernels with registers to spare read the first stage's V operands now, so the reads run under the
+    // softmax arithmetic
+    bf16x8 vbuf[DT];
+    if constexpr (kPrefetchV) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vbuf[dt] = read_v(0, dt);
     }
     // usable keys among the lane's NE (bit e <-> key_of(e))
     uint32_t kvis = (1u << NE) - 1u;
@@ -417,8 +445,13 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
             vis &= anc || jn < 0 ? 0xffffffffu : ~(1u << e);
           }
         }
+        // the empty asm keeps the compiler from merging these selects into the unmasked path (as
+        // selects against an all-ones mask)
 #pragma unroll
-        for (int e = 0; e < NE; ++e) sv[e] = ((vis >> e) & 1u) ? sc[rw][e >> 2][e & 3] : -INFINITY;
+        for (int e = 0; e < NE; ++e) {
+          sv[e] = ((vis >> e) & 1u) ? sc[rw][e >> 2][e & 3] : -INFINITY;
+          asm volatile("" : "+v"(sv[e]));
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < NE; ++e) sv[e] = sc[rw][e >> 2][e & 3];
@@ -452,28 +485,17 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
         lacc[rw] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pop[rw][ss], lacc[rw], 0, 0, 0);
       }
     }
-    // V^T operand for head-dim column dt*16 + (lane & 15): keys g4 + {0..3} and 16 + g4 + {0..3} of each
-    // stage (the same keys, in the same order, as the lane's P^T column). Two transposing reads: lane i
-    // of each 16-lane group points at key 16 h + g4 + i/4, columns 16 dt + 4 (i % 4) .. +3.
-    const int q4 = l15 >> 2;        // key & 3 of the row this lane points at
-    const int cl = (l15 & 3) >> 1;  // which 16-byte chunk of the 32-byte column group
-    const int e4 = 4 * (l15 & 1);   // element offset inside the chunk
 #pragma unroll
     for (int ss = 0; ss < SPS; ++ss) {
-      const unsigned char* vb = ring + ((slot + ss) % NS) * STAGE_B + TILE_B;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        s16x4 half[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int key = 16 * h + g4 + q4;
-          const int chunk = (2 * dt + cl) ^ v_swz<D>(key);
-          half[h] = lds_read_tr16(vb + key * ROWB + 16 * chunk + 2 * e4);
-        }
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 vop = kPrefetchV ? vbuf[dt] : read_v(ss, dt);
 #pragma unroll
         for (int rw = 0; rw < RW; ++rw)
           acc[rw][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rw][ss], acc[rw][dt], 0, 0, 0);
+        if constexpr (kPrefetchV) {
+          if (ss + 1 < SPS) vbuf[dt] = read_v(ss + 1, dt);  // the next stage's operand, once this one is consumed
+        }
       }
     }
   };
@@ -629,7 +651,8 @@ AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_p
     int nw = 0, rw = 0, ns = 0, sps = 1;
     const int n = sscanf(env, "%d,%d,%d,%d", &nw, &rw, &ns, &sps);
     const bool single = (nw == 4 || nw == 8) && (rw == 1 || (rw == 2 && nw == 4)) && (ns == 3 || ns == 4) && sps == 1;
-    const bool pair = rw == 1 && (nw == 4 || nw == 8) && (ns == 4 || ns == 6 || ns == 8) && sps == 2;
+    const bool pair = ((rw == 1 && (nw == 4 || nw == 8) && (ns == 4 || ns == 6 || ns == 8)) ||
+                       (rw == 2 && ((nw == 4 && ns == 4) || (nw == 8 && (ns == 6 || ns == 8))))) && sps == 2;
     if (n >= 3 && (single || pair)) pl.sh = AttnShape{nw, rw, ns, sps};
   }
   if (d == 64) pl.sh.NW = 4;
@@ -660,6 +683,19 @@ AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_p
 
 template <int D, int NW, int RW>
 void launch_ns(const AttnPlan& pl, const AttnParams& prm, dim3 grid, hipStream_t st) {
+  if constexpr (D == 128 && RW == 2) {  // two row tiles per wave, two-stage steps
+    if (pl.sh.SPS == 2) {
+      if constexpr (NW == 8) {  // one block per CU (256 registers per lane)
+        if (pl.sh.NS == 8)
+          hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 8, 2>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+        else
+          hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 6, 2>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+      } else {
+        hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 4, 2>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+      }
+      return;
+    }
+  }
   if constexpr (D == 128 && RW == 1) {  // two-stage steps
     if (pl.sh.SPS == 2) {
       if (pl.sh.NS == 8)
@@ -671,10 +707,12 @@ void launch_ns(const AttnPlan& pl, const AttnParams& prm, dim3 grid, hipStream_t
       return;
     }
   }
-  if (pl.sh.NS == 3)
-    hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 3, 1>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
-  else
-    hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 4, 1>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+  if constexpr (NW == 4 || RW == 1) {  // one-stage steps (8-wave blocks have the registers for one row tile only)
+    if (pl.sh.NS == 3)
+      hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 3, 1>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+    else
+      hipLaunchKernelGGL((tree_attn_kernel<D, NW, RW, 4, 1>), grid, dim3(64 * NW), pl.lds_dyn, st, prm);
+  }
 }
 
 template <int D>
@@ -689,6 +727,8 @@ void launch_d(const AttnPlan& pl, const AttnParams& prm, dim3 grid, hipStream_t 
       launch_ns<D, 4, 1>(pl, prm, grid, st);
     else if (pl.sh.NW == 4)
       launch_ns<D, 4, 2>(pl, prm, grid, st);
+    else if (pl.sh.RW == 2)
+      launch_ns<D, 8, 2>(pl, prm, grid, st);
     else
       launch_ns<D, 8, 1>(pl, prm, grid, st);
   }
