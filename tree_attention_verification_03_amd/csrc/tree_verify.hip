@@ -41,7 +41,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kSampleSlice = 8192;  // row elements per sampling work item
-constexpr int kGreedySlice = 8192;  // row elements per greedy block (one round trip of loads)
+constexpr int kGreedySlice = 8192;  // row elements per greedy block (one round trip of loads) ...
+constexpr int kGreedySliceMax = 3 * kGreedySlice;  // ... up to three times that when the rows need many blocks
+constexpr int kGreedyBlocksTarget = 448;           // greedy blocks one launch keeps resident (2 per CU, less room)
 constexpr int kMaxWorkers = 512;  // persistent sampling blocks (2 per CU are resident)
 
 struct NodeState {  // one sampling node; all zero between calls (written by its decision blocks only)
@@ -62,7 +64,8 @@ struct VerifyWs {
   int32_t* acc_child;  // [B*max_T] sampling: accepted child node or -1
   int32_t* bonus;      // [B*max_T] sampling: bonus token when the walk stops here
   uint32_t* nflag;     // [B*max_T] sampling node flags
-  uint32_t* tickets;   // [B] greedy: slice blocks done; sampling: nodes done
+  uint32_t* tickets;   // [B] greedy: rows done; sampling: nodes done
+  uint32_t* rtick;     // [B*max_T] greedy: slice blocks of the row done
   NodeState* node;     // [B*max_T]
   uint64_t* ssum;      // [B*max_T][nsl][2] u128 slice sums of the node's last pass (pass 0: of fx(p))
   uint64_t* psum;      // [B*max_T][nsl][3] pass 0 per slice: sum of fx(q), argmax key of fx(p), NaN bits
@@ -90,6 +93,7 @@ VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
   w.bonus = reinterpret_cast<int32_t*>(take(4 * n));
   w.nflag = reinterpret_cast<uint32_t*>(take(4 * n));
   w.tickets = reinterpret_cast<uint32_t*>(take(4 * size_t(B)));
+  w.rtick = reinterpret_cast<uint32_t*>(take(4 * n));
   w.node = reinterpret_cast<NodeState*>(take(sizeof(NodeState) * n));
   w.ssum = reinterpret_cast<uint64_t*>(take(16 * n * nsl));
   w.psum = reinterpret_cast<uint64_t*>(take(24 * n * nsl));
@@ -128,7 +132,7 @@ __device__ __forceinline__ uint64_t argmax_key(float x, int v) {
 }
 
 // ------------------------------------------------------------------ greedy
-template <bool VEC>
+template <bool VEC, int NV>
 __device__ __forceinline__ void greedy_slice(const VerifyWs& w, const VerifyArgs& a, int row, int lo) {
   __shared__ uint64_t red[kWaves];
   __shared__ uint32_t nanred[kWaves];
@@ -137,8 +141,7 @@ __device__ __forceinline__ void greedy_slice(const VerifyWs& w, const VerifyArgs
   const float* r = a.target + size_t(row) * a.V;
   uint64_t best = 0;
   bool nan = false;
-  if (VEC) {  // a slice is at most kGreedySlice elements: all of a thread's loads in one round trip
-    constexpr int NV = kGreedySlice / (4 * kThreads);
+  if (VEC) {  // a slice is at most 4 * kThreads * NV elements: all of a thread's loads in one round trip
     float4 xs[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
@@ -947,11 +950,29 @@ __global__ void __launch_bounds__(kThreads, 2) verify_kernel(VerifyWs w, VerifyA
   const int x = blockIdx.x % a.n_slices, row = blockIdx.x / a.n_slices;
   const int b = row / a.max_T, u = row - b * a.max_T;
   if (a.mode[b] == SPEC_MODE_SAMPLE) return;
-  if (u < seq_T(a.T_b, b, a.max_T)) greedy_slice<VEC>(w, a, row, x * a.slice);
-  // every slice block of a greedy sequence counts; the last one to arrive walks the tree
+  if (u < seq_T(a.T_b, b, a.max_T)) {
+    if (a.slice == kGreedySlice)
+      greedy_slice<VEC, kGreedySlice / (4 * kThreads)>(w, a, row, x * a.slice);
+    else if (a.slice == 2 * kGreedySlice)
+      greedy_slice<VEC, 2 * kGreedySlice / (4 * kThreads)>(w, a, row, x * a.slice);
+    else
+      greedy_slice<VEC, kGreedySliceMax / (4 * kThreads)>(w, a, row, x * a.slice);
+  }
+  // two-level count, so no ticket takes more than max(n_slices, max_T) increments (one counter per
+  // sequence took n_slices * max_T, over a thousand on a 65-node tree at V = 128256, and those
+  // same-address atomics serialised): the last slice block of a row counts the row for its
+  // sequence; the block that counts the sequence's last row walks the tree. Each block's argmax
+  // atomic has completed (vmcnt) before its row ticket, and a row's before its sequence ticket.
   wait_global_stores();
   __syncthreads();
-  if (threadIdx.x == 0) last_s = ticket_add(w.tickets + b) == uint32_t(a.n_slices * a.max_T - 1);
+  if (threadIdx.x == 0) {
+    int last = 0;
+    if (ticket_add(w.rtick + row) == uint32_t(a.n_slices - 1)) {
+      ticket_reset(w.rtick + row);  // leave the workspace ready for the next call
+      last = ticket_add(w.tickets + b) == uint32_t(a.max_T - 1);
+    }
+    last_s = last;
+  }
   __syncthreads();
   if (!last_s) return;
   if (threadIdx.x == 0) ticket_reset(w.tickets + b);  // leave the workspace ready for the next call
@@ -988,8 +1009,11 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
   size_t need = 0;
   VerifyWs w = carve(ws, B, max_T, V, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_verify: workspace %zu < %zu bytes", ws_bytes, need);
-  // greedy slices of kGreedySlice elements (one round trip per block; fewer blocks per sequence ticket)
-  const long long sl = kGreedySlice;
+  // greedy slices of kGreedySlice elements (one round trip of loads per block), doubled or tripled when
+  // the rows would otherwise need more blocks than a launch keeps resident (2 per CU at this kernel's
+  // register count): a 65-node tree at V = 128256 takes 390 blocks of 24 K instead of 1040 of 8 K
+  long long sl = kGreedySlice;
+  while (sl < kGreedySliceMax && rows * ((V + sl - 1) / sl) > kGreedyBlocksTarget) sl += kGreedySlice;
   VerifyArgs a;
   a.target = target;
   a.draft = draft_probs;
