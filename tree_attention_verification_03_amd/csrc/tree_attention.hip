@@ -48,9 +48,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kTile = 32;         // keys per ring stage
-constexpr int kMaxChunk = 2048;   // keys per work item, at most
+constexpr int kMaxChunk = 1792;   // keys per work item, at most (mixed-length batch: 545 us at 1792, 814 us at 2048)
 constexpr float kTau = 8.f;       // log2 headroom of the lazily moved reference max
 constexpr int kTargetBlocks = 384;  // ~1.5 blocks per CU: fewer, longer items beat full occupancy (measured)
+constexpr int kTargetBlocks8 = 440;  // 8-wave (compute-heavy) plans: 64-node tree 44 us at 440 blocks, 50 us at 400
 
 struct AttnParams {
   const uint16_t* q;
@@ -661,7 +662,8 @@ AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_p
   pl.tpb = (pl.tiles + pl.n_rb - 1) / pl.n_rb;  // row tiles spread evenly over the row blocks
   const long long slots = (long long)max_pages * page;
   const long long groups = (long long)B * Hkv * pl.n_rb;
-  long long n = (kTargetBlocks + groups - 1) / groups;  // items per (b, g, row block)
+  const long long target = pl.sh.NW == 8 ? kTargetBlocks8 : kTargetBlocks;
+  long long n = (target + groups - 1) / groups;  // items per (b, g, row block)
   long long chunk = (slots + n - 1) / n;
   if (const char* env = getenv("SPEC_TREE_ATTN_CHUNK")) {
     const long long c = atoll(env);
