@@ -36,6 +36,12 @@ ATTN_CASES = [
     ("many_items", 2, 8, 2, 128, [5000, 4100], [9, 33], 16, "random", 128),  # 40 items: several combine batches
     ("pipelined_g4", 3, 16, 4, 128, [1500, 700, 2100], [9, 17, 5], 16, "random", 512),
     ("pipelined_d64", 2, 8, 2, 64, [999, 1536], [33, 65], 16, "chain", 1024),
+    # batches of >= 8 sequences with >= 8 item slots: the combine reads each sequence's own items only
+    # (lengths from 1 to 19 items, one-item sequences written by the main kernel, two combine batches)
+    ("known_items_b8", 8, 8, 2, 128, [50, 700, 1300, 0, 333, 1024, 5, 3000], [9, 3, 17, 1, 9, 5, 2, 33], 16, "random",
+     160),
+    ("known_items_b9_d64", 9, 4, 4, 64, [10, 3000, 64, 1500, 777, 0, 2048, 96, 400], [2, 9, 5, 17, 3, 1, 33, 9, 4], 16,
+     "chain", 128),
 ]
 
 

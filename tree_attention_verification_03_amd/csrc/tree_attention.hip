@@ -588,7 +588,10 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
 // are combined in fixed order, online against the running maximum reference max:
 // out = sum_i w_i O_i / sum_i w_i l_i with w_i = 2^(m_i - max_j m_j). Sequences whose keys fit one
 // item were written directly by the main kernel.
-template <int D>
+// KNOWN: the lengths are loaded first and only the sequence's own items are read (one more round trip,
+// used for batches of many sequences, whose lengths may differ: a short sequence then reads its one or
+// two items instead of every slot of the longest).
+template <int D, bool KNOWN>
 __global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
   constexpr int TPR = D / 4;     // threads per row
   constexpr int RPB = 64 / TPR;  // rows per block
@@ -607,19 +610,28 @@ __global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
   const size_t ITEM = size_t(TR) * (D + 2);
   const float* grp = p.part + size_t(rbg) * p.n_splits * ITEM;
   RowMerge mr;
-  int n_items = CB;  // known after the first batch's loads
+  int n_items = CB;  // known after the first batch's loads (before them with KNOWN)
+  if constexpr (KNOWN) {
+    const int T = min(max(T_raw, 1), p.max_T);
+    const int cap = p.max_pages << p.page_shift;
+    const int L = min(max(L_raw, 0), cap - T);  // the main kernel's clamp
+    n_items = (L + T + p.chunk - 1) / p.chunk;
+    if (n_items == 1 || r >= p.G * T) return;
+  }
 #pragma unroll 1
   for (int ib = 0; ib < n_items; ib += CB) {
     float mi[CB], li[CB];
     f32x4 ai[CB];
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      const float* base = grp + size_t(min(ib + u, p.n_splits - 1)) * ITEM;
+      // without KNOWN, slots past the sequence's items repeat the last slot (loaded, never used)
+      const int item = KNOWN ? min(ib + u, n_items - 1) : min(ib + u, p.n_splits - 1);
+      const float* base = grp + size_t(item) * ITEM;
       mi[u] = base[size_t(TR) * D + row];
       li[u] = base[size_t(TR) * (D + 1) + row];
       ai[u] = *reinterpret_cast<const f32x4*>(base + size_t(row) * D + 4 * c);
     }
-    if (ib == 0) {
+    if (!KNOWN && ib == 0) {
       const int T = min(max(T_raw, 1), p.max_T);
       const int cap = p.max_pages << p.page_shift;
       const int L = min(max(L_raw, 0), cap - T);  // the main kernel's clamp
@@ -812,14 +824,27 @@ extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const
                                   : dim3(pl.n_splits, pl.n_rb, B * Hkv);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int rows_used = std::min(pl.tpb * 16, pl.G * max_T);  // rows of a row block any tree can have
+  // many sequences with many item slots: read each sequence's own items only (mixed-length batch of 32:
+  // the combine read 352 MB for 170 MB of partials)
+  const bool known = B >= 8 && pl.n_splits >= 8;
   if (d == 64) {
     launch_d<64>(pl, prm, grid, st);
     const dim3 cgrid(unsigned((rows_used + 3) / 4), unsigned(pl.n_rb * B * Hkv));
-    if (pl.n_splits > 1) hipLaunchKernelGGL((tree_attn_combine<64>), cgrid, dim3(64), 0, st, prm);
+    if (pl.n_splits > 1) {
+      if (known)
+        hipLaunchKernelGGL((tree_attn_combine<64, true>), cgrid, dim3(64), 0, st, prm);
+      else
+        hipLaunchKernelGGL((tree_attn_combine<64, false>), cgrid, dim3(64), 0, st, prm);
+    }
   } else {
     launch_d<128>(pl, prm, grid, st);
     const dim3 cgrid(unsigned((rows_used + 1) / 2), unsigned(pl.n_rb * B * Hkv));
-    if (pl.n_splits > 1) hipLaunchKernelGGL((tree_attn_combine<128>), cgrid, dim3(64), 0, st, prm);
+    if (pl.n_splits > 1) {
+      if (known)
+        hipLaunchKernelGGL((tree_attn_combine<128, true>), cgrid, dim3(64), 0, st, prm);
+      else
+        hipLaunchKernelGGL((tree_attn_combine<128, false>), cgrid, dim3(64), 0, st, prm);
+    }
   }
   return check_launch("spec_tree_attention");
 }
