@@ -114,6 +114,7 @@ struct VerifyArgs {
   const int8_t* mode;
   uint64_t key0, key1, offset;
   int B, max_T, R, V, n_slices, slice, nsl, n_greedy_blocks, n_workers;
+  int row_tickets;  // greedy: count slice blocks per row first (sequences with many slice blocks)
   int32_t* accept_len;
   int32_t* accept_nodes;
   int32_t* out_tokens;
@@ -958,16 +959,19 @@ __global__ void __launch_bounds__(kThreads, 2) verify_kernel(VerifyWs w, VerifyA
     else
       greedy_slice<VEC, kGreedySliceMax / (4 * kThreads)>(w, a, row, x * a.slice);
   }
-  // two-level count, so no ticket takes more than max(n_slices, max_T) increments (one counter per
-  // sequence took n_slices * max_T, over a thousand on a 65-node tree at V = 128256, and those
-  // same-address atomics serialised): the last slice block of a row counts the row for its
-  // sequence; the block that counts the sequence's last row walks the tree. Each block's argmax
-  // atomic has completed (vmcnt) before its row ticket, and a row's before its sequence ticket.
+  // the block that completes the sequence walks its tree. With many slice blocks per sequence the
+  // count has two levels, so no ticket takes more than max(n_slices, max_T) increments (one counter
+  // took n_slices * max_T, over a thousand on a 65-node tree at V = 128256, and those same-address
+  // atomics serialised): the last slice block of a row counts the row for its sequence. Each block's
+  // argmax atomic has completed (vmcnt) before its row ticket, and a row's before its sequence ticket.
+  // A few slice blocks per sequence share one counter (no second atomic round trip).
   wait_global_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
     int last = 0;
-    if (ticket_add(w.rtick + row) == uint32_t(a.n_slices - 1)) {
+    if (!a.row_tickets) {
+      last = ticket_add(w.tickets + b) == uint32_t(a.n_slices * a.max_T - 1);
+    } else if (ticket_add(w.rtick + row) == uint32_t(a.n_slices - 1)) {
       ticket_reset(w.rtick + row);  // leave the workspace ready for the next call
       last = ticket_add(w.tickets + b) == uint32_t(a.max_T - 1);
     }
@@ -1033,6 +1037,7 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
   a.n_slices = int((V + sl - 1) / sl);
   a.nsl = int(nsl);
   a.n_greedy_blocks = int(rows) * a.n_slices;
+  a.row_tickets = (long long)a.n_slices * max_T > 256;
   a.n_workers = int(std::min<long long>(kMaxWorkers, rows * nsl));
   a.accept_len = accept_len;
   a.accept_nodes = accept_nodes;
