@@ -168,6 +168,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--verify-logits", action="store_true",
+                    help="verify with spec_tree_verify_logits (sampling distributions formed from the target logits and "
+                         "temperatures inside the library) instead of supplied probabilities")
     ap.add_argument("--details", default=None, help="write per-stage details as JSON to this path")
     ap.add_argument("--profile-kernels", type=int, default=0, metavar="N",
                     help="profiling mode (run under rocprofv3): N eager attention calls over the replicas, then one "
@@ -190,13 +193,13 @@ def main():
     spec = get_config(cfg_key)
     eprint(f"[bench] workload {spec.name}: generating inputs")
     w = from_spec(spec)
-    dw0 = DeviceWorkload(w)
+    dw0 = DeviceWorkload(w, logits=args.verify_logits)
     per_replica = sum(t.numel() * t.element_size() for t in vars(dw0).values() if hasattr(t, "element_size"))
     R = max(2, int(np.ceil(args.rotate_gib * 2**30 / per_replica)))
     R = min(R, 512)
     eprint(f"[bench] replica {per_replica / 2**20:.1f} MiB x {R} replicas")
     replicas = [dw0] + [clone_device_workload(dw0) for _ in range(R - 1)]
-    steps = [SpecTreeStep(d, attn_status=False) for d in replicas]
+    steps = [SpecTreeStep(d, attn_status=False, verify_from_logits=args.verify_logits) for d in replicas]
     compact = bool(spec.compact)
 
     # eager warm-up and the reference outputs of replica 0
@@ -307,7 +310,8 @@ def main():
         "config": {"workload": spec.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
                    "prefix": int(w.prefix_lens.max()), "draft_tokens": int(w.num_draft.max()), "vocab": w.V,
                    "step": "tree build + tree attention + verify" + (" + KV compaction" if compact else ""),
-                   "replicas": R, "graphs": not args.eager},
+                   "replicas": R, "graphs": not args.eager,
+                   "verify_input": "target logits + temperature" if args.verify_logits else "target probabilities"},
         "gpu_ms_per_step": round(gpu_ms, 5),
         "stage_us": {k: round(v * 1e3, 3) for k, v in stage_ms.items()},
         "attn_verify_draft_tokens_per_s": round(n_draft / ((stage_ms["attention"] + stage_ms["verify"]) * 1e-3), 1),

@@ -222,6 +222,43 @@ int32_t spec_tree_verify(const float* target, const float* draft_probs, const in
                          int32_t* out_tokens, uint32_t* status, void* ws, size_t ws_bytes, void* stream);
 
 /* ----------------------------------------------------------------------------
+ * Tree verification from target logits - the same rule as spec_tree_verify,
+ * with the sampling sequences' target distributions formed inside the library
+ * from the target's logits and a per-sequence temperature (n1n.ai page,
+ * "Mathematical Proof of Lossless Speedup": p is the target model's
+ * distribution; SGLang "Speculative Decoding": temperature is a sampling
+ * parameter of the request).
+ *
+ * logits      fp32 [B, max_T, V]: node u's target logits (every sequence).
+ * temperature fp32 [B] or NULL (= 1 for every sequence); read for sampling
+ *             sequences only.
+ * Greedy sequences: exactly spec_tree_verify on the logits (argmax).
+ * Sampling sequences: p = softmax(logits / temperature[b]) per row, computed
+ * in fp32 (x = l * (1 / T), the row's max, sum of exp(x - max) over slices of
+ * the row merged in slice order, p = exp(x - max) / sum; every reduction in a
+ * fixed order, so repeated calls agree bit for bit), then
+ * exactly the sampling rule of spec_tree_verify on p. Because p is formed in
+ * fp32 rather than supplied, its values can differ from an exact softmax by a
+ * few units in the last place, and a decision whose margin is below that can
+ * differ from one taken on exact probabilities (a draft row q equal to the
+ * exact p is such a case: the exact residual max(0, p - q) is zero, the one
+ * left by fp32 p is not). A non-finite logit gives a
+ * NaN probability (zero in the rule, SPEC_STATUS_NAN_INPUT); a temperature
+ * that is not a finite positive number makes all of that sequence's
+ * probabilities NaN.
+ * Other arguments, outputs and errors as spec_tree_verify. The workspace
+ * (spec_tree_verify_logits_workspace_size) also holds the probabilities:
+ * B * max_T * V fp32 beyond the verify workspace. Requires B * max_T <= 65535.
+ * ------------------------------------------------------------------------- */
+size_t spec_tree_verify_logits_workspace_size(int32_t B, int32_t max_T, int32_t V);
+int32_t spec_tree_verify_logits(const float* logits, const float* temperature, const float* draft_probs,
+                                const int32_t* q_row, const int32_t* tokens, const int32_t* parents,
+                                const int32_t* T_b, const int8_t* mode, uint64_t philox_key0, uint64_t philox_key1,
+                                uint64_t philox_offset, int32_t B, int32_t max_T, int32_t R, int32_t V,
+                                int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens, uint32_t* status,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
  * Accepted-path KV compaction - tanhdev section 2 sequence diagram ("Retain
  * Accepted Path KV & Discard Rejected Branches"); lesty.tech section 6
  * ("Paged Tree KV-Cache Allocation").

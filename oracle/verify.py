@@ -34,6 +34,15 @@ If no child is accepted the bonus is the smallest v with
 gives the smallest-index argmax of P. A node without children (or whose q row
 is missing / sums to zero) resamples from P.
 
+Probabilities from logits (tree_verify_logits): the target distribution the
+rule consumes is the target model's (n1n.ai, "Mathematical Proof of Lossless
+Speedup"), at the request's temperature (SGLang "Speculative Decoding": a
+sampling parameter). Reading: p = softmax(l / T) per row, evaluated here in
+fp64 and stored fp32 like supplied probabilities; a logit whose fp32 quotient
+l / T is not finite gets a NaN probability and stays out of the normalisation;
+a temperature that is not a finite positive number makes every probability of
+the sequence NaN. Greedy sequences use the logits themselves.
+
 Status bits (per sequence): INVALID_PARENT - a parent outside [0, i) (the node
 is then a child of the root); INVALID_TOKEN - a draft token outside [0, V)
 (never accepted, never tested); NAN_INPUT - a NaN in any target row of the tree
@@ -193,6 +202,34 @@ def verify_sequence(target_rows, draft_rows, q_row, tokens, parents, T, mode, ke
             continue
         out = [int(tokens[n]) for n in path[1:]] + [bonus]
         return len(path) - 1, path, out, status
+
+
+def target_probs_from_logits(logits_row, temperature) -> np.ndarray:
+    """softmax(logits / temperature) of one row, fp64 arithmetic, stored fp32 (readings in the header)."""
+    l32 = np.asarray(logits_row, dtype=np.float32)
+    T = np.float32(temperature)
+    out = np.full(l32.shape, np.nan, dtype=np.float64)
+    if not (np.isfinite(T) and T > 0):
+        return out.astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        finite = np.isfinite(l32 / T)  # the fp32 quotient decides which logits take part
+    x = l32.astype(np.float64) / float(T)
+    if finite.any():
+        m = x[finite].max()
+        e = np.exp(x[finite] - m)
+        out[finite] = e / e.sum()
+    return out.astype(np.float32)
+
+
+def tree_verify_logits(logits, temperature, draft_probs, q_row, tokens, parents, T_b, modes, key, offset, seqs=None):
+    """tree_verify with each sampling sequence's target rows formed from its logits and temperature."""
+    target = np.array(logits, dtype=np.float32, copy=True)
+    for b in range(target.shape[0]):
+        if int(modes[b]) == MODE_SAMPLE:
+            t_b = 1.0 if temperature is None else float(temperature[b])
+            for u in range(target.shape[1]):
+                target[b, u] = target_probs_from_logits(logits[b, u], t_b)
+    return tree_verify(target, draft_probs, q_row, tokens, parents, T_b, modes, key, offset, seqs)
 
 
 def tree_verify(target, draft_probs, q_row, tokens, parents, T_b, modes, key, offset, seqs=None):

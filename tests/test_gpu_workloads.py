@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from gpu_support import (ATTN_MAX_ABS, ATTN_REL_L2, LSE_ABS, check_build, check_verify, compare_attention, log,
-                         oracle_trees, parents_array, run_pipeline)
+                         oracle_trees, parents_array, run_pipeline, to_np)
 from oracle.kvcompact import kv_compact as oracle_kv_compact
 from workloads import get_config
 from workloads.synth import from_spec
@@ -106,3 +106,32 @@ def test_full_pipeline_with_planted_acceptance_and_compaction():
     assert np.array_equal(dw.k_pages.view(torch.int16).cpu().numpy().view(np.uint16), k_ref[0])
     assert np.array_equal(dw.v_pages.view(torch.int16).cpu().numpy().view(np.uint16), v_ref[0])
     assert host["new_prefix_lens"].tolist() == l_ref.tolist()
+
+
+@pytest.mark.parametrize("cfg", [2, 4], ids=lambda i: get_config(i).name)
+def test_full_verify_from_logits(cfg):
+    """spec_tree_verify_logits on the sampling workloads: the library forms p = softmax(logits / T) itself."""
+    from oracle.verify import tree_verify_logits
+    from tree_attention_verification_03_amd.pipeline import DeviceWorkload, SpecTreeStep
+
+    spec = get_config(cfg)
+    log(f"[full] generating {spec.name}")
+    w = from_spec(spec)
+    dw = DeviceWorkload(w, logits=True)
+    step = SpecTreeStep(dw, verify_from_logits=True)
+    step.build()
+    step.verify()
+    torch.cuda.synchronize()
+    host = {k: to_np(getattr(step.o, k)) for k in ("tokens", "parents", "q_row", "accept_len", "accept_nodes",
+                                                   "out_tokens", "status")}
+    seqs = [b for b in range(w.B) if int(w.modes[b]) == 1][:8] + [b for b in range(w.B) if int(w.modes[b]) == 0][:2]
+    log(f"[full] oracle verify from logits on {spec.name} ({len(seqs)} sequences)")
+    res = tree_verify_logits(w.target_logits, w.temperature, w.draft_probs, host["q_row"], host["tokens"],
+                             host["parents"], w.T_b, w.modes, w.philox_key, w.philox_offset, seqs)
+    for b, (n, nodes, out, st) in zip(seqs, res):
+        assert int(host["accept_len"][b]) == n, f"accept_len b={b}"
+        assert host["accept_nodes"][b, : n + 1].tolist() == nodes, f"accept_nodes b={b}"
+        assert host["out_tokens"][b, : n + 1].tolist() == out, f"out_tokens b={b}"
+        assert int(host["status"][b]) == st, f"status b={b}"
+    del dw, step
+    torch.cuda.empty_cache()

@@ -239,3 +239,64 @@ def test_second_token_of_accepted_chain_follows_child_row():
     assert reached > trials * 0.9
     chi2 = ((counts - reached * p1n) ** 2 / (reached * p1n)).sum()
     assert stats.chi2.sf(chi2, V - 1) > 1e-3
+
+
+# ---------------------------------------------------------------- probabilities from logits
+def test_probs_from_logits_match_scipy_softmax():
+    from scipy.special import softmax
+
+    from oracle.verify import target_probs_from_logits
+
+    rng = np.random.default_rng(11)
+    for T in (1.0, 0.7, 2.5):
+        l = (rng.standard_normal(1000) * 3.0).astype(np.float32)
+        p = target_probs_from_logits(l, np.float32(T))
+        ref = softmax(l.astype(np.float64) / float(np.float32(T)))
+        assert p.dtype == np.float32
+        np.testing.assert_allclose(p, ref, rtol=2e-7, atol=0)
+        assert abs(float(p.astype(np.float64).sum()) - 1.0) < 1e-5
+
+
+def test_probs_from_logits_shift_and_temperature():
+    from oracle.verify import target_probs_from_logits
+
+    rng = np.random.default_rng(12)
+    l = (rng.standard_normal(777) * 3.0).astype(np.float32)
+    base = target_probs_from_logits(l, 1.0)
+    np.testing.assert_allclose(target_probs_from_logits(l + np.float32(40.0), 1.0), base, rtol=1e-5)
+    # T = 1/2 on l is T = 1 on 2 l (both quotients exact in fp32)
+    np.testing.assert_array_equal(target_probs_from_logits(l, 0.5), target_probs_from_logits(2 * l, 1.0))
+    # a small temperature concentrates the mass on the argmax
+    sharp = target_probs_from_logits(l, 0.01)
+    assert int(np.argmax(sharp)) == int(np.argmax(l)) and sharp.max() > 0.99
+
+
+def test_probs_from_logits_non_finite():
+    from oracle.verify import target_probs_from_logits
+
+    l = np.arange(10, dtype=np.float32)
+    l[3], l[7] = np.nan, np.inf
+    p = target_probs_from_logits(l, 1.0)
+    assert np.isnan(p[3]) and np.isnan(p[7])
+    keep = np.array([i for i in range(10) if i not in (3, 7)])
+    e = np.exp(l[keep].astype(np.float64) - l[keep].max())
+    np.testing.assert_allclose(p[keep], (e / e.sum()).astype(np.float32), rtol=1e-7)
+    for T in (0.0, -1.0, np.nan, np.inf):
+        assert np.isnan(target_probs_from_logits(np.ones(5, np.float32), T)).all()
+
+
+def test_workload_sampling_rows_are_the_softmax_of_their_logits():
+    from oracle.verify import target_probs_from_logits
+    from workloads import make_workload
+
+    w = make_workload(name="lg", B=4, Hq=2, Hkv=1, d=64, prefix=16, topk=2, depth=2, num_draft=3, V=500,
+                      verify="alternate", temperature=0.7, seed=21)
+    for b in range(w.B):
+        for u in range(w.max_T):
+            if int(w.modes[b]) == 1:
+                # the generator divides by the temperature as the fp64 value 0.7, the logits path by the fp32
+                # temperature array (0.7 rounded, 1.7e-8 relative away): quotients of ~10 move by ~2e-7
+                np.testing.assert_allclose(target_probs_from_logits(w.target_logits[b, u], w.temperature[b]),
+                                           w.target[b, u], rtol=1e-6)
+            else:
+                np.testing.assert_array_equal(w.target_logits[b, u], w.target[b, u])

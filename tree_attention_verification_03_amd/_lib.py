@@ -31,6 +31,9 @@ SIGNATURES = {
     "spec_tree_verify_workspace_size": (c_sz, [c_i32, c_i32, c_i32]),
     "spec_tree_verify": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_u64, c_u64, c_u64, c_i32, c_i32, c_i32,
                                  c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "spec_tree_verify_logits_workspace_size": (c_sz, [c_i32, c_i32, c_i32]),
+    "spec_tree_verify_logits": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_u64, c_u64, c_u64, c_i32, c_i32,
+                                        c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "spec_kv_compact": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                 c_i32, c_i64, c_vp, c_vp]),
 }

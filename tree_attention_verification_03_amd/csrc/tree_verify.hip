@@ -106,6 +106,7 @@ VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
 
 struct VerifyArgs {
   const float* target;
+  const float* prob;  // sampling rows' probabilities when they are formed from logits here, else null
   const float* draft;
   const int32_t* q_row;
   const int32_t* tokens;
@@ -124,6 +125,11 @@ struct VerifyArgs {
 __device__ __forceinline__ int seq_T(const int32_t* T_b, int b, int max_T) {
   int T = T_b ? T_b[b] : max_T;
   return T < 1 ? 1 : (T > max_T ? max_T : T);
+}
+
+// node's target probabilities for the sampling rule: formed here from logits, or supplied by the caller
+__device__ __forceinline__ const float* sample_row(const VerifyArgs& a, size_t node) {
+  return (a.prob ? a.prob : a.target) + node * size_t(a.V);
 }
 
 __device__ __forceinline__ uint64_t argmax_key(float x, int v) {
@@ -381,7 +387,7 @@ template <bool VEC>
 __device__ __forceinline__ void sample_pass0(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T, int s) {
   __shared__ uint64_t red[kWaves][3];
   const size_t node = size_t(b) * a.max_T + u;
-  const float* prow = a.target + node * a.V;
+  const float* prow = sample_row(a, node);
   const float* qrow = node_qrow_any(a, b, u);
   const int lo = s * kSampleSlice, hi = min(a.V, lo + kSampleSlice);
   uint64_t sp = 0, sq = 0, am = 0;
@@ -423,7 +429,7 @@ __device__ __forceinline__ void sample_passN(const VerifyWs& w, const VerifyArgs
   __shared__ uint64_t red[kWaves][3];
   const size_t node = size_t(b) * a.max_T + u;
   NodeState* ns = w.node + node;
-  const float* prow = a.target + node * a.V;
+  const float* prow = sample_row(a, node);
   const float* qrow = node_qrow_any(a, b, u);  // present: only tested nodes have residual passes
   const uint64_t S_Q = ld_agent(&ns->sq), gamma = ld_agent(&ns->gamma);
   const int lo = s * kSampleSlice, hi = min(a.V, lo + kSampleSlice);
@@ -461,7 +467,7 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, max_T = a.max_T, V = a.V;
   const size_t node = size_t(b) * max_T + u;
   NodeState* ns = w.node + node;
-  const float* prow = a.target + node * V;
+  const float* prow = sample_row(a, node);
   // a decision is one serial chain that every later pass of the node waits for, while the blocks
   // around it run throughput work: its waves take issue priority until it is done
   __builtin_amdgcn_s_setprio(3);
@@ -983,6 +989,111 @@ __global__ void __launch_bounds__(kThreads, 2) verify_kernel(VerifyWs w, VerifyA
   walk(w, a, b);
 }
 
+// ------------------------------------------------------------------ probabilities from logits
+// p = softmax(logits / T_b) of every sampling row (b, u < T_b) into prob, fp32, over slices of kSmSlice
+// elements: softmax_partial_kernel takes each slice's (max of x = l * (1 / T_b), sum of exp(x - max)),
+// softmax_write_kernel merges the row's slice partials (max M, S = sum_s sum_s' exp(max_s - M)) and writes
+// p = exp(x - M) / S. Every reduction runs in a fixed order, so repeated calls agree bit for bit. A
+// non-finite x gives a NaN probability and stays out of the maximum and the sum; a temperature that is not
+// a finite positive number makes the whole row NaN (NaN probabilities count as zero in the sampling rule
+// and raise SPEC_STATUS_NAN_INPUT).
+constexpr int kSmThreads = 256;
+constexpr int kSmPer = 32;                       // elements per thread
+constexpr int kSmSlice = kSmThreads * kSmPer;    // elements per block
+
+__device__ __forceinline__ float sm_block_reduce(float x, bool is_max, float* red) {
+  constexpr int NW = kSmThreads / kWave;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float y = __shfl_xor(x, o, kWave);
+    x = is_max ? fmaxf(x, y) : x + y;
+  }
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  __syncthreads();  // the previous reduction's reads of red are done
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+  return r;
+}
+
+__device__ __forceinline__ bool sm_row(const int32_t* T_b, const int8_t* mode, int max_T, int row) {
+  const int b = row / max_T, u = row - b * max_T;
+  return mode[b] == SPEC_MODE_SAMPLE && u < seq_T(T_b, b, max_T);
+}
+
+__device__ __forceinline__ float sm_temperature(const float* temperature, int b) {
+  const float T = temperature ? temperature[b] : 1.f;
+  return (T > 0.f && isfinite(T)) ? T : 0.f;  // 0 = invalid
+}
+
+__global__ void __launch_bounds__(kSmThreads) softmax_partial_kernel(const float* logits, const float* temperature,
+                                                                      const int32_t* T_b, const int8_t* mode,
+                                                                      int max_T, int V, float2* part) {
+  __shared__ float red[kSmThreads / kWave];
+  const int s = blockIdx.x, row = blockIdx.y, nsl = gridDim.x, tid = threadIdx.x;
+  if (!sm_row(T_b, mode, max_T, row)) return;
+  const float T = sm_temperature(temperature, row / max_T);
+  if (T == 0.f) return;  // the write kernel fills the row with NaN
+  const float inv = 1.f / T;
+  const float* l = logits + size_t(row) * V;
+  float x[kSmPer];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kSmPer; ++i) {
+    const int v = s * kSmSlice + i * kSmThreads + tid;
+    x[i] = v < V ? l[v] * inv : -INFINITY;
+    if (isfinite(x[i])) m = fmaxf(m, x[i]);
+  }
+  m = sm_block_reduce(m, true, red);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSmPer; ++i)
+    if (isfinite(x[i])) sum += expf(x[i] - m);
+  sum = sm_block_reduce(sum, false, red);
+  if (tid == 0) part[size_t(row) * nsl + s] = make_float2(m, sum);
+}
+
+__global__ void __launch_bounds__(kSmThreads) softmax_write_kernel(const float* logits, const float* temperature,
+                                                                    const int32_t* T_b, const int8_t* mode, int max_T,
+                                                                    int V, const float2* part, float* prob) {
+  const int s = blockIdx.x, row = blockIdx.y, nsl = gridDim.x, tid = threadIdx.x;
+  if (!sm_row(T_b, mode, max_T, row)) return;
+  const float T = sm_temperature(temperature, row / max_T);
+  const float* l = logits + size_t(row) * V;
+  float* p = prob + size_t(row) * V;
+  if (T == 0.f) {
+#pragma unroll
+    for (int i = 0; i < kSmPer; ++i) {
+      const int v = s * kSmSlice + i * kSmThreads + tid;
+      if (v < V) p[v] = NAN;
+    }
+    return;
+  }
+  const float inv = 1.f / T;
+  float x[kSmPer];
+#pragma unroll
+  for (int i = 0; i < kSmPer; ++i) {
+    const int v = s * kSmSlice + i * kSmThreads + tid;
+    x[i] = v < V ? l[v] * inv : 0.f;
+  }
+  // the row's maximum and sum from every slice's partial, in slice order (each thread the same way)
+  const float2* pr = part + size_t(row) * nsl;
+  float M = -INFINITY;
+  for (int j = 0; j < nsl; ++j) M = fmaxf(M, pr[j].x);
+  float S = 0.f;
+  for (int j = 0; j < nsl; ++j) {
+    const float2 q = pr[j];
+    if (q.x != -INFINITY) S += q.y * expf(q.x - M);
+  }
+#pragma unroll
+  for (int i = 0; i < kSmPer; ++i) {
+    const int v = s * kSmSlice + i * kSmThreads + tid;
+    if (v < V) p[v] = isfinite(x[i]) ? expf(x[i] - M) / S : NAN;
+  }
+}
+
 }  // namespace
 }  // namespace spectree
 
@@ -995,24 +1106,25 @@ extern "C" size_t spec_tree_verify_workspace_size(int32_t B, int32_t max_T, int3
   return total;
 }
 
-extern "C" int32_t spec_tree_verify(const float* target, const float* draft_probs, const int32_t* q_row,
+static int32_t verify_impl(const char* who, const float* target, float* prob, float2* sm_part, const float* temperature,
+                           const float* draft_probs, const int32_t* q_row,
                                     const int32_t* tokens, const int32_t* parents, const int32_t* T_b,
                                     const int8_t* mode, uint64_t philox_key0, uint64_t philox_key1,
                                     uint64_t philox_offset, int32_t B, int32_t max_T, int32_t R, int32_t V,
                                     int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens, uint32_t* status,
                                     void* ws, size_t ws_bytes, void* stream) {
-  if (B < 1 || max_T < 1) return fail(SPEC_E_INVAL, "spec_tree_verify: B=%d max_T=%d", B, max_T);
-  if (max_T > 65) return fail(SPEC_E_UNSUPPORTED, "spec_tree_verify: max_T=%d > 65", max_T);
-  if (V < 1 || V >= (1 << 24)) return fail(SPEC_E_UNSUPPORTED, "spec_tree_verify: V=%d not in [1, 2^24)", V);
-  if (draft_probs && (R < 1 || !q_row)) return fail(SPEC_E_INVAL, "spec_tree_verify: draft_probs needs R >= 1 and q_row");
+  if (B < 1 || max_T < 1) return fail(SPEC_E_INVAL, "%s: B=%d max_T=%d", who, B, max_T);
+  if (max_T > 65) return fail(SPEC_E_UNSUPPORTED, "%s: max_T=%d > 65", who, max_T);
+  if (V < 1 || V >= (1 << 24)) return fail(SPEC_E_UNSUPPORTED, "%s: V=%d not in [1, 2^24)", who, V);
+  if (draft_probs && (R < 1 || !q_row)) return fail(SPEC_E_INVAL, "%s: draft_probs needs R >= 1 and q_row", who);
   if (!target || !tokens || !parents || !mode || !accept_len || !accept_nodes || !out_tokens || !status)
-    return fail(SPEC_E_INVAL, "spec_tree_verify: null pointer");
+    return fail(SPEC_E_INVAL, "%s: null pointer", who);
   const long long rows = (long long)B * max_T;
   const long long nsl = sample_slices(V);
-  if (rows * nsl >= (1LL << 31)) return fail(SPEC_E_UNSUPPORTED, "spec_tree_verify: B*max_T*ceil(V/%d) too large", kSampleSlice);
+  if (rows * nsl >= (1LL << 31)) return fail(SPEC_E_UNSUPPORTED, "%s: B*max_T*ceil(V/%d) too large", who, kSampleSlice);
   size_t need = 0;
   VerifyWs w = carve(ws, B, max_T, V, &need);
-  if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_verify: workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
   // greedy slices of kGreedySlice elements (one round trip of loads per block), doubled or tripled when
   // the rows would otherwise need more blocks than a launch keeps resident (2 per CU at this kernel's
   // register count): a 65-node tree at V = 128256 takes 390 blocks of 24 K instead of 1040 of 8 K
@@ -1020,6 +1132,7 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
   while (sl < kGreedySliceMax && rows * ((V + sl - 1) / sl) > kGreedyBlocksTarget) sl += kGreedySlice;
   VerifyArgs a;
   a.target = target;
+  a.prob = prob;
   a.draft = draft_probs;
   a.q_row = q_row;
   a.tokens = tokens;
@@ -1044,13 +1157,71 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
   a.out_tokens = out_tokens;
   a.status = status;
   if ((long long)a.n_greedy_blocks + a.n_workers >= (1LL << 31))
-    return fail(SPEC_E_UNSUPPORTED, "spec_tree_verify: grid too large");
-  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target) | reinterpret_cast<uintptr_t>(draft_probs)) & 15) == 0;
+    return fail(SPEC_E_UNSUPPORTED, "%s: grid too large", who);
+  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target) | reinterpret_cast<uintptr_t>(draft_probs) |
+                                     reinterpret_cast<uintptr_t>(prob)) & 15) == 0;
   const dim3 grid(a.n_greedy_blocks + a.n_workers);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (prob) {  // sampling rows' probabilities from the logits first (same stream: the verify launch waits)
+    const dim3 sgrid(unsigned((V + kSmSlice - 1) / kSmSlice), unsigned(rows));
+    hipLaunchKernelGGL(softmax_partial_kernel, sgrid, dim3(kSmThreads), 0, st, target, temperature, T_b, mode, max_T, V,
+                       sm_part);
+    hipLaunchKernelGGL(softmax_write_kernel, sgrid, dim3(kSmThreads), 0, st, target, temperature, T_b, mode, max_T, V,
+                       sm_part, prob);
+  }
   if (vec)
     hipLaunchKernelGGL(verify_kernel<true>, grid, dim3(kThreads), 0, st, w, a);
   else
     hipLaunchKernelGGL(verify_kernel<false>, grid, dim3(kThreads), 0, st, w, a);
-  return check_launch("spec_tree_verify");
+  return check_launch(who);
+}
+
+extern "C" int32_t spec_tree_verify(const float* target, const float* draft_probs, const int32_t* q_row,
+                                    const int32_t* tokens, const int32_t* parents, const int32_t* T_b,
+                                    const int8_t* mode, uint64_t philox_key0, uint64_t philox_key1,
+                                    uint64_t philox_offset, int32_t B, int32_t max_T, int32_t R, int32_t V,
+                                    int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens, uint32_t* status,
+                                    void* ws, size_t ws_bytes, void* stream) {
+  return verify_impl("spec_tree_verify", target, nullptr, nullptr, nullptr, draft_probs, q_row, tokens, parents, T_b, mode, philox_key0,
+                     philox_key1, philox_offset, B, max_T, R, V, accept_len, accept_nodes, out_tokens, status, ws,
+                     ws_bytes, stream);
+}
+
+// the logits entry point's workspace: the verify workspace, then the sampling rows' probabilities
+static size_t logits_prob_offset(int32_t B, int32_t max_T, int32_t V) {
+  size_t total = 0;
+  carve(nullptr, B, max_T, V, &total);
+  return align_up(total, 256);
+}
+
+// ... and the slices' softmax partials after the probabilities
+static size_t logits_part_offset(int32_t B, int32_t max_T, int32_t V) {
+  return logits_prob_offset(B, max_T, V) + align_up(size_t(B) * max_T * V * sizeof(float), 256);
+}
+
+extern "C" size_t spec_tree_verify_logits_workspace_size(int32_t B, int32_t max_T, int32_t V) {
+  if (B < 1 || max_T < 1 || max_T > 65 || V < 1) return 0;
+  const size_t nsl = (size_t(V) + kSmSlice - 1) / kSmSlice;
+  return logits_part_offset(B, max_T, V) + align_up(size_t(B) * max_T * nsl * sizeof(float2), 256);
+}
+
+extern "C" int32_t spec_tree_verify_logits(const float* logits, const float* temperature, const float* draft_probs,
+                                           const int32_t* q_row, const int32_t* tokens, const int32_t* parents,
+                                           const int32_t* T_b, const int8_t* mode, uint64_t philox_key0,
+                                           uint64_t philox_key1, uint64_t philox_offset, int32_t B, int32_t max_T,
+                                           int32_t R, int32_t V, int32_t* accept_len, int32_t* accept_nodes,
+                                           int32_t* out_tokens, uint32_t* status, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  const char* who = "spec_tree_verify_logits";
+  if (B < 1 || max_T < 1) return fail(SPEC_E_INVAL, "%s: B=%d max_T=%d", who, B, max_T);
+  if (max_T > 65) return fail(SPEC_E_UNSUPPORTED, "%s: max_T=%d > 65", who, max_T);
+  if (V < 1 || V >= (1 << 24)) return fail(SPEC_E_UNSUPPORTED, "%s: V=%d not in [1, 2^24)", who, V);
+  if ((long long)B * max_T > 65535) return fail(SPEC_E_UNSUPPORTED, "%s: B*max_T=%lld > 65535", who, (long long)B * max_T);
+  const size_t need = spec_tree_verify_logits_workspace_size(B, max_T, V);
+  if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  const size_t off = logits_prob_offset(B, max_T, V);
+  float* prob = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
+  float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + logits_part_offset(B, max_T, V));
+  return verify_impl(who, logits, prob, part, temperature, draft_probs, q_row, tokens, parents, T_b, mode, philox_key0, philox_key1,
+                     philox_offset, B, max_T, R, V, accept_len, accept_nodes, out_tokens, status, ws, off, stream);
 }

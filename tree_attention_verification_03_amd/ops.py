@@ -191,6 +191,39 @@ def spec_tree_verify(target, draft_probs, q_row, tokens, parents, T_b, mode, phi
     return ws
 
 
+def spec_tree_verify_logits_workspace_size(B: int, max_T: int, V: int) -> int:
+    return int(load().spec_tree_verify_logits_workspace_size(B, max_T, V))
+
+
+def spec_tree_verify_logits(logits, temperature, draft_probs, q_row, tokens, parents, T_b, mode, philox_key,
+                            philox_offset, accept_len, accept_nodes, out_tokens, status, ws=None):
+    """spec_tree_verify with the sampling sequences' target distributions formed from ``logits`` (fp32
+    [B, max_T, V]) and ``temperature`` (fp32 [B] or None = 1) inside the library."""
+    _dev(logits, torch.float32, "logits")
+    B, max_T, V = logits.shape
+    if temperature is not None:
+        _dev(temperature, torch.float32, "temperature")
+    R = 0
+    if draft_probs is not None:
+        _dev(draft_probs, torch.float32, "draft_probs")
+        R = draft_probs.shape[1]
+        _dev(q_row, torch.int32, "q_row")
+    for n, t in (("tokens", tokens), ("parents", parents), ("accept_len", accept_len),
+                 ("accept_nodes", accept_nodes), ("out_tokens", out_tokens), ("status", status)):
+        _dev(t, torch.int32, n)
+    _dev(mode, torch.int8, "mode")
+    if ws is None:
+        ws = zeroed_workspace(spec_tree_verify_logits_workspace_size(B, max_T, V), logits.device)
+    k0, k1 = (int(x) & 0xFFFFFFFFFFFFFFFF for x in philox_key)
+    rc = load().spec_tree_verify_logits(_ptr(logits), _ptr(temperature), _ptr(draft_probs), _ptr(q_row), _ptr(tokens),
+                                        _ptr(parents), _ptr(T_b), _ptr(mode), k0, k1,
+                                        int(philox_offset) & 0xFFFFFFFFFFFFFFFF, B, max_T, R, V, _ptr(accept_len),
+                                        _ptr(accept_nodes), _ptr(out_tokens), _ptr(status), _ptr(ws), ws.numel(),
+                                        _stream(logits))
+    check(rc, "spec_tree_verify_logits")
+    return ws
+
+
 # ------------------------------------------------------------------ compaction
 def spec_kv_compact(k_pages, v_pages, page_table, prefix_lens, accept_nodes, accept_len, new_prefix_lens,
                     num_layers: int = 1, layer_stride_elems: int = 0):

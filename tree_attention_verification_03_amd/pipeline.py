@@ -30,7 +30,8 @@ def step_row_range(step: int, max_topk: int):
 class DeviceWorkload:
     """Device copies of a ``workloads.Workload``."""
 
-    def __init__(self, w, device="cuda"):
+    def __init__(self, w, device="cuda", logits: bool = False):
+        """``logits``: also upload the target logits and temperatures (verification from logits)."""
         self.w = w
         dev = torch.device(device)
         self.device = dev
@@ -49,6 +50,9 @@ class DeviceWorkload:
         self.draft_logprobs = torch.from_numpy(w.draft_logprobs).to(dev)
         self.draft_probs = torch.from_numpy(w.draft_probs).to(dev)
         self.target = torch.from_numpy(w.target).to(dev)
+        if logits:
+            self.target_logits = torch.from_numpy(w.target_logits).to(dev)
+            self.temperature = torch.from_numpy(np.ascontiguousarray(w.temperature, dtype=np.float32)).to(dev)
 
 
 @dataclass
@@ -70,9 +74,13 @@ class StepOutputs:
 
 
 class SpecTreeStep:
-    def __init__(self, dw: DeviceWorkload, attn_status: bool = True, fused_finish: bool = True):
+    def __init__(self, dw: DeviceWorkload, attn_status: bool = True, fused_finish: bool = True,
+                 verify_from_logits: bool = False):
+        """``verify_from_logits``: verify with spec_tree_verify_logits on the target logits and temperatures
+        (the DeviceWorkload must have been made with ``logits=True``)."""
         w = dw.w
         self.dw = dw
+        self.from_logits = verify_from_logits
         self.fused_finish = fused_finish
         dev = dw.device
         B, T = w.B, w.max_T
@@ -85,7 +93,9 @@ class SpecTreeStep:
         self.ws_build = ops.zeroed_workspace(ops.spec_tree_build_workspace_size(B, w.max_topk, w.max_depth), dev)
         self.ws_attn = ops.zeroed_workspace(
             ops.spec_tree_attention_workspace_size(B, T, w.Hq, w.Hkv, w.d, w.page, w.max_pages), dev)
-        self.ws_verify = ops.zeroed_workspace(ops.spec_tree_verify_workspace_size(B, T, w.V), dev)
+        self.ws_verify = ops.zeroed_workspace(
+            (ops.spec_tree_verify_logits_workspace_size if verify_from_logits else ops.spec_tree_verify_workspace_size)(
+                B, T, w.V), dev)
         self.sampling = bool((w.modes == ops.MODE_SAMPLE).any())
         # the attention status word is OR-ed into, so collecting it costs a fill per step
         self.attn_status = attn_status
@@ -119,6 +129,12 @@ class SpecTreeStep:
 
     def verify(self):
         w, dw, o = self.dw.w, self.dw, self.o
+        if self.from_logits:
+            ops.spec_tree_verify_logits(dw.target_logits, dw.temperature, dw.draft_probs if self.sampling else None,
+                                        o.q_row, o.tokens, o.parents, dw.T_b, dw.modes, w.philox_key,
+                                        w.philox_offset, o.accept_len, o.accept_nodes, o.out_tokens, o.status,
+                                        self.ws_verify)
+            return
         ops.spec_tree_verify(dw.target, dw.draft_probs if self.sampling else None, o.q_row, o.tokens, o.parents,
                              dw.T_b, dw.modes, w.philox_key, w.philox_offset, o.accept_len, o.accept_nodes,
                              o.out_tokens, o.status, self.ws_verify)

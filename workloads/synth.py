@@ -17,7 +17,8 @@ does not shift the others):
   row 0 is the root row (step 1), row ``1 + (d - 2) * max_topk + f`` is step
   d's row for frontier slot f;
 * target rows ``[B, T_max, V]``: fp32 logits ~ N(0, 3) for greedy sequences;
-  for sampling sequences fp64 softmax(logits / temperature), stored fp32;
+  for sampling sequences fp64 softmax(logits / temperature), stored fp32 (the
+  logits themselves are kept as ``target_logits`` for every row);
 * root tokens uniform in [0, V); Philox key = (seed, 0x5EED), offset 0.
 
 Nothing here builds trees, masks, attends or verifies.
@@ -103,6 +104,7 @@ class Workload:
     sm_scale: float
     compact: bool = False
     extra: dict = field(default_factory=dict)
+    target_logits: np.ndarray = None  # float32 [B, max_T, V]: the logits every target row was formed from
 
     @property
     def R(self) -> int:
@@ -223,8 +225,10 @@ def make_workload(
     # ---- target rows ---------------------------------------------------
     r_t = np.random.Generator(np.random.PCG64(s_target))
     target = np.empty((B, max_T, V), dtype=np.float32)
+    target_logits = np.empty((B, max_T, V), dtype=np.float32)
     for b in range(B):
         z = r_t.standard_normal((max_T, V), dtype=np.float32) * np.float32(3.0)
+        target_logits[b] = z
         if modes[b] == MODE_SAMPLE:
             target[b] = np.exp(_fp64_log_softmax(z.astype(np.float64) / float(temperature))).astype(np.float32)
         else:
@@ -239,7 +243,7 @@ def make_workload(
         prefix_lens=prefix_lens, topk=topk_b, depth=depth_b, num_draft=nd_b, T_b=T_b,
         modes=modes, temperature=temps, page_table=page_table, num_pages=num_pages,
         k_pages=k_pages, v_pages=v_pages, q=q, root_tokens=root_tokens,
-        draft_logprobs=draft_logprobs, draft_probs=draft_probs, target=target,
+        draft_logprobs=draft_logprobs, draft_probs=draft_probs, target=target, target_logits=target_logits,
         philox_key=(int(seed) & 0xFFFFFFFFFFFFFFFF, 0x5EED), philox_offset=0,
         sm_scale=float(1.0 / np.sqrt(d)), compact=compact,
     )
