@@ -57,6 +57,9 @@ struct NodeState {  // one sampling node; all zero between calls (written by its
 };
 
 constexpr int kMaxKids = 64;  // children of one node (T <= 65)
+// the queue counters sit 128 bytes apart, so the waiters' polls of one do not queue behind the claims and
+// reservations made on another
+constexpr int kQ = 32;
 
 struct VerifyWs {
   uint64_t* keys;      // [B*max_T] greedy argmax keys (0 = empty)
@@ -71,7 +74,7 @@ struct VerifyWs {
   uint64_t* psum;      // [B*max_T][nsl][3] pass 0 per slice: sum of fx(q), argmax key of fx(p), NaN bits
   uint64_t* kidpq;     // [B*max_T][kMaxKids] children: (fx(p[t]) << 32) | fx(q[t]), ~0 = invalid token
   uint32_t* queue;     // [B*max_T*nsl] published dynamic items (node * nsl + slice + 1), 0 = empty
-  uint32_t* qctl;      // [4] head, tail, nodes done, workers exited
+  uint32_t* qctl;      // head, tail, nodes done, workers exited: at qctl[kQ * i], 128 bytes apart
 };
 
 int sample_slices(int V) { return (V + kSampleSlice - 1) / kSampleSlice; }
@@ -99,7 +102,7 @@ VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
   w.psum = reinterpret_cast<uint64_t*>(take(24 * n * nsl));
   w.kidpq = reinterpret_cast<uint64_t*>(take(8 * n * kMaxKids));
   w.queue = reinterpret_cast<uint32_t*>(take(4 * n * nsl));
-  w.qctl = reinterpret_cast<uint32_t*>(take(16));
+  w.qctl = reinterpret_cast<uint32_t*>(take(4 * kQ * sizeof(uint32_t)));
   *total = off;
   return w;
 }
@@ -605,7 +608,7 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
         st_agent(&ns->sq, S_Q);
         st_agent(&ns->am, AM);
       }
-      const uint32_t pos = ticket_add_n(&w.qctl[1], uint32_t(a.nsl));
+      const uint32_t pos = ticket_add_n(&w.qctl[1 * kQ], uint32_t(a.nsl));
       wait_global_stores();  // this wave's state and children-cache stores are complete
       for (int sl = 0; sl < a.nsl; ++sl) st_agent(&w.queue[pos + sl], uint32_t(node * a.nsl + sl + 1));
       break;
@@ -860,7 +863,7 @@ __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArg
       st_agent(&ns->pass, 0);
     }
     wait_global_stores();
-    ticket_add(&w.qctl[2]);
+    ticket_add(&w.qctl[2 * kQ]);
     last_s = ticket_add(&w.tickets[b]) == uint32_t(a.max_T - 1);
   }
   __syncthreads();
@@ -885,7 +888,7 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
   const uint32_t n_static = rows * uint32_t(a.nsl), cap = n_static;
   for (;;) {
     if (tid == 0) {
-      const uint32_t i = ticket_add(&w.qctl[0]);
+      const uint32_t i = ticket_add(&w.qctl[0 * kQ]);
       uint32_t it = 0;  // 1 + static index, or 1 + n_static + node * nsl + slice, or 0 = stop
       if (i < n_static) {
         it = 1 + i;
@@ -902,7 +905,7 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
               break;
             }
           }
-          if (ld_agent(&w.qctl[2]) >= total) break;
+          if (ld_agent(&w.qctl[2 * kQ]) >= total) break;
           for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
           nap = nap < 4 ? 2 * nap : 4;
         }
@@ -939,11 +942,11 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
       sample_pass0<VEC>(w, a, b, u, T, sl);
   }
   // the last worker out leaves the queue counters at zero for the next call
-  if (tid == 0 && ticket_add(&w.qctl[3]) == uint32_t(a.n_workers - 1)) {
-    ticket_reset(&w.qctl[0]);
-    ticket_reset(&w.qctl[1]);
-    ticket_reset(&w.qctl[2]);
-    ticket_reset(&w.qctl[3]);
+  if (tid == 0 && ticket_add(&w.qctl[3 * kQ]) == uint32_t(a.n_workers - 1)) {
+    ticket_reset(&w.qctl[0 * kQ]);
+    ticket_reset(&w.qctl[1 * kQ]);
+    ticket_reset(&w.qctl[2 * kQ]);
+    ticket_reset(&w.qctl[3 * kQ]);
   }
 }
 
