@@ -37,6 +37,7 @@ constexpr int kCand = kCandPerLane * kWave;  // candidates per draft row (n_slic
 constexpr int kMaxEpl = 16;                  // row elements per thread and load batch: 8 or 16
 constexpr int kMaxBatches = 2;               // load batches per slice the block-count target may ask for
 constexpr int kFinishThreads = 256;
+constexpr int kTicketStride = 32;  // uint32: each sequence's ticket on its own 128-byte line
 
 struct BuildWs {
   int32_t* tok;    // [B, P]
@@ -46,7 +47,7 @@ struct BuildWs {
   double* score;   // [B, P]
   int32_t* frontier;  // [B, max_topk] pool indices, rank order
   double* fscore;     // [B, max_topk] their scores
-  uint32_t* ticket;   // [B] blocks of the sequence's step that have finished
+  uint32_t* ticket;   // [B * kTicketStride] blocks of the sequence's step that have finished (own 128-byte lines)
   uint64_t* cand;     // [B, max_topk, kCand] per-slice top-k keys, slice x at x * k
 };
 
@@ -71,7 +72,7 @@ BuildWs carve(void* ws, int B, int max_topk, int max_depth, size_t* total) {
   w.fslot = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * P));
   w.frontier = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * max_topk));
   w.fscore = reinterpret_cast<double*>(take(sizeof(double) * B * max_topk));
-  w.ticket = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B));
+  w.ticket = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B * kTicketStride));
   w.cand = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * B * max_topk * kCand));
   *total = off;
   return w;
@@ -507,10 +508,10 @@ __global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, i
   }
   wait_global_stores();
   __syncthreads();
-  if (tid == 0) last = (ticket_add(w.ticket + b) == uint32_t(n_slices * rows - 1));
+  if (tid == 0) last = (ticket_add(w.ticket + size_t(b) * kTicketStride) == uint32_t(n_slices * rows - 1));
   __syncthreads();
   if (!last) return;
-  if (tid == 0) ticket_reset(w.ticket + b);  // leave the workspace ready for the next step
+  if (tid == 0) ticket_reset(w.ticket + size_t(b) * kTicketStride);  // leave the workspace ready for the next step
 
   // every row's n_slices * k <= kCand candidates (0 = empty); wave w merges rows w and w + NWV,
   // each lane holding up to four candidates of a row

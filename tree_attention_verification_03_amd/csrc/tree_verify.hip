@@ -46,7 +46,7 @@ constexpr int kGreedySliceMax = 3 * kGreedySlice;  // ... up to three times that
 constexpr int kGreedyBlocksTarget = 448;           // greedy blocks one launch keeps resident (2 per CU, less room)
 constexpr int kMaxWorkers = 512;  // persistent sampling blocks (2 per CU are resident)
 
-struct NodeState {  // one sampling node; all zero between calls (written by its decision blocks only)
+struct alignas(128) NodeState {  // one sampling node (own 128-byte line); all zero between calls (written by its decision blocks only)
   uint64_t sp, sq, am;  // from pass 0: sums of fx(p) and fx(q), argmax key of fx(p)
   uint64_t gamma;       // gamma of the pass in flight
   uint32_t ticket;      // slices of the pass in flight that are done
@@ -58,8 +58,9 @@ struct NodeState {  // one sampling node; all zero between calls (written by its
 
 constexpr int kMaxKids = 64;  // children of one node (T <= 65)
 // the queue counters sit 128 bytes apart, so the waiters' polls of one do not queue behind the claims and
-// reservations made on another
+// reservations made on another; likewise every ticket (kQ uint32 apart) and greedy argmax key (kKS uint64)
 constexpr int kQ = 32;
+constexpr int kKS = 16;
 
 struct VerifyWs {
   uint64_t* keys;      // [B*max_T] greedy argmax keys (0 = empty)
@@ -90,13 +91,13 @@ VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
     return r;
   };
   VerifyWs w;
-  w.keys = reinterpret_cast<uint64_t*>(take(8 * n));
+  w.keys = reinterpret_cast<uint64_t*>(take(8 * n * kKS));
   w.rowflag = reinterpret_cast<uint32_t*>(take(4 * n));
   w.acc_child = reinterpret_cast<int32_t*>(take(4 * n));
   w.bonus = reinterpret_cast<int32_t*>(take(4 * n));
   w.nflag = reinterpret_cast<uint32_t*>(take(4 * n));
-  w.tickets = reinterpret_cast<uint32_t*>(take(4 * size_t(B)));
-  w.rtick = reinterpret_cast<uint32_t*>(take(4 * n));
+  w.tickets = reinterpret_cast<uint32_t*>(take(4 * size_t(B) * kQ));
+  w.rtick = reinterpret_cast<uint32_t*>(take(4 * n * kQ));
   w.node = reinterpret_cast<NodeState*>(take(sizeof(NodeState) * n));
   w.ssum = reinterpret_cast<uint64_t*>(take(16 * n * nsl));
   w.psum = reinterpret_cast<uint64_t*>(take(24 * n * nsl));
@@ -192,7 +193,7 @@ __device__ __forceinline__ void greedy_slice(const VerifyWs& w, const VerifyArgs
       m = red[i] > m ? red[i] : m;
       f |= nanred[i];
     }
-    atomicMax(reinterpret_cast<unsigned long long*>(w.keys + row), (unsigned long long)m);
+    atomicMax(reinterpret_cast<unsigned long long*>(w.keys + size_t(row) * kKS), (unsigned long long)m);
     if (f) atomicOr(w.rowflag + row, 1u);
   }
 }
@@ -758,12 +759,12 @@ __device__ __forceinline__ void walk(const VerifyWs& w, const VerifyArgs& a, int
   int nacc, bonus;
   uint32_t rootf;
   if (greedy) {
-    const uint64_t k0 = ld_agent(w.keys + base);
+    const uint64_t k0 = ld_agent(w.keys + base * kKS);
     const uint32_t rf0 = ld_agent(w.rowflag + base);
     uint64_t k = 0;
     uint32_t rf = 0;
     if (real) {
-      k = ld_agent(w.keys + base + n);
+      k = ld_agent(w.keys + (base + n) * kKS);
       rf = ld_agent(w.rowflag + base + n);
     }
     const int am0 = int(0xffffffffu - uint32_t(k0)), am = int(0xffffffffu - uint32_t(k));
@@ -771,11 +772,11 @@ __device__ __forceinline__ void walk(const VerifyWs& w, const VerifyArgs& a, int
     rootf = rf0 ? SPEC_STATUS_NAN_INPUT : 0u;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every lane has read the root before it is cleared
     if (real) {  // leave the workspace zeroed
-      st_agent(w.keys + base + n, uint64_t(0));
+      st_agent(w.keys + (base + n) * kKS, uint64_t(0));
       st_agent(w.rowflag + base + n, 0u);
     }
     if (lane == 0) {
-      st_agent(w.keys + base, uint64_t(0));
+      st_agent(w.keys + base * kKS, uint64_t(0));
       st_agent(w.rowflag + base, 0u);
     }
     const int par_am = __shfl(am, par > 0 ? par - 1 : lane);
@@ -864,11 +865,11 @@ __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArg
     }
     wait_global_stores();
     ticket_add(&w.qctl[2 * kQ]);
-    last_s = ticket_add(&w.tickets[b]) == uint32_t(a.max_T - 1);
+    last_s = ticket_add(&w.tickets[size_t(b) * kQ]) == uint32_t(a.max_T - 1);
   }
   __syncthreads();
   if (!last_s) return;
-  if (threadIdx.x == 0) ticket_reset(&w.tickets[b]);
+  if (threadIdx.x == 0) ticket_reset(&w.tickets[size_t(b) * kQ]);
   walk(w, a, b);
 }
 
@@ -979,16 +980,16 @@ __global__ void __launch_bounds__(kThreads, 2) verify_kernel(VerifyWs w, VerifyA
   if (threadIdx.x == 0) {
     int last = 0;
     if (!a.row_tickets) {
-      last = ticket_add(w.tickets + b) == uint32_t(a.n_slices * a.max_T - 1);
-    } else if (ticket_add(w.rtick + row) == uint32_t(a.n_slices - 1)) {
-      ticket_reset(w.rtick + row);  // leave the workspace ready for the next call
-      last = ticket_add(w.tickets + b) == uint32_t(a.max_T - 1);
+      last = ticket_add(w.tickets + size_t(b) * kQ) == uint32_t(a.n_slices * a.max_T - 1);
+    } else if (ticket_add(w.rtick + size_t(row) * kQ) == uint32_t(a.n_slices - 1)) {
+      ticket_reset(w.rtick + size_t(row) * kQ);  // leave the workspace ready for the next call
+      last = ticket_add(w.tickets + size_t(b) * kQ) == uint32_t(a.max_T - 1);
     }
     last_s = last;
   }
   __syncthreads();
   if (!last_s) return;
-  if (threadIdx.x == 0) ticket_reset(w.tickets + b);  // leave the workspace ready for the next call
+  if (threadIdx.x == 0) ticket_reset(w.tickets + size_t(b) * kQ);  // leave the workspace ready for the next call
   walk(w, a, b);
 }
 
