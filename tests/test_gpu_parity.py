@@ -87,6 +87,27 @@ def test_attention_small(case, monkeypatch):
         assert np.isnan(out[b, T[b]:]).all()
 
 
+def test_attention_large_values_through_split_partials(monkeypatch):
+    """V scaled by 2^20 (exact in bf16): split-K partial outputs far beyond fp16's range must come back exactly
+    scaled (their per-row power-of-two scale), so out / 2^20 matches the oracle on the unscaled values."""
+    import copy
+
+    from workloads.synth import bf16_bits_to_f32, f32_to_bf16_bits
+
+    monkeypatch.setenv("SPEC_TREE_ATTN_CHUNK", "128")
+    w, parents = _attn_case(2, 16, 4, 128, [1000, 333], [17, 9], 16, "random", seed=31)
+    big = copy.copy(w)
+    big.v_pages = f32_to_bf16_bits(bf16_bits_to_f32(w.v_pages) * np.float32(2.0**20))
+    assert np.array_equal(bf16_bits_to_f32(big.v_pages), bf16_bits_to_f32(w.v_pages) * np.float32(2.0**20))
+    log("[attn] V x 2^20 through the split-K partials")
+    out, lse, status = _run_attention(big, parents)
+    max_abs, rel, lse_err = compare_attention(w, out / np.float32(2.0**20), lse, parents)
+    log(f"[attn] large values: max_abs={max_abs:.3e} rel_l2={rel:.3e} lse_err={lse_err:.3e}")
+    assert all(np.isfinite(out[b, : w.T_b[b]]).all() for b in range(w.B))  # rows past T_b are never written
+    assert max_abs <= ATTN_MAX_ABS and rel <= ATTN_REL_L2 and lse_err <= LSE_ABS
+    assert (status == 0).all()
+
+
 def test_attention_invalid_parent_hangs_off_root():
     w, parents = _attn_case(2, 8, 2, 128, [40, 90], [6, 9], 16, "random", seed=5)
     parents[0, 3] = 7  # >= i

@@ -43,6 +43,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -78,6 +80,11 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// four fp32 -> packed fp16, round-to-nearest-even
+__device__ __forceinline__ uint2 pack4_f16(f32x4 v) {
+  return __builtin_bit_cast(uint2, __builtin_convertvector(v, f16x4));
+}
 
 // two fp32 -> packed bf16 pair, hardware round-to-nearest-even
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
@@ -131,8 +138,8 @@ constexpr int blocks_per_cu(int D, int NS) { return NS * 128 * D + 4096 <= 160 *
 // SPS ring stages of 32 keys form one softmax step (one barrier, one running-max update per step)
 
 // Split-K merge of one output row, item by item in fixed order against the running maximum
-// reference max: out = sum_i w_i O_i / sum_i w_i l_i with w_i = 2^(m_i - max_j m_j). A thread owns
-// 4 columns (o) of the row.
+// reference max: out = sum_i w_i l_i o_i / sum_i w_i l_i with w_i = 2^(m_i - max_j m_j) and o_i = O_i / l_i
+// the item's normalised output (stored fp16 times a power-of-two row scale). A thread owns 4 columns (o).
 struct RowMerge {
   float mx = -INFINITY, ls = 0.f;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
@@ -150,8 +157,8 @@ struct RowMerge {
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
       if (u < navail && mi[u] != -INFINITY) {  // guarded, not weighted
-        const float w = fast_exp2(mi[u] - mb);
-        ls += w * li[u];
+        const float w = fast_exp2(mi[u] - mb) * li[u];
+        ls += w;
         o += ai[u] * w;
       }
     }
@@ -558,11 +565,13 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
     return;
   }
 
-  // ---- this item's partial (unnormalised O, reference max m, row sum l) for the combine kernel.
-  // Layout per (b, g, row block, item): O [tpb * 16][D], then m [tpb * 16], then l [tpb * 16].
+  // ---- this item's partial for the combine kernel: o = O / (l sc) in fp16 (the merge weights m and l stay
+  // fp32, so its rounding, 2^-12 relative, stays below the bf16 output's own), reference max m, row sum l,
+  // and sc, a power of two that keeps the row's |o| below 2^14 (1 unless |O / l| reaches 2^14: fp16 stops at
+  // 65504). Layout per (b, g, row block, item): o fp16 [tpb * 16][D], then m, l, sc fp32 [tpb * 16] each.
   if (!active) return;
   const int TR = p.tpb * 16;
-  const size_t ITEM = size_t(TR) * (D + 2);
+  const size_t ITEM = size_t(TR) * (D / 2 + 3);  // in floats
   float* const mine = p.part + ((size_t(bg) * p.n_rb + rb) * size_t(p.n_splits) + s) * ITEM;
 #pragma unroll
   for (int rw = 0; rw < RW; ++rw) {
@@ -570,12 +579,24 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
     if (lt >= p.tpb || t0 + lt >= ntM) continue;
     const int row = lt * 16 + l15;
     if (16 * (t0 + lt) + l15 >= M) continue;  // rows past this tree: never read
-    float* o = mine + size_t(row) * D + g4;
+    uint16_t* o = reinterpret_cast<uint16_t*>(mine) + size_t(row) * D + g4;
+    const float inv = l_run[rw] > 0.f ? 1.f / l_run[rw] : 0.f;
+    float amax = 0.f;  // the row's largest |O|: this lane's columns, then the row's four lanes
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(o + 16 * dt) = acc[rw][dt];
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fabsf(acc[rw][dt][k]));
+    amax = lanegroup_max(amax) * inv;
+    int ex = 0;
+    (void)frexpf(amax, &ex);  // amax < 2^ex
+    const float sc = ex > 14 ? ldexpf(1.f, ex - 14) : 1.f;
+    const float mul = inv * (1.f / sc);  // sc is a power of two: exact
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<uint2*>(o + 16 * dt) = pack4_f16(acc[rw][dt] * mul);
     if (lane < 16) {
-      mine[size_t(TR) * D + row] = m_run[rw];
-      mine[size_t(TR) * (D + 1) + row] = l_run[rw];
+      mine[size_t(TR) * (D / 2) + row] = m_run[rw];
+      mine[size_t(TR) * (D / 2 + 1) + row] = l_run[rw];
+      mine[size_t(TR) * (D / 2 + 2) + row] = sc;
     }
   }
 }
@@ -607,7 +628,7 @@ __global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
   if (row >= TR || r >= p.G * p.max_T) return;
   const int T_raw = p.T_b ? p.T_b[b] : p.max_T;
   const int L_raw = p.prefix_lens[b];
-  const size_t ITEM = size_t(TR) * (D + 2);
+  const size_t ITEM = size_t(TR) * (D / 2 + 3);  // in floats: o fp16 [TR][D], m, l, sc [TR]
   const float* grp = p.part + size_t(rbg) * p.n_splits * ITEM;
   RowMerge mr;
   int n_items = CB;  // known after the first batch's loads (before them with KNOWN)
@@ -627,9 +648,11 @@ __global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
       // without KNOWN, slots past the sequence's items repeat the last slot (loaded, never used)
       const int item = KNOWN ? min(ib + u, n_items - 1) : min(ib + u, p.n_splits - 1);
       const float* base = grp + size_t(item) * ITEM;
-      mi[u] = base[size_t(TR) * D + row];
-      li[u] = base[size_t(TR) * (D + 1) + row];
-      ai[u] = *reinterpret_cast<const f32x4*>(base + size_t(row) * D + 4 * c);
+      mi[u] = base[size_t(TR) * (D / 2) + row];
+      li[u] = base[size_t(TR) * (D / 2 + 1) + row];
+      const float scu = base[size_t(TR) * (D / 2 + 2) + row];
+      const uint2 h = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + size_t(row) * D + 4 * c);
+      ai[u] = __builtin_convertvector(__builtin_bit_cast(f16x4, h), f32x4) * scu;
     }
     if (!KNOWN && ib == 0) {
       const int T = min(max(T_raw, 1), p.max_T);
@@ -688,7 +711,7 @@ AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_p
   pl.chunk = int(chunk);
   pl.n_splits = int((slots + chunk - 1) / chunk);
   pl.npg = int((chunk - 1) / page) + 2;  // a chunk may straddle one page more than it covers
-  const size_t item = size_t(pl.tpb) * 16 * (d + 2);
+  const size_t item = size_t(pl.tpb) * 16 * (d / 2 + 3);  // floats: o fp16 [rows][d], m, l, sc
   pl.zero_bytes = 1024;  // never written: stays as zero-filled as the caller provided it
   pl.part_bytes = align_up(size_t(groups) * pl.n_splits * item * sizeof(float), 256);
   pl.lds_dyn = size_t(pl.npg) * sizeof(int);
