@@ -61,6 +61,7 @@ constexpr int kMaxKids = 64;  // children of one node (T <= 65)
 // reservations made on another; likewise every ticket (kQ uint32 apart) and greedy argmax key (kKS uint64)
 constexpr int kQ = 32;
 constexpr int kKS = 16;
+constexpr int kMaxSampleMap = 2048;  // sampling sequences a worker lists in LDS
 
 struct VerifyWs {
   uint64_t* keys;      // [B*max_T] greedy argmax keys (0 = empty)
@@ -877,16 +878,34 @@ __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArg
 template <bool VEC>
 __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArgs& a) {
   __shared__ int item_s;
-  const int tid = threadIdx.x, max_T = a.max_T;
+  __shared__ int smap[kMaxSampleMap];  // the sampling sequences in index order (when they fit)
+  __shared__ int wcnt[kWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, max_T = a.max_T;
   int nseq = 0;
   for (int b0 = 0; b0 < a.B; b0 += kThreads) {
     const int b = b0 + tid;
-    nseq += __syncthreads_count(b < a.B && a.mode[b] == SPEC_MODE_SAMPLE);
+    const bool f = b < a.B && a.mode[b] == SPEC_MODE_SAMPLE;
+    const uint64_t m = __ballot(f);
+    if (lane == 0) wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int off = nseq, tot = 0;
+    for (int i = 0; i < kWaves; ++i) {
+      off += i < wave ? wcnt[i] : 0;
+      tot += wcnt[i];
+    }
+    off += __popcll(m & ((1ull << lane) - 1));
+    if (f && off < kMaxSampleMap) smap[off] = b;
+    nseq += tot;
+    __syncthreads();
   }
   if (nseq == 0) return;  // nothing to sample: the queue is never touched
   const uint32_t total = uint32_t(nseq) * uint32_t(max_T);
   const uint32_t rows = uint32_t(a.B) * uint32_t(max_T);
-  const uint32_t n_static = rows * uint32_t(a.nsl), cap = n_static;
+  // pass-0 items over the sampling sequences only when their list fits (a mixed batch's greedy rows then
+  // cost no claims), else over every sequence, greedy ones skipped
+  const bool mapped = nseq <= kMaxSampleMap;
+  const uint32_t n_static = (mapped ? uint32_t(nseq) * uint32_t(max_T) : rows) * uint32_t(a.nsl);
+  const uint32_t cap = rows * uint32_t(a.nsl);  // queue slots
   for (;;) {
     if (tid == 0) {
       const uint32_t i = ticket_add(&w.qctl[0 * kQ]);
@@ -925,9 +944,10 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
       sl = int(k % uint32_t(a.nsl));
     } else {  // pass 0 items by tree position first (every sequence's root, then node 1, ...): the
               // nodes near the root, whose passes form the longest chains, start first
-      const uint32_t per_u = uint32_t(a.B) * uint32_t(a.nsl);
+      const uint32_t per_u = (mapped ? uint32_t(nseq) : uint32_t(a.B)) * uint32_t(a.nsl);
       const uint32_t uu = k / per_u, rem = k - uu * per_u;
-      node = int(rem / uint32_t(a.nsl)) * max_T + int(uu);
+      const int si = int(rem / uint32_t(a.nsl));
+      node = (mapped ? smap[si] : si) * max_T + int(uu);
       sl = int(rem % uint32_t(a.nsl));
     }
     const int b = node / max_T, u = node - b * max_T;
