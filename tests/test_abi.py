@@ -99,6 +99,22 @@ def test_verify_build_compact_mask_host_validation(lib):
     assert lib.spec_tree_mask(None, None, 1, 9, None, None, None, None) == SPEC_E_INVAL
 
 
+def test_verify_logits_host_validation(lib):
+    p = ctypes.c_void_p(1 << 20)
+    big = 1 << 40
+    v = lambda **kw: lib.spec_tree_verify_logits(p, None, None, None, kw.get("tok", p), p, None, p, 1, 2, 0,
+                                                 kw.get("B", 1), kw.get("T", 9), 0, kw.get("V", 1000), p, p, p, p, p,
+                                                 kw.get("ws", big), None)
+    assert v(T=66) == SPEC_E_UNSUPPORTED
+    assert v(V=1 << 24) == SPEC_E_UNSUPPORTED
+    assert v(B=2000, T=65) == SPEC_E_UNSUPPORTED  # B * max_T > 65535
+    assert v(ws=8) == SPEC_E_WORKSPACE
+    assert v(tok=None) == SPEC_E_INVAL  # argument errors before any launch, also past the workspace check
+    # the logits workspace holds the verify workspace plus the probabilities and the slice partials
+    base = lib.spec_tree_verify_workspace_size(4, 9, 1000)
+    assert lib.spec_tree_verify_logits_workspace_size(4, 9, 1000) >= base + 4 * 9 * 1000 * 4
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     from tree_attention_verification_03_amd import _lib
 

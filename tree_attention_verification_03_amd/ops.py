@@ -203,6 +203,8 @@ def spec_tree_verify_logits(logits, temperature, draft_probs, q_row, tokens, par
     B, max_T, V = logits.shape
     if temperature is not None:
         _dev(temperature, torch.float32, "temperature")
+        if temperature.numel() < B:
+            raise ValueError(f"temperature holds {temperature.numel()} values for {B} sequences")
     R = 0
     if draft_probs is not None:
         _dev(draft_probs, torch.float32, "draft_probs")
