@@ -235,9 +235,12 @@ int32_t spec_tree_verify(const float* target, const float* draft_probs, const in
  * Greedy sequences: exactly spec_tree_verify on the logits (argmax).
  * Sampling sequences: p = softmax(logits / temperature[b]) per row, computed
  * in fp32 (x = l * (1 / T), the row's max, sum of exp(x - max) over slices of
- * the row merged in slice order, p = exp(x - max) / sum; every reduction in a
- * fixed order, so repeated calls agree bit for bit), then
- * exactly the sampling rule of spec_tree_verify on p. Because p is formed in
+ * the row merged in a fixed order, p = exp(x - max) * (1 / sum), exp of the
+ * non-positive x - max through the hardware base-2 exponential; every
+ * reduction in a fixed order, so repeated calls agree bit for bit), then
+ * exactly the sampling rule of spec_tree_verify on p. p is never stored: one
+ * pass over the logits keeps each slice's max and sum, and the sampling
+ * passes form p from the logits as they read them. Because p is formed in
  * fp32 rather than supplied, its values can differ from an exact softmax by a
  * few units in the last place, and a decision whose margin is below that can
  * differ from one taken on exact probabilities (a draft row q equal to the
@@ -247,8 +250,9 @@ int32_t spec_tree_verify(const float* target, const float* draft_probs, const in
  * that is not a finite positive number makes all of that sequence's
  * probabilities NaN.
  * Other arguments, outputs and errors as spec_tree_verify. The workspace
- * (spec_tree_verify_logits_workspace_size) also holds the probabilities:
- * B * max_T * V fp32 beyond the verify workspace. Requires B * max_T <= 65535.
+ * (spec_tree_verify_logits_workspace_size) also holds the slices' partials:
+ * 8 bytes per 8192 logits beyond the verify workspace. Requires
+ * B * max_T <= 65535.
  * ------------------------------------------------------------------------- */
 size_t spec_tree_verify_logits_workspace_size(int32_t B, int32_t max_T, int32_t V);
 int32_t spec_tree_verify_logits(const float* logits, const float* temperature, const float* draft_probs,

@@ -110,9 +110,13 @@ def test_verify_logits_host_validation(lib):
     assert v(B=2000, T=65) == SPEC_E_UNSUPPORTED  # B * max_T > 65535
     assert v(ws=8) == SPEC_E_WORKSPACE
     assert v(tok=None) == SPEC_E_INVAL  # argument errors before any launch, also past the workspace check
-    # the logits workspace holds the verify workspace plus the probabilities and the slice partials
-    base = lib.spec_tree_verify_workspace_size(4, 9, 1000)
-    assert lib.spec_tree_verify_logits_workspace_size(4, 9, 1000) >= base + 4 * 9 * 1000 * 4
+    # the logits workspace holds the verify workspace plus one 8-byte partial per 8192-logit slice of a row
+    # (the probabilities are never stored)
+    for B, T, V in ((4, 9, 1000), (32, 33, 128256)):
+        base = lib.spec_tree_verify_workspace_size(B, T, V)
+        extra = lib.spec_tree_verify_logits_workspace_size(B, T, V) - base
+        parts = B * T * -(-V // 8192) * 8
+        assert parts <= extra < parts + 512
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

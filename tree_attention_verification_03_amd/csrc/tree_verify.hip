@@ -111,7 +111,9 @@ VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
 
 struct VerifyArgs {
   const float* target;
-  const float* prob;  // sampling rows' probabilities when they are formed from logits here, else null
+  const float2* sm_part;     // logits given: every sampling row's slice partials (max, sum of exp), else null
+  const float* temperature;  // logits given: per-sequence temperatures (null: 1)
+  int sm_nsl;                // logits given: partials per row
   const float* draft;
   const int32_t* q_row;
   const int32_t* tokens;
@@ -132,9 +134,71 @@ __device__ __forceinline__ int seq_T(const int32_t* T_b, int b, int max_T) {
   return T < 1 ? 1 : (T > max_T ? max_T : T);
 }
 
-// node's target probabilities for the sampling rule: formed here from logits, or supplied by the caller
+// e^t for t <= 0 (a softmax term against its row's maximum): the hardware base-2 exponential of t log2(e).
+// Rounding t log2(e) costs at most half an ulp of t in the exponent, the same order as the rounding of
+// t itself; results below 2^-126 flush toward zero, far below the 2^-32 resolution of the sampling rule.
+__device__ __forceinline__ float exp_nonpos(float t) { return __builtin_amdgcn_exp2f(t * 1.4426950408889634f); }
+
+// a sequence's sampling temperature, 0 when it is not a finite positive number
+__device__ __forceinline__ float sm_temperature(const float* temperature, int b) {
+  const float T = temperature ? temperature[b] : 1.f;
+  return (T > 0.f && isfinite(T)) ? T : 0.f;
+}
+
+// A node's target probabilities for the sampling rule: the row as the caller supplies it (LG false), or
+// formed from the target's logits (LG true) as p[v] = exp(x - M) * (1 / S) with x = l[v] * (1 / T_b), where
+// M and S are the row's maximum and sum of exponentials merged from its slice partials in a fixed order.
+// Every block merges them the same way, so p[v] is the same number in every pass that reads it. A non-finite l[v] / T_b gives NaN,
+// and so does every element of a row whose temperature is not a finite positive number (NaN probabilities
+// count as zero and raise SPEC_STATUS_NAN_INPUT).
+template <bool LG>
+struct ProbRow {
+  float inv = 1.f, M = 0.f, rS = 1.f;  // rS = 1 / S
+  __device__ __forceinline__ float operator()(float l) const {
+    if constexpr (!LG) {
+      return l;
+    } else {
+      const float x = l * inv;
+      return isfinite(x) ? exp_nonpos(x - M) * rS : NAN;
+    }
+  }
+};
+
+// the row's partials are merged across each wave's lanes (lane j takes partials j, j + 64, ...) with xor
+// butterflies, the same fixed order in every wave, block and pass (fp32 max and add are commutative, so every
+// lane ends with the same M and S)
+template <bool LG>
+__device__ __forceinline__ ProbRow<LG> prob_row(const VerifyArgs& a, size_t node) {
+  ProbRow<LG> r;
+  if constexpr (LG) {
+    const float T = sm_temperature(a.temperature, int(node / size_t(a.max_T)));
+    if (T == 0.f) {
+      r.inv = NAN;
+      return r;
+    }
+    r.inv = 1.f / T;
+    const float2* pr = a.sm_part + node * size_t(a.sm_nsl);
+    const int lane = threadIdx.x & (kWave - 1), n = a.sm_nsl;
+    const float2 q0 = lane < n ? pr[lane] : make_float2(-INFINITY, 0.f);
+    float M = q0.x;
+    for (int j = lane + kWave; j < n; j += kWave) M = fmaxf(M, pr[j].x);
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+    float S = q0.x != -INFINITY ? q0.y * exp_nonpos(q0.x - M) : 0.f;
+    for (int j = lane + kWave; j < n; j += kWave) {
+      const float2 q = pr[j];
+      if (q.x != -INFINITY) S += q.y * exp_nonpos(q.x - M);
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) S += __shfl_xor(S, o, kWave);
+    r.M = M;
+    r.rS = 1.f / S;
+  }
+  return r;
+}
+
 __device__ __forceinline__ const float* sample_row(const VerifyArgs& a, size_t node) {
-  return (a.prob ? a.prob : a.target) + node * size_t(a.V);
+  return a.target + node * size_t(a.V);
 }
 
 __device__ __forceinline__ uint64_t argmax_key(float x, int v) {
@@ -317,10 +381,11 @@ __device__ __forceinline__ const float* node_qrow_any(const VerifyArgs& a, int b
   return (a.draft != nullptr && qr >= 0 && qr < a.R) ? a.draft + (size_t(b) * a.R + qr) * a.V : nullptr;
 }
 
-// f(v, p, q) over this thread's elements of [lo, hi) (q may be null: then 0); a slice is at most
-// kSampleSlice elements, so the vector path loads all of a thread's elements in one round trip
-template <bool VEC, typename F>
-__device__ __forceinline__ void slice_for(const float* p, const float* q, int lo, int hi, F&& f) {
+// f(v, p, q) over this thread's elements of [lo, hi) (q may be null: then 0), p taken through the
+// transform that pre() returns once the elements' loads are issued; a slice is at most kSampleSlice
+// elements, so the vector path loads all of a thread's elements in one round trip
+template <bool VEC, typename Pre, typename F>
+__device__ __forceinline__ void slice_for(const float* p, const float* q, int lo, int hi, Pre&& pre, F&& f) {
   const int tid = threadIdx.x;
   if (VEC) {
     constexpr int NV = kSampleSlice / (4 * kThreads);
@@ -331,18 +396,20 @@ __device__ __forceinline__ void slice_for(const float* p, const float* q, int lo
       x[i] = v < hi ? *reinterpret_cast<const float4*>(p + v) : make_float4(0.f, 0.f, 0.f, 0.f);
       y[i] = (q && v < hi) ? *reinterpret_cast<const float4*>(q + v) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    const auto tr = pre();
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = lo + 4 * tid + 4 * kThreads * i;
       if (v < hi) {
-        f(v, x[i].x, y[i].x);
-        f(v + 1, x[i].y, y[i].y);
-        f(v + 2, x[i].z, y[i].z);
-        f(v + 3, x[i].w, y[i].w);
+        f(v, tr(x[i].x), y[i].x);
+        f(v + 1, tr(x[i].y), y[i].y);
+        f(v + 2, tr(x[i].z), y[i].z);
+        f(v + 3, tr(x[i].w), y[i].w);
       }
     }
   } else {
-    for (int v = lo + tid; v < hi; v += kThreads) f(v, p[v], q ? q[v] : 0.f);
+    const auto tr = pre();
+    for (int v = lo + tid; v < hi; v += kThreads) f(v, tr(p[v]), q ? q[v] : 0.f);
   }
 }
 
@@ -370,10 +437,10 @@ __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArg
                               bool trivial);
 
 // after a slice of a pass: the block finishing the node's pass takes the node's next decision
-template <bool VEC>
+template <bool VEC, bool LG>
 __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T);
 
-template <bool VEC>
+template <bool VEC, bool LG>
 __device__ __forceinline__ void pass_done(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
   __shared__ int last_s;
   NodeState* ns = w.node + (size_t(b) * a.max_T + u);
@@ -383,12 +450,12 @@ __device__ __forceinline__ void pass_done(const VerifyWs& w, const VerifyArgs& a
   __syncthreads();
   if (!last_s) return;
   if (threadIdx.x == 0) ticket_reset(&ns->ticket);
-  sample_decide<VEC>(w, a, b, u, T);
+  sample_decide<VEC, LG>(w, a, b, u, T);
 }
 
 // pass 0 over slice s: sums of fx(p) and fx(q), argmax key of fx(p), NaN bits, published per slice
 // (the node's decision block reduces them)
-template <bool VEC>
+template <bool VEC, bool LG>
 __device__ __forceinline__ void sample_pass0(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T, int s) {
   __shared__ uint64_t red[kWaves][3];
   const size_t node = size_t(b) * a.max_T + u;
@@ -397,7 +464,7 @@ __device__ __forceinline__ void sample_pass0(const VerifyWs& w, const VerifyArgs
   const int lo = s * kSampleSlice, hi = min(a.V, lo + kSampleSlice);
   uint64_t sp = 0, sq = 0, am = 0;
   uint32_t nan = 0;
-  slice_for<VEC>(prow, qrow, lo, hi, [&](int v, float x, float y) {
+  slice_for<VEC>(prow, qrow, lo, hi, [&] { return prob_row<LG>(a, node); }, [&](int v, float x, float y) {
     nan |= (x != x ? 1u : 0u) | (y != y ? 2u : 0u);
     const uint32_t P = fx(x);
     sp += P;
@@ -424,12 +491,12 @@ __device__ __forceinline__ void sample_pass0(const VerifyWs& w, const VerifyArgs
       st_agent(ps + 2, uint64_t(((nn & 15u) ? 1u : 0u) | ((nn >> 4) ? 2u : 0u)));
     }
   }
-  pass_done<VEC>(w, a, b, u, T);
+  pass_done<VEC, LG>(w, a, b, u, T);
 }
 
 // residual pass over slice s under the node's current gamma: the slice's sum of
 // N[v] = max(0, fx(p[v]) S_Q - gamma fx(q[v])) (32-bit limb sums), published per slice
-template <bool VEC>
+template <bool VEC, bool LG>
 __device__ __forceinline__ void sample_passN(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T, int s) {
   __shared__ uint64_t red[kWaves][3];
   const size_t node = size_t(b) * a.max_T + u;
@@ -439,7 +506,7 @@ __device__ __forceinline__ void sample_passN(const VerifyWs& w, const VerifyArgs
   const uint64_t S_Q = ld_agent(&ns->sq), gamma = ld_agent(&ns->gamma);
   const int lo = s * kSampleSlice, hi = min(a.V, lo + kSampleSlice);
   uint64_t l0 = 0, l1 = 0, l2 = 0;
-  slice_for<VEC>(prow, qrow, lo, hi, [&](int, float x, float y) {
+  slice_for<VEC>(prow, qrow, lo, hi, [&] { return prob_row<LG>(a, node); }, [&](int, float x, float y) {
     const u128 n = residual(fx(x), fx(y), S_Q, gamma, false);
     l0 += uint32_t(n);
     l1 += uint32_t(n >> 32);
@@ -452,10 +519,10 @@ __device__ __forceinline__ void sample_passN(const VerifyWs& w, const VerifyArgs
     st_agent(ss, uint64_t(v));
     st_agent(ss + 1, uint64_t(v >> 64));
   }
-  pass_done<VEC>(w, a, b, u, T);
+  pass_done<VEC, LG>(w, a, b, u, T);
 }
 
-template <bool VEC>
+template <bool VEC, bool LG>
 __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
   __shared__ int kid_s[kMaxKids], nkid_s;
   __shared__ uint64_t kpq_s[kMaxKids];  // children: (fx(p[t]) << 32) | fx(q[t]), ~0 = invalid token
@@ -473,6 +540,7 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
   const size_t node = size_t(b) * max_T + u;
   NodeState* ns = w.node + node;
   const float* prow = sample_row(a, node);
+  const ProbRow<LG> pr = prob_row<LG>(a, node);
   // a decision is one serial chain that every later pass of the node waits for, while the blocks
   // around it run throughput work: its waves take issue priority until it is done
   __builtin_amdgcn_s_setprio(3);
@@ -548,7 +616,7 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
   if (pass_s == 0) {  // first decision: the children's p and q at their tokens (cached for later passes)
     if (wave == 0 && kslot >= 0) {
       uint64_t pq = ~0ull;
-      if (c_tok >= 0 && c_tok < V) pq = (uint64_t(fx(prow[c_tok])) << 32) | (qrow ? fx(qrow[c_tok]) : 0u);
+      if (c_tok >= 0 && c_tok < V) pq = (uint64_t(fx(pr(prow[c_tok]))) << 32) | (qrow ? fx(qrow[c_tok]) : 0u);
       kpq_s[kslot] = pq;
       st_agent(w.kidpq + node * kMaxKids + kslot, pq);
     }
@@ -686,7 +754,7 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
 #pragma unroll
         for (int i = 0; i < E; i += 4) {
           const float4 x = *reinterpret_cast<const float4*>(prow + e0 + i);
-          pv[i] = fx(x.x); pv[i + 1] = fx(x.y); pv[i + 2] = fx(x.z); pv[i + 3] = fx(x.w);
+          pv[i] = fx(pr(x.x)); pv[i + 1] = fx(pr(x.y)); pv[i + 2] = fx(pr(x.z)); pv[i + 3] = fx(pr(x.w));
           const float4 y = qrow ? *reinterpret_cast<const float4*>(qrow + e0 + i) : make_float4(0.f, 0.f, 0.f, 0.f);
           qv[i] = fx(y.x); qv[i + 1] = fx(y.y); qv[i + 2] = fx(y.z); qv[i + 3] = fx(y.w);
         }
@@ -694,7 +762,7 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
 #pragma unroll
         for (int i = 0; i < E; ++i) {
           const int v = e0 + i;
-          pv[i] = v < whi ? fx(prow[v]) : 0u;  // past the slice: adds nothing
+          pv[i] = v < whi ? fx(pr(prow[v])) : 0u;  // past the slice: adds nothing
           qv[i] = (qrow && v < whi) ? fx(qrow[v]) : 0u;
         }
       }
@@ -875,7 +943,7 @@ __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArg
 }
 
 // persistent sampling worker: takes items until every sampling node is done
-template <bool VEC>
+template <bool VEC, bool LG>
 __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArgs& a) {
   __shared__ int item_s;
   __shared__ int smap[kMaxSampleMap];  // the sampling sequences in index order (when they fit)
@@ -958,9 +1026,9 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
       continue;
     }
     if (dynamic)
-      sample_passN<VEC>(w, a, b, u, T, sl);
+      sample_passN<VEC, LG>(w, a, b, u, T, sl);
     else
-      sample_pass0<VEC>(w, a, b, u, T, sl);
+      sample_pass0<VEC, LG>(w, a, b, u, T, sl);
   }
   // the last worker out leaves the queue counters at zero for the next call
   if (tid == 0 && ticket_add(&w.qctl[3 * kQ]) == uint32_t(a.n_workers - 1)) {
@@ -971,11 +1039,11 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
   }
 }
 
-template <bool VEC>
+template <bool VEC, bool LG>
 __global__ void __launch_bounds__(kThreads, 2) verify_kernel(VerifyWs w, VerifyArgs a) {
   __shared__ int last_s;
   if (int(blockIdx.x) >= a.n_greedy_blocks) {
-    sample_worker<VEC>(w, a);
+    sample_worker<VEC, LG>(w, a);
     return;
   }
   const int x = blockIdx.x % a.n_slices, row = blockIdx.x / a.n_slices;
@@ -1014,13 +1082,11 @@ __global__ void __launch_bounds__(kThreads, 2) verify_kernel(VerifyWs w, VerifyA
 }
 
 // ------------------------------------------------------------------ probabilities from logits
-// p = softmax(logits / T_b) of every sampling row (b, u < T_b) into prob, fp32, over slices of kSmSlice
-// elements: softmax_partial_kernel takes each slice's (max of x = l * (1 / T_b), sum of exp(x - max)),
-// softmax_write_kernel merges the row's slice partials (max M, S = sum_s sum_s' exp(max_s - M)) and writes
-// p = exp(x - M) / S. Every reduction runs in a fixed order, so repeated calls agree bit for bit. A
-// non-finite x gives a NaN probability and stays out of the maximum and the sum; a temperature that is not
-// a finite positive number makes the whole row NaN (NaN probabilities count as zero in the sampling rule
-// and raise SPEC_STATUS_NAN_INPUT).
+// p = softmax(logits / T_b) of every sampling row (b, u < T_b) is never stored: softmax_partial_kernel
+// takes each slice of kSmSlice elements to (max of x = l * (1 / T_b), sum of exp(x - max)), in a fixed
+// order, and the sampling passes form p from the logits and the row's merged partials as they read it
+// (ProbRow). A non-finite x stays out of the maximum and the sum; rows whose temperature is invalid have
+// no partials.
 constexpr int kSmThreads = 256;
 constexpr int kSmPer = 32;                       // elements per thread
 constexpr int kSmSlice = kSmThreads * kSmPer;    // elements per block
@@ -1047,11 +1113,6 @@ __device__ __forceinline__ bool sm_row(const int32_t* T_b, const int8_t* mode, i
   return mode[b] == SPEC_MODE_SAMPLE && u < seq_T(T_b, b, max_T);
 }
 
-__device__ __forceinline__ float sm_temperature(const float* temperature, int b) {
-  const float T = temperature ? temperature[b] : 1.f;
-  return (T > 0.f && isfinite(T)) ? T : 0.f;  // 0 = invalid
-}
-
 __global__ void __launch_bounds__(kSmThreads) softmax_partial_kernel(const float* logits, const float* temperature,
                                                                       const int32_t* T_b, const int8_t* mode,
                                                                       int max_T, int V, float2* part) {
@@ -1074,48 +1135,9 @@ __global__ void __launch_bounds__(kSmThreads) softmax_partial_kernel(const float
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < kSmPer; ++i)
-    if (isfinite(x[i])) sum += expf(x[i] - m);
+    if (isfinite(x[i])) sum += exp_nonpos(x[i] - m);
   sum = sm_block_reduce(sum, false, red);
   if (tid == 0) part[size_t(row) * nsl + s] = make_float2(m, sum);
-}
-
-__global__ void __launch_bounds__(kSmThreads) softmax_write_kernel(const float* logits, const float* temperature,
-                                                                    const int32_t* T_b, const int8_t* mode, int max_T,
-                                                                    int V, const float2* part, float* prob) {
-  const int s = blockIdx.x, row = blockIdx.y, nsl = gridDim.x, tid = threadIdx.x;
-  if (!sm_row(T_b, mode, max_T, row)) return;
-  const float T = sm_temperature(temperature, row / max_T);
-  const float* l = logits + size_t(row) * V;
-  float* p = prob + size_t(row) * V;
-  if (T == 0.f) {
-#pragma unroll
-    for (int i = 0; i < kSmPer; ++i) {
-      const int v = s * kSmSlice + i * kSmThreads + tid;
-      if (v < V) p[v] = NAN;
-    }
-    return;
-  }
-  const float inv = 1.f / T;
-  float x[kSmPer];
-#pragma unroll
-  for (int i = 0; i < kSmPer; ++i) {
-    const int v = s * kSmSlice + i * kSmThreads + tid;
-    x[i] = v < V ? l[v] * inv : 0.f;
-  }
-  // the row's maximum and sum from every slice's partial, in slice order (each thread the same way)
-  const float2* pr = part + size_t(row) * nsl;
-  float M = -INFINITY;
-  for (int j = 0; j < nsl; ++j) M = fmaxf(M, pr[j].x);
-  float S = 0.f;
-  for (int j = 0; j < nsl; ++j) {
-    const float2 q = pr[j];
-    if (q.x != -INFINITY) S += q.y * expf(q.x - M);
-  }
-#pragma unroll
-  for (int i = 0; i < kSmPer; ++i) {
-    const int v = s * kSmSlice + i * kSmThreads + tid;
-    if (v < V) p[v] = isfinite(x[i]) ? expf(x[i] - M) / S : NAN;
-  }
 }
 
 }  // namespace
@@ -1130,7 +1152,7 @@ extern "C" size_t spec_tree_verify_workspace_size(int32_t B, int32_t max_T, int3
   return total;
 }
 
-static int32_t verify_impl(const char* who, const float* target, float* prob, float2* sm_part, const float* temperature,
+static int32_t verify_impl(const char* who, const float* target, float2* sm_part, const float* temperature,
                            const float* draft_probs, const int32_t* q_row,
                                     const int32_t* tokens, const int32_t* parents, const int32_t* T_b,
                                     const int8_t* mode, uint64_t philox_key0, uint64_t philox_key1,
@@ -1156,7 +1178,9 @@ static int32_t verify_impl(const char* who, const float* target, float* prob, fl
   while (sl < kGreedySliceMax && rows * ((V + sl - 1) / sl) > kGreedyBlocksTarget) sl += kGreedySlice;
   VerifyArgs a;
   a.target = target;
-  a.prob = prob;
+  a.sm_part = sm_part;
+  a.temperature = temperature;
+  a.sm_nsl = int((V + kSmSlice - 1) / kSmSlice);
   a.draft = draft_probs;
   a.q_row = q_row;
   a.tokens = tokens;
@@ -1182,21 +1206,22 @@ static int32_t verify_impl(const char* who, const float* target, float* prob, fl
   a.status = status;
   if ((long long)a.n_greedy_blocks + a.n_workers >= (1LL << 31))
     return fail(SPEC_E_UNSUPPORTED, "%s: grid too large", who);
-  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target) | reinterpret_cast<uintptr_t>(draft_probs) |
-                                     reinterpret_cast<uintptr_t>(prob)) & 15) == 0;
+  const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target) | reinterpret_cast<uintptr_t>(draft_probs)) & 15) == 0;
   const dim3 grid(a.n_greedy_blocks + a.n_workers);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (prob) {  // sampling rows' probabilities from the logits first (same stream: the verify launch waits)
-    const dim3 sgrid(unsigned((V + kSmSlice - 1) / kSmSlice), unsigned(rows));
+  if (sm_part) {  // the sampling rows' softmax partials first (same stream: the verify launch waits)
+    const dim3 sgrid(unsigned(a.sm_nsl), unsigned(rows));
     hipLaunchKernelGGL(softmax_partial_kernel, sgrid, dim3(kSmThreads), 0, st, target, temperature, T_b, mode, max_T, V,
                        sm_part);
-    hipLaunchKernelGGL(softmax_write_kernel, sgrid, dim3(kSmThreads), 0, st, target, temperature, T_b, mode, max_T, V,
-                       sm_part, prob);
+    if (vec)
+      hipLaunchKernelGGL((verify_kernel<true, true>), grid, dim3(kThreads), 0, st, w, a);
+    else
+      hipLaunchKernelGGL((verify_kernel<false, true>), grid, dim3(kThreads), 0, st, w, a);
+  } else if (vec) {
+    hipLaunchKernelGGL((verify_kernel<true, false>), grid, dim3(kThreads), 0, st, w, a);
+  } else {
+    hipLaunchKernelGGL((verify_kernel<false, false>), grid, dim3(kThreads), 0, st, w, a);
   }
-  if (vec)
-    hipLaunchKernelGGL(verify_kernel<true>, grid, dim3(kThreads), 0, st, w, a);
-  else
-    hipLaunchKernelGGL(verify_kernel<false>, grid, dim3(kThreads), 0, st, w, a);
   return check_launch(who);
 }
 
@@ -1206,21 +1231,16 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
                                     uint64_t philox_offset, int32_t B, int32_t max_T, int32_t R, int32_t V,
                                     int32_t* accept_len, int32_t* accept_nodes, int32_t* out_tokens, uint32_t* status,
                                     void* ws, size_t ws_bytes, void* stream) {
-  return verify_impl("spec_tree_verify", target, nullptr, nullptr, nullptr, draft_probs, q_row, tokens, parents, T_b, mode, philox_key0,
+  return verify_impl("spec_tree_verify", target, nullptr, nullptr, draft_probs, q_row, tokens, parents, T_b, mode, philox_key0,
                      philox_key1, philox_offset, B, max_T, R, V, accept_len, accept_nodes, out_tokens, status, ws,
                      ws_bytes, stream);
 }
 
-// the logits entry point's workspace: the verify workspace, then the sampling rows' probabilities
-static size_t logits_prob_offset(int32_t B, int32_t max_T, int32_t V) {
+// the logits entry point's workspace: the verify workspace, then the slices' softmax partials
+static size_t logits_part_offset(int32_t B, int32_t max_T, int32_t V) {
   size_t total = 0;
   carve(nullptr, B, max_T, V, &total);
   return align_up(total, 256);
-}
-
-// ... and the slices' softmax partials after the probabilities
-static size_t logits_part_offset(int32_t B, int32_t max_T, int32_t V) {
-  return logits_prob_offset(B, max_T, V) + align_up(size_t(B) * max_T * V * sizeof(float), 256);
 }
 
 extern "C" size_t spec_tree_verify_logits_workspace_size(int32_t B, int32_t max_T, int32_t V) {
@@ -1243,9 +1263,8 @@ extern "C" int32_t spec_tree_verify_logits(const float* logits, const float* tem
   if ((long long)B * max_T > 65535) return fail(SPEC_E_UNSUPPORTED, "%s: B*max_T=%lld > 65535", who, (long long)B * max_T);
   const size_t need = spec_tree_verify_logits_workspace_size(B, max_T, V);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
-  const size_t off = logits_prob_offset(B, max_T, V);
-  float* prob = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
-  float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + logits_part_offset(B, max_T, V));
-  return verify_impl(who, logits, prob, part, temperature, draft_probs, q_row, tokens, parents, T_b, mode, philox_key0, philox_key1,
+  const size_t off = logits_part_offset(B, max_T, V);
+  float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + off);
+  return verify_impl(who, logits, part, temperature, draft_probs, q_row, tokens, parents, T_b, mode, philox_key0, philox_key1,
                      philox_offset, B, max_T, R, V, accept_len, accept_nodes, out_tokens, status, ws, off, stream);
 }
