@@ -167,6 +167,77 @@ __device__ __forceinline__ void lane_top2(const float* xs, int base, int hi, uin
   }
 }
 
+// Compare-exchange of two keys: a holds the larger afterwards.
+__device__ __forceinline__ void cas_key(uint64_t& a, uint64_t& b) {
+  const bool sw = b > a;
+  const uint64_t hi = sw ? b : a;
+  b = sw ? a : b;
+  a = hi;
+}
+
+// The four largest of two descending 4-lists, descending, into a: max(a[i], b[3 - i]) are the four
+// largest of the union and form a bitonic sequence, which two rounds of compare-exchange sort.
+__device__ __forceinline__ void top4_merge(uint64_t* a, const uint64_t* b) {
+  uint64_t m[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m[i] = a[i] > b[3 - i] ? a[i] : b[3 - i];
+  cas_key(m[0], m[2]);
+  cas_key(m[1], m[3]);
+  cas_key(m[0], m[1]);
+  cas_key(m[2], m[3]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = m[i];
+}
+
+// Two descending pairs merged into one descending 4-list (odd-even merge: heads, tails, then the
+// middle two).
+__device__ __forceinline__ void pair_merge(uint64_t a0, uint64_t a1, uint64_t b0, uint64_t b1, uint64_t* out) {
+  cas_key(a0, b0);
+  cas_key(a1, b1);
+  cas_key(b0, a1);
+  out[0] = a0;
+  out[1] = b0;
+  out[2] = a1;
+  out[3] = b1;
+}
+
+// Four largest keys of this thread's elements of one batch (those below `below` if BOUNDED), folded
+// into the descending cache c[0..4) (0 = none): each group of 8 elements is sorted down to its top
+// four by a fixed network (pairs, two pair merges, one 4-list merge; independent compare chains) and
+// merged into the cache one group at a time, which bounds the live registers.
+template <bool VEC, int EPL, bool BOUNDED>
+__device__ __forceinline__ void lane_top4(const float* xs, int base, int hi, uint64_t below, uint64_t* c) {
+  constexpr int G = 8;
+  const bool full = base + EPL * kRowThreads <= hi;
+#pragma unroll
+  for (int g0 = 0; g0 < EPL; g0 += G) {
+    uint64_t k[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int v = batch_token<VEC>(base, g0 + j);
+      uint64_t key = (full || v < hi) ? lp_key(xs[g0 + j], v) : 0ull;
+      if (BOUNDED) key = key < below ? key : 0ull;
+      k[j] = key;
+    }
+#pragma unroll
+    for (int j = 0; j < G; j += 2) cas_key(k[j], k[j + 1]);
+    uint64_t q0[4], q1[4];
+    pair_merge(k[0], k[1], k[2], k[3], q0);
+    pair_merge(k[4], k[5], k[6], k[7], q1);
+    top4_merge(q0, q1);
+    top4_merge(c, q0);
+  }
+}
+
+// The NC (2 or 4) largest keys of this thread's elements of one batch into the descending cache c.
+template <int NC, bool VEC, int EPL, bool BOUNDED>
+__device__ __forceinline__ void lane_top(const float* xs, int base, int hi, uint64_t below, uint64_t* c) {
+  if constexpr (NC == 4)
+    lane_top4<VEC, EPL, BOUNDED>(xs, base, hi, below, c);
+  else
+    lane_top2<VEC, EPL, BOUNDED>(xs, base, hi, below, c);
+}
+
 // ------------------------------------------------------------------ wave-wide selection
 // Wave maximum of a u32, uniform: DPP steps within each 16-lane row (fused into the max), the row
 // broadcasts carry rows 0-1 into 1 and 2-3 into 3, then 0-1 into 2-3, so lane 63 holds the maximum.
@@ -219,10 +290,13 @@ __device__ __forceinline__ Popped wave_pop(uint64_t* c) {
 
 // Block-wide top-k (k <= 8) of row[lo, hi) in rank order (0 = none) in out_key[0..k); with per_wave
 // each wave's own top k are returned instead (lane r holds the wave's r-th key) and out_key is unused.
-// xs holds the first batch (load_batch(row, lo, hi, xs)). Every lane keeps the two largest keys of
-// its own elements; each wave pops its k largest (a lane that gives up both refills them with its
+// xs holds the first batch (load_batch(row, lo, hi, xs)). Every lane keeps the NC largest keys of
+// its own elements; each wave pops its k largest (a lane that gives up all NC refills them with its
 // largest keys below the last one taken, so the pops are exact), and wave 0 pops the k best of the
-// waves' lists. xs is consumed (free after the lane pass).
+// waves' lists. NC is 4 with 16 elements per thread and batch: a lane holds two of a wave's first seven
+// picks about once in four waves (a birthday collision over 64 lanes), four of them about once in ten
+// thousand, and every refill re-reads the slice batch after batch. With 8 elements per thread (short
+// rows, one batch) the cheaper two-key lane pass wins. xs is consumed (free after the lane pass).
 template <bool VEC, int EPL>
 __device__ __forceinline__ uint64_t block_slice_topk(const float* row, int lo, int hi, int k, bool per_wave,
                                                      float* xs, uint64_t* out_key) {
@@ -230,12 +304,15 @@ __device__ __forceinline__ uint64_t block_slice_topk(const float* row, int lo, i
   constexpr int kBatch = EPL * kRowThreads;
   __shared__ uint64_t wk[NWV * kMaxTopk];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  uint64_t c[2] = {0, 0};
+  constexpr int NC = EPL >= 16 ? 4 : 2;
+  uint64_t c[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) c[i] = 0;
   for (int base = lo; base < hi; base += kBatch) {
     float nxt[EPL];  // the next batch's loads are in flight while this one is reduced
     const bool more = base + kBatch < hi;
     if (more) load_batch<VEC, EPL>(row, base + kBatch, hi, nxt);
-    lane_top2<VEC, EPL, false>(xs, base, hi, 0, c);
+    lane_top<NC, VEC, EPL, false>(xs, base, hi, 0, c);
     if (more) {
 #pragma unroll
       for (int j = 0; j < EPL; ++j) xs[j] = nxt[j];
@@ -243,15 +320,15 @@ __device__ __forceinline__ uint64_t block_slice_topk(const float* row, int lo, i
   }
   uint64_t mine = 0;
   for (int r = 0; r < k; ++r) {
-    const Popped p = wave_pop<2>(c);
+    const Popped p = wave_pop<NC>(c);
     if (lane == r) mine = p.key;
     if (lane == p.lane && p.key != 0 && c[0] == 0 && r + 1 < k) {
-      // this lane gave both cached keys: refill with its two largest below the one just taken
+      // this lane gave all its cached keys: refill with its NC largest below the one just taken
       // (re-read from memory, so the batch's registers are free during the pops)
       for (int base = lo; base < hi; base += kBatch) {
         float ys[EPL];
         load_batch<VEC, EPL>(row, base, hi, ys);
-        lane_top2<VEC, EPL, true>(ys, base, hi, p.key, c);
+        lane_top<NC, VEC, EPL, true>(ys, base, hi, p.key, c);
       }
     }
   }
