@@ -199,9 +199,10 @@ def test_tree_build_deep(V, fused):
     check_build(w, host, oracle_trees(w))
 
 
-# large vocabularies (slices of one or several load batches, up to four candidates per lane in the
-# row merge) with rows that make one thread hold several of a slice's best keys
-@pytest.mark.parametrize("V", [128256, 300000, 300001])
+# vocabularies from 8-element lanes (two cached keys per lane) to large ones (16-element lanes, four
+# cached keys, slices of one or several load batches, up to four candidates per lane in the row merge)
+# with rows that make one thread hold several of a slice's best keys, so its cache runs dry mid-selection
+@pytest.mark.parametrize("V", [4099, 32000, 128256, 300000, 300001])
 def test_tree_build_structured_rows(V):
     rng = np.random.default_rng(V)
     B = 2
