@@ -24,7 +24,14 @@ Readings taken where the pages leave the rule open:
   closed under taking parents and parents[i] < i;
 * draft log-probs are clamped: NaN -> -inf, values >= 0 (including -0) -> +0;
 * scores are fp64: score(child) = score(parent) + double(logprob), with
-  score(root) = 0.
+  score(root) = 0;
+* truncated draft vocabulary (SGLang page, "EAGLE-2 Decoding via
+  Frequency-Ranked Speculative Sampling": the draft's LM head covers only a
+  high-frequency token subset, given as a token map): the draft rows hold
+  V_draft entries, entry i standing for token token_map[i]; the ranking above
+  runs on the draft index i (ties to the smaller index, i.e. the
+  higher-ranked token of the subset) and a node's token is token_map[i].
+  Without a map the index is the token.
 
 Mask (tanhdev "Tech Radar: SGLang EAGLE-2", section 2 "Dynamic Tree-Attention
 Verification": node i attends exactly to its ancestors and itself; section 5
@@ -94,13 +101,16 @@ def draft_row_index(step: int, slot: int, max_topk: int) -> int:
     return 1 + (step - 2) * max_topk + slot
 
 
-def build_tree(rows, root_token: int, k: int, D: int, N: int, max_topk: int) -> BuiltTree:
+def build_tree(rows, root_token: int, k: int, D: int, N: int, max_topk: int, token_map=None) -> BuiltTree:
     """Build one sequence's draft tree.
 
     ``rows`` is the per-sequence draft log-prob array [R, V] laid out as in
     ``draft_row_index``: row 0 is the root's row (step 1), and step d's row for
-    frontier slot f is ``draft_row_index(d, f, max_topk)``.
+    frontier slot f is ``draft_row_index(d, f, max_topk)``. With ``token_map``
+    (int [V]) row entry i stands for token ``token_map[i]`` (truncated draft
+    vocabulary); ranking uses i, node tokens are mapped.
     """
+    tok_of = (lambda i: int(i)) if token_map is None else (lambda i: int(token_map[i]))
     V = rows.shape[-1]
     if not (1 <= k <= V and D >= 1):
         raise ValueError("need 1 <= topk <= V and depth >= 1")
@@ -111,8 +121,8 @@ def build_tree(rows, root_token: int, k: int, D: int, N: int, max_topk: int) -> 
     frontier_tokens: List[List[int]] = []
 
     # step 1: the root's top-k children
-    for rank, (tok, lp) in enumerate(row_topk(rows[draft_row_index(1, 0, max_topk)], k)):
-        pool.append(PoolEntry(tok, -1, 0.0 + lp, 1, frontier_slot=rank))
+    for rank, (idx, lp) in enumerate(row_topk(rows[draft_row_index(1, 0, max_topk)], k)):
+        pool.append(PoolEntry(tok_of(idx), -1, 0.0 + lp, 1, frontier_slot=rank))
     frontier = list(range(k))
     frontier_tokens.append([pool[i].token for i in frontier])
 
@@ -121,8 +131,8 @@ def build_tree(rows, root_token: int, k: int, D: int, N: int, max_topk: int) -> 
         base = len(pool)
         for f, parent in enumerate(frontier):
             row = rows[draft_row_index(d, f, max_topk)]
-            for tok, lp in row_topk(row, k):
-                pool.append(PoolEntry(tok, parent, pool[parent].score + lp, d))
+            for idx, lp in row_topk(row, k):
+                pool.append(PoolEntry(tok_of(idx), parent, pool[parent].score + lp, d))
         cands = list(range(base, base + k * k))
         ranked = sorted(cands, key=lambda i: (-pool[i].score, i))
         frontier = ranked[:k]

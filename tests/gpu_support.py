@@ -44,7 +44,7 @@ def run_pipeline(w, compact=False):
 
 def oracle_trees(w):
     return [build_tree(w.draft_logprobs[b], int(w.root_tokens[b]), int(w.topk[b]), int(w.depth[b]),
-                       int(w.num_draft[b]), w.max_topk) for b in range(w.B)]
+                       int(w.num_draft[b]), w.max_topk, token_map=w.token_map) for b in range(w.B)]
 
 
 def check_build(w, host, trees):

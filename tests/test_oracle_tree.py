@@ -158,3 +158,64 @@ def test_mask_invalid_parent_becomes_root_child():
     assert status == STATUS_INVALID_PARENT
     assert [int(x) for x in anc] == [0, 0b001, 0b010, 0b101]
     assert depth.tolist() == [0, 1, 1, 2]
+
+
+# ---- truncated draft vocabulary (token map)
+def _same_tree(a, b):
+    assert a.tokens.tolist() == b.tokens.tolist()
+    assert a.parents.tolist() == b.parents.tolist()
+    assert a.depth.tolist() == b.depth.tolist()
+    assert [int(x) for x in a.anc] == [int(x) for x in b.anc]
+    assert a.q_row.tolist() == b.q_row.tolist()
+    assert a.frontier_tokens == b.frontier_tokens
+
+
+def _scatter_rows(rows, token_map, V):
+    full = np.full(rows.shape[:-1] + (V,), -np.inf, dtype=np.float32)
+    full[..., token_map] = rows
+    return full
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_token_map_identity_changes_nothing(seed):
+    w = make_workload(B=1, Hq=2, Hkv=1, d=64, prefix=8, topk=4, depth=4, num_draft=30, V=300, seed=seed)
+    plain = build_tree(w.draft_logprobs[0], 5, 4, 4, 30, 4)
+    mapped = build_tree(w.draft_logprobs[0], 5, 4, 4, 30, 4, token_map=np.arange(300))
+    _same_tree(plain, mapped)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_token_map_monotone_equals_full_vocabulary_with_ties(seed):
+    """A subset listed in increasing token order ranks ties the same way by index and by token, so the
+    truncated build equals the full-vocabulary build on rows that are -inf outside the subset, even with
+    ties (log-probs quantised to halves)."""
+    rng = np.random.default_rng(seed)
+    V, Vd, k, D, N = 1000, 120, 5, 4, 50
+    token_map = np.sort(rng.choice(V, size=Vd, replace=False))
+    rows = np.round(rng.normal(-6.0, 2.0, size=(1 + (D - 1) * k, Vd)) * 2.0) / 2.0
+    rows = np.minimum(rows, 0.0).astype(np.float32)
+    t_map = build_tree(rows, 7, k, D, N, k, token_map=token_map)
+    t_full = build_tree(_scatter_rows(rows, token_map, V), 7, k, D, N, k)
+    _same_tree(t_map, t_full)
+    assert set(t_map.tokens[1:].tolist()) <= set(token_map.tolist())
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_token_map_random_order_equals_full_vocabulary_without_ties(seed):
+    w = make_workload(B=1, Hq=2, Hkv=1, d=64, prefix=8, topk=6, depth=5, num_draft=64, V=4000, draft_vocab=512,
+                      seed=seed)
+    assert w.draft_logprobs.shape[-1] == 512 and len(set(w.token_map.tolist())) == 512
+    assert not (np.diff(w.token_map) > 0).all()  # not in token order
+    t_map = build_tree(w.draft_logprobs[0], 3, 6, 5, 64, 6, token_map=w.token_map)
+    t_full = build_tree(_scatter_rows(w.draft_logprobs[0], w.token_map, 4000), 3, 6, 5, 64, 6)
+    _same_tree(t_map, t_full)
+
+
+def test_truncated_workload_draft_probabilities():
+    w = make_workload(B=2, Hq=2, Hkv=1, d=64, prefix=8, topk=4, depth=3, num_draft=12, V=2000, draft_vocab=300,
+                      verify="sample", seed=11)
+    outside = np.setdiff1d(np.arange(2000), w.token_map)
+    assert (w.draft_probs[:, :, outside] == 0).all()
+    np.testing.assert_allclose(w.draft_probs.sum(axis=-1), 1.0, rtol=1e-5)
+    np.testing.assert_allclose(np.exp(w.draft_logprobs.astype(np.float64)), w.draft_probs[:, :, w.token_map],
+                               rtol=1e-6, atol=1e-12)

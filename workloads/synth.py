@@ -19,7 +19,12 @@ does not shift the others):
 * target rows ``[B, T_max, V]``: fp32 logits ~ N(0, 3) for greedy sequences;
   for sampling sequences fp64 softmax(logits / temperature), stored fp32 (the
   logits themselves are kept as ``target_logits`` for every row);
-* root tokens uniform in [0, V); Philox key = (seed, 0x5EED), offset 0.
+* root tokens uniform in [0, V); Philox key = (seed, 0x5EED), offset 0;
+* truncated draft vocabulary (``draft_vocab`` = V_d < V): a token map of V_d
+  distinct token ids drawn without replacement from [0, V) in random order
+  (a frequency ranking has no relation to token ids); the draft rows hold V_d
+  entries (logits ~ N(0, 2) over the subset) and the draft probabilities are
+  scattered to the full vocabulary (zero outside the subset).
 
 Nothing here builds trees, masks, attends or verifies.
 """
@@ -105,6 +110,7 @@ class Workload:
     compact: bool = False
     extra: dict = field(default_factory=dict)
     target_logits: np.ndarray = None  # float32 [B, max_T, V]: the logits every target row was formed from
+    token_map: Optional[np.ndarray] = None  # int32 [V_d]: draft row entry i stands for token token_map[i]
 
     @property
     def R(self) -> int:
@@ -156,6 +162,7 @@ def make_workload(
     max_topk: Optional[int] = None,
     max_depth: Optional[int] = None,
     extra_pages: int = 0,
+    draft_vocab: Optional[int] = None,
 ) -> Workload:
     """Draw one workload. ``prefix``/``topk``/``depth``/``num_draft`` are an int,
     an inclusive (lo, hi) tuple range, or an explicit per-sequence list."""
@@ -214,13 +221,24 @@ def make_workload(
     # ---- draft rows ----------------------------------------------------
     R = 1 + (max_depth - 1) * max_topk
     r_draft = np.random.Generator(np.random.PCG64(s_draft))
-    draft_logprobs = np.empty((B, R, V), dtype=np.float32)
-    draft_probs = np.empty((B, R, V), dtype=np.float32)
+    token_map = None
+    Vd = V
+    if draft_vocab is not None and int(draft_vocab) != V:
+        Vd = int(draft_vocab)
+        if not (max_topk <= Vd < V):
+            raise ValueError("draft_vocab must be in [max_topk, V)")
+        r_map = np.random.Generator(np.random.PCG64(ss.spawn(1)[0]))
+        token_map = r_map.choice(V, size=Vd, replace=False).astype(np.int32)
+    draft_logprobs = np.empty((B, R, Vd), dtype=np.float32)
+    draft_probs = np.zeros((B, R, V), dtype=np.float32)
     for b in range(B):
-        z = r_draft.standard_normal((R, V), dtype=np.float32) * np.float32(2.0)
+        z = r_draft.standard_normal((R, Vd), dtype=np.float32) * np.float32(2.0)
         lp = _fp64_log_softmax(z)
         draft_logprobs[b] = lp.astype(np.float32)
-        draft_probs[b] = np.exp(lp).astype(np.float32)
+        if token_map is None:
+            draft_probs[b] = np.exp(lp).astype(np.float32)
+        else:
+            draft_probs[b][:, token_map] = np.exp(lp).astype(np.float32)
 
     # ---- target rows ---------------------------------------------------
     r_t = np.random.Generator(np.random.PCG64(s_target))
@@ -245,13 +263,14 @@ def make_workload(
         k_pages=k_pages, v_pages=v_pages, q=q, root_tokens=root_tokens,
         draft_logprobs=draft_logprobs, draft_probs=draft_probs, target=target, target_logits=target_logits,
         philox_key=(int(seed) & 0xFFFFFFFFFFFFFFFF, 0x5EED), philox_offset=0,
-        sm_scale=float(1.0 / np.sqrt(d)), compact=compact,
+        sm_scale=float(1.0 / np.sqrt(d)), compact=compact, token_map=token_map,
     )
 
 
-def from_spec(spec: WorkloadSpec, seed: Optional[int] = None) -> Workload:
-    """Draw the named workload at full size."""
+def from_spec(spec: WorkloadSpec, seed: Optional[int] = None, draft_vocab: Optional[int] = None) -> Workload:
+    """Draw the named workload at full size (optionally with a truncated draft vocabulary)."""
     return make_workload(
+        draft_vocab=draft_vocab,
         name=spec.name, B=spec.batch, Hq=spec.q_heads, Hkv=spec.kv_heads, d=spec.head_dim,
         prefix=spec.prefix, topk=spec.topk, depth=spec.depth, num_draft=spec.num_draft,
         V=spec.vocab, verify=spec.verify, temperature=spec.temperature if spec.verify != "greedy" else 1.0,
