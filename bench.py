@@ -64,7 +64,7 @@ def algorithmic_work(w, host):
             ver_rows += len(set(int(p) for p in par))  # q rows of internal nodes
     verify_bytes = ver_rows * V * 4
     build_rows = int(sum(1 + (int(w.depth[b]) - 1) * int(w.topk[b]) for b in range(B)))
-    build_bytes = build_rows * V * 4
+    build_bytes = build_rows * w.draft_logprobs.shape[-1] * 4  # draft rows: V, or the truncated vocabulary
     return dict(attn_bytes=attn_bytes, attn_flops=attn_flops, verify_bytes=verify_bytes, build_bytes=build_bytes)
 
 
@@ -133,7 +133,7 @@ def cpu_baseline(w, seconds):
     t0 = time.perf_counter()
     while True:
         trees = [oracle.tree.build_tree(w.draft_logprobs[b], int(w.root_tokens[b]), int(w.topk[b]), int(w.depth[b]),
-                                        int(w.num_draft[b]), w.max_topk) for b in range(w.B)]
+                                        int(w.num_draft[b]), w.max_topk, token_map=w.token_map) for b in range(w.B)]
         par = np.full((w.B, w.max_T), -1, dtype=np.int32)
         for b, t in enumerate(trees):
             par[b, : len(t.parents)] = t.parents
@@ -171,6 +171,9 @@ def main():
     ap.add_argument("--verify-logits", action="store_true",
                     help="verify with spec_tree_verify_logits (sampling distributions formed from the target logits and "
                          "temperatures inside the library) instead of supplied probabilities")
+    ap.add_argument("--draft-vocab", type=int, default=None, metavar="N",
+                    help="truncated draft vocabulary: draft rows over N tokens with a token map into the target's "
+                         "vocabulary (frequency-ranked speculative sampling)")
     ap.add_argument("--details", default=None, help="write per-stage details as JSON to this path")
     ap.add_argument("--profile-kernels", type=int, default=0, metavar="N",
                     help="profiling mode (run under rocprofv3): N eager attention calls over the replicas, then one "
@@ -192,7 +195,7 @@ def main():
     cfg_key = int(args.config) if args.config.isdigit() else args.config
     spec = get_config(cfg_key)
     eprint(f"[bench] workload {spec.name}: generating inputs")
-    w = from_spec(spec)
+    w = from_spec(spec, draft_vocab=args.draft_vocab)
     dw0 = DeviceWorkload(w, logits=args.verify_logits)
     per_replica = sum(t.numel() * t.element_size() for t in vars(dw0).values() if hasattr(t, "element_size"))
     R = max(2, int(np.ceil(args.rotate_gib * 2**30 / per_replica)))
@@ -311,7 +314,8 @@ def main():
                    "prefix": int(w.prefix_lens.max()), "draft_tokens": int(w.num_draft.max()), "vocab": w.V,
                    "step": "tree build + tree attention + verify" + (" + KV compaction" if compact else ""),
                    "replicas": R, "graphs": not args.eager,
-                   "verify_input": "target logits + temperature" if args.verify_logits else "target probabilities"},
+                   "verify_input": "target logits + temperature" if args.verify_logits else "target probabilities",
+                   "draft_vocab": int(w.draft_logprobs.shape[-1])},
         "gpu_ms_per_step": round(gpu_ms, 5),
         "stage_us": {k: round(v * 1e3, 3) for k, v in stage_ms.items()},
         "attn_verify_draft_tokens_per_s": round(n_draft / ((stage_ms["attention"] + stage_ms["verify"]) * 1e-3), 1),

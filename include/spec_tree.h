@@ -136,6 +136,29 @@ int32_t spec_tree_build_step_finish(void* ws, size_t ws_bytes, int32_t step, con
                                     int32_t* tokens, int32_t* parents, int32_t* depth_out, uint64_t* anc_mask,
                                     int32_t* q_row, void* stream);
 
+/* Truncated draft vocabulary - SGLang "Speculative Decoding" page, section
+ * "EAGLE-2 Decoding via Frequency-Ranked Speculative Sampling" (the draft's
+ * LM head covers only a high-frequency token subset, passed as a token map).
+ * The same calls with the draft rows over that subset: V is the subset size
+ * (the row length) and token_map (device int32 [V]) gives the token that row
+ * entry i stands for. Ranking runs on the entry index exactly as above (ties
+ * to the smaller index, i.e. the higher-ranked token of the subset); every
+ * token the build writes (frontier_tokens, tokens) is token_map[i]. Map
+ * values are copied as given (verification checks tokens against its own
+ * vocabulary). token_map NULL: identical to the calls without _map. The
+ * draft probabilities that spec_tree_verify reads stay over the target's
+ * vocabulary (zero outside the subset). Errors: those of the plain calls. */
+int32_t spec_tree_build_step_map(void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
+                                 const int32_t* token_map, int64_t seq_stride, const int32_t* topk,
+                                 const int32_t* depth, int32_t B, int32_t max_topk, int32_t max_depth, int32_t V,
+                                 int32_t* frontier_tokens, void* stream);
+int32_t spec_tree_build_step_finish_map(void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
+                                        const int32_t* token_map, int64_t seq_stride, const int32_t* topk,
+                                        const int32_t* depth, int32_t B, int32_t max_topk, int32_t max_depth,
+                                        int32_t V, int32_t* frontier_tokens, const int32_t* root_tokens,
+                                        const int32_t* num_draft, int32_t max_T, int32_t* tokens, int32_t* parents,
+                                        int32_t* depth_out, uint64_t* anc_mask, int32_t* q_row, void* stream);
+
 /* ----------------------------------------------------------------------------
  * Tree mask - tanhdev "Tech Radar: SGLang EAGLE-2", section 2 "Dynamic
  * Tree-Attention Verification" (node i attends exactly to its ancestors and

@@ -135,3 +135,19 @@ def test_full_verify_from_logits(cfg):
         assert int(host["status"][b]) == st, f"status b={b}"
     del dw, step
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", [2, 3], ids=lambda i: get_config(i).name)
+def test_full_pipeline_truncated_draft_vocabulary(cfg):
+    """Frequency-ranked drafting: draft rows over a 32768-token subset with a token map, then attention and
+    verification over the full 128256-token vocabulary (draft probabilities zero outside the subset)."""
+    spec = get_config(cfg)
+    log(f"[full] generating {spec.name} with a 32768-token draft vocabulary")
+    w = from_spec(spec, draft_vocab=32768)
+    dw, step, host = run_pipeline(w, compact=False)
+    trees = oracle_trees(w)
+    check_build(w, host, trees)
+    log(f"[full] oracle verify on {spec.name} (truncated draft vocabulary)")
+    check_verify(w, host, trees)
+    del dw, step
+    torch.cuda.empty_cache()

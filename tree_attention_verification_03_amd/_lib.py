@@ -22,6 +22,10 @@ SIGNATURES = {
     "spec_tree_build_step": (c_i32, [c_vp, c_sz, c_i32, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "spec_tree_build_step_finish": (c_i32, [c_vp, c_sz, c_i32, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                             c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "spec_tree_build_step_map": (c_i32, [c_vp, c_sz, c_i32, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                         c_vp, c_vp]),
+    "spec_tree_build_step_finish_map": (c_i32, [c_vp, c_sz, c_i32, c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_i32, c_i32,
+                                                c_i32, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "spec_tree_build_finish": (c_i32, [c_vp, c_sz, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
                                        c_vp, c_vp, c_vp, c_vp]),
     "spec_tree_mask": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),

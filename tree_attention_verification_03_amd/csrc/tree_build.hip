@@ -95,6 +95,10 @@ __device__ __forceinline__ float key_value(uint64_t key) {
 
 __device__ __forceinline__ int key_token(uint64_t key) { return int(0xffffffffu - uint32_t(key)); }
 
+// A draft-row index as a token: through the token map of a truncated draft vocabulary (entry i of a
+// row stands for token map[i]), or the index itself without a map.
+__device__ __forceinline__ int map_token(const int32_t* map, int idx) { return (map && idx >= 0) ? map[idx] : idx; }
+
 // Element j of a thread in the batch that starts at `base`: VEC -> base + 4 * tid + 4 * kRowThreads *
 // (j / 4) + j % 4, scalar -> base + tid + kRowThreads * j (both visit a thread's tokens in increasing
 // order).
@@ -500,19 +504,21 @@ __device__ __forceinline__ void finish_sequence(const BuildWs& w, int P, int b, 
 // pops of their scores' order keys, where the lowest lane wins ties.
 __device__ __forceinline__ void step_children(const BuildWs& w, int P, int b, int step, int k, int base,
                                               int max_topk, const uint64_t* top, const double* fsc_s,
-                                              const int* cpar, int32_t* frontier_tokens) {
+                                              const int* cpar, const int32_t* token_map, int32_t* frontier_tokens) {
   const int lane = threadIdx.x & (kWave - 1);
   {
     const int n = k * k;
     const int r = lane / k, c = lane - r * k;
     double sc = 0.0;
     uint64_t key = 0, sk = 0;
+    int tok = -1;
     if (lane < n) {
       key = top[r * kMaxTopk + c];
+      tok = map_token(token_map, key_token(key));
       sc = fsc_s[r] + double(key_value(key));
       sk = f64_order_key(sc + 0.0);  // no NaN; +0.0 folds -0 into +0
       const size_t e = size_t(b) * P + base + lane;
-      w.tok[e] = key_token(key);
+      w.tok[e] = tok;
       w.par[e] = cpar[r];
       w.depth[e] = step;
       w.score[e] = sc;
@@ -527,7 +533,7 @@ __device__ __forceinline__ void step_children(const BuildWs& w, int P, int b, in
       if (rank >= 0) {
         w.frontier[b * max_topk + rank] = base + lane;
         w.fscore[b * max_topk + rank] = sc;
-        frontier_tokens[b * max_topk + rank] = key_token(key);
+        frontier_tokens[b * max_topk + rank] = tok;
       }
     }
   }
@@ -546,7 +552,8 @@ __global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, i
                                                                   int64_t seq_stride, const int32_t* topk,
                                                                   const int32_t* depth, int max_topk, int max_depth,
                                                                   int V, int slice, int per_wave, int early_k,
-                                                                  int32_t* frontier_tokens, FinishArgs fa) {
+                                                                  int32_t* frontier_tokens, const int32_t* token_map,
+                                                                  FinishArgs fa) {
   constexpr int NWV = kRowThreads / kWave;
   __shared__ uint64_t keys[kMaxTopk];
   __shared__ uint64_t top[kMaxTopk * kMaxTopk];  // [row][rank]
@@ -649,7 +656,7 @@ __global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, i
       if (c < k) {
         const size_t e = size_t(b) * P + c;
         const double sc = 0.0 + double(key_value(top[c]));
-        tok = key_token(top[c]);
+        tok = map_token(token_map, key_token(top[c]));
         w.tok[e] = tok;
         w.par[e] = -1;
         w.depth[e] = 1;
@@ -661,7 +668,7 @@ __global__ void __launch_bounds__(kRowThreads, 5) build_step_kernel(BuildWs w, i
       frontier_tokens[b * max_topk + c] = tok;
     }
   } else if (wave == 0) {
-    step_children(w, P, b, step, k, base, max_topk, top, fsc_s, cpar, frontier_tokens);
+    step_children(w, P, b, step, k, base, max_topk, top, fsc_s, cpar, token_map, frontier_tokens);
   }
   if (fa.tokens && step == D) {  // the sequence's last step: rerank now (its pool is complete)
     wait_global_stores();
@@ -702,7 +709,7 @@ namespace spectree {
 namespace {
 
 int32_t launch_step(const char* who, void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
-                    int64_t seq_stride, const int32_t* topk, const int32_t* depth, int32_t B, int32_t max_topk,
+                    const int32_t* token_map, int64_t seq_stride, const int32_t* topk, const int32_t* depth, int32_t B, int32_t max_topk,
                     int32_t max_depth, int32_t V, int32_t* frontier_tokens, const FinishArgs& fa, void* stream) {
   int32_t rc = check_build(who, B, max_topk, max_depth);
   if (rc != SPEC_OK) return rc;
@@ -754,7 +761,7 @@ int32_t launch_step(const char* who, void* ws, size_t ws_bytes, int32_t step, co
   const bool vec = (V % 4 == 0) && (seq_stride % 4 == 0) && ((reinterpret_cast<uintptr_t>(draft_logprobs) & 15) == 0);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kRowThreads), 0, st, w, P, step, draft_logprobs, seq_stride, topk, depth,
-                       max_topk, max_depth, V, slice, per_wave, early_k, frontier_tokens, fa);
+                       max_topk, max_depth, V, slice, per_wave, early_k, frontier_tokens, token_map, fa);
   };
   if (vec) {
     if (epl == 8) go(build_step_kernel<true, 8>);
@@ -776,8 +783,30 @@ extern "C" int32_t spec_tree_build_step(void* ws, size_t ws_bytes, int32_t step,
                                         int32_t max_topk, int32_t max_depth, int32_t V, int32_t* frontier_tokens,
                                         void* stream) {
   const FinishArgs none{};
-  return launch_step("spec_tree_build_step", ws, ws_bytes, step, draft_logprobs, seq_stride, topk, depth, B, max_topk,
-                     max_depth, V, frontier_tokens, none, stream);
+  return launch_step("spec_tree_build_step", ws, ws_bytes, step, draft_logprobs, nullptr, seq_stride, topk, depth, B,
+                     max_topk, max_depth, V, frontier_tokens, none, stream);
+}
+
+extern "C" int32_t spec_tree_build_step_map(void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
+                                            const int32_t* token_map, int64_t seq_stride, const int32_t* topk,
+                                            const int32_t* depth, int32_t B, int32_t max_topk, int32_t max_depth,
+                                            int32_t V, int32_t* frontier_tokens, void* stream) {
+  const FinishArgs none{};
+  return launch_step("spec_tree_build_step_map", ws, ws_bytes, step, draft_logprobs, token_map, seq_stride, topk,
+                     depth, B, max_topk, max_depth, V, frontier_tokens, none, stream);
+}
+
+static int32_t step_finish(const char* who, void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
+                           const int32_t* token_map, int64_t seq_stride, const int32_t* topk, const int32_t* depth,
+                           int32_t B, int32_t max_topk, int32_t max_depth, int32_t V, int32_t* frontier_tokens,
+                           const int32_t* root_tokens, const int32_t* num_draft, int32_t max_T, int32_t* tokens,
+                           int32_t* parents, int32_t* depth_out, uint64_t* anc_mask, int32_t* q_row, void* stream) {
+  if (max_T < 2 || max_T > 65) return fail(SPEC_E_UNSUPPORTED, "%s: max_T=%d not in [2, 65]", who, max_T);
+  if (!root_tokens || !num_draft || !tokens || !parents || !depth_out || !anc_mask || !q_row)
+    return fail(SPEC_E_INVAL, "%s: null pointer", who);
+  const FinishArgs fa{root_tokens, num_draft, max_T, tokens, parents, depth_out, anc_mask, q_row};
+  return launch_step(who, ws, ws_bytes, step, draft_logprobs, token_map, seq_stride, topk, depth, B, max_topk,
+                     max_depth, V, frontier_tokens, fa, stream);
 }
 
 extern "C" int32_t spec_tree_build_step_finish(void* ws, size_t ws_bytes, int32_t step, const float* draft_logprobs,
@@ -787,13 +816,22 @@ extern "C" int32_t spec_tree_build_step_finish(void* ws, size_t ws_bytes, int32_
                                                const int32_t* num_draft, int32_t max_T, int32_t* tokens,
                                                int32_t* parents, int32_t* depth_out, uint64_t* anc_mask,
                                                int32_t* q_row, void* stream) {
-  const char* who = "spec_tree_build_step_finish";
-  if (max_T < 2 || max_T > 65) return fail(SPEC_E_UNSUPPORTED, "%s: max_T=%d not in [2, 65]", who, max_T);
-  if (!root_tokens || !num_draft || !tokens || !parents || !depth_out || !anc_mask || !q_row)
-    return fail(SPEC_E_INVAL, "%s: null pointer", who);
-  const FinishArgs fa{root_tokens, num_draft, max_T, tokens, parents, depth_out, anc_mask, q_row};
-  return launch_step(who, ws, ws_bytes, step, draft_logprobs, seq_stride, topk, depth, B, max_topk, max_depth, V,
-                     frontier_tokens, fa, stream);
+  return step_finish("spec_tree_build_step_finish", ws, ws_bytes, step, draft_logprobs, nullptr, seq_stride, topk,
+                     depth, B, max_topk, max_depth, V, frontier_tokens, root_tokens, num_draft, max_T, tokens, parents,
+                     depth_out, anc_mask, q_row, stream);
+}
+
+extern "C" int32_t spec_tree_build_step_finish_map(void* ws, size_t ws_bytes, int32_t step,
+                                                   const float* draft_logprobs, const int32_t* token_map,
+                                                   int64_t seq_stride, const int32_t* topk, const int32_t* depth,
+                                                   int32_t B, int32_t max_topk, int32_t max_depth, int32_t V,
+                                                   int32_t* frontier_tokens, const int32_t* root_tokens,
+                                                   const int32_t* num_draft, int32_t max_T, int32_t* tokens,
+                                                   int32_t* parents, int32_t* depth_out, uint64_t* anc_mask,
+                                                   int32_t* q_row, void* stream) {
+  return step_finish("spec_tree_build_step_finish_map", ws, ws_bytes, step, draft_logprobs, token_map, seq_stride,
+                     topk, depth, B, max_topk, max_depth, V, frontier_tokens, root_tokens, num_draft, max_T, tokens,
+                     parents, depth_out, anc_mask, q_row, stream);
 }
 
 extern "C" int32_t spec_tree_build_finish(void* ws, size_t ws_bytes, const int32_t* root_tokens, const int32_t* topk,

@@ -70,15 +70,26 @@ def zeroed_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 # ------------------------------------------------------------------ tree build
-def spec_tree_build_step(ws: torch.Tensor, step: int, draft_logprobs: torch.Tensor, topk: torch.Tensor,
-                         depth: torch.Tensor, max_topk: int, max_depth: int, frontier_tokens: torch.Tensor):
-    """draft_logprobs: fp32 [B, F, V] view (rows contiguous; any batch stride)."""
+def _draft_rows(draft_logprobs, step, max_topk):
     _dev(draft_logprobs, torch.float32, "draft_logprobs", contiguous=False)
     B, F, V = draft_logprobs.shape
     if draft_logprobs.stride(2) != 1 or (F > 1 and draft_logprobs.stride(1) != V):
         raise ValueError("draft_logprobs rows must be contiguous [.., F, V]")
     if F < (1 if step == 1 else max_topk):
         raise ValueError(f"step {step} needs {1 if step == 1 else max_topk} draft rows per sequence, got {F}")
+    return B, V
+
+
+def _token_map(token_map, V):
+    _dev(token_map, torch.int32, "token_map")
+    if token_map.numel() != V:
+        raise ValueError(f"token_map has {token_map.numel()} entries, the draft rows {V}")
+
+
+def spec_tree_build_step(ws: torch.Tensor, step: int, draft_logprobs: torch.Tensor, topk: torch.Tensor,
+                         depth: torch.Tensor, max_topk: int, max_depth: int, frontier_tokens: torch.Tensor):
+    """draft_logprobs: fp32 [B, F, V] view (rows contiguous; any batch stride)."""
+    B, V = _draft_rows(draft_logprobs, step, max_topk)
     _dev(topk, torch.int32, "topk")
     _dev(depth, torch.int32, "depth")
     _dev(frontier_tokens, torch.int32, "frontier_tokens")
@@ -89,27 +100,61 @@ def spec_tree_build_step(ws: torch.Tensor, step: int, draft_logprobs: torch.Tens
     check(rc, "spec_tree_build_step")
 
 
-def spec_tree_build_step_finish(ws: torch.Tensor, step: int, draft_logprobs: torch.Tensor, topk: torch.Tensor,
-                                depth: torch.Tensor, max_topk: int, max_depth: int, frontier_tokens: torch.Tensor,
-                                root_tokens, num_draft, max_T, tokens, parents, depth_out, anc_mask, q_row):
-    """Step ``step`` plus the finish of the sequences whose depth is ``step`` (one launch)."""
-    _dev(draft_logprobs, torch.float32, "draft_logprobs", contiguous=False)
-    B, F, V = draft_logprobs.shape
-    if draft_logprobs.stride(2) != 1 or (F > 1 and draft_logprobs.stride(1) != V):
-        raise ValueError("draft_logprobs rows must be contiguous [.., F, V]")
-    if F < (1 if step == 1 else max_topk):
-        raise ValueError(f"step {step} needs {1 if step == 1 else max_topk} draft rows per sequence, got {F}")
+def spec_tree_build_step_map(ws: torch.Tensor, step: int, draft_logprobs: torch.Tensor, token_map: torch.Tensor,
+                             topk: torch.Tensor, depth: torch.Tensor, max_topk: int, max_depth: int,
+                             frontier_tokens: torch.Tensor):
+    """spec_tree_build_step over a truncated draft vocabulary: draft_logprobs fp32 [B, F, V_d], token_map
+    int32 [V_d] (row entry i stands for token token_map[i])."""
+    B, V = _draft_rows(draft_logprobs, step, max_topk)
+    _token_map(token_map, V)
+    _dev(topk, torch.int32, "topk")
+    _dev(depth, torch.int32, "depth")
+    _dev(frontier_tokens, torch.int32, "frontier_tokens")
+    _dev(ws, torch.uint8, "ws")
+    rc = load().spec_tree_build_step_map(_ptr(ws), ws.numel(), step, _ptr(draft_logprobs), _ptr(token_map),
+                                         draft_logprobs.stride(0), _ptr(topk), _ptr(depth), B, max_topk, max_depth,
+                                         V, _ptr(frontier_tokens), _stream(ws))
+    check(rc, "spec_tree_build_step_map")
+
+
+def _finish_outputs(topk, depth, frontier_tokens, root_tokens, num_draft, tokens, parents, depth_out, anc_mask, q_row,
+                    ws):
     for n, t in (("topk", topk), ("depth", depth), ("frontier_tokens", frontier_tokens), ("root_tokens", root_tokens),
                  ("num_draft", num_draft), ("tokens", tokens), ("parents", parents), ("depth_out", depth_out),
                  ("q_row", q_row)):
         _dev(t, torch.int32, n)
     _dev(anc_mask, torch.int64, "anc_mask")  # uint64 bit patterns
     _dev(ws, torch.uint8, "ws")
+
+
+def spec_tree_build_step_finish(ws: torch.Tensor, step: int, draft_logprobs: torch.Tensor, topk: torch.Tensor,
+                                depth: torch.Tensor, max_topk: int, max_depth: int, frontier_tokens: torch.Tensor,
+                                root_tokens, num_draft, max_T, tokens, parents, depth_out, anc_mask, q_row):
+    """Step ``step`` plus the finish of the sequences whose depth is ``step`` (one launch)."""
+    B, V = _draft_rows(draft_logprobs, step, max_topk)
+    _finish_outputs(topk, depth, frontier_tokens, root_tokens, num_draft, tokens, parents, depth_out, anc_mask, q_row,
+                    ws)
     rc = load().spec_tree_build_step_finish(
         _ptr(ws), ws.numel(), step, _ptr(draft_logprobs), draft_logprobs.stride(0), _ptr(topk), _ptr(depth), B,
         max_topk, max_depth, V, _ptr(frontier_tokens), _ptr(root_tokens), _ptr(num_draft), max_T, _ptr(tokens),
         _ptr(parents), _ptr(depth_out), _ptr(anc_mask), _ptr(q_row), _stream(ws))
     check(rc, "spec_tree_build_step_finish")
+
+
+def spec_tree_build_step_finish_map(ws: torch.Tensor, step: int, draft_logprobs: torch.Tensor,
+                                    token_map: torch.Tensor, topk: torch.Tensor, depth: torch.Tensor, max_topk: int,
+                                    max_depth: int, frontier_tokens: torch.Tensor, root_tokens, num_draft, max_T,
+                                    tokens, parents, depth_out, anc_mask, q_row):
+    """spec_tree_build_step_finish over a truncated draft vocabulary (token_map int32 [V_d])."""
+    B, V = _draft_rows(draft_logprobs, step, max_topk)
+    _token_map(token_map, V)
+    _finish_outputs(topk, depth, frontier_tokens, root_tokens, num_draft, tokens, parents, depth_out, anc_mask, q_row,
+                    ws)
+    rc = load().spec_tree_build_step_finish_map(
+        _ptr(ws), ws.numel(), step, _ptr(draft_logprobs), _ptr(token_map), draft_logprobs.stride(0), _ptr(topk),
+        _ptr(depth), B, max_topk, max_depth, V, _ptr(frontier_tokens), _ptr(root_tokens), _ptr(num_draft), max_T,
+        _ptr(tokens), _ptr(parents), _ptr(depth_out), _ptr(anc_mask), _ptr(q_row), _stream(ws))
+    check(rc, "spec_tree_build_step_finish_map")
 
 
 def spec_tree_build_finish(ws, root_tokens, topk, depth, num_draft, max_topk, max_depth, max_T, tokens, parents,

@@ -50,6 +50,7 @@ class DeviceWorkload:
         self.draft_logprobs = torch.from_numpy(w.draft_logprobs).to(dev)
         self.draft_probs = torch.from_numpy(w.draft_probs).to(dev)
         self.target = torch.from_numpy(w.target).to(dev)
+        self.token_map = None if w.token_map is None else i32(w.token_map)  # truncated draft vocabulary
         if logits:
             self.target_logits = torch.from_numpy(w.target_logits).to(dev)
             self.temperature = torch.from_numpy(np.ascontiguousarray(w.temperature, dtype=np.float32)).to(dev)
@@ -108,10 +109,18 @@ class SpecTreeStep:
         for step in range(1, w.max_depth + 1):
             lo, hi = step_row_range(step, w.max_topk)
             rows = dw.draft_logprobs[:, lo:hi, :]
-            if self.fused_finish:
+            if self.fused_finish and dw.token_map is not None:
+                ops.spec_tree_build_step_finish_map(self.ws_build, step, rows, dw.token_map, dw.topk, dw.depth,
+                                                    w.max_topk, w.max_depth, o.frontier, dw.root_tokens,
+                                                    dw.num_draft, w.max_T, o.tokens, o.parents, o.depth, o.anc,
+                                                    o.q_row)
+            elif self.fused_finish:
                 ops.spec_tree_build_step_finish(self.ws_build, step, rows, dw.topk, dw.depth, w.max_topk,
                                                 w.max_depth, o.frontier, dw.root_tokens, dw.num_draft, w.max_T,
                                                 o.tokens, o.parents, o.depth, o.anc, o.q_row)
+            elif dw.token_map is not None:
+                ops.spec_tree_build_step_map(self.ws_build, step, rows, dw.token_map, dw.topk, dw.depth, w.max_topk,
+                                             w.max_depth, o.frontier)
             else:
                 ops.spec_tree_build_step(self.ws_build, step, rows, dw.topk, dw.depth, w.max_topk, w.max_depth,
                                          o.frontier)
