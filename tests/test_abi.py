@@ -95,6 +95,16 @@ def test_verify_build_compact_mask_host_validation(lib):
     assert fused(p, 1 << 20, 1, p, 1000, p, p, 1, 4, 3, 1000, p, None, p, 17, p, p, p, p, p, None) == SPEC_E_INVAL
     assert fused(p, 1 << 20, 0, p, 1000, p, p, 1, 4, 3, 1000, p, p, p, 17, p, p, p, p, p, None) == SPEC_E_INVAL
     assert fused(p, 8, 1, p, 1000, p, p, 1, 4, 3, 1000, p, p, p, 17, p, p, p, p, p, None) == SPEC_E_WORKSPACE
+    # the token-map variants check the same arguments as the plain calls before any launch
+    step_map = lib.spec_tree_build_step_map
+    assert step_map(p, 1 << 20, 0, p, p, 1000, p, p, 1, 4, 3, 1000, p, None) == SPEC_E_INVAL
+    assert step_map(p, 1 << 20, 1, p, p, 1000, p, p, 1, 9, 3, 1000, p, None) == SPEC_E_UNSUPPORTED
+    assert step_map(p, 8, 1, p, None, 1000, p, p, 1, 4, 3, 1000, p, None) == SPEC_E_WORKSPACE
+    fused_map = lib.spec_tree_build_step_finish_map
+    assert fused_map(p, 1 << 20, 1, p, p, 1000, p, p, 1, 4, 3, 1000, p, p, p, 70, p, p, p, p, p, None) == \
+        SPEC_E_UNSUPPORTED
+    assert fused_map(p, 1 << 20, 1, p, p, 1000, p, p, 1, 4, 3, 1000, p, None, p, 17, p, p, p, p, p, None) == SPEC_E_INVAL
+    assert fused_map(p, 8, 1, p, p, 1000, p, p, 1, 4, 3, 1000, p, p, p, 17, p, p, p, p, p, None) == SPEC_E_WORKSPACE
     assert lib.spec_kv_compact(p, p, p, p, p, p, 1, 9, 2, 80, 16, 4, 4, 1, 0, p, None) == SPEC_E_UNSUPPORTED
     assert lib.spec_tree_mask(None, None, 1, 9, None, None, None, None) == SPEC_E_INVAL
 
