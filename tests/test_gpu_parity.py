@@ -426,14 +426,16 @@ def test_kv_compact_multilayer():
 
 
 # ---------------------------------------------------------------- HIP graph replay
-@pytest.mark.parametrize("from_logits", [False, True], ids=["probs", "logits"])
-def test_graph_replay_matches_eager(from_logits):
+@pytest.mark.parametrize("from_logits,draft_vocab", [(False, None), (True, None), (False, 1200)],
+                         ids=["probs", "logits", "token_map"])
+def test_graph_replay_matches_eager(from_logits, draft_vocab):
     """A captured step replays to the eager result, replay after replay, with eager work in between (with the
-    sampling distributions supplied, or formed from logits inside the library)."""
+    sampling distributions supplied, or formed from logits inside the library, or with the tree built over a
+    truncated draft vocabulary)."""
     from tree_attention_verification_03_amd.pipeline import DeviceWorkload, SpecTreeStep
 
     w = make_workload(name="graph", B=3, Hq=8, Hkv=2, d=128, prefix=[300, 17, 1200], topk=3, depth=3, num_draft=9,
-                      V=5000, verify="alternate", temperature=0.8, seed=21)
+                      V=5000, verify="alternate", temperature=0.8, seed=21, draft_vocab=draft_vocab)
     dw = DeviceWorkload(w, logits=from_logits)
     step = SpecTreeStep(dw, verify_from_logits=from_logits)
     step.run(compact=False)
