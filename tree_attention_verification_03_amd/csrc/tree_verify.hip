@@ -148,9 +148,9 @@ __device__ __forceinline__ float sm_temperature(const float* temperature, int b)
 // A node's target probabilities for the sampling rule: the row as the caller supplies it (LG false), or
 // formed from the target's logits (LG true) as p[v] = exp(x - M) * (1 / S) with x = l[v] * (1 / T_b), where
 // M and S are the row's maximum and sum of exponentials merged from its slice partials in a fixed order.
-// Every block merges them the same way, so p[v] is the same number in every pass that reads it. A non-finite l[v] / T_b gives NaN,
-// and so does every element of a row whose temperature is not a finite positive number (NaN probabilities
-// count as zero and raise SPEC_STATUS_NAN_INPUT).
+// Every block merges them the same way, so p[v] is the same number in every pass that reads it. A
+// non-finite x gives NaN, and so does every element of a row whose temperature is not a finite positive
+// number (NaN probabilities count as zero and raise SPEC_STATUS_NAN_INPUT).
 template <bool LG>
 struct ProbRow {
   float inv = 1.f, M = 0.f, rS = 1.f;  // rS = 1 / S
