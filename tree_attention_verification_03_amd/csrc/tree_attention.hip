@@ -616,7 +616,7 @@ template <int D, bool KNOWN>
 __global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
   constexpr int TPR = D / 4;     // threads per row
   constexpr int RPB = 64 / TPR;  // rows per block
-  constexpr int CB = 16;         // items per batch
+  constexpr int CB = 16;         // items per batch at most
   const int tid = threadIdx.x;
   const int rsub = tid / TPR, c = tid - rsub * TPR;
   const int rbg = blockIdx.y;
@@ -631,7 +631,38 @@ __global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
   const size_t ITEM = size_t(TR) * (D / 2 + 3);  // in floats: o fp16 [TR][D], m, l, sc [TR]
   const float* grp = p.part + size_t(rbg) * p.n_splits * ITEM;
   RowMerge mr;
-  int n_items = CB;  // known after the first batch's loads (before them with KNOWN)
+  // n_items: the sequence's item count (KNOWN: loaded before the items), else the first batch's loads go
+  // out with the lengths, clamped to the call's split count, and the count is known after them. Slots past
+  // the last item repeat a loaded one (never folded), so the batch size CBV follows the count that bounds
+  // it (4, 8, 12 or 16): fewer wasted load instructions for sequences with few items
+  auto merge = [&](auto cbv, int n_items) {
+    constexpr int CBV = decltype(cbv)::value;
+#pragma unroll 1
+    for (int ib = 0; ib < n_items; ib += CBV) {
+      float mi[CBV], li[CBV];
+      f32x4 ai[CBV];
+#pragma unroll
+      for (int u = 0; u < CBV; ++u) {
+        const int item = KNOWN ? min(ib + u, n_items - 1) : min(ib + u, p.n_splits - 1);
+        const float* base = grp + size_t(item) * ITEM;
+        mi[u] = base[size_t(TR) * (D / 2) + row];
+        li[u] = base[size_t(TR) * (D / 2 + 1) + row];
+        const float scu = base[size_t(TR) * (D / 2 + 2) + row];
+        const uint2 h = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + size_t(row) * D + 4 * c);
+        ai[u] = __builtin_convertvector(__builtin_bit_cast(f16x4, h), f32x4) * scu;
+      }
+      if (!KNOWN && ib == 0) {
+        const int T = min(max(T_raw, 1), p.max_T);
+        const int cap = p.max_pages << p.page_shift;
+        const int L = min(max(L_raw, 0), cap - T);  // the main kernel's clamp
+        n_items = (L + T + p.chunk - 1) / p.chunk;
+        if (n_items == 1 || r >= p.G * T) return false;
+      }
+      mr.fold<CBV>(mi, li, ai, n_items - ib);
+    }
+    return true;
+  };
+  int n_items = p.n_splits;  // an upper bound until the lengths are known
   if constexpr (KNOWN) {
     const int T = min(max(T_raw, 1), p.max_T);
     const int cap = p.max_pages << p.page_shift;
@@ -639,30 +670,16 @@ __global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
     n_items = (L + T + p.chunk - 1) / p.chunk;
     if (n_items == 1 || r >= p.G * T) return;
   }
-#pragma unroll 1
-  for (int ib = 0; ib < n_items; ib += CB) {
-    float mi[CB], li[CB];
-    f32x4 ai[CB];
-#pragma unroll
-    for (int u = 0; u < CB; ++u) {
-      // without KNOWN, slots past the sequence's items repeat the last slot (loaded, never used)
-      const int item = KNOWN ? min(ib + u, n_items - 1) : min(ib + u, p.n_splits - 1);
-      const float* base = grp + size_t(item) * ITEM;
-      mi[u] = base[size_t(TR) * (D / 2) + row];
-      li[u] = base[size_t(TR) * (D / 2 + 1) + row];
-      const float scu = base[size_t(TR) * (D / 2 + 2) + row];
-      const uint2 h = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + size_t(row) * D + 4 * c);
-      ai[u] = __builtin_convertvector(__builtin_bit_cast(f16x4, h), f32x4) * scu;
-    }
-    if (!KNOWN && ib == 0) {
-      const int T = min(max(T_raw, 1), p.max_T);
-      const int cap = p.max_pages << p.page_shift;
-      const int L = min(max(L_raw, 0), cap - T);  // the main kernel's clamp
-      n_items = (L + T + p.chunk - 1) / p.chunk;
-      if (n_items == 1 || r >= p.G * T) return;
-    }
-    mr.fold<CB>(mi, li, ai, n_items - ib);
-  }
+  bool done;
+  if (n_items <= 4)
+    done = merge(std::integral_constant<int, 4>{}, n_items);
+  else if (n_items <= 8)
+    done = merge(std::integral_constant<int, 8>{}, n_items);
+  else if (n_items <= 12)
+    done = merge(std::integral_constant<int, 12>{}, n_items);
+  else
+    done = merge(std::integral_constant<int, CB>{}, n_items);
+  if (!done) return;
   mr.write<D>(p, b, g, r, c);
 }
 
