@@ -526,6 +526,20 @@ def test_verify_logits_planted(seed, verify):
         assert np.array_equal(host[k], again[k]), f"repeat differs: {k}"
 
 
+# rows of more than 64 softmax slices (V > 524288): each lane of a wave merges several slice partials
+@pytest.mark.parametrize("V", [600000, 600001])
+def test_verify_logits_long_rows(V):
+    w, trees, tok, par, qr = _small_verify_workload(2, "alternate", V=V, B=3, temperature=0.9)
+    logits, draft = w.target_logits.copy(), w.draft_probs.copy()
+    for b, t in enumerate(trees):  # the first child of the root on top of the root's row
+        kids = [i for i in range(1, len(t.tokens)) if t.parents[i] == 0]
+        if kids:
+            logits[b, 0, t.tokens[kids[0]]] = logits[b, 0].max() + (8.0 if int(w.modes[b]) == 1 else 1.0)
+    log(f"[verify-logits] long rows V={V}")
+    host = _verify_logits(w, tok, par, qr, logits, draft, w.temperature)
+    _check_logits(w, host, tok, par, qr, logits, draft, w.temperature)
+
+
 def test_verify_logits_degenerate_inputs():
     w, trees, tok, par, qr = _small_verify_workload(4, "sample", V=300, B=6, temperature=0.8)
     logits, draft = w.target_logits.copy(), w.draft_probs.copy()
