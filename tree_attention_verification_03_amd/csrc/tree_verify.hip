@@ -1113,6 +1113,9 @@ __device__ __forceinline__ bool sm_row(const int32_t* T_b, const int8_t* mode, i
   return mode[b] == SPEC_MODE_SAMPLE && u < seq_T(T_b, b, max_T);
 }
 
+// VEC: each thread loads its 32 elements as 8 float4 (V a multiple of 4, logits 16-byte aligned), else
+// one float per lane and load
+template <bool VEC>
 __global__ void __launch_bounds__(kSmThreads) softmax_partial_kernel(const float* logits, const float* temperature,
                                                                       const int32_t* T_b, const int8_t* mode,
                                                                       int max_T, int V, float2* part) {
@@ -1120,17 +1123,31 @@ __global__ void __launch_bounds__(kSmThreads) softmax_partial_kernel(const float
   const int s = blockIdx.x, row = blockIdx.y, nsl = gridDim.x, tid = threadIdx.x;
   if (!sm_row(T_b, mode, max_T, row)) return;
   const float T = sm_temperature(temperature, row / max_T);
-  if (T == 0.f) return;  // the write kernel fills the row with NaN
+  if (T == 0.f) return;  // no partials: every probability of the row is NaN
   const float inv = 1.f / T;
   const float* l = logits + size_t(row) * V;
   float x[kSmPer];
+  if (VEC) {
+#pragma unroll
+    for (int i = 0; i < kSmPer / 4; ++i) {
+      const int v = s * kSmSlice + 4 * (i * kSmThreads + tid);
+      const float4 q = v < V ? *reinterpret_cast<const float4*>(l + v) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      x[4 * i] = q.x * inv;
+      x[4 * i + 1] = q.y * inv;
+      x[4 * i + 2] = q.z * inv;
+      x[4 * i + 3] = q.w * inv;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSmPer; ++i) {
+      const int v = s * kSmSlice + i * kSmThreads + tid;
+      x[i] = v < V ? l[v] * inv : -INFINITY;
+    }
+  }
   float m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kSmPer; ++i) {
-    const int v = s * kSmSlice + i * kSmThreads + tid;
-    x[i] = v < V ? l[v] * inv : -INFINITY;
+  for (int i = 0; i < kSmPer; ++i)
     if (isfinite(x[i])) m = fmaxf(m, x[i]);
-  }
   m = sm_block_reduce(m, true, red);
   float sum = 0.f;
 #pragma unroll
@@ -1211,8 +1228,12 @@ static int32_t verify_impl(const char* who, const float* target, float2* sm_part
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (sm_part) {  // the sampling rows' softmax partials first (same stream: the verify launch waits)
     const dim3 sgrid(unsigned(a.sm_nsl), unsigned(rows));
-    hipLaunchKernelGGL(softmax_partial_kernel, sgrid, dim3(kSmThreads), 0, st, target, temperature, T_b, mode, max_T, V,
-                       sm_part);
+    if ((V % 4 == 0) && (reinterpret_cast<uintptr_t>(target) & 15) == 0)
+      hipLaunchKernelGGL(softmax_partial_kernel<true>, sgrid, dim3(kSmThreads), 0, st, target, temperature, T_b, mode,
+                         max_T, V, sm_part);
+    else
+      hipLaunchKernelGGL(softmax_partial_kernel<false>, sgrid, dim3(kSmThreads), 0, st, target, temperature, T_b, mode,
+                         max_T, V, sm_part);
     if (vec)
       hipLaunchKernelGGL((verify_kernel<true, true>), grid, dim3(kThreads), 0, st, w, a);
     else
