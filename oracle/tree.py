@@ -49,16 +49,6 @@ import numpy as np
 STATUS_INVALID_PARENT = 1
 
 
-def canon_logprob(x) -> float:
-    """Clamp one fp32 draft log-prob: NaN -> -inf, x >= 0 -> +0.0."""
-    x = float(np.float32(x))
-    if x != x:
-        return float("-inf")
-    if x >= 0.0:
-        return 0.0
-    return x
-
-
 def row_topk(row: np.ndarray, k: int):
     """Top-k (token, value) of one draft row by (value desc, token asc)."""
     vals = np.asarray(row, dtype=np.float32).astype(np.float64)
@@ -184,9 +174,3 @@ def tree_mask(parents: Sequence[int], T: int):
         depth[i] = depth[p] + 1
     return anc, depth, status
 
-
-def visible(anc_i: int, i: int, j: int) -> bool:
-    """Does tree node i attend to tree node j? (root always; drafts via bit j-1)."""
-    if j == 0:
-        return True
-    return bool((int(anc_i) >> (j - 1)) & 1)

@@ -300,3 +300,81 @@ def test_workload_sampling_rows_are_the_softmax_of_their_logits():
                                            w.target[b, u], rtol=1e-6)
             else:
                 np.testing.assert_array_equal(w.target_logits[b, u], w.target[b, u])
+
+
+def _dispatch_case(seed=31):
+    """Alternate-mode trees (even sequences greedy, odd sampling) at distinct fp32-exact temperatures, with
+    acceptance planted on some sampling sequences (their q rows on a path are set to the target's p there) and
+    a greedy root row whose top two logits collapse to one value under an fp32 softmax."""
+    from scipy.special import softmax
+
+    from oracle.tree import build_tree
+    from workloads import make_workload
+
+    w = make_workload(name="disp", B=6, Hq=2, Hkv=1, d=64, prefix=16, topk=3, depth=3, num_draft=8, V=300,
+                      verify="alternate", temperature=1.0, seed=seed)
+    temps = np.array([0.0, 0.5, 0.0, 2.0, 0.0, 1.0], dtype=np.float32)
+    trees = [build_tree(w.draft_logprobs[b], int(w.root_tokens[b]), int(w.topk[b]), int(w.depth[b]),
+                        int(w.num_draft[b]), w.max_topk) for b in range(w.B)]
+    logits = w.target_logits.copy()
+    # greedy sequence 0: logits 0.01 and the fp32 value just below it at tokens 5 and 2; a softmax in fp32
+    # rounds both to one probability, so only the logits themselves make token 5 the argmax
+    logits[0, 0, :] = -10.0
+    logits[0, 0, 5] = np.float32(0.01)
+    logits[0, 0, 2] = np.nextafter(np.float32(0.01), np.float32(0))
+    draft = w.draft_probs.copy()
+
+    def probs(b, T):
+        return softmax(logits[b].astype(np.float64) / float(T), axis=-1).astype(np.float32)
+
+    for b in (1, 5):  # plant along the first-child path: the child's token leads the logits, and the
+        t = trees[b]  # node's q row is the target's p there
+        u, path = 0, []
+        while True:
+            kids = [i for i in range(1, len(t.tokens)) if t.parents[i] == u]
+            if not kids or t.q_row[u] < 0:
+                break
+            logits[b, u, t.tokens[kids[0]]] = logits[b, u].max() + np.float32(1.0)
+            path.append(u)
+            u = kids[0]
+        p = probs(b, temps[b])
+        for u in path:
+            draft[b, t.q_row[u]] = p[u]
+    T = len(trees[0].tokens)
+    tok = np.stack([t.tokens for t in trees])
+    par = np.stack([t.parents for t in trees])
+    qr = np.stack([t.q_row for t in trees])
+    T_b = np.full(w.B, T, dtype=np.int32)
+    return w, logits, temps, draft, qr, tok, par, T_b, probs
+
+
+def test_verify_from_logits_dispatch():
+    """Pins tree_verify_logits: each sampling sequence b verifies against softmax(logits / temperature[b]) formed
+    independently here (scipy, fp64, stored fp32), each greedy sequence against its raw logits, and a missing
+    temperature array means 1 for every sequence (the tree_verify results on those rows are the reference)."""
+    from oracle.verify import tree_verify, tree_verify_logits
+
+    w, logits, temps, draft, qr, tok, par, T_b, probs = _dispatch_case()
+    key, off = w.philox_key, w.philox_offset
+
+    def reference(tvals):
+        target = logits.copy()
+        for b in range(w.B):
+            if int(w.modes[b]) == MODE_SAMPLE:
+                target[b] = probs(b, tvals[b])
+        return tree_verify(target, draft, qr, tok, par, T_b, w.modes, key, off)
+
+    got = tree_verify_logits(logits, temps, draft, qr, tok, par, T_b, w.modes, key, off)
+    want = reference(temps)
+    assert got == want
+    # the case is sensitive: planted sequences accept, the greedy root's bonus is token 5 (the fp32 logit
+    # argmax), and the sampling outcomes change when the temperatures are swapped between sequences
+    assert got[1][0] > 0 and got[5][0] > 0
+    assert got[0][2][-1] == 5 or 5 in got[0][2]
+    swapped = temps.copy()
+    swapped[[1, 3]] = swapped[[3, 1]]
+    assert reference(swapped) != want
+    # no temperature array: every sampling sequence at T = 1
+    got1 = tree_verify_logits(logits, None, draft, qr, tok, par, T_b, w.modes, key, off)
+    assert got1 == reference(np.ones(w.B, dtype=np.float32))
+    assert got1 != want
