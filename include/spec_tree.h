@@ -293,9 +293,11 @@ int32_t spec_tree_verify_logits(const float* logits, const float* temperature, c
  * and KV head, the k-th accepted node n_k (accept_nodes[b, k], k = 1..
  * accept_len[b]) moves from slot L_b + n_k to slot L_b + k; the root stays
  * at L_b. All sources are read before any destination is written.
- * new_prefix_lens int32 [B] = L_b + 1 + accept_len[b]. k_pages / v_pages are
- * modified in place; other inputs are read only. Invalid accept_len or
- * accept_nodes (not increasing, >= max_T) leave that sequence's cache untouched.
+ * new_prefix_lens int32 [B] = L_b + 1 + accept_len[b]; it must not overlap
+ * prefix_lens (SPEC_E_INVAL), since other blocks still read L_b while it is
+ * written. k_pages / v_pages are modified in place; other inputs are read only.
+ * Invalid accept_len or accept_nodes (not increasing, >= max_T) leave that
+ * sequence's cache untouched.
  * ------------------------------------------------------------------------- */
 int32_t spec_kv_compact(void* k_pages, void* v_pages, const int32_t* page_table, const int32_t* prefix_lens,
                         const int32_t* accept_nodes, const int32_t* accept_len, int32_t B, int32_t max_T,

@@ -106,6 +106,10 @@ def test_verify_build_compact_mask_host_validation(lib):
     assert fused_map(p, 1 << 20, 1, p, p, 1000, p, p, 1, 4, 3, 1000, p, None, p, 17, p, p, p, p, p, None) == SPEC_E_INVAL
     assert fused_map(p, 8, 1, p, p, 1000, p, p, 1, 4, 3, 1000, p, p, p, 17, p, p, p, p, p, None) == SPEC_E_WORKSPACE
     assert lib.spec_kv_compact(p, p, p, p, p, p, 1, 9, 2, 80, 16, 4, 4, 1, 0, p, None) == SPEC_E_UNSUPPORTED
+    # new_prefix_lens overlapping prefix_lens is refused before any launch
+    q = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.spec_kv_compact(p, p, p, p, p, p, 2, 9, 2, 128, 16, 4, 4, 1, 0, q, None) == SPEC_E_INVAL
+    assert b"overlaps" in lib.spec_last_error()
     assert lib.spec_tree_mask(None, None, 1, 9, None, None, None, None) == SPEC_E_INVAL
 
 

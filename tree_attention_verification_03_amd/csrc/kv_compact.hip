@@ -144,6 +144,11 @@ extern "C" int32_t spec_kv_compact(void* k_pages, void* v_pages, const int32_t* 
   if (!is_pow2(page) || page > 1024) return fail(SPEC_E_UNSUPPORTED, "spec_kv_compact: page %d not a power of two <= 1024", page);
   if (!k_pages || !v_pages || !page_table || !prefix_lens || !accept_nodes || !accept_len || !new_prefix_lens)
     return fail(SPEC_E_INVAL, "spec_kv_compact: null pointer");
+  {  // new_prefix_lens is written while other blocks still read prefix_lens: the two must not overlap
+    const uintptr_t n0 = reinterpret_cast<uintptr_t>(new_prefix_lens), p0 = reinterpret_cast<uintptr_t>(prefix_lens);
+    const uintptr_t nb = sizeof(int32_t) * size_t(B);
+    if (n0 < p0 + nb && p0 < n0 + nb) return fail(SPEC_E_INVAL, "spec_kv_compact: new_prefix_lens overlaps prefix_lens");
+  }
   const int64_t pool_elems = int64_t(num_pages) * page * Hkv * d;
   if (num_layers > 1 && layer_stride_elems < pool_elems)
     return fail(SPEC_E_INVAL, "spec_kv_compact: layer_stride_elems %lld < pool size %lld", (long long)layer_stride_elems,

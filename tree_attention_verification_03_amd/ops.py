@@ -27,20 +27,56 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _dev(t: torch.Tensor, dtype, name: str, contiguous: bool = True):
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on the GPU (got {t.device})")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
-    if contiguous and not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    return t
+def _check(*specs):
+    """Validate tensor arguments before any launch: specs are (name, tensor, dtype, shape, contiguous);
+    a shape entry of None matches any size. Every argument's type, dtype, shape and layout is checked
+    first, then that all of them sit on one GPU, so a mistake in any argument raises here on the host
+    instead of reaching a kernel that indexes by the declared sizes."""
+    _check_layout(*specs)
+    _check_device(*specs)
+
+
+def _check_layout(*specs):
+    for name, t, dtype, shape, contiguous in specs:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor (got {type(t).__name__})")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+        if shape is not None and (t.dim() != len(shape)
+                                  or any(w is not None and int(g) != int(w) for g, w in zip(t.shape, shape))):
+            want = tuple("*" if w is None else int(w) for w in shape)
+            raise ValueError(f"{name} must have shape {want} (got {tuple(t.shape)})")
+        if contiguous and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _check_device(*specs):
+    dev = None
+    for name, t, _, _, _ in specs:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU (got {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+
+
+def _spec(name, t, dtype, shape=None, contiguous=True):
+    return (name, t, dtype, shape, contiguous)
+
+
+def _opt(name, t, dtype, shape=None, contiguous=True):
+    """An optional argument: no spec when it is None."""
+    return () if t is None else ((name, t, dtype, shape, contiguous),)
 
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
+
+
+def _overlap(a: torch.Tensor, b: torch.Tensor) -> bool:
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    return a0 < b0 + b.numel() * b.element_size() and b0 < a0 + a.numel() * a.element_size()
 
 
 def spec_abi_version() -> int:
@@ -71,7 +107,9 @@ def zeroed_workspace(nbytes: int, device) -> torch.Tensor:
 
 # ------------------------------------------------------------------ tree build
 def _draft_rows(draft_logprobs, step, max_topk):
-    _dev(draft_logprobs, torch.float32, "draft_logprobs", contiguous=False)
+    """Shape of a step's draft rows: fp32 [B, F, V] view whose rows are contiguous (any batch stride)."""
+    if not isinstance(draft_logprobs, torch.Tensor) or draft_logprobs.dim() != 3:
+        raise ValueError("draft_logprobs must be a 3-D tensor [B, F, V]")
     B, F, V = draft_logprobs.shape
     if draft_logprobs.stride(2) != 1 or (F > 1 and draft_logprobs.stride(1) != V):
         raise ValueError("draft_logprobs rows must be contiguous [.., F, V]")
@@ -80,20 +118,26 @@ def _draft_rows(draft_logprobs, step, max_topk):
     return B, V
 
 
-def _token_map(token_map, V):
-    _dev(token_map, torch.int32, "token_map")
-    if token_map.numel() != V:
-        raise ValueError(f"token_map has {token_map.numel()} entries, the draft rows {V}")
+def _step_specs(ws, draft_logprobs, topk, depth, frontier_tokens, B, max_topk):
+    return (_spec("draft_logprobs", draft_logprobs, torch.float32, contiguous=False),
+            _spec("topk", topk, torch.int32, (B,)), _spec("depth", depth, torch.int32, (B,)),
+            _spec("frontier_tokens", frontier_tokens, torch.int32, (B, max_topk)),
+            _spec("ws", ws, torch.uint8, (None,)))
+
+
+def _finish_specs(root_tokens, num_draft, tokens, parents, depth_out, anc_mask, q_row, B, max_T):
+    return (_spec("root_tokens", root_tokens, torch.int32, (B,)), _spec("num_draft", num_draft, torch.int32, (B,)),
+            _spec("tokens", tokens, torch.int32, (B, max_T)), _spec("parents", parents, torch.int32, (B, max_T)),
+            _spec("depth_out", depth_out, torch.int32, (B, max_T)),
+            _spec("anc_mask", anc_mask, torch.int64, (B, max_T)),  # uint64 bit patterns
+            _spec("q_row", q_row, torch.int32, (B, max_T)))
 
 
 def spec_tree_build_step(ws: torch.Tensor, step: int, draft_logprobs: torch.Tensor, topk: torch.Tensor,
                          depth: torch.Tensor, max_topk: int, max_depth: int, frontier_tokens: torch.Tensor):
     """draft_logprobs: fp32 [B, F, V] view (rows contiguous; any batch stride)."""
     B, V = _draft_rows(draft_logprobs, step, max_topk)
-    _dev(topk, torch.int32, "topk")
-    _dev(depth, torch.int32, "depth")
-    _dev(frontier_tokens, torch.int32, "frontier_tokens")
-    _dev(ws, torch.uint8, "ws")
+    _check(*_step_specs(ws, draft_logprobs, topk, depth, frontier_tokens, B, max_topk))
     rc = load().spec_tree_build_step(_ptr(ws), ws.numel(), step, _ptr(draft_logprobs), draft_logprobs.stride(0),
                                      _ptr(topk), _ptr(depth), B, max_topk, max_depth, V, _ptr(frontier_tokens),
                                      _stream(ws))
@@ -106,25 +150,12 @@ def spec_tree_build_step_map(ws: torch.Tensor, step: int, draft_logprobs: torch.
     """spec_tree_build_step over a truncated draft vocabulary: draft_logprobs fp32 [B, F, V_d], token_map
     int32 [V_d] (row entry i stands for token token_map[i])."""
     B, V = _draft_rows(draft_logprobs, step, max_topk)
-    _token_map(token_map, V)
-    _dev(topk, torch.int32, "topk")
-    _dev(depth, torch.int32, "depth")
-    _dev(frontier_tokens, torch.int32, "frontier_tokens")
-    _dev(ws, torch.uint8, "ws")
+    _check(*_step_specs(ws, draft_logprobs, topk, depth, frontier_tokens, B, max_topk),
+           _spec("token_map", token_map, torch.int32, (V,)))
     rc = load().spec_tree_build_step_map(_ptr(ws), ws.numel(), step, _ptr(draft_logprobs), _ptr(token_map),
                                          draft_logprobs.stride(0), _ptr(topk), _ptr(depth), B, max_topk, max_depth,
                                          V, _ptr(frontier_tokens), _stream(ws))
     check(rc, "spec_tree_build_step_map")
-
-
-def _finish_outputs(topk, depth, frontier_tokens, root_tokens, num_draft, tokens, parents, depth_out, anc_mask, q_row,
-                    ws):
-    for n, t in (("topk", topk), ("depth", depth), ("frontier_tokens", frontier_tokens), ("root_tokens", root_tokens),
-                 ("num_draft", num_draft), ("tokens", tokens), ("parents", parents), ("depth_out", depth_out),
-                 ("q_row", q_row)):
-        _dev(t, torch.int32, n)
-    _dev(anc_mask, torch.int64, "anc_mask")  # uint64 bit patterns
-    _dev(ws, torch.uint8, "ws")
 
 
 def spec_tree_build_step_finish(ws: torch.Tensor, step: int, draft_logprobs: torch.Tensor, topk: torch.Tensor,
@@ -132,8 +163,8 @@ def spec_tree_build_step_finish(ws: torch.Tensor, step: int, draft_logprobs: tor
                                 root_tokens, num_draft, max_T, tokens, parents, depth_out, anc_mask, q_row):
     """Step ``step`` plus the finish of the sequences whose depth is ``step`` (one launch)."""
     B, V = _draft_rows(draft_logprobs, step, max_topk)
-    _finish_outputs(topk, depth, frontier_tokens, root_tokens, num_draft, tokens, parents, depth_out, anc_mask, q_row,
-                    ws)
+    _check(*_step_specs(ws, draft_logprobs, topk, depth, frontier_tokens, B, max_topk),
+           *_finish_specs(root_tokens, num_draft, tokens, parents, depth_out, anc_mask, q_row, B, max_T))
     rc = load().spec_tree_build_step_finish(
         _ptr(ws), ws.numel(), step, _ptr(draft_logprobs), draft_logprobs.stride(0), _ptr(topk), _ptr(depth), B,
         max_topk, max_depth, V, _ptr(frontier_tokens), _ptr(root_tokens), _ptr(num_draft), max_T, _ptr(tokens),
@@ -147,9 +178,9 @@ def spec_tree_build_step_finish_map(ws: torch.Tensor, step: int, draft_logprobs:
                                     tokens, parents, depth_out, anc_mask, q_row):
     """spec_tree_build_step_finish over a truncated draft vocabulary (token_map int32 [V_d])."""
     B, V = _draft_rows(draft_logprobs, step, max_topk)
-    _token_map(token_map, V)
-    _finish_outputs(topk, depth, frontier_tokens, root_tokens, num_draft, tokens, parents, depth_out, anc_mask, q_row,
-                    ws)
+    _check(*_step_specs(ws, draft_logprobs, topk, depth, frontier_tokens, B, max_topk),
+           _spec("token_map", token_map, torch.int32, (V,)),
+           *_finish_specs(root_tokens, num_draft, tokens, parents, depth_out, anc_mask, q_row, B, max_T))
     rc = load().spec_tree_build_step_finish_map(
         _ptr(ws), ws.numel(), step, _ptr(draft_logprobs), _ptr(token_map), draft_logprobs.stride(0), _ptr(topk),
         _ptr(depth), B, max_topk, max_depth, V, _ptr(frontier_tokens), _ptr(root_tokens), _ptr(num_draft), max_T,
@@ -159,11 +190,12 @@ def spec_tree_build_step_finish_map(ws: torch.Tensor, step: int, draft_logprobs:
 
 def spec_tree_build_finish(ws, root_tokens, topk, depth, num_draft, max_topk, max_depth, max_T, tokens, parents,
                            depth_out, anc_mask, q_row):
-    for n, t in (("root_tokens", root_tokens), ("topk", topk), ("depth", depth), ("num_draft", num_draft),
-                 ("tokens", tokens), ("parents", parents), ("depth_out", depth_out), ("q_row", q_row)):
-        _dev(t, torch.int32, n)
-    _dev(anc_mask, torch.int64, "anc_mask")  # uint64 bit patterns
+    if not isinstance(root_tokens, torch.Tensor) or root_tokens.dim() != 1:
+        raise ValueError("root_tokens must be a 1-D tensor [B]")
     B = root_tokens.shape[0]
+    _check(_spec("topk", topk, torch.int32, (B,)), _spec("depth", depth, torch.int32, (B,)),
+           _spec("ws", ws, torch.uint8, (None,)),
+           *_finish_specs(root_tokens, num_draft, tokens, parents, depth_out, anc_mask, q_row, B, max_T))
     rc = load().spec_tree_build_finish(_ptr(ws), ws.numel(), _ptr(root_tokens), _ptr(topk), _ptr(depth),
                                        _ptr(num_draft), B, max_topk, max_depth, max_T, _ptr(tokens), _ptr(parents),
                                        _ptr(depth_out), _ptr(anc_mask), _ptr(q_row), _stream(ws))
@@ -171,9 +203,14 @@ def spec_tree_build_finish(ws, root_tokens, topk, depth, num_draft, max_topk, ma
 
 
 def spec_tree_mask(parents, T_b, anc_mask, depth=None, status=None):
-    _dev(parents, torch.int32, "parents")
-    _dev(anc_mask, torch.int64, "anc_mask")
+    """parents int32 [B, max_T]; T_b int32 [B] or None; anc_mask int64 [B, max_T] (uint64 bits); depth int32
+    [B, max_T] or None; status int32 [B] or None (uint32 bits)."""
+    if not isinstance(parents, torch.Tensor) or parents.dim() != 2:
+        raise ValueError("parents must be a 2-D tensor [B, max_T]")
     B, max_T = parents.shape
+    _check(_spec("parents", parents, torch.int32, (B, max_T)), *_opt("T_b", T_b, torch.int32, (B,)),
+           _spec("anc_mask", anc_mask, torch.int64, (B, max_T)), *_opt("depth", depth, torch.int32, (B, max_T)),
+           *_opt("status", status, torch.int32, (B,)))
     rc = load().spec_tree_mask(_ptr(parents), _ptr(T_b), B, max_T, _ptr(anc_mask), _ptr(depth), _ptr(status),
                                _stream(parents))
     check(rc, "spec_tree_mask")
@@ -183,24 +220,19 @@ def spec_tree_mask(parents, T_b, anc_mask, depth=None, status=None):
 def spec_tree_attention(q, k_pages, v_pages, page_table, prefix_lens, parents, T_b, sm_scale, out, lse=None,
                         status=None, ws=None):
     """q: bf16 [B, max_T, Hq, d]; k/v_pages: bf16 [P, page, Hkv, d]; page_table int32 [B, max_pages]."""
-    _dev(q, torch.bfloat16, "q")
-    _dev(k_pages, torch.bfloat16, "k_pages")
-    _dev(v_pages, torch.bfloat16, "v_pages")
-    _dev(page_table, torch.int32, "page_table")
-    _dev(prefix_lens, torch.int32, "prefix_lens")
-    _dev(parents, torch.int32, "parents")
-    _dev(out, torch.bfloat16, "out")
-    if T_b is not None:
-        _dev(T_b, torch.int32, "T_b")
-    if lse is not None:
-        _dev(lse, torch.float32, "lse")
-    if status is not None:
-        _dev(status, torch.int32, "status")
+    for name, t, nd in (("q", q, 4), ("k_pages", k_pages, 4), ("page_table", page_table, 2)):
+        if not isinstance(t, torch.Tensor) or t.dim() != nd:
+            raise ValueError(f"{name} must be a {nd}-D tensor")
     B, max_T, Hq, d = q.shape
-    P, page, Hkv, d2 = k_pages.shape
-    if d2 != d or v_pages.shape != k_pages.shape or out.shape != q.shape or parents.shape != (B, max_T):
-        raise ValueError("inconsistent attention shapes")
+    P, page, Hkv = k_pages.shape[:3]
     max_pages = page_table.shape[1]
+    _check(_spec("q", q, torch.bfloat16), _spec("k_pages", k_pages, torch.bfloat16, (P, page, Hkv, d)),
+           _spec("v_pages", v_pages, torch.bfloat16, (P, page, Hkv, d)),
+           _spec("page_table", page_table, torch.int32, (B, max_pages)),
+           _spec("prefix_lens", prefix_lens, torch.int32, (B,)), _spec("parents", parents, torch.int32, (B, max_T)),
+           *_opt("T_b", T_b, torch.int32, (B,)), _spec("out", out, torch.bfloat16, (B, max_T, Hq, d)),
+           *_opt("lse", lse, torch.float32, (B, max_T, Hq)), *_opt("status", status, torch.int32, (B,)),
+           *_opt("ws", ws, torch.uint8, (None,)))
     if ws is None:
         ws = zeroed_workspace(spec_tree_attention_workspace_size(B, max_T, Hq, Hkv, d, page, max_pages), q.device)
     rc = load().spec_tree_attention(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table), _ptr(prefix_lens),
@@ -212,19 +244,33 @@ def spec_tree_attention(q, k_pages, v_pages, page_table, prefix_lens, parents, T
 
 
 # ------------------------------------------------------------------ verify
-def spec_tree_verify(target, draft_probs, q_row, tokens, parents, T_b, mode, philox_key, philox_offset, accept_len,
-                     accept_nodes, out_tokens, status, ws=None):
-    _dev(target, torch.float32, "target")
-    B, max_T, V = target.shape
+def _verify_specs(rows, rows_name, draft_probs, q_row, tokens, parents, T_b, mode, accept_len, accept_nodes,
+                  out_tokens, status, ws):
+    if not isinstance(rows, torch.Tensor) or rows.dim() != 3:
+        raise ValueError(f"{rows_name} must be a 3-D tensor [B, max_T, V]")
+    B, max_T, V = rows.shape
     R = 0
     if draft_probs is not None:
-        _dev(draft_probs, torch.float32, "draft_probs")
+        if not isinstance(draft_probs, torch.Tensor) or draft_probs.dim() != 3:
+            raise ValueError("draft_probs must be a 3-D tensor [B, R, V]")
         R = draft_probs.shape[1]
-        _dev(q_row, torch.int32, "q_row")
-    for n, t in (("tokens", tokens), ("parents", parents), ("accept_len", accept_len),
-                 ("accept_nodes", accept_nodes), ("out_tokens", out_tokens), ("status", status)):
-        _dev(t, torch.int32, n)
-    _dev(mode, torch.int8, "mode")
+        if q_row is None:
+            raise ValueError("draft_probs needs q_row")
+    specs = (_spec(rows_name, rows, torch.float32), *_opt("draft_probs", draft_probs, torch.float32, (B, None, V)),
+             *_opt("q_row", q_row, torch.int32, (B, max_T)), _spec("tokens", tokens, torch.int32, (B, max_T)),
+             _spec("parents", parents, torch.int32, (B, max_T)), *_opt("T_b", T_b, torch.int32, (B,)),
+             _spec("mode", mode, torch.int8, (B,)), _spec("accept_len", accept_len, torch.int32, (B,)),
+             _spec("accept_nodes", accept_nodes, torch.int32, (B, max_T)),
+             _spec("out_tokens", out_tokens, torch.int32, (B, max_T)), _spec("status", status, torch.int32, (B,)),
+             *_opt("ws", ws, torch.uint8, (None,)))
+    return B, max_T, V, R, specs
+
+
+def spec_tree_verify(target, draft_probs, q_row, tokens, parents, T_b, mode, philox_key, philox_offset, accept_len,
+                     accept_nodes, out_tokens, status, ws=None):
+    B, max_T, V, R, specs = _verify_specs(target, "target", draft_probs, q_row, tokens, parents, T_b, mode,
+                                          accept_len, accept_nodes, out_tokens, status, ws)
+    _check(*specs)
     if ws is None:
         ws = zeroed_workspace(spec_tree_verify_workspace_size(B, max_T, V), target.device)
     k0, k1 = (int(x) & 0xFFFFFFFFFFFFFFFF for x in philox_key)
@@ -244,21 +290,9 @@ def spec_tree_verify_logits(logits, temperature, draft_probs, q_row, tokens, par
                             philox_offset, accept_len, accept_nodes, out_tokens, status, ws=None):
     """spec_tree_verify with the sampling sequences' target distributions formed from ``logits`` (fp32
     [B, max_T, V]) and ``temperature`` (fp32 [B] or None = 1) inside the library."""
-    _dev(logits, torch.float32, "logits")
-    B, max_T, V = logits.shape
-    if temperature is not None:
-        _dev(temperature, torch.float32, "temperature")
-        if temperature.numel() < B:
-            raise ValueError(f"temperature holds {temperature.numel()} values for {B} sequences")
-    R = 0
-    if draft_probs is not None:
-        _dev(draft_probs, torch.float32, "draft_probs")
-        R = draft_probs.shape[1]
-        _dev(q_row, torch.int32, "q_row")
-    for n, t in (("tokens", tokens), ("parents", parents), ("accept_len", accept_len),
-                 ("accept_nodes", accept_nodes), ("out_tokens", out_tokens), ("status", status)):
-        _dev(t, torch.int32, n)
-    _dev(mode, torch.int8, "mode")
+    B, max_T, V, R, specs = _verify_specs(logits, "logits", draft_probs, q_row, tokens, parents, T_b, mode,
+                                          accept_len, accept_nodes, out_tokens, status, ws)
+    _check(*specs, *_opt("temperature", temperature, torch.float32, (B,)))
     if ws is None:
         ws = zeroed_workspace(spec_tree_verify_logits_workspace_size(B, max_T, V), logits.device)
     k0, k1 = (int(x) & 0xFFFFFFFFFFFFFFFF for x in philox_key)
@@ -274,11 +308,31 @@ def spec_tree_verify_logits(logits, temperature, draft_probs, q_row, tokens, par
 # ------------------------------------------------------------------ compaction
 def spec_kv_compact(k_pages, v_pages, page_table, prefix_lens, accept_nodes, accept_len, new_prefix_lens,
                     num_layers: int = 1, layer_stride_elems: int = 0):
-    """k_pages / v_pages: bf16 [P, page, Hkv, d] (layer 0 of ``num_layers`` pools ``layer_stride_elems`` apart)."""
-    _dev(k_pages, torch.bfloat16, "k_pages", contiguous=False)
-    _dev(v_pages, torch.bfloat16, "v_pages", contiguous=False)
+    """k_pages / v_pages: bf16 [P, page, Hkv, d], dense; layer l's pool starts ``l * layer_stride_elems`` elements
+    after layer 0's (a contiguous [num_layers, P, page, Hkv, d] tensor passes its layer-0 view and
+    P * page * Hkv * d). ``new_prefix_lens`` must not overlap ``prefix_lens``."""
+    for name, t, nd in (("k_pages", k_pages, 4), ("accept_nodes", accept_nodes, 2), ("page_table", page_table, 2)):
+        if not isinstance(t, torch.Tensor) or t.dim() != nd:
+            raise ValueError(f"{name} must be a {nd}-D tensor")
     P, page, Hkv, d = k_pages.shape
     B, max_T = accept_nodes.shape
+    specs = (_spec("k_pages", k_pages, torch.bfloat16, (P, page, Hkv, d)),
+             _spec("v_pages", v_pages, torch.bfloat16, (P, page, Hkv, d)),
+             _spec("page_table", page_table, torch.int32, (B, None)),
+             _spec("prefix_lens", prefix_lens, torch.int32, (B,)),
+             _spec("accept_nodes", accept_nodes, torch.int32, (B, max_T)),
+             _spec("accept_len", accept_len, torch.int32, (B,)),
+             _spec("new_prefix_lens", new_prefix_lens, torch.int32, (B,)))
+    _check_layout(*specs)
+    if _overlap(new_prefix_lens, prefix_lens):
+        raise ValueError("new_prefix_lens must not overlap prefix_lens (blocks still read L_b while it is written)")
+    if num_layers < 1:
+        raise ValueError("num_layers must be >= 1")
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+        need = t.storage_offset() + (num_layers - 1) * int(layer_stride_elems) + t.numel()
+        if t.untyped_storage().nbytes() // t.element_size() < need:
+            raise ValueError(f"{name}: {num_layers} layers {layer_stride_elems} elements apart exceed its storage")
+    _check_device(*specs)
     rc = load().spec_kv_compact(_ptr(k_pages), _ptr(v_pages), _ptr(page_table), _ptr(prefix_lens), _ptr(accept_nodes),
                                 _ptr(accept_len), B, max_T, Hkv, d, page, page_table.shape[1], P, num_layers,
                                 layer_stride_elems, _ptr(new_prefix_lens), _stream(k_pages))
