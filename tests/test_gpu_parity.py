@@ -130,6 +130,51 @@ def test_attention_deterministic_many_splits(monkeypatch):
         assert np.array_equal(ref[1], again[1])
 
 
+# ---------------------------------------------------------------- standalone tree mask
+@pytest.mark.parametrize("with_T_b", [True, False], ids=["ragged_T", "full_T"])
+@pytest.mark.parametrize("with_outputs", [True, False], ids=["depth_status", "mask_only"])
+def test_tree_mask_matches_oracle(with_T_b, with_outputs):
+    """spec_tree_mask: ancestry words, depths and INVALID_PARENT status bit-exact against the oracle on random,
+    chain, star and invalid-parent trees of 1 to 65 nodes; entries past T_b come back zero, parents past T_b
+    are never read, and the optional outputs may be omitted."""
+    from oracle.tree import tree_mask as oracle_mask
+    from tree_attention_verification_03_amd import ops
+
+    rng = np.random.default_rng(77 + 2 * with_T_b + with_outputs)
+    max_T = 65
+    Ts = [1, 2, 65, 33, 17, 65, 9, 64, 5, 65, 40, 3] if with_T_b else [max_T] * 12
+    kinds = ["random", "chain", "star", "random", "chain", "random", "star", "random", "random", "bad", "bad",
+             "random"]
+    B = len(Ts)
+    parents = rng.integers(-1000, 1000, size=(B, max_T)).astype(np.int32)  # garbage past T_b
+    for b, (T, kind) in enumerate(zip(Ts, kinds)):
+        parents[b, :T] = random_parents(rng, T, "random" if kind == "bad" else kind)
+        if kind == "bad" and T > 4:  # parents outside [0, i): at or past the node, and negative
+            parents[b, 3] = 3
+            parents[b, T - 1] = T + 5
+            parents[b, T // 2] = -1
+    dev = torch.device("cuda")
+    par = torch.from_numpy(parents).to(dev)
+    T_b = torch.tensor(Ts, dtype=torch.int32, device=dev) if with_T_b else None
+    anc = torch.full((B, max_T), 0x5A5A5A5A5A5A5A5A, dtype=torch.int64, device=dev)
+    depth = torch.full((B, max_T), -7, dtype=torch.int32, device=dev) if with_outputs else None
+    status = torch.full((B,), 0x55, dtype=torch.int32, device=dev) if with_outputs else None
+    log(f"[mask] B={B} T_b={'ragged' if with_T_b else 'none'} outputs={with_outputs}")
+    ops.spec_tree_mask(par, T_b, anc, depth, status)
+    torch.cuda.synchronize()
+    anc_h = anc.cpu().numpy()
+    for b, T in enumerate(Ts):
+        want_anc, want_depth, want_status = oracle_mask(parents[b], T)
+        assert [int(x) & 0xFFFFFFFFFFFFFFFF for x in anc_h[b, :T]] == [int(x) for x in want_anc], f"anc b={b}"
+        assert (anc_h[b, T:] == 0).all(), f"anc past T_b b={b}"
+        if with_outputs:
+            assert depth[b, :T].cpu().numpy().tolist() == want_depth.tolist(), f"depth b={b}"
+            assert (depth[b, T:].cpu().numpy() == 0).all()
+            assert int(status[b]) == want_status, f"status b={b}"
+    if with_outputs:
+        assert any(int(s) for s in status.cpu().numpy())  # the invalid-parent trees raised the bit
+
+
 # ---------------------------------------------------------------- tree build, small cases
 @pytest.mark.parametrize("fused", [True, False], ids=["fused_finish", "finish_launch"])
 @pytest.mark.parametrize("seed", range(6))

@@ -1,9 +1,8 @@
 """GPU parity on the five workloads at full size, against the CPU oracle.
 
 Tree build, masks, accepted paths, tokens and status bit-exact; attention
-within max-abs 1e-2 and relative L2 5e-3 over every (sequence, head) pair, or
-for the largest workload over sampled pairs the oracle recomputes one by one
-(shortest and longest sequences and others, two heads of every KV group).
+within max-abs 1e-2 and relative L2 5e-3 over every (sequence, head) pair of
+every workload, the largest included, and bit-identical on repeated calls.
 Also the 64-node-tree workload with planted acceptance followed by KV
 compaction.
 """
@@ -42,15 +41,8 @@ def test_full_tree_build(full):
 def test_full_attention(full):
     w, host = full["w"], full["host"]
     parents = parents_array(w, full["trees"])
-    pairs = None
-    if w.B * w.Hq > 512:  # largest workload: sample sequences (shortest, longest, others) x heads of every KV group
-        order = np.argsort(w.prefix_lens)
-        seqs = sorted(set([int(order[0]), int(order[-1])] + [int(x) for x in order[:: max(1, w.B // 6)]]))
-        G = w.Hq // w.Hkv
-        heads = sorted(set([g * G for g in range(w.Hkv)] + [g * G + G - 1 for g in range(w.Hkv)]))
-        pairs = [(b, h) for b in seqs for h in heads]
-    log(f"[full] oracle attention on {w.name} ({'all' if pairs is None else len(pairs)} pairs)")
-    max_abs, rel, lse_err = compare_attention(w, host["attn_out"], host["lse"], parents, pairs)
+    log(f"[full] oracle attention on {w.name} (all {w.B * w.Hq} sequence x head pairs)")
+    max_abs, rel, lse_err = compare_attention(w, host["attn_out"], host["lse"], parents)
     log(f"[full] {w.name}: max_abs={max_abs:.3e} rel_l2={rel:.3e} lse_err={lse_err:.3e}")
     assert max_abs <= ATTN_MAX_ABS and rel <= ATTN_REL_L2 and lse_err <= LSE_ABS
     assert (host["attn_status"] == 0).all()
@@ -62,9 +54,9 @@ def test_full_verify(full):
 
 
 def test_full_attention_deterministic(full):
+    """Repeated calls give bit-identical outputs (split-K partials merged in a fixed order, no float atomics)."""
     step = full["step"]
-    if full["w"].B * full["w"].Hq > 512:
-        pytest.skip("covered on the smaller workloads")
+    log(f"[full] attention determinism x3 on {full['w'].name}")
     a = step.o.attn_out.clone()
     for _ in range(3):
         step.attention()
@@ -124,8 +116,8 @@ def test_full_verify_from_logits(cfg):
     torch.cuda.synchronize()
     host = {k: to_np(getattr(step.o, k)) for k in ("tokens", "parents", "q_row", "accept_len", "accept_nodes",
                                                    "out_tokens", "status")}
-    seqs = [b for b in range(w.B) if int(w.modes[b]) == 1][:8] + [b for b in range(w.B) if int(w.modes[b]) == 0][:2]
-    log(f"[full] oracle verify from logits on {spec.name} ({len(seqs)} sequences)")
+    seqs = list(range(w.B))
+    log(f"[full] oracle verify from logits on {spec.name} (all {len(seqs)} sequences)")
     res = tree_verify_logits(w.target_logits, w.temperature, w.draft_probs, host["q_row"], host["tokens"],
                              host["parents"], w.T_b, w.modes, w.philox_key, w.philox_offset, seqs)
     for b, (n, nodes, out, st) in zip(seqs, res):
