@@ -32,6 +32,8 @@
 //                        so the loop cannot deadlock whatever is resident.
 // The walk emits the longest valid path (greedy) or the chain of ACCEPT links
 // (sampling), the tokens, bonus and status, and re-zeroes the workspace.
+#include <stdlib.h>
+
 #include "api_common.h"
 #include "spec_common.h"
 
@@ -62,6 +64,24 @@ constexpr int kMaxKids = 64;  // children of one node (T <= 65)
 constexpr int kQ = 32;
 constexpr int kKS = 16;
 constexpr int kMaxSampleMap = 2048;  // sampling sequences a worker lists in LDS
+constexpr uint32_t kSpinLimit = 1u << 22;  // polls a worker makes for a queue slot before it gives up
+
+// Residual mass from a window of ratio bins (the fast path). Over a node's row, the mass after j rejections,
+// W(G) = sum_v max(0, P[v] S_Q - G Q[v]) with G = gamma_j, only counts elements whose ratio P/Q exceeds
+// theta = G / S_Q. Pass 0 sorts each slice's elements with P > 0 by n = floor(8 P / Q): for 1/2 <= P/Q < 8
+// into bins 0..59 (bin n - 4, keeping the bin's sums of P and Q and the elements themselves, grouped by
+// bin), P/Q >= 8 or Q = 0 into the high set (sums only), smaller ratios nowhere. For 1/2 <= theta < 8 every
+// element of a bin above floor(8 theta) counts in full (P S_Q - G Q >= 0) and every element below it not at
+// all, so W(G) is the high set's and those bins' sums plus an exact per-element sum over the one bin that
+// holds theta: no pass over the row. theta_1 = S_P / S_Q (1 for normalised rows) and each rejection adds at
+// most theta_1, so a node with up to 8 children stays inside the window; outside it, or when a slice holds
+// more window elements than it keeps, the node takes residual passes over its row as before.
+constexpr int kWinBins = 60;     // window bins (ratios 1/2 .. 8 in steps of 1/8)
+constexpr int kWinHi = 60;       // record slot of the high set
+constexpr int kWinSlots = 64;    // record slots per slice (bins, high set, padding)
+constexpr int kWinCap = 2048;    // window elements a slice keeps (a quarter of its elements)
+constexpr int kFastMaxSl = 16;   // slices per row the decision keeps in LDS (V <= 131072)
+constexpr uint64_t kWinOverflow = 4;  // pass-0 slice flag: the window was not (fully) recorded
 
 struct VerifyWs {
   uint64_t* keys;      // [B*max_T] greedy argmax keys (0 = empty)
@@ -77,6 +97,10 @@ struct VerifyWs {
   uint64_t* kidpq;     // [B*max_T][kMaxKids] children: (fx(p[t]) << 32) | fx(q[t]), ~0 = invalid token
   uint32_t* queue;     // [B*max_T*nsl] published dynamic items (node * nsl + slice + 1), 0 = empty
   uint32_t* qctl;      // head, tail, nodes done, workers exited: at qctl[kQ * i], 128 bytes apart
+  // window records (null when a row has more than kFastMaxSl slices), written by pass 0 of a node with a q row
+  uint32_t* wcnt;      // [B*max_T*nsl][kWinSlots] elements per window bin; slot kWinHi: all window elements
+  uint64_t* wsum;      // [B*max_T*nsl][kWinSlots][2] sums of P and Q per bin; slot kWinHi: the high set
+  uint64_t* wel;       // [B*max_T*nsl][kWinCap] window elements (P << 32 | Q), grouped by bin
 };
 
 int sample_slices(int V) { return (V + kSampleSlice - 1) / kSampleSlice; }
@@ -105,6 +129,14 @@ VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
   w.kidpq = reinterpret_cast<uint64_t*>(take(8 * n * kMaxKids));
   w.queue = reinterpret_cast<uint32_t*>(take(4 * n * nsl));
   w.qctl = reinterpret_cast<uint32_t*>(take(4 * kQ * sizeof(uint32_t)));
+  w.wcnt = nullptr;
+  w.wsum = nullptr;
+  w.wel = nullptr;
+  if (nsl <= size_t(kFastMaxSl)) {
+    w.wcnt = reinterpret_cast<uint32_t*>(take(4 * n * nsl * kWinSlots));
+    w.wsum = reinterpret_cast<uint64_t*>(take(16 * n * nsl * kWinSlots));
+    w.wel = reinterpret_cast<uint64_t*>(take(8 * n * nsl * kWinCap));
+  }
   *total = off;
   return w;
 }
@@ -123,6 +155,8 @@ struct VerifyArgs {
   uint64_t key0, key1, offset;
   int B, max_T, R, V, n_slices, slice, nsl, n_greedy_blocks, n_workers;
   int row_tickets;  // greedy: count slice blocks per row first (sequences with many slice blocks)
+  int fast;         // sampling: residual masses from the window records when they allow it
+  uint32_t spin_limit;  // sampling: polls of a worker waiting for a queue slot before it gives up
   int32_t* accept_len;
   int32_t* accept_nodes;
   int32_t* out_tokens;
@@ -453,43 +487,146 @@ __device__ __forceinline__ void pass_done(const VerifyWs& w, const VerifyArgs& a
   sample_decide<VEC, LG>(w, a, b, u, T);
 }
 
-// pass 0 over slice s: sums of fx(p) and fx(q), argmax key of fx(p), NaN bits, published per slice
-// (the node's decision block reduces them)
+// window bin of an element (see kWinBins): 0..kWinBins-1 for 1/2 <= P/Q < 8 (floor(8 P / Q) - 4), kWinHi
+// for P/Q >= 8 or Q = 0, -1 for P = 0 or P/Q < 1/2. e = 8 P / Q from a hardware reciprocal is within 3e-5 of
+// the exact quotient wherever it matters (below 64.0001), so floor(e) is exact unless e lies within 1e-4 of
+// an integer; only then do 64-bit integer products decide
+__device__ __forceinline__ int win_bin(uint32_t P, uint32_t Q) {
+  if (P == 0u) return -1;
+  if (Q == 0u) return kWinHi;
+  const float e = float(P) * 8.f * __builtin_amdgcn_rcpf(float(Q));
+  if (e >= 64.0001f) return kWinHi;
+  if (e < 3.9999f) return -1;
+  int n = int(e);
+  const float r = rintf(e);
+  if (fabsf(e - r) < 1e-4f) {  // near a bin edge k: 8 P >= k Q decides
+    const int k = int(r);
+    n = (uint64_t(P) << 3) >= uint64_t(k) * Q ? k : k - 1;
+  }
+  return n >= 64 ? kWinHi : (n < 4 ? -1 : n - 4);
+}
+
+// pass 0 over slice s: sums of fx(p) and fx(q), argmax key of fx(p), NaN bits, published per slice (the
+// node's decision block reduces them); for a node with a q row also the slice's window record and its window
+// elements grouped by bin. Window elements are first staged in LDS, each wave in its own region at a running
+// ballot offset, then counted and summed per bin, then placed by per-bin cursors: the order inside a bin is
+// arbitrary, and nothing depends on it.
 template <bool VEC, bool LG>
 __device__ __forceinline__ void sample_pass0(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T, int s) {
   __shared__ uint64_t red[kWaves][3];
+  __shared__ uint64_t amr[kWaves];
+  __shared__ uint32_t wc_s[kWinSlots], wcur_s[kWinSlots], wn_s[kWaves];
+  __shared__ unsigned long long wp_s[kWinSlots], wq_s[kWinSlots];
+  __shared__ uint64_t stage_s[kWinCap];
+  __shared__ uint8_t sbin_s[kWinCap];
+  const int tid = threadIdx.x, lane = tid & 63;
   const size_t node = size_t(b) * a.max_T + u;
+  const size_t rec = node * a.nsl + s;
   const float* prow = sample_row(a, node);
   const float* qrow = node_qrow_any(a, b, u);
   const int lo = s * kSampleSlice, hi = min(a.V, lo + kSampleSlice);
-  uint64_t sp = 0, sq = 0, am = 0;
+  const bool win = a.fast && qrow != nullptr && w.wcnt != nullptr;
+  if (win && tid < kWinSlots) {
+    wc_s[tid] = 0u;
+    wp_s[tid] = 0ull;
+    wq_s[tid] = 0ull;
+  }
+  if (win) __syncthreads();
+  constexpr uint32_t kCapW = kWinCap / kWaves;  // staging slots per wave
+  uint64_t* const stage_w = stage_s + (tid >> 6) * kCapW;
+  uint8_t* const sbin_w = sbin_s + (tid >> 6) * kCapW;
+  uint32_t run = 0;  // the wave's window elements so far (wave-uniform)
+  uint64_t sp = 0, sq = 0, am = 0, hp = 0, hq = 0;
   uint32_t nan = 0;
   slice_for<VEC>(prow, qrow, lo, hi, [&] { return prob_row<LG>(a, node); }, [&](int v, float x, float y) {
     nan |= (x != x ? 1u : 0u) | (y != y ? 2u : 0u);
-    const uint32_t P = fx(x);
+    const uint32_t P = fx(x), Q = fx(y);
     sp += P;
+    sq += Q;
     const uint64_t k = (uint64_t(P) << 32) | uint64_t(0xffffffffu - uint32_t(v));
     am = k > am ? k : am;
-    sq += fx(y);
+    if (win) {
+      const int bin = win_bin(P, Q);
+      if (bin == kWinHi) {
+        hp += P;
+        hq += Q;
+      }
+      const bool in = bin >= 0 && bin < kWinBins;
+      const uint64_t m = __ballot(in);
+      const uint32_t pos = run + uint32_t(__popcll(m & ((1ull << lane) - 1)));
+      if (in && pos < kCapW) {
+        stage_w[pos] = (uint64_t(P) << 32) | Q;
+        sbin_w[pos] = uint8_t(bin);
+      }
+      run += uint32_t(__popcll(m));
+    }
   });
+  if (win && lane == 0) wn_s[tid >> 6] = run;
   am = wave_max_u64(am);
   // NaN bits travel through the block sum as counts (lane 0 of each wave): p in bits 0-3, q in bits 4-7
   const uint32_t nw = wave_or_u32(nan);
-  uint64_t nn = (threadIdx.x & 63) == 0 ? uint64_t(nw & 1u) + ((nw & 2u) ? 16u : 0u) : 0u;
-  {
-    __shared__ uint64_t amr[kWaves];
-    if ((threadIdx.x & 63) == 0) amr[threadIdx.x >> 6] = am;
-    block_sum3(sp, sq, nn, red);
-    if (threadIdx.x == 0) {
-      for (int i = 1; i < kWaves; ++i) am = amr[i] > am ? amr[i] : am;
-      uint64_t* ss = w.ssum + (node * a.nsl + s) * 2;
-      uint64_t* ps = w.psum + (node * a.nsl + s) * 3;
-      st_agent(ss, sp);
-      st_agent(ss + 1, uint64_t(0));
-      st_agent(ps, sq);
-      st_agent(ps + 1, am);
-      st_agent(ps + 2, uint64_t(((nn & 15u) ? 1u : 0u) | ((nn >> 4) ? 2u : 0u)));
+  uint64_t nn = lane == 0 ? uint64_t(nw & 1u) + ((nw & 2u) ? 16u : 0u) : 0u;
+  if (lane == 0) amr[tid >> 6] = am;
+  if (win) {
+    hp = wave_sum_u64(hp);
+    hq = wave_sum_u64(hq);
+    if (lane == 0) {
+      atomicAdd(&wp_s[kWinHi], (unsigned long long)hp);
+      atomicAdd(&wq_s[kWinHi], (unsigned long long)hq);
     }
+  }
+  block_sum3(sp, sq, nn, red);  // its barrier also completes the staging
+  uint64_t wflag = kWinOverflow;
+  if (win) {
+    uint32_t total = 0;
+    bool over = false;
+    for (int i = 0; i < kWaves; ++i) {
+      total += wn_s[i];
+      over |= wn_s[i] > kCapW;
+    }
+    // staged element j: wave region j / kCapW, slot j % kCapW, valid below that wave's count
+    auto staged = [&](int j) { return uint32_t(j % kCapW) < min(wn_s[j / kCapW], kCapW); };
+    for (int j = tid; j < kWinCap; j += kThreads) {  // per-bin counts and sums
+      if (!staged(j)) continue;
+      const int bin = sbin_s[j];
+      const uint64_t pq = stage_s[j];
+      atomicAdd(&wc_s[bin], 1u);
+      atomicAdd(&wp_s[bin], (unsigned long long)(pq >> 32));
+      atomicAdd(&wq_s[bin], (unsigned long long)uint32_t(pq));
+    }
+    __syncthreads();
+    if (tid < kWave) {  // the bins' offsets
+      const uint32_t c = tid < kWinBins ? wc_s[tid] : 0u;
+      uint32_t incl = c;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+      }
+      wcur_s[tid] = incl - c;
+    }
+    __syncthreads();
+    if (!over) {
+      wflag = 0;
+      uint64_t* el = w.wel + rec * kWinCap;
+      for (int j = tid; j < kWinCap; j += kThreads)
+        if (staged(j)) st_agent(el + atomicAdd(&wcur_s[sbin_s[j]], 1u), stage_s[j]);
+    }
+    if (tid < kWinSlots) {
+      st_agent(w.wcnt + rec * kWinSlots + tid, tid < kWinBins ? wc_s[tid] : (tid == kWinHi ? total : 0u));
+      st_agent(w.wsum + (rec * kWinSlots + tid) * 2, uint64_t(wp_s[tid]));
+      st_agent(w.wsum + (rec * kWinSlots + tid) * 2 + 1, uint64_t(wq_s[tid]));
+    }
+  }
+  if (tid == 0) {
+    for (int i = 1; i < kWaves; ++i) am = amr[i] > am ? amr[i] : am;
+    uint64_t* ss = w.ssum + rec * 2;
+    uint64_t* ps = w.psum + rec * 3;
+    st_agent(ss, sp);
+    st_agent(ss + 1, uint64_t(0));
+    st_agent(ps, sq);
+    st_agent(ps + 1, am);
+    st_agent(ps + 2, uint64_t(((nn & 15u) ? 1u : 0u) | ((nn >> 4) ? 2u : 0u)) | wflag);
   }
   pass_done<VEC, LG>(w, a, b, u, T);
 }
@@ -522,20 +659,103 @@ __device__ __forceinline__ void sample_passN(const VerifyWs& w, const VerifyArgs
   pass_done<VEC, LG>(w, a, b, u, T);
 }
 
+// LDS of a decision's fast path: the node's window records, per slice and bin
+struct WinLds {
+  uint32_t cnt[kFastMaxSl][kWinSlots];
+  uint64_t sp[kFastMaxSl][kWinSlots], sq[kFastMaxSl][kWinSlots];  // slot kWinHi: the high set; above it zero
+};
+
+// the node's window records into LDS (every thread; no barrier: the caller's next one publishes them)
+__device__ __forceinline__ void win_load(const VerifyWs& w, const VerifyArgs& a, size_t node, WinLds& L) {
+  for (int i = threadIdx.x; i < a.nsl * kWinSlots; i += kThreads) {
+    const int sl = i / kWinSlots, n = i - sl * kWinSlots;
+    const size_t r = (node * a.nsl + sl) * kWinSlots + n;
+    L.cnt[sl][n] = n < kWinBins ? ld_agent(w.wcnt + r) : 0u;
+    L.sp[sl][n] = n <= kWinHi ? ld_agent(w.wsum + r * 2) : 0ull;
+    L.sq[sl][n] = n <= kWinHi ? ld_agent(w.wsum + r * 2 + 1) : 0ull;
+  }
+}
+
+// the window admits gamma: 1/2 <= gamma / S_Q < 8
+__device__ __forceinline__ bool win_admits(uint64_t gamma, uint64_t S_Q) {
+  const u128 g8 = u128(gamma) << 3;
+  return g8 >= (u128(S_Q) << 2) && g8 < (u128(S_Q) << 6);
+}
+
+// sum over each 16-lane row of a wave (DPP only)
+__device__ __forceinline__ u128 row16_sum_u128(u128 x) {
+  x += dpp_u128<dpp::kXor1>(x);
+  x += dpp_u128<dpp::kXor2>(x);
+  x += dpp_u128<dpp::kHalfMirror>(x);
+  return x + dpp_u128<dpp::kMirror>(x);
+}
+
+__device__ __forceinline__ uint64_t row16_sum_u64(uint64_t x) {
+  x += dpp_u64<dpp::kXor1>(x);
+  x += dpp_u64<dpp::kXor2>(x);
+  x += dpp_u64<dpp::kHalfMirror>(x);
+  return x + dpp_u64<dpp::kMirror>(x);
+}
+
+// Residual masses under gamma (admitted by the window) of every slice of the row into ssl, their total
+// returned (every thread). Slice s is served by the 16 threads of row s of the block: bins above the
+// straddling one and the high set from their sums, the straddling bin element by element.
+__device__ __forceinline__ u128 win_mass(const VerifyWs& w, const VerifyArgs& a, size_t node, uint64_t S_Q, uint64_t gamma,
+                                         const WinLds& L, u128* ssl) {
+  const int tid = threadIdx.x, sl = tid >> 4, j = tid & 15, nsl = a.nsl;
+  const int nb = int(div_u128_u64(u128(gamma) << 3, S_Q)) - 4;  // straddling bin, in [0, kWinBins)
+  uint32_t below = 0, cnt = 0;
+  uint64_t fp = 0, fq = 0;
+  if (sl < nsl) {
+#pragma unroll
+    for (int n = j; n < kWinSlots; n += 16) {
+      const uint32_t c = L.cnt[sl][n];
+      below += n < nb ? c : 0u;
+      cnt += n == nb ? c : 0u;
+      fp += n > nb ? L.sp[sl][n] : 0ull;
+      fq += n > nb ? L.sq[sl][n] : 0ull;
+    }
+  }
+  below = uint32_t(row16_sum_u64(below));
+  cnt = uint32_t(row16_sum_u64(cnt));
+  fp = row16_sum_u64(fp);
+  fq = row16_sum_u64(fq);
+  u128 acc = 0;
+  if (sl < nsl) {
+    const uint64_t* el = w.wel + (node * nsl + sl) * kWinCap + below;
+    for (int e0 = j; e0 < int(cnt); e0 += 8 * 16) {  // eight independent loads per round trip
+      uint64_t pq[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pq[k] = e0 + 16 * k < int(cnt) ? ld_agent(el + e0 + 16 * k) : 0ull;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += residual(uint32_t(pq[k] >> 32), uint32_t(pq[k]), S_Q, gamma, false);
+    }
+  }
+  acc = row16_sum_u128(acc);
+  if (sl < nsl && j == 0) ssl[sl] = u128(S_Q) * fp - u128(gamma) * fq + acc;
+  __syncthreads();
+  u128 W = 0;
+  for (int i = 0; i < nsl; ++i) W += ssl[i];
+  return W;
+}
+
 template <bool VEC, bool LG>
 __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
   __shared__ int kid_s[kMaxKids], nkid_s;
   __shared__ uint64_t kpq_s[kMaxKids];  // children: (fx(p[t]) << 32) | fx(q[t]), ~0 = invalid token
-  __shared__ int act_s;  // accepted child, -1: residual pass enqueued, -2: resample
-  __shared__ u128 W_s, excl_s, wtot_s[kWaves];
-  __shared__ uint64_t SQ_s, gamma_s, AM_s;
+  __shared__ uint64_t km_s[kMaxKids];   // node c's acceptance integer m at km_s[c - 1]
+  __shared__ int act_s;  // accepted child; -1: a rejection needs the next residual mass; -2: resample
+  __shared__ int fast_s, fastok_s, ki_s, tested_s, test_s;
+  __shared__ u128 W_s, wtot_s[kWaves];
+  __shared__ uint64_t SP_s, SQ_s, gamma_s, AM_s, K_s;
   __shared__ uint32_t flags_s;
   __shared__ int plain_s, bonus_s, pass_s;
-  __shared__ u128 ssl_s[kThreads];  // the pass's slice sums (the first kThreads slices)
+  __shared__ u128 ssl_s[kThreads];  // per-slice masses of the current W (the first kThreads slices)
   __shared__ u128 wred_s[kWaves];
   __shared__ uint64_t red_s[kWaves][3];
   __shared__ int found_s;
   __shared__ u128 run_s, tau_s;
+  __shared__ WinLds win_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, max_T = a.max_T, V = a.V;
   const size_t node = size_t(b) * max_T + u;
   NodeState* ns = w.node + node;
@@ -548,7 +768,9 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
     __device__ ~PrioRestore() { __builtin_amdgcn_s_setprio(0); }
   } prio_restore;
 
-  // ---- one round trip: the node's state, every slice's results, its children and their cache
+  // ---- one round trip: the node's state, every slice's results, its children and their cache, and (a node
+  // that may test children) its window records; meanwhile wave 1 draws the uniforms of every potential child
+  // and the node's own resampling uniform
   int pass = 0, kid = 0, tested = 0;
   uint32_t flags = 0;
   uint64_t gamma = 0, SPc = 0, SQc = 0, AMc = 0;
@@ -563,6 +785,8 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
     SQc = ld_agent(&ns->sq);
     AMc = ld_agent(&ns->am);
   }
+  const bool may_win = a.fast && w.wcnt != nullptr && qr >= 0 && qr < a.R && a.draft != nullptr;
+  if (may_win) win_load(w, a, node, win_s);
   u128 wsum = 0;  // sum of the pass's slice sums (pass 0: of fx(p))
   uint64_t sq = 0, am = 0, nanb = 0;
   for (int sl = tid; sl < a.nsl; sl += kThreads) {
@@ -587,6 +811,14 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
       c_tok = a.tokens[size_t(b) * max_T + c];
     }
     cached = ld_agent(w.kidpq + node * kMaxKids + lane);
+  } else if (wave == 1) {
+    if (lane + 1 < T) {
+      const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(lane + 1), 0, a.key0, a.key1);
+      km_s[lane] = (r.w[0] >> 40) + 1;  // r = m / 2^24 in (0, 1]
+    }
+  } else if (wave == 2 && lane == 0) {
+    const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(u), 0, a.key0, a.key1);
+    K_s = r.w[1] >> 32;
   }
   // ---- reductions (u128 sum, sum, max, or) and the child list in index order
   wsum = wave_sum_u128(wsum);
@@ -644,71 +876,106 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
       W = wsum;
       if (W == 0) flags |= SPEC_STATUS_ZERO_RESIDUAL;
     }
-    int act = -2;
-    for (int ki = kid; test && ki < nkid; ++ki) {
-      const int c = kid_s[ki];
-      const uint64_t pq = kpq_s[ki];
-      if (pq == ~0ull) continue;  // invalid draft token: never tested
-      tested = 1;
-      const uint32_t Pt = uint32_t(pq >> 32), Qt = uint32_t(pq);
-      const u128 Nt = residual(Pt, Qt, S_Q, gamma, false);
-      const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(c), 0, a.key0, a.key1);
-      const uint64_t m = (r.w[0] >> 40) + 1;  // r = m / 2^24 in (0, 1]
-      bool accept = false;
-      if (Nt > 0) {
-        const U192 lhs = mul_u128_u64(W, m * uint64_t(Qt));  // m Q_t W
-        const U192 rhs = shl_u192(mul_u128_u64(Nt, S_Q), 24);  // 2^24 N_t S_Q
-        accept = le_u192(lhs, rhs);
-      }
-      if (accept) {
-        act = c;
-        break;
-      }
-      // rejected: residual <- norm(max(0, residual - q)); its mass needs a pass over the row. The
-      // state and the queue reservation go out together; the items are published once both are done.
-      gamma = gamma + div_u128_u64(W, S_Q);
-      act = -1;
-      st_agent(&ns->gamma, gamma);
-      st_agent(&ns->kid, ki + 1);
-      st_agent(&ns->tested, 1);
-      st_agent(&ns->flags, flags);
-      st_agent(&ns->pass, pass + 1);
-      if (pass == 0) {
-        st_agent(&ns->sp, S_P);
-        st_agent(&ns->sq, S_Q);
-        st_agent(&ns->am, AM);
-      }
-      const uint32_t pos = ticket_add_n(&w.qctl[1 * kQ], uint32_t(a.nsl));
-      wait_global_stores();  // this wave's state and children-cache stores are complete
-      for (int sl = 0; sl < a.nsl; ++sl) st_agent(&w.queue[pos + sl], uint32_t(node * a.nsl + sl + 1));
-      break;
-    }
-    act_s = act;
-    plain_s = !tested;
-    W_s = tested ? W : u128(S_P);
+    SP_s = S_P;
     SQ_s = S_Q;
-    gamma_s = gamma;
     AM_s = AM;
+    W_s = W;
+    gamma_s = gamma;
     flags_s = flags;
+    ki_s = kid;
+    tested_s = tested;
+    test_s = test;
+    fastok_s = test && may_win && !(nanb & kWinOverflow);
   }
   __syncthreads();
-  if (act_s == -1) return;
+  // ---- the children in index order: the block tests them one after another (thread 0); after a rejection
+  // the next residual mass comes from the window records when they admit the new gamma, else from a
+  // residual pass over the row that a later decision of this node picks up
+  for (;;) {
+    if (tid == 0) {
+      int act = -2, ki = ki_s, tst = tested_s;
+      const u128 W = W_s;
+      const uint64_t S_Q = SQ_s;
+      uint64_t g = gamma_s;
+      for (; test_s && ki < nkid; ++ki) {
+        const int c = kid_s[ki];
+        const uint64_t pq = kpq_s[ki];
+        if (pq == ~0ull) continue;  // invalid draft token: never tested
+        tst = 1;
+        const uint32_t Pt = uint32_t(pq >> 32), Qt = uint32_t(pq);
+        const u128 Nt = residual(Pt, Qt, S_Q, g, false);
+        const uint64_t m = km_s[c - 1];
+        bool accept = false;
+        if (Nt > 0) {
+          const U192 lhs = mul_u128_u64(W, m * uint64_t(Qt));  // m Q_t W
+          const U192 rhs = shl_u192(mul_u128_u64(Nt, S_Q), 24);  // 2^24 N_t S_Q
+          accept = le_u192(lhs, rhs);
+        }
+        if (accept) {
+          act = c;
+          break;
+        }
+        // rejected: residual <- norm(max(0, residual - q)), whose mass is needed next
+        g = g + div_u128_u64(W, S_Q);
+        act = -1;
+        ++ki;
+        break;
+      }
+      ki_s = ki;
+      tested_s = tst;
+      gamma_s = g;
+      act_s = act;
+      fast_s = act == -1 && fastok_s && win_admits(g, S_Q);
+    }
+    __syncthreads();
+    if (act_s != -1) break;
+    if (!fast_s) {
+      // a residual pass over the row: the state and the queue reservation go out together; the items are
+      // published once both are done
+      if (tid == 0) {
+        st_agent(&ns->gamma, gamma_s);
+        st_agent(&ns->kid, ki_s);
+        st_agent(&ns->tested, 1);
+        st_agent(&ns->flags, flags_s);
+        st_agent(&ns->pass, pass + 1);
+        if (pass == 0) {
+          st_agent(&ns->sp, SP_s);
+          st_agent(&ns->sq, SQ_s);
+          st_agent(&ns->am, AM_s);
+        }
+        const uint32_t pos = ticket_add_n(&w.qctl[1 * kQ], uint32_t(a.nsl));
+        wait_global_stores();  // this wave's state and children-cache stores are complete
+        for (int sl = 0; sl < a.nsl; ++sl) st_agent(&w.queue[pos + sl], uint32_t(node * a.nsl + sl + 1));
+      }
+      return;
+    }
+    // the mass (and every slice's share, for a resample) from the window records
+    const u128 W = win_mass(w, a, node, SQ_s, gamma_s, win_s, ssl_s);
+    if (tid == 0) {
+      W_s = W;
+      if (W == 0) flags_s |= SPEC_STATUS_ZERO_RESIDUAL;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    plain_s = !tested_s;
+    if (!tested_s) W_s = u128(SP_s);
+  }
+  __syncthreads();
   if (act_s >= 0) {
     sample_finish(w, a, b, u, act_s, -1, flags_s, false);
     return;
   }
-  // ---- no draft accepted: resample from the residual (or from p if nothing was tested)
+  // ---- no draft accepted: resample from the residual (or from p if nothing was tested); ssl_s holds the
+  // masses of the first kThreads slices (of the pass that gave W, or from the window records)
   const u128 W = W_s;
   const bool plain = plain_s;
   if (W == 0) {
     if (tid == 0) bonus_s = int(0xffffffffu - uint32_t(AM_s));  // smallest-index argmax of p
   } else {
     // threshold: smallest v with 2^32 * prefix(v) > K W  <=>  prefix(v) > floor(K W / 2^32)
-    // threshold: smallest v with 2^32 * prefix(v) > K W  <=>  prefix(v) > floor(K W / 2^32)
     if (tid == 0) {
-      const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(u), 0, a.key0, a.key1);
-      const uint64_t K = r.w[1] >> 32;
-      const U192 kw = mul_u128_u64(W, K);
+      const U192 kw = mul_u128_u64(W, K_s);
       tau_s = (u128(kw.hi) << 96) | (u128(kw.mid) << 32) | u128(kw.lo >> 32);
       run_s = 0;
       found_s = -1;
@@ -740,50 +1007,42 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
       }
     }
     __syncthreads();
-    // the block searches the chosen slice in two halves; per half each thread sums a contiguous range
-    // of E elements (held in registers), a block scan gives every range's prefix, and the one range
-    // holding the crossing is walked element by element
+    // the block searches the chosen slice in one pass: each thread sums a contiguous range of E elements, a
+    // block scan gives every range's prefix, and the one thread whose range holds the crossing reads its
+    // range again and walks it element by element
     const uint64_t S_Q = SQ_s, gamma = gamma_s;
-    constexpr int E = kSampleSlice / (2 * kThreads);
-    const int wlo = found_s * kSampleSlice, whi = min(V, wlo + kSampleSlice);
-    u128 rem = tau_s - run_s;  // remaining threshold inside the slice
-    for (int half = 0; half < 2; ++half) {
-      const int e0 = wlo + half * (kSampleSlice / 2) + tid * E;
-      uint32_t pv[E], qv[E];
+    constexpr int E = kSampleSlice / kThreads;
+    const int e0 = found_s * kSampleSlice + tid * E, whi = min(V, found_s * kSampleSlice + kSampleSlice);
+    const u128 rem = tau_s - run_s;  // remaining threshold inside the slice
+    auto range_for = [&](auto&& f) {  // f(i, P, Q) over this thread's range in index order
       if (VEC && e0 + E <= whi) {
 #pragma unroll
         for (int i = 0; i < E; i += 4) {
           const float4 x = *reinterpret_cast<const float4*>(prow + e0 + i);
-          pv[i] = fx(pr(x.x)); pv[i + 1] = fx(pr(x.y)); pv[i + 2] = fx(pr(x.z)); pv[i + 3] = fx(pr(x.w));
           const float4 y = qrow ? *reinterpret_cast<const float4*>(qrow + e0 + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-          qv[i] = fx(y.x); qv[i + 1] = fx(y.y); qv[i + 2] = fx(y.z); qv[i + 3] = fx(y.w);
+          f(i, fx(pr(x.x)), fx(y.x));
+          f(i + 1, fx(pr(x.y)), fx(y.y));
+          f(i + 2, fx(pr(x.z)), fx(y.z));
+          f(i + 3, fx(pr(x.w)), fx(y.w));
         }
       } else {
-#pragma unroll
         for (int i = 0; i < E; ++i) {
           const int v = e0 + i;
-          pv[i] = v < whi ? fx(pr(prow[v])) : 0u;  // past the slice: adds nothing
-          qv[i] = (qrow && v < whi) ? fx(qrow[v]) : 0u;
+          if (v < whi) f(i, fx(pr(prow[v])), qrow ? fx(qrow[v]) : 0u);  // past the slice: adds nothing
         }
       }
-      u128 tsum = 0;
-#pragma unroll
-      for (int i = 0; i < E; ++i) tsum += residual(pv[i], qv[i], S_Q, gamma, plain);
-      const u128 ex = block_exclusive_scan_u128(tsum, wtot_s);
-      if (tsum > 0 && ex <= rem && rem < ex + tsum) {
-        u128 run = ex;
-#pragma unroll
-        for (int i = 0; i < E; ++i) {
-          run += residual(pv[i], qv[i], S_Q, gamma, plain);
-          if (run > rem && bonus_s < 0) bonus_s = e0 + i;
-        }
-      }
-      // total of this half (last thread's inclusive prefix) for the second half's threshold
-      if (tid == kThreads - 1) excl_s = ex + tsum;
-      __syncthreads();
-      if (bonus_s >= 0) break;
-      rem -= excl_s;
-      __syncthreads();
+    };
+    u128 tsum = 0;
+    range_for([&](int, uint32_t P, uint32_t Q) { tsum += residual(P, Q, S_Q, gamma, plain); });
+    const u128 ex = block_exclusive_scan_u128(tsum, wtot_s);
+    if (tsum > 0 && ex <= rem && rem < ex + tsum) {
+      u128 run = ex;
+      int hit = -1;
+      range_for([&](int i, uint32_t P, uint32_t Q) {
+        run += residual(P, Q, S_Q, gamma, plain);
+        if (run > rem && hit < 0) hit = e0 + i;
+      });
+      bonus_s = hit;
     }
   }
   __syncthreads();
@@ -942,6 +1201,39 @@ __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArg
   walk(w, a, b);
 }
 
+// A sampling sequence whose nodes did not all finish (its node count is neither 0 - walked and reset, or
+// never started, which cannot happen since leaves need no residual pass - nor complete): outputs voided
+// (accept_len 0, accept_nodes {0, -1, ...}, out_tokens all -1), status SPEC_STATUS_VERIFY_TIMEOUT, its node
+// states and count cleared; every queue slot still holding an item is emptied, so the next call starts clean.
+__device__ __forceinline__ void timeout_cleanup(const VerifyWs& w, const VerifyArgs& a, uint32_t cap) {
+  const int max_T = a.max_T;
+  for (int b = threadIdx.x; b < a.B; b += kThreads) {
+    if (a.mode[b] != SPEC_MODE_SAMPLE || ld_agent(&w.tickets[size_t(b) * kQ]) == 0u) continue;
+    const size_t base = size_t(b) * max_T;
+    a.accept_len[b] = 0;
+    a.status[b] = SPEC_STATUS_VERIFY_TIMEOUT;
+    for (int k = 0; k < max_T; ++k) {
+      a.accept_nodes[base + k] = k == 0 ? 0 : -1;
+      a.out_tokens[base + k] = -1;
+      NodeState* ns = w.node + base + k;
+      st_agent(&ns->sp, uint64_t(0));
+      st_agent(&ns->sq, uint64_t(0));
+      st_agent(&ns->am, uint64_t(0));
+      st_agent(&ns->gamma, uint64_t(0));
+      st_agent(&ns->ticket, 0u);
+      st_agent(&ns->flags, 0u);
+      st_agent(&ns->kid, 0);
+      st_agent(&ns->tested, 0);
+      st_agent(&ns->pass, 0);
+    }
+    ticket_reset(&w.tickets[size_t(b) * kQ]);
+  }
+  for (uint32_t i = threadIdx.x; i < cap; i += kThreads)
+    if (ld_agent(&w.queue[i]) != 0u) st_agent(&w.queue[i], 0u);
+  wait_global_stores();
+  __syncthreads();
+}
+
 // persistent sampling worker: takes items until every sampling node is done
 template <bool VEC, bool LG>
 __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArgs& a) {
@@ -984,7 +1276,7 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
         const uint32_t j = i - n_static;
         // wait for slot j to be published, or for every node to be done (bounded: never a hang)
         int nap = 1;  // polls back off from ~0.05 us to ~0.2 us
-        for (uint32_t spin = 0; spin < (1u << 22); ++spin) {
+        for (uint32_t spin = 0; spin < a.spin_limit; ++spin) {
           if (j < cap) {
             const uint32_t v = ld_agent(&w.queue[j]);
             if (v) {
@@ -1030,8 +1322,19 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
     else
       sample_pass0<VEC, LG>(w, a, b, u, T, sl);
   }
-  // the last worker out leaves the queue counters at zero for the next call
-  if (tid == 0 && ticket_add(&w.qctl[3 * kQ]) == uint32_t(a.n_workers - 1)) {
+  // the last worker out leaves the queue counters at zero for the next call. Every other worker has left its
+  // loop by then, so no sampling work is in flight; if some node never finished (a worker gave up waiting
+  // for a queue slot that was published later), its sequence was never walked: the last worker voids it
+  __shared__ int last_s, undone_s;
+  wait_global_stores();
+  if (tid == 0) {
+    last_s = ticket_add(&w.qctl[3 * kQ]) == uint32_t(a.n_workers - 1);
+    undone_s = last_s && ld_agent(&w.qctl[2 * kQ]) < total;
+  }
+  __syncthreads();
+  if (!last_s) return;
+  if (undone_s) timeout_cleanup(w, a, rows * uint32_t(a.nsl));
+  if (tid == 0) {
     ticket_reset(&w.qctl[0 * kQ]);
     ticket_reset(&w.qctl[1 * kQ]);
     ticket_reset(&w.qctl[2 * kQ]);
@@ -1169,6 +1472,23 @@ extern "C" size_t spec_tree_verify_workspace_size(int32_t B, int32_t max_T, int3
   return total;
 }
 
+// Host settings read at each call (for measurements and tests): SPEC_TREE_VERIFY_FAST=0 takes every residual
+// mass from passes over the row (no window records); SPEC_TREE_VERIFY_SPIN_LIMIT=n bounds a sampling worker's
+// wait for a queue slot to n polls (default 2^22; 0 makes every wait give up at once, so that the timeout
+// path can be exercised with every kernel still exiting normally).
+static int verify_fast_enabled() {
+  const char* e = getenv("SPEC_TREE_VERIFY_FAST");
+  return !(e && e[0] == '0' && e[1] == 0);
+}
+
+static uint32_t verify_spin_limit() {
+  const char* e = getenv("SPEC_TREE_VERIFY_SPIN_LIMIT");
+  if (!e || !*e) return kSpinLimit;
+  char* end = nullptr;
+  const unsigned long v = strtoul(e, &end, 10);
+  return (end && *end == 0 && v <= kSpinLimit) ? uint32_t(v) : kSpinLimit;
+}
+
 static int32_t verify_impl(const char* who, const float* target, float2* sm_part, const float* temperature,
                            const float* draft_probs, const int32_t* q_row,
                                     const int32_t* tokens, const int32_t* parents, const int32_t* T_b,
@@ -1217,6 +1537,8 @@ static int32_t verify_impl(const char* who, const float* target, float2* sm_part
   a.n_greedy_blocks = int(rows) * a.n_slices;
   a.row_tickets = (long long)a.n_slices * max_T > 256;
   a.n_workers = int(std::min<long long>(kMaxWorkers, rows * nsl));
+  a.fast = verify_fast_enabled();
+  a.spin_limit = verify_spin_limit();
   a.accept_len = accept_len;
   a.accept_nodes = accept_nodes;
   a.out_tokens = out_tokens;
