@@ -60,7 +60,6 @@ extern "C" {
 #define SPEC_STATUS_ZERO_RESIDUAL 16u  /* sampling node on the path whose residual max(0, p - q) became zero */
 #define SPEC_STATUS_INVALID_PAGE 32u   /* page-table entry outside [0, num_pages): its keys are skipped */
 #define SPEC_STATUS_INVALID_LENGTH 64u /* prefix_lens[b] < 0 or prefix + T_b beyond the page table: clamped */
-#define SPEC_STATUS_VERIFY_TIMEOUT 128u /* sampling: a worker's bounded wait gave up; outputs void (see spec_tree_verify) */
 
 /* verification modes (per sequence, int8) */
 #define SPEC_MODE_GREEDY 0

@@ -11,27 +11,26 @@
 // wins and one more token is emitted).
 //
 // Every node's outcome depends only on its own rows, its children's tokens and
-// the node's uniforms, so all nodes are evaluated in parallel, in one launch of
-// 256-thread blocks with two roles:
-//   greedy slice blocks  reduce a slice of a greedy row to a packed 64-bit key
-//                        (order(value) << 32 | ~index) merged with a 64-bit
-//                        atomicMax - order-free, bit-exact; the last slice block
-//                        of a greedy sequence (ticket) walks its tree;
-//   sampling workers     persistent blocks that pull (node, slice) items from a
-//                        device queue. Pass 0 of every sampling node (sums and
-//                        argmax of fx(p), sums of fx(q)) is a static item list;
-//                        the block finishing a node's pass (ticket) takes the
-//                        node's next decision - accept a child, or move gamma
-//                        and enqueue the residual pass, or resample - so one
-//                        node's passes spread over many CUs. Sums are exact
-//                        integers: per-slice 32-bit limb sums added with 64-bit
-//                        atomics. The block finishing a sequence's last node
-//                        walks its tree. A worker only ever waits for a queue
-//                        slot to be published or for every node to be done, and
-//                        an item is only published by a block that is running,
-//                        so the loop cannot deadlock whatever is resident.
-// The walk emits the longest valid path (greedy) or the chain of ACCEPT links
-// (sampling), the tokens, bonus and status, and re-zeroes the workspace.
+// the node's uniforms, so all nodes are evaluated in parallel, in two launches
+// of 256-thread blocks:
+//   rows kernel    greedy slice blocks reduce a slice of a greedy row to a
+//                  packed 64-bit key (order(value) << 32 | ~index) merged with
+//                  a 64-bit atomicMax - order-free, bit-exact; the last slice
+//                  block of a greedy sequence (ticket) walks its tree. Sampling
+//                  slice blocks take every (node, slice) of the sampling
+//                  sequences by a fixed stride and publish the slice's exact
+//                  integer sums of fx(p) and fx(q), the argmax of fx(p), and
+//                  its ratio-bin window record (below).
+//   decide kernel  one block per sampling node: it tests the node's children in
+//                  index order against the residual, each rejection's residual
+//                  mass from the window records, or (outside the window) from
+//                  a pass of its own over the row, then resamples if no child
+//                  is accepted; the block finishing a sequence's last node
+//                  (ticket) walks its tree.
+// Nothing waits on another block: hand-offs are the kernel boundary and
+// last-arriver tickets. The walk emits the longest valid path (greedy) or the
+// chain of ACCEPT links (sampling), the tokens, bonus and status, and
+// re-zeroes the workspace's tickets and keys.
 #include <stdlib.h>
 
 #include "api_common.h"
@@ -42,46 +41,33 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kSampleSlice = 8192;  // row elements per sampling work item
+constexpr int kSampleSlice = 8192;  // row elements per sampling slice block
 constexpr int kGreedySlice = 8192;  // row elements per greedy block (one round trip of loads) ...
 constexpr int kGreedySliceMax = 3 * kGreedySlice;  // ... up to three times that when the rows need many blocks
 constexpr int kGreedyBlocksTarget = 448;           // greedy blocks one launch keeps resident (2 per CU, less room)
-constexpr int kMaxWorkers = 512;  // persistent sampling blocks (2 per CU are resident)
-
-struct alignas(128) NodeState {  // one sampling node (own 128-byte line); all zero between calls (written by its decision blocks only)
-  uint64_t sp, sq, am;  // from pass 0: sums of fx(p) and fx(q), argmax key of fx(p)
-  uint64_t gamma;       // gamma of the pass in flight
-  uint32_t ticket;      // slices of the pass in flight that are done
-  uint32_t flags;       // status flags so far
-  int32_t kid;          // index (in the node's child list) of the next child to test
-  int32_t tested;       // some child was tested
-  int32_t pass;         // passes completed
-};
-
+constexpr int kMaxSampleBlocks = 2048;  // sampling slice blocks of one rows launch (items by a fixed stride)
 constexpr int kMaxKids = 64;  // children of one node (T <= 65)
-// the queue counters sit 128 bytes apart, so the waiters' polls of one do not queue behind the claims and
-// reservations made on another; likewise every ticket (kQ uint32 apart) and greedy argmax key (kKS uint64)
+// every ticket (kQ uint32 apart) and greedy argmax key (kKS uint64) sits on its own 128-byte line
 constexpr int kQ = 32;
 constexpr int kKS = 16;
-constexpr int kMaxSampleMap = 2048;  // sampling sequences a worker lists in LDS
-constexpr uint32_t kSpinLimit = 1u << 22;  // polls a worker makes for a queue slot before it gives up
+constexpr int kMaxSampleMap = 2048;  // sampling sequences a block lists in LDS
 
-// Residual mass from a window of ratio bins (the fast path). Over a node's row, the mass after j rejections,
+// Residual mass from a window of ratio bins. Over a node's row, the mass after j rejections,
 // W(G) = sum_v max(0, P[v] S_Q - G Q[v]) with G = gamma_j, only counts elements whose ratio P/Q exceeds
-// theta = G / S_Q. Pass 0 sorts each slice's elements with P > 0 by n = floor(8 P / Q): for 1/2 <= P/Q < 8
+// theta = G / S_Q. Each slice block sorts its elements with P > 0 by n = floor(8 P / Q): for 1/2 <= P/Q < 8
 // into bins 0..59 (bin n - 4, keeping the bin's sums of P and Q and the elements themselves, grouped by
 // bin), P/Q >= 8 or Q = 0 into the high set (sums only), smaller ratios nowhere. For 1/2 <= theta < 8 every
 // element of a bin above floor(8 theta) counts in full (P S_Q - G Q >= 0) and every element below it not at
 // all, so W(G) is the high set's and those bins' sums plus an exact per-element sum over the one bin that
 // holds theta: no pass over the row. theta_1 = S_P / S_Q (1 for normalised rows) and each rejection adds at
 // most theta_1, so a node with up to 8 children stays inside the window; outside it, or when a slice holds
-// more window elements than it keeps, the node takes residual passes over its row as before.
+// more window elements than it keeps, the deciding block takes a pass over the row instead.
 constexpr int kWinBins = 60;     // window bins (ratios 1/2 .. 8 in steps of 1/8)
 constexpr int kWinHi = 60;       // record slot of the high set
 constexpr int kWinSlots = 64;    // record slots per slice (bins, high set, padding)
 constexpr int kWinCap = 2048;    // window elements a slice keeps (a quarter of its elements)
 constexpr int kFastMaxSl = 16;   // slices per row the decision keeps in LDS (V <= 131072)
-constexpr uint64_t kWinOverflow = 4;  // pass-0 slice flag: the window was not (fully) recorded
+constexpr uint64_t kWinOverflow = 4;  // slice flag: the window was not (fully) recorded
 
 struct VerifyWs {
   uint64_t* keys;      // [B*max_T] greedy argmax keys (0 = empty)
@@ -91,13 +77,10 @@ struct VerifyWs {
   uint32_t* nflag;     // [B*max_T] sampling node flags
   uint32_t* tickets;   // [B] greedy: rows done; sampling: nodes done
   uint32_t* rtick;     // [B*max_T] greedy: slice blocks of the row done
-  NodeState* node;     // [B*max_T]
-  uint64_t* ssum;      // [B*max_T][nsl][2] u128 slice sums of the node's last pass (pass 0: of fx(p))
-  uint64_t* psum;      // [B*max_T][nsl][3] pass 0 per slice: sum of fx(q), argmax key of fx(p), NaN bits
-  uint64_t* kidpq;     // [B*max_T][kMaxKids] children: (fx(p[t]) << 32) | fx(q[t]), ~0 = invalid token
-  uint32_t* queue;     // [B*max_T*nsl] published dynamic items (node * nsl + slice + 1), 0 = empty
-  uint32_t* qctl;      // head, tail, nodes done, workers exited: at qctl[kQ * i], 128 bytes apart
-  // window records (null when a row has more than kFastMaxSl slices), written by pass 0 of a node with a q row
+  uint64_t* ssum;      // [B*max_T][nsl] slice sums of fx(p)
+  uint64_t* psum;      // [B*max_T][nsl][3] slice sum of fx(q), argmax key of fx(p), NaN / window bits
+  uint64_t* smass;     // [B*max_T][nsl][2] a decision's own row pass: per-slice residual masses (u128)
+  // window records (null when a row has more than kFastMaxSl slices)
   uint32_t* wcnt;      // [B*max_T*nsl][kWinSlots] elements per window bin; slot kWinHi: all window elements
   uint64_t* wsum;      // [B*max_T*nsl][kWinSlots][2] sums of P and Q per bin; slot kWinHi: the high set
   uint64_t* wel;       // [B*max_T*nsl][kWinCap] window elements (P << 32 | Q), grouped by bin
@@ -123,12 +106,9 @@ VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
   w.nflag = reinterpret_cast<uint32_t*>(take(4 * n));
   w.tickets = reinterpret_cast<uint32_t*>(take(4 * size_t(B) * kQ));
   w.rtick = reinterpret_cast<uint32_t*>(take(4 * n * kQ));
-  w.node = reinterpret_cast<NodeState*>(take(sizeof(NodeState) * n));
-  w.ssum = reinterpret_cast<uint64_t*>(take(16 * n * nsl));
+  w.ssum = reinterpret_cast<uint64_t*>(take(8 * n * nsl));
   w.psum = reinterpret_cast<uint64_t*>(take(24 * n * nsl));
-  w.kidpq = reinterpret_cast<uint64_t*>(take(8 * n * kMaxKids));
-  w.queue = reinterpret_cast<uint32_t*>(take(4 * n * nsl));
-  w.qctl = reinterpret_cast<uint32_t*>(take(4 * kQ * sizeof(uint32_t)));
+  w.smass = reinterpret_cast<uint64_t*>(take(16 * n * nsl));
   w.wcnt = nullptr;
   w.wsum = nullptr;
   w.wel = nullptr;
@@ -153,10 +133,9 @@ struct VerifyArgs {
   const int32_t* T_b;
   const int8_t* mode;
   uint64_t key0, key1, offset;
-  int B, max_T, R, V, n_slices, slice, nsl, n_greedy_blocks, n_workers;
+  int B, max_T, R, V, n_slices, slice, nsl, n_greedy_blocks, n_sample_blocks;
   int row_tickets;  // greedy: count slice blocks per row first (sequences with many slice blocks)
   int fast;         // sampling: residual masses from the window records when they allow it
-  uint32_t spin_limit;  // sampling: polls of a worker waiting for a queue slot before it gives up
   int32_t* accept_len;
   int32_t* accept_nodes;
   int32_t* out_tokens;
@@ -470,23 +449,6 @@ __device__ __forceinline__ void block_sum3(uint64_t& x0, uint64_t& x1, uint64_t&
 __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArgs& a, int b, int u, int acc, int bonus, uint32_t flags,
                               bool trivial);
 
-// after a slice of a pass: the block finishing the node's pass takes the node's next decision
-template <bool VEC, bool LG>
-__device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T);
-
-template <bool VEC, bool LG>
-__device__ __forceinline__ void pass_done(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
-  __shared__ int last_s;
-  NodeState* ns = w.node + (size_t(b) * a.max_T + u);
-  wait_global_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) last_s = ticket_add(&ns->ticket) == uint32_t(a.nsl - 1);
-  __syncthreads();
-  if (!last_s) return;
-  if (threadIdx.x == 0) ticket_reset(&ns->ticket);
-  sample_decide<VEC, LG>(w, a, b, u, T);
-}
-
 // window bin of an element (see kWinBins): 0..kWinBins-1 for 1/2 <= P/Q < 8 (floor(8 P / Q) - 4), kWinHi
 // for P/Q >= 8 or Q = 0, -1 for P = 0 or P/Q < 1/2. e = 8 P / Q from a hardware reciprocal is within 3e-5 of
 // the exact quotient wherever it matters (below 64.0001), so floor(e) is exact unless e lies within 1e-4 of
@@ -506,13 +468,13 @@ __device__ __forceinline__ int win_bin(uint32_t P, uint32_t Q) {
   return n >= 64 ? kWinHi : (n < 4 ? -1 : n - 4);
 }
 
-// pass 0 over slice s: sums of fx(p) and fx(q), argmax key of fx(p), NaN bits, published per slice (the
-// node's decision block reduces them); for a node with a q row also the slice's window record and its window
+// slice s of a sampling node: sums of fx(p) and fx(q), argmax key of fx(p), NaN bits, published per slice
+// (the node's decision block reduces them); for a node with a q row also the slice's window record and its window
 // elements grouped by bin. Window elements are first staged in LDS, each wave in its own region at a running
 // ballot offset, then counted and summed per bin, then placed by per-bin cursors: the order inside a bin is
 // arbitrary, and nothing depends on it.
 template <bool VEC, bool LG>
-__device__ __forceinline__ void sample_pass0(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T, int s) {
+__device__ __forceinline__ void sample_slice(const VerifyWs& w, const VerifyArgs& a, int b, int u, int s) {
   __shared__ uint64_t red[kWaves][3];
   __shared__ uint64_t amr[kWaves];
   __shared__ uint32_t wc_s[kWinSlots], wcur_s[kWinSlots], wn_s[kWaves];
@@ -610,53 +572,22 @@ __device__ __forceinline__ void sample_pass0(const VerifyWs& w, const VerifyArgs
       wflag = 0;
       uint64_t* el = w.wel + rec * kWinCap;
       for (int j = tid; j < kWinCap; j += kThreads)
-        if (staged(j)) st_agent(el + atomicAdd(&wcur_s[sbin_s[j]], 1u), stage_s[j]);
+        if (staged(j)) el[atomicAdd(&wcur_s[sbin_s[j]], 1u)] = stage_s[j];
     }
     if (tid < kWinSlots) {
-      st_agent(w.wcnt + rec * kWinSlots + tid, tid < kWinBins ? wc_s[tid] : (tid == kWinHi ? total : 0u));
-      st_agent(w.wsum + (rec * kWinSlots + tid) * 2, uint64_t(wp_s[tid]));
-      st_agent(w.wsum + (rec * kWinSlots + tid) * 2 + 1, uint64_t(wq_s[tid]));
+      w.wcnt[rec * kWinSlots + tid] = tid < kWinBins ? wc_s[tid] : (tid == kWinHi ? total : 0u);
+      w.wsum[(rec * kWinSlots + tid) * 2] = uint64_t(wp_s[tid]);
+      w.wsum[(rec * kWinSlots + tid) * 2 + 1] = uint64_t(wq_s[tid]);
     }
   }
   if (tid == 0) {
     for (int i = 1; i < kWaves; ++i) am = amr[i] > am ? amr[i] : am;
-    uint64_t* ss = w.ssum + rec * 2;
     uint64_t* ps = w.psum + rec * 3;
-    st_agent(ss, sp);
-    st_agent(ss + 1, uint64_t(0));
-    st_agent(ps, sq);
-    st_agent(ps + 1, am);
-    st_agent(ps + 2, uint64_t(((nn & 15u) ? 1u : 0u) | ((nn >> 4) ? 2u : 0u)) | wflag);
+    w.ssum[rec] = sp;
+    ps[0] = sq;
+    ps[1] = am;
+    ps[2] = uint64_t(((nn & 15u) ? 1u : 0u) | ((nn >> 4) ? 2u : 0u)) | wflag;
   }
-  pass_done<VEC, LG>(w, a, b, u, T);
-}
-
-// residual pass over slice s under the node's current gamma: the slice's sum of
-// N[v] = max(0, fx(p[v]) S_Q - gamma fx(q[v])) (32-bit limb sums), published per slice
-template <bool VEC, bool LG>
-__device__ __forceinline__ void sample_passN(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T, int s) {
-  __shared__ uint64_t red[kWaves][3];
-  const size_t node = size_t(b) * a.max_T + u;
-  NodeState* ns = w.node + node;
-  const float* prow = sample_row(a, node);
-  const float* qrow = node_qrow_any(a, b, u);  // present: only tested nodes have residual passes
-  const uint64_t S_Q = ld_agent(&ns->sq), gamma = ld_agent(&ns->gamma);
-  const int lo = s * kSampleSlice, hi = min(a.V, lo + kSampleSlice);
-  uint64_t l0 = 0, l1 = 0, l2 = 0;
-  slice_for<VEC>(prow, qrow, lo, hi, [&] { return prob_row<LG>(a, node); }, [&](int, float x, float y) {
-    const u128 n = residual(fx(x), fx(y), S_Q, gamma, false);
-    l0 += uint32_t(n);
-    l1 += uint32_t(n >> 32);
-    l2 += uint64_t(n >> 64);
-  });
-  block_sum3(l0, l1, l2, red);
-  if (threadIdx.x == 0) {
-    const u128 v = u128(l0) + (u128(l1) << 32) + (u128(l2) << 64);
-    uint64_t* ss = w.ssum + (node * a.nsl + s) * 2;
-    st_agent(ss, uint64_t(v));
-    st_agent(ss + 1, uint64_t(v >> 64));
-  }
-  pass_done<VEC, LG>(w, a, b, u, T);
 }
 
 // LDS of a decision's fast path: the node's window records, per slice and bin
@@ -670,9 +601,9 @@ __device__ __forceinline__ void win_load(const VerifyWs& w, const VerifyArgs& a,
   for (int i = threadIdx.x; i < a.nsl * kWinSlots; i += kThreads) {
     const int sl = i / kWinSlots, n = i - sl * kWinSlots;
     const size_t r = (node * a.nsl + sl) * kWinSlots + n;
-    L.cnt[sl][n] = n < kWinBins ? ld_agent(w.wcnt + r) : 0u;
-    L.sp[sl][n] = n <= kWinHi ? ld_agent(w.wsum + r * 2) : 0ull;
-    L.sq[sl][n] = n <= kWinHi ? ld_agent(w.wsum + r * 2 + 1) : 0ull;
+    L.cnt[sl][n] = n < kWinBins ? w.wcnt[r] : 0u;
+    L.sp[sl][n] = n <= kWinHi ? w.wsum[r * 2] : 0ull;
+    L.sq[sl][n] = n <= kWinHi ? w.wsum[r * 2 + 1] : 0ull;
   }
 }
 
@@ -726,7 +657,7 @@ __device__ __forceinline__ u128 win_mass(const VerifyWs& w, const VerifyArgs& a,
     for (int e0 = j; e0 < int(cnt); e0 += 8 * 16) {  // eight independent loads per round trip
       uint64_t pq[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) pq[k] = e0 + 16 * k < int(cnt) ? ld_agent(el + e0 + 16 * k) : 0ull;
+      for (int k = 0; k < 8; ++k) pq[k] = e0 + 16 * k < int(cnt) ? el[e0 + 16 * k] : 0ull;
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc += residual(uint32_t(pq[k] >> 32), uint32_t(pq[k]), S_Q, gamma, false);
     }
@@ -739,17 +670,47 @@ __device__ __forceinline__ u128 win_mass(const VerifyWs& w, const VerifyArgs& a,
   return W;
 }
 
+// Residual masses under gamma from a pass of the deciding block over the row (outside the window): slice by
+// slice, each wave sums its share and one thread adds the four shares in order (one barrier per slice,
+// alternating LDS buffers); per-slice masses go to ssl (the first kThreads) and to smass, the total to W_out
 template <bool VEC, bool LG>
-__device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
+__device__ __forceinline__ void row_mass(const VerifyWs& w, const VerifyArgs& a, size_t node, const float* prow,
+                                         const float* qrow, const ProbRow<LG>& pr, uint64_t S_Q, uint64_t gamma,
+                                         u128* ssl, u128 (*part)[kWaves], u128* W_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nsl = a.nsl, V = a.V;
+  u128 total = 0;
+  for (int sl = 0; sl < nsl; ++sl) {
+    const int lo = sl * kSampleSlice, hi = min(V, lo + kSampleSlice);
+    u128 acc = 0;
+    slice_for<VEC>(prow, qrow, lo, hi, [&] { return pr; },
+                   [&](int, float x, float y) { acc += residual(fx(x), fx(y), S_Q, gamma, false); });
+    acc = wave_sum_u128(acc);
+    if (lane == 0) part[sl & 1][wave] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      const u128 m = part[sl & 1][0] + part[sl & 1][1] + part[sl & 1][2] + part[sl & 1][3];
+      if (sl < kThreads) ssl[sl] = m;
+      uint64_t* sm = w.smass + (node * nsl + sl) * 2;
+      sm[0] = uint64_t(m);
+      sm[1] = uint64_t(m >> 64);
+      total += m;
+    }
+  }
+  if (tid == 0) *W_out = total;
+  __syncthreads();
+}
+
+template <bool VEC, bool LG>
+__device__ __forceinline__ void decide_node(const VerifyWs& w, const VerifyArgs& a, int b, int u, int T) {
   __shared__ int kid_s[kMaxKids], nkid_s;
   __shared__ uint64_t kpq_s[kMaxKids];  // children: (fx(p[t]) << 32) | fx(q[t]), ~0 = invalid token
   __shared__ uint64_t km_s[kMaxKids];   // node c's acceptance integer m at km_s[c - 1]
   __shared__ int act_s;  // accepted child; -1: a rejection needs the next residual mass; -2: resample
-  __shared__ int fast_s, fastok_s, ki_s, tested_s, test_s;
-  __shared__ u128 W_s, wtot_s[kWaves];
+  __shared__ int fast_s, fastok_s, ki_s, tested_s, test_s, src_s;
+  __shared__ u128 W_s, wtot_s[kWaves], part_s[2][kWaves];
   __shared__ uint64_t SP_s, SQ_s, gamma_s, AM_s, K_s;
   __shared__ uint32_t flags_s;
-  __shared__ int plain_s, bonus_s, pass_s;
+  __shared__ int plain_s, bonus_s;
   __shared__ u128 ssl_s[kThreads];  // per-slice masses of the current W (the first kThreads slices)
   __shared__ u128 wred_s[kWaves];
   __shared__ uint64_t red_s[kWaves][3];
@@ -758,50 +719,27 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
   __shared__ WinLds win_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, max_T = a.max_T, V = a.V;
   const size_t node = size_t(b) * max_T + u;
-  NodeState* ns = w.node + node;
   const float* prow = sample_row(a, node);
   const ProbRow<LG> pr = prob_row<LG>(a, node);
-  // a decision is one serial chain that every later pass of the node waits for, while the blocks
-  // around it run throughput work: its waves take issue priority until it is done
-  __builtin_amdgcn_s_setprio(3);
-  struct PrioRestore {
-    __device__ ~PrioRestore() { __builtin_amdgcn_s_setprio(0); }
-  } prio_restore;
 
-  // ---- one round trip: the node's state, every slice's results, its children and their cache, and (a node
-  // that may test children) its window records; meanwhile wave 1 draws the uniforms of every potential child
-  // and the node's own resampling uniform
-  int pass = 0, kid = 0, tested = 0;
-  uint32_t flags = 0;
-  uint64_t gamma = 0, SPc = 0, SQc = 0, AMc = 0;
+  // ---- one round trip: every slice's sums, the node's children, and (a node that may test children) its
+  // window records; meanwhile wave 1 draws the uniforms of every potential child and wave 2 the node's own
+  // resampling uniform
   const int qr = a.q_row ? a.q_row[node] : -1;
-  if (tid == 0) {
-    pass = ld_agent(&ns->pass);
-    kid = ld_agent(&ns->kid);
-    tested = ld_agent(&ns->tested);
-    flags = ld_agent(&ns->flags);
-    gamma = ld_agent(&ns->gamma);
-    SPc = ld_agent(&ns->sp);
-    SQc = ld_agent(&ns->sq);
-    AMc = ld_agent(&ns->am);
-  }
   const bool may_win = a.fast && w.wcnt != nullptr && qr >= 0 && qr < a.R && a.draft != nullptr;
   if (may_win) win_load(w, a, node, win_s);
-  u128 wsum = 0;  // sum of the pass's slice sums (pass 0: of fx(p))
-  uint64_t sq = 0, am = 0, nanb = 0;
+  uint64_t sp = 0, sq = 0, am = 0, nanb = 0;
   for (int sl = tid; sl < a.nsl; sl += kThreads) {
-    const uint64_t* s2 = w.ssum + (node * a.nsl + sl) * 2;
-    const uint64_t* p3 = w.psum + (node * a.nsl + sl) * 3;
-    const u128 v = u128(ld_agent(s2)) | (u128(ld_agent(s2 + 1)) << 64);
-    const uint64_t q = ld_agent(p3), m = ld_agent(p3 + 1), f = ld_agent(p3 + 2);
-    if (sl < kThreads) ssl_s[sl] = v;
-    wsum += v;
-    sq += q;
-    am = m > am ? m : am;
-    nanb |= f;
+    const size_t r = node * a.nsl + sl;
+    const uint64_t v = w.ssum[r];
+    const uint64_t* p3 = w.psum + r * 3;
+    if (sl < kThreads) ssl_s[sl] = u128(v);
+    sp += v;
+    sq += p3[0];
+    am = p3[1] > am ? p3[1] : am;
+    nanb |= p3[2];
   }
   int c_kid = 0, c_tok = -1;  // wave 0, lane l: the tree's node l + 1 if it is a child of u, its token
-  uint64_t cached = 0;
   if (wave == 0) {
     const int c = lane + 1;
     if (c < T) {
@@ -810,7 +748,6 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
       c_kid = pc == u;
       c_tok = a.tokens[size_t(b) * max_T + c];
     }
-    cached = ld_agent(w.kidpq + node * kMaxKids + lane);
   } else if (wave == 1) {
     if (lane + 1 < T) {
       const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(lane + 1), 0, a.key0, a.key1);
@@ -820,13 +757,13 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
     const U64x4 r = philox4x64_10(a.offset, uint64_t(b), uint64_t(u), 0, a.key0, a.key1);
     K_s = r.w[1] >> 32;
   }
-  // ---- reductions (u128 sum, sum, max, or) and the child list in index order
-  wsum = wave_sum_u128(wsum);
+  // ---- reductions (sum, sum, max, or) and the child list in index order
+  sp = wave_sum_u64(sp);
   sq = wave_sum_u64(sq);
   am = wave_max_u64(am);
   nanb = wave_or_u32(uint32_t(nanb));
   if (lane == 0) {
-    wred_s[wave] = wsum;
+    wred_s[wave] = u128(sp);
     red_s[wave][0] = sq;
     red_s[wave][1] = am;
     red_s[wave][2] = nanb;
@@ -840,57 +777,44 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
     }
     if (lane == 0) nkid_s = __popcll(m);
   }
-  if (tid == 0) pass_s = pass;
   __syncthreads();
   const int nkid = nkid_s;
   // the node's q row, or null if it has none (no children, no draft tensor, or q_row out of range)
   const float* qrow = (nkid > 0 && a.draft != nullptr && qr >= 0 && qr < a.R) ? a.draft + (size_t(b) * a.R + qr) * V : nullptr;
-  if (pass_s == 0) {  // first decision: the children's p and q at their tokens (cached for later passes)
-    if (wave == 0 && kslot >= 0) {
-      uint64_t pq = ~0ull;
-      if (c_tok >= 0 && c_tok < V) pq = (uint64_t(fx(pr(prow[c_tok]))) << 32) | (qrow ? fx(qrow[c_tok]) : 0u);
-      kpq_s[kslot] = pq;
-      st_agent(w.kidpq + node * kMaxKids + kslot, pq);
-    }
-  } else if (wave == 0) {
-    kpq_s[lane] = cached;
+  if (wave == 0 && kslot >= 0) {  // the children's p and q at their tokens
+    uint64_t pq = ~0ull;
+    if (c_tok >= 0 && c_tok < V) pq = (uint64_t(fx(pr(prow[c_tok]))) << 32) | (qrow ? fx(qrow[c_tok]) : 0u);
+    kpq_s[kslot] = pq;
   }
   __syncthreads();
   if (tid == 0) {
+    uint64_t S_P = uint64_t(wred_s[0]);  // S_P < V 2^32 < 2^56
     for (int i = 1; i < kWaves; ++i) {
-      wsum += wred_s[i];
+      S_P += uint64_t(wred_s[i]);
       sq += red_s[i][0];
       am = red_s[i][1] > am ? red_s[i][1] : am;
       nanb |= red_s[i][2];
     }
-    const uint64_t S_P = pass == 0 ? uint64_t(wsum) : SPc;  // S_P < V 2^32 < 2^56
-    const uint64_t S_Q = pass == 0 ? (qrow ? sq : 0) : SQc;
-    const uint64_t AM = pass == 0 ? am : AMc;
+    const uint64_t S_Q = qrow ? sq : 0;
     const bool test = nkid > 0 && qrow != nullptr && S_Q > 0;
-    u128 W;
-    if (pass == 0) {
-      flags = ((nanb & 1u) || ((nanb & 2u) && qrow)) ? SPEC_STATUS_NAN_INPUT : 0u;
-      if (nkid > 0 && !test) flags |= SPEC_STATUS_ZERO_Q;
-      W = u128(S_P) * S_Q;
-    } else {
-      W = wsum;
-      if (W == 0) flags |= SPEC_STATUS_ZERO_RESIDUAL;
-    }
+    uint32_t flags = ((nanb & 1u) || ((nanb & 2u) && qrow)) ? SPEC_STATUS_NAN_INPUT : 0u;
+    if (nkid > 0 && !test) flags |= SPEC_STATUS_ZERO_Q;
     SP_s = S_P;
     SQ_s = S_Q;
-    AM_s = AM;
-    W_s = W;
-    gamma_s = gamma;
+    AM_s = am;
+    W_s = u128(S_P) * S_Q;
+    gamma_s = 0;
     flags_s = flags;
-    ki_s = kid;
-    tested_s = tested;
+    ki_s = 0;
+    tested_s = 0;
     test_s = test;
+    src_s = 0;  // the per-slice masses are pass 0's sums of fx(p)
     fastok_s = test && may_win && !(nanb & kWinOverflow);
   }
   __syncthreads();
   // ---- the children in index order: the block tests them one after another (thread 0); after a rejection
-  // the next residual mass comes from the window records when they admit the new gamma, else from a
-  // residual pass over the row that a later decision of this node picks up
+  // the next residual mass comes from the window records when they admit the new gamma, else from a pass of
+  // this block over the row
   for (;;) {
     if (tid == 0) {
       int act = -2, ki = ki_s, tst = tested_s;
@@ -929,32 +853,17 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
     }
     __syncthreads();
     if (act_s != -1) break;
-    if (!fast_s) {
-      // a residual pass over the row: the state and the queue reservation go out together; the items are
-      // published once both are done
+    if (fast_s) {  // the mass (and every slice's share, for a resample) from the window records
+      const u128 W = win_mass(w, a, node, SQ_s, gamma_s, win_s, ssl_s);
       if (tid == 0) {
-        st_agent(&ns->gamma, gamma_s);
-        st_agent(&ns->kid, ki_s);
-        st_agent(&ns->tested, 1);
-        st_agent(&ns->flags, flags_s);
-        st_agent(&ns->pass, pass + 1);
-        if (pass == 0) {
-          st_agent(&ns->sp, SP_s);
-          st_agent(&ns->sq, SQ_s);
-          st_agent(&ns->am, AM_s);
-        }
-        const uint32_t pos = ticket_add_n(&w.qctl[1 * kQ], uint32_t(a.nsl));
-        wait_global_stores();  // this wave's state and children-cache stores are complete
-        for (int sl = 0; sl < a.nsl; ++sl) st_agent(&w.queue[pos + sl], uint32_t(node * a.nsl + sl + 1));
+        W_s = W;
+        src_s = 1;
       }
-      return;
+    } else {
+      row_mass<VEC, LG>(w, a, node, prow, qrow, pr, SQ_s, gamma_s, ssl_s, part_s, &W_s);
+      if (tid == 0) src_s = 2;
     }
-    // the mass (and every slice's share, for a resample) from the window records
-    const u128 W = win_mass(w, a, node, SQ_s, gamma_s, win_s, ssl_s);
-    if (tid == 0) {
-      W_s = W;
-      if (W == 0) flags_s |= SPEC_STATUS_ZERO_RESIDUAL;
-    }
+    if (tid == 0 && W_s == 0) flags_s |= SPEC_STATUS_ZERO_RESIDUAL;
     __syncthreads();
   }
   if (tid == 0) {
@@ -967,7 +876,7 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
     return;
   }
   // ---- no draft accepted: resample from the residual (or from p if nothing was tested); ssl_s holds the
-  // masses of the first kThreads slices (of the pass that gave W, or from the window records)
+  // masses of the first kThreads slices (pass 0's sums of fx(p), the window's, or this block's row pass)
   const u128 W = W_s;
   const bool plain = plain_s;
   if (W == 0) {
@@ -987,9 +896,9 @@ __device__ __forceinline__ void sample_decide(const VerifyWs& w, const VerifyArg
       __syncthreads();
       if (found_s >= 0) break;
       const int sl = c0 + tid;
-      if (c0 > 0 && sl < a.nsl) {
-        const uint64_t* q2 = w.ssum + (node * a.nsl + sl) * 2;
-        ssl_s[tid] = u128(ld_agent(q2)) | (u128(ld_agent(q2 + 1)) << 64);
+      if (c0 > 0 && sl < a.nsl) {  // past the first kThreads slices (never with window masses)
+        const size_t r = node * a.nsl + sl;
+        ssl_s[tid] = src_s == 0 ? u128(w.ssum[r]) : (u128(w.smass[r * 2]) | (u128(w.smass[r * 2 + 1]) << 64));
       }
       __syncthreads();
       if (tid == 0) {
@@ -1169,9 +1078,8 @@ __device__ __forceinline__ void walk(const VerifyWs& w, const VerifyArgs& a, int
   }
 }
 
-// a node's outcome is final: publish it, clear the node's state, count it for its sequence and for the
-// worker loop; the block finishing a sequence's last node walks the tree. Rows past T_b are finished
-// without outcome (trivial).
+// a node's outcome is final: publish it and count it for its sequence; the block finishing a sequence's last
+// node walks the tree. Rows past T_b are counted without outcome (trivial).
 __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArgs& a, int b, int u, int acc, int bonus, uint32_t flags,
                               bool trivial) {
   __shared__ int last_s;
@@ -1181,18 +1089,8 @@ __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArg
       st_agent(w.acc_child + node, acc);
       st_agent(w.bonus + node, bonus);
       st_agent(w.nflag + node, flags);
-      NodeState* ns = w.node + node;  // back to all-zero for the next call
-      st_agent(&ns->sp, uint64_t(0));
-      st_agent(&ns->sq, uint64_t(0));
-      st_agent(&ns->am, uint64_t(0));
-      st_agent(&ns->gamma, uint64_t(0));
-      st_agent(&ns->flags, 0u);
-      st_agent(&ns->kid, 0);
-      st_agent(&ns->tested, 0);
-      st_agent(&ns->pass, 0);
     }
     wait_global_stores();
-    ticket_add(&w.qctl[2 * kQ]);
     last_s = ticket_add(&w.tickets[size_t(b) * kQ]) == uint32_t(a.max_T - 1);
   }
   __syncthreads();
@@ -1201,46 +1099,9 @@ __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArg
   walk(w, a, b);
 }
 
-// A sampling sequence whose nodes did not all finish (its node count is neither 0 - walked and reset, or
-// never started, which cannot happen since leaves need no residual pass - nor complete): outputs voided
-// (accept_len 0, accept_nodes {0, -1, ...}, out_tokens all -1), status SPEC_STATUS_VERIFY_TIMEOUT, its node
-// states and count cleared; every queue slot still holding an item is emptied, so the next call starts clean.
-__device__ __forceinline__ void timeout_cleanup(const VerifyWs& w, const VerifyArgs& a, uint32_t cap) {
-  const int max_T = a.max_T;
-  for (int b = threadIdx.x; b < a.B; b += kThreads) {
-    if (a.mode[b] != SPEC_MODE_SAMPLE || ld_agent(&w.tickets[size_t(b) * kQ]) == 0u) continue;
-    const size_t base = size_t(b) * max_T;
-    a.accept_len[b] = 0;
-    a.status[b] = SPEC_STATUS_VERIFY_TIMEOUT;
-    for (int k = 0; k < max_T; ++k) {
-      a.accept_nodes[base + k] = k == 0 ? 0 : -1;
-      a.out_tokens[base + k] = -1;
-      NodeState* ns = w.node + base + k;
-      st_agent(&ns->sp, uint64_t(0));
-      st_agent(&ns->sq, uint64_t(0));
-      st_agent(&ns->am, uint64_t(0));
-      st_agent(&ns->gamma, uint64_t(0));
-      st_agent(&ns->ticket, 0u);
-      st_agent(&ns->flags, 0u);
-      st_agent(&ns->kid, 0);
-      st_agent(&ns->tested, 0);
-      st_agent(&ns->pass, 0);
-    }
-    ticket_reset(&w.tickets[size_t(b) * kQ]);
-  }
-  for (uint32_t i = threadIdx.x; i < cap; i += kThreads)
-    if (ld_agent(&w.queue[i]) != 0u) st_agent(&w.queue[i], 0u);
-  wait_global_stores();
-  __syncthreads();
-}
-
-// persistent sampling worker: takes items until every sampling node is done
-template <bool VEC, bool LG>
-__device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArgs& a) {
-  __shared__ int item_s;
-  __shared__ int smap[kMaxSampleMap];  // the sampling sequences in index order (when they fit)
-  __shared__ int wcnt[kWaves];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, max_T = a.max_T;
+// The sampling sequences in index order into smap (when there are at most kMaxSampleMap); returns their count
+__device__ __forceinline__ int sampling_map(const VerifyArgs& a, int* smap, int* wcnt) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   int nseq = 0;
   for (int b0 = 0; b0 < a.B; b0 += kThreads) {
     const int b = b0 + tid;
@@ -1258,95 +1119,36 @@ __device__ __forceinline__ void sample_worker(const VerifyWs& w, const VerifyArg
     nseq += tot;
     __syncthreads();
   }
-  if (nseq == 0) return;  // nothing to sample: the queue is never touched
-  const uint32_t total = uint32_t(nseq) * uint32_t(max_T);
-  const uint32_t rows = uint32_t(a.B) * uint32_t(max_T);
-  // pass-0 items over the sampling sequences only when their list fits (a mixed batch's greedy rows then
-  // cost no claims), else over every sequence, greedy ones skipped
+  return nseq;
+}
+
+// sampling slice blocks of the rows kernel: the (node, slice) items of the sampling sequences, taken by a
+// fixed stride (items numbered node-major over the listed sampling sequences when they fit, else over every
+// sequence with the greedy ones skipped)
+template <bool VEC, bool LG>
+__device__ __forceinline__ void sample_slices(const VerifyWs& w, const VerifyArgs& a) {
+  __shared__ int smap[kMaxSampleMap];
+  __shared__ int wcnt[kWaves];
+  const int nseq = sampling_map(a, smap, wcnt);
+  if (nseq == 0) return;
   const bool mapped = nseq <= kMaxSampleMap;
-  const uint32_t n_static = (mapped ? uint32_t(nseq) * uint32_t(max_T) : rows) * uint32_t(a.nsl);
-  const uint32_t cap = rows * uint32_t(a.nsl);  // queue slots
-  for (;;) {
-    if (tid == 0) {
-      const uint32_t i = ticket_add(&w.qctl[0 * kQ]);
-      uint32_t it = 0;  // 1 + static index, or 1 + n_static + node * nsl + slice, or 0 = stop
-      if (i < n_static) {
-        it = 1 + i;
-      } else {
-        const uint32_t j = i - n_static;
-        // wait for slot j to be published, or for every node to be done (bounded: never a hang)
-        int nap = 1;  // polls back off from ~0.05 us to ~0.2 us
-        for (uint32_t spin = 0; spin < a.spin_limit; ++spin) {
-          if (j < cap) {
-            const uint32_t v = ld_agent(&w.queue[j]);
-            if (v) {
-              st_agent(&w.queue[j], 0u);  // leave the slot empty for the next call
-              it = 1 + n_static + (v - 1);
-              break;
-            }
-          }
-          if (ld_agent(&w.qctl[2 * kQ]) >= total) break;
-          for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
-          nap = nap < 4 ? 2 * nap : 4;
-        }
-      }
-      item_s = int(it);
-    }
-    __syncthreads();
-    const uint32_t it = uint32_t(item_s);
-    __syncthreads();
-    if (it == 0) break;
-    const bool dynamic = it > n_static;
-    const uint32_t k = dynamic ? it - 1 - n_static : it - 1;
-    int node, sl;
-    if (dynamic) {  // node * nsl + slice
-      node = int(k / uint32_t(a.nsl));
-      sl = int(k % uint32_t(a.nsl));
-    } else {  // pass 0 items by tree position first (every sequence's root, then node 1, ...): the
-              // nodes near the root, whose passes form the longest chains, start first
-      const uint32_t per_u = (mapped ? uint32_t(nseq) : uint32_t(a.B)) * uint32_t(a.nsl);
-      const uint32_t uu = k / per_u, rem = k - uu * per_u;
-      const int si = int(rem / uint32_t(a.nsl));
-      node = (mapped ? smap[si] : si) * max_T + int(uu);
-      sl = int(rem % uint32_t(a.nsl));
-    }
-    const int b = node / max_T, u = node - b * max_T;
-    if (a.mode[b] != SPEC_MODE_SAMPLE) continue;  // a greedy row's static item
-    const int T = seq_T(a.T_b, b, max_T);
-    if (u >= T) {
-      if (sl == 0) sample_finish(w, a, b, u, -1, -1, 0u, true);
-      continue;
-    }
-    if (dynamic)
-      sample_passN<VEC, LG>(w, a, b, u, T, sl);
-    else
-      sample_pass0<VEC, LG>(w, a, b, u, T, sl);
-  }
-  // the last worker out leaves the queue counters at zero for the next call. Every other worker has left its
-  // loop by then, so no sampling work is in flight; if some node never finished (a worker gave up waiting
-  // for a queue slot that was published later), its sequence was never walked: the last worker voids it
-  __shared__ int last_s, undone_s;
-  wait_global_stores();
-  if (tid == 0) {
-    last_s = ticket_add(&w.qctl[3 * kQ]) == uint32_t(a.n_workers - 1);
-    undone_s = last_s && ld_agent(&w.qctl[2 * kQ]) < total;
-  }
-  __syncthreads();
-  if (!last_s) return;
-  if (undone_s) timeout_cleanup(w, a, rows * uint32_t(a.nsl));
-  if (tid == 0) {
-    ticket_reset(&w.qctl[0 * kQ]);
-    ticket_reset(&w.qctl[1 * kQ]);
-    ticket_reset(&w.qctl[2 * kQ]);
-    ticket_reset(&w.qctl[3 * kQ]);
+  const long long items = (long long)(mapped ? nseq : a.B) * a.max_T * a.nsl;
+  for (long long it = int(blockIdx.x) - a.n_greedy_blocks; it < items; it += a.n_sample_blocks) {
+    const int sl = int(it % a.nsl);
+    const long long nd = it / a.nsl;
+    const int u = int(nd % a.max_T), si = int(nd / a.max_T);
+    const int b = mapped ? smap[si] : si;
+    if (a.mode[b] != SPEC_MODE_SAMPLE || u >= seq_T(a.T_b, b, a.max_T)) continue;
+    sample_slice<VEC, LG>(w, a, b, u, sl);
+    __syncthreads();  // the slice's LDS is free for the next item
   }
 }
 
 template <bool VEC, bool LG>
-__global__ void __launch_bounds__(kThreads, 2) verify_kernel(VerifyWs w, VerifyArgs a) {
+__global__ void __launch_bounds__(kThreads) verify_rows_kernel(VerifyWs w, VerifyArgs a) {
   __shared__ int last_s;
   if (int(blockIdx.x) >= a.n_greedy_blocks) {
-    sample_worker<VEC, LG>(w, a);
+    sample_slices<VEC, LG>(w, a);
     return;
   }
   const int x = blockIdx.x % a.n_slices, row = blockIdx.x / a.n_slices;
@@ -1382,6 +1184,27 @@ __global__ void __launch_bounds__(kThreads, 2) verify_kernel(VerifyWs w, VerifyA
   if (!last_s) return;
   if (threadIdx.x == 0) ticket_reset(w.tickets + size_t(b) * kQ);  // leave the workspace ready for the next call
   walk(w, a, b);
+}
+
+// one block per sampling node (the listed sampling sequences node by node, else every row with the greedy
+// ones skipped); the rows kernel's slice results are complete at launch
+template <bool VEC, bool LG>
+__global__ void __launch_bounds__(kThreads) verify_decide_kernel(VerifyWs w, VerifyArgs a) {
+  __shared__ int smap[kMaxSampleMap];
+  __shared__ int wcnt[kWaves];
+  const int nseq = sampling_map(a, smap, wcnt);
+  const bool mapped = nseq <= kMaxSampleMap;
+  const int i = blockIdx.x;
+  if (i >= (mapped ? nseq : a.B) * a.max_T) return;
+  const int si = i / a.max_T, u = i - si * a.max_T;
+  const int b = mapped ? smap[si] : si;
+  if (a.mode[b] != SPEC_MODE_SAMPLE) return;
+  const int T = seq_T(a.T_b, b, a.max_T);
+  if (u >= T) {
+    sample_finish(w, a, b, u, -1, -1, 0u, true);
+    return;
+  }
+  decide_node<VEC, LG>(w, a, b, u, T);
 }
 
 // ------------------------------------------------------------------ probabilities from logits
@@ -1472,21 +1295,11 @@ extern "C" size_t spec_tree_verify_workspace_size(int32_t B, int32_t max_T, int3
   return total;
 }
 
-// Host settings read at each call (for measurements and tests): SPEC_TREE_VERIFY_FAST=0 takes every residual
-// mass from passes over the row (no window records); SPEC_TREE_VERIFY_SPIN_LIMIT=n bounds a sampling worker's
-// wait for a queue slot to n polls (default 2^22; 0 makes every wait give up at once, so that the timeout
-// path can be exercised with every kernel still exiting normally).
+// SPEC_TREE_VERIFY_FAST=0 (read at each call, for measurements and tests) takes every residual mass from a
+// pass of the deciding block over the row, with no window records.
 static int verify_fast_enabled() {
   const char* e = getenv("SPEC_TREE_VERIFY_FAST");
   return !(e && e[0] == '0' && e[1] == 0);
-}
-
-static uint32_t verify_spin_limit() {
-  const char* e = getenv("SPEC_TREE_VERIFY_SPIN_LIMIT");
-  if (!e || !*e) return kSpinLimit;
-  char* end = nullptr;
-  const unsigned long v = strtoul(e, &end, 10);
-  return (end && *end == 0 && v <= kSpinLimit) ? uint32_t(v) : kSpinLimit;
 }
 
 static int32_t verify_impl(const char* who, const float* target, float2* sm_part, const float* temperature,
@@ -1536,19 +1349,19 @@ static int32_t verify_impl(const char* who, const float* target, float2* sm_part
   a.nsl = int(nsl);
   a.n_greedy_blocks = int(rows) * a.n_slices;
   a.row_tickets = (long long)a.n_slices * max_T > 256;
-  a.n_workers = int(std::min<long long>(kMaxWorkers, rows * nsl));
+  a.n_sample_blocks = int(std::min<long long>(kMaxSampleBlocks, rows * nsl));
   a.fast = verify_fast_enabled();
-  a.spin_limit = verify_spin_limit();
   a.accept_len = accept_len;
   a.accept_nodes = accept_nodes;
   a.out_tokens = out_tokens;
   a.status = status;
-  if ((long long)a.n_greedy_blocks + a.n_workers >= (1LL << 31))
+  if ((long long)a.n_greedy_blocks + a.n_sample_blocks >= (1LL << 31))
     return fail(SPEC_E_UNSUPPORTED, "%s: grid too large", who);
   const bool vec = (V % 4 == 0) && ((reinterpret_cast<uintptr_t>(target) | reinterpret_cast<uintptr_t>(draft_probs)) & 15) == 0;
-  const dim3 grid(a.n_greedy_blocks + a.n_workers);
+  const dim3 grid(a.n_greedy_blocks + a.n_sample_blocks);
+  const dim3 dgrid{unsigned(rows), 1, 1};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (sm_part) {  // the sampling rows' softmax partials first (same stream: the verify launch waits)
+  if (sm_part) {  // the sampling rows' softmax partials first (same stream: the verify launches wait)
     const dim3 sgrid(unsigned(a.sm_nsl), unsigned(rows));
     if ((V % 4 == 0) && (reinterpret_cast<uintptr_t>(target) & 15) == 0)
       hipLaunchKernelGGL(softmax_partial_kernel<true>, sgrid, dim3(kSmThreads), 0, st, target, temperature, T_b, mode,
@@ -1556,14 +1369,19 @@ static int32_t verify_impl(const char* who, const float* target, float2* sm_part
     else
       hipLaunchKernelGGL(softmax_partial_kernel<false>, sgrid, dim3(kSmThreads), 0, st, target, temperature, T_b, mode,
                          max_T, V, sm_part);
-    if (vec)
-      hipLaunchKernelGGL((verify_kernel<true, true>), grid, dim3(kThreads), 0, st, w, a);
-    else
-      hipLaunchKernelGGL((verify_kernel<false, true>), grid, dim3(kThreads), 0, st, w, a);
+    if (vec) {
+      hipLaunchKernelGGL((verify_rows_kernel<true, true>), grid, dim3(kThreads), 0, st, w, a);
+      hipLaunchKernelGGL((verify_decide_kernel<true, true>), dgrid, dim3(kThreads), 0, st, w, a);
+    } else {
+      hipLaunchKernelGGL((verify_rows_kernel<false, true>), grid, dim3(kThreads), 0, st, w, a);
+      hipLaunchKernelGGL((verify_decide_kernel<false, true>), dgrid, dim3(kThreads), 0, st, w, a);
+    }
   } else if (vec) {
-    hipLaunchKernelGGL((verify_kernel<true, false>), grid, dim3(kThreads), 0, st, w, a);
+    hipLaunchKernelGGL((verify_rows_kernel<true, false>), grid, dim3(kThreads), 0, st, w, a);
+    hipLaunchKernelGGL((verify_decide_kernel<true, false>), dgrid, dim3(kThreads), 0, st, w, a);
   } else {
-    hipLaunchKernelGGL((verify_kernel<false, false>), grid, dim3(kThreads), 0, st, w, a);
+    hipLaunchKernelGGL((verify_rows_kernel<false, false>), grid, dim3(kThreads), 0, st, w, a);
+    hipLaunchKernelGGL((verify_decide_kernel<false, false>), dgrid, dim3(kThreads), 0, st, w, a);
   }
   return check_launch(who);
 }
