@@ -201,6 +201,21 @@ int32_t spec_tree_attention(const void* q, const void* k_pages, const void* v_pa
                             int32_t num_pages, float sm_scale, void* out, float* lse, uint32_t* status, void* ws,
                             size_t ws_bytes, void* stream);
 
+/* spec_tree_attention for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * split-K workspace is a library-held device array of 64 MiB per GPU (reserved
+ * when the library is loaded, held until the process ends); the call allocates
+ * nothing and takes no ws argument. A call whose workspace would exceed 64 MiB
+ * (spec_tree_attention_workspace_size) fails with SPEC_E_WORKSPACE and enqueues
+ * nothing. All calls on one GPU share that GPU's array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and must not be made.
+ * Arguments, outputs and other errors: those of spec_tree_attention. */
+int32_t spec_tree_attention_noalloc(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
+                                    const int32_t* prefix_lens, const int32_t* parents, const int32_t* T_b, int32_t B,
+                                    int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d, int32_t page, int32_t max_pages,
+                                    int32_t num_pages, float sm_scale, void* out, float* lse, uint32_t* status,
+                                    void* stream);
+
 /* ----------------------------------------------------------------------------
  * Tree verification - greedy, or rejection sampling with residual resampling
  * (n1n.ai page, section "Mathematical Proof of Lossless Speedup", steps 1-3;

@@ -78,6 +78,20 @@ def test_attention_host_validation(lib):
                                    None, None, None, 0, None) == SPEC_E_INVAL
 
 
+def test_attention_noalloc_host_validation(lib):
+    p = ctypes.c_void_p(1 << 20)
+    na = lambda **kw: lib.spec_tree_attention_noalloc(p, p, p, p, p, p, None, kw.get("B", 1), kw.get("T", 9),
+                                                      kw.get("Hq", 8), kw.get("Hkv", 2),
+                                                      kw.get("d", 128), 16, kw.get("mp", 64), 64, 0.1, p, None, None,
+                                                      None)
+    assert na(d=96) == SPEC_E_UNSUPPORTED
+    assert na(Hq=7) == SPEC_E_INVAL
+    # a call whose split-K workspace exceeds the library's 64 MiB scratch is refused before any device call
+    assert lib.spec_tree_attention_workspace_size(32, 33, 64, 8, 128, 16, 1029) > 64 << 20
+    assert na(B=32, T=33, Hq=64, Hkv=8, mp=1029) == SPEC_E_WORKSPACE
+    assert b"scratch" in lib.spec_last_error()
+
+
 def test_verify_build_compact_mask_host_validation(lib):
     p = ctypes.c_void_p(1 << 20)
     v = lambda **kw: lib.spec_tree_verify(p, None, None, p, p, None, p, 1, 2, 0, kw.get("B", 1), kw.get("T", 9), 0,

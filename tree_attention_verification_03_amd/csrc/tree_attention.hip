@@ -31,6 +31,8 @@
 //   whose sequence needs more than one item writes its partial (O, m, l) to
 //   the workspace; a second, small kernel combines the partials of each row
 //   in fixed item order and writes out / lse. Deterministic; no atomics.
+#include <mutex>
+
 #include "api_common.h"
 #include "spec_common.h"
 
@@ -815,24 +817,50 @@ extern "C" size_t spec_tree_attention_workspace_size(int32_t B, int32_t max_T, i
   return pl.zero_bytes + pl.part_bytes;
 }
 
+// argument checks of both attention entry points (everything but the workspace), and the call's plan
+static int32_t attention_validate(const char* who, const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* page_table, const int32_t* prefix_lens, const int32_t* parents, int32_t B,
+                                  int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d, int32_t page, int32_t max_pages,
+                                  int32_t num_pages, float sm_scale, void* out, AttnPlan* pl) {
+  int32_t rc = check_shapes(B, max_T, Hq, Hkv, d, page, max_pages);
+  if (rc != SPEC_OK) return rc;
+  if (!q || !k_pages || !v_pages || !page_table || !prefix_lens || !parents || !out)
+    return fail(SPEC_E_INVAL, "%s: null tensor pointer", who);
+  if (num_pages < 1) return fail(SPEC_E_INVAL, "%s: num_pages=%d", who, num_pages);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SPEC_E_INVAL, "%s: sm_scale must be finite and > 0", who);
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages)) & 15)
+    return fail(SPEC_E_INVAL, "%s: q, k_pages and v_pages must be 16-byte aligned", who);
+  *pl = make_plan(B, max_T, Hq, Hkv, d, page, max_pages);
+  return SPEC_OK;
+}
+
+static int32_t attention_launch(const AttnPlan& pl, const void* q, const void* k_pages, const void* v_pages,
+                                const int32_t* page_table, const int32_t* prefix_lens, const int32_t* parents,
+                                const int32_t* T_b, int32_t B, int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d,
+                                int32_t page, int32_t max_pages, int32_t num_pages, float sm_scale, void* out, float* lse,
+                                uint32_t* status, void* ws, hipStream_t st);
+
 extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
                                        const int32_t* prefix_lens, const int32_t* parents, const int32_t* T_b, int32_t B,
                                        int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d, int32_t page, int32_t max_pages,
                                        int32_t num_pages, float sm_scale, void* out, float* lse, uint32_t* status, void* ws,
                                        size_t ws_bytes, void* stream) {
-  int32_t rc = check_shapes(B, max_T, Hq, Hkv, d, page, max_pages);
+  AttnPlan pl;
+  const int32_t rc = attention_validate("spec_tree_attention", q, k_pages, v_pages, page_table, prefix_lens, parents, B,
+                                        max_T, Hq, Hkv, d, page, max_pages, num_pages, sm_scale, out, &pl);
   if (rc != SPEC_OK) return rc;
-  if (!q || !k_pages || !v_pages || !page_table || !prefix_lens || !parents || !out)
-    return fail(SPEC_E_INVAL, "spec_tree_attention: null tensor pointer");
-  if (num_pages < 1) return fail(SPEC_E_INVAL, "spec_tree_attention: num_pages=%d", num_pages);
-  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SPEC_E_INVAL, "spec_tree_attention: sm_scale must be finite and > 0");
-  const AttnPlan pl = make_plan(B, max_T, Hq, Hkv, d, page, max_pages);
   const size_t need = pl.zero_bytes + pl.part_bytes;
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_attention: workspace %zu bytes < %zu", ws_bytes, need);
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages) |
-       reinterpret_cast<uintptr_t>(ws)) & 15)
-    return fail(SPEC_E_INVAL, "spec_tree_attention: q, k_pages, v_pages and ws must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(SPEC_E_INVAL, "spec_tree_attention: ws must be 16-byte aligned");
+  return attention_launch(pl, q, k_pages, v_pages, page_table, prefix_lens, parents, T_b, B, max_T, Hq, Hkv, d, page,
+                          max_pages, num_pages, sm_scale, out, lse, status, ws, static_cast<hipStream_t>(stream));
+}
 
+static int32_t attention_launch(const AttnPlan& pl, const void* q, const void* k_pages, const void* v_pages,
+                                const int32_t* page_table, const int32_t* prefix_lens, const int32_t* parents,
+                                const int32_t* T_b, int32_t B, int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d,
+                                int32_t page, int32_t max_pages, int32_t num_pages, float sm_scale, void* out, float* lse,
+                                uint32_t* status, void* ws, hipStream_t st) {
   AttnParams prm;
   prm.q = static_cast<const uint16_t*>(q);
   prm.k = static_cast<const uint16_t*>(k_pages);
@@ -862,7 +890,6 @@ extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const
   prm.n_groups = B * Hkv * pl.n_splits;
   const dim3 grid = pl.sh.NW == 8 ? dim3(unsigned((prm.n_groups + kXcds - 1) / kXcds * kXcds * pl.n_rb))
                                   : dim3(pl.n_splits, pl.n_rb, B * Hkv);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   const int rows_used = std::min(pl.tpb * 16, pl.G * max_T);  // rows of a row block any tree can have
   // many sequences with many item slots: read each sequence's own items only (mixed-length batch of 32:
   // the combine read 352 MB for 170 MB of partials)
@@ -887,4 +914,66 @@ extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const
     }
   }
   return check_launch("spec_tree_attention");
+}
+
+// ---------------------------------------------------------------- no-allocation entry point
+// The split-K workspace in a library-held device array: `scratch` (kScratchBytes, zero at load). Host code
+// never passes the array's name to a kernel: it takes the array's address on each device once, with that
+// device current, through hipGetSymbolAddress, and uses that address.
+namespace spectree {
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void __launch_bounds__(256) zero_fill_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+}  // namespace
+}  // namespace spectree
+
+static __device__ __align__(256) unsigned char scratch[spectree::kScratchBytes];
+
+// the current device's address of `scratch` (looked up on the device's first call, then kept)
+static int32_t scratch_address(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(SPEC_E_DEVICE, "%s: no usable current device (%s)", who, hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(SPEC_E_DEVICE, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+
+extern "C" int32_t spec_tree_attention_noalloc(const void* q, const void* k_pages, const void* v_pages,
+                                               const int32_t* page_table, const int32_t* prefix_lens,
+                                               const int32_t* parents, const int32_t* T_b, int32_t B, int32_t max_T,
+                                               int32_t Hq, int32_t Hkv, int32_t d, int32_t page, int32_t max_pages,
+                                               int32_t num_pages, float sm_scale, void* out, float* lse,
+                                               uint32_t* status, void* stream) {
+  const char* who = "spec_tree_attention_noalloc";
+  AttnPlan pl;
+  int32_t rc = attention_validate(who, q, k_pages, v_pages, page_table, prefix_lens, parents, B, max_T, Hq, Hkv, d, page,
+                                  max_pages, num_pages, sm_scale, out, &pl);
+  if (rc != SPEC_OK) return rc;
+  const size_t need = pl.zero_bytes + pl.part_bytes;
+  if (need > kScratchBytes)
+    return fail(SPEC_E_WORKSPACE, "%s: this call needs %zu bytes of split-K scratch; the library holds %zu per device "
+                "(use spec_tree_attention with a workspace)", who, need, kScratchBytes);
+  void* ws = nullptr;
+  rc = scratch_address(who, &ws);
+  if (rc != SPEC_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the zero row the kernels read for masked loads: never written, cleared anyway (a kernel, so the call
+  // stays capturable)
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(1), dim3(256), 0, st, static_cast<uint32_t*>(ws), int(pl.zero_bytes / 4));
+  return attention_launch(pl, q, k_pages, v_pages, page_table, prefix_lens, parents, T_b, B, max_T, Hq, Hkv, d, page,
+                          max_pages, num_pages, sm_scale, out, lse, status, ws, st);
 }

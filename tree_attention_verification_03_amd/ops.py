@@ -243,6 +243,28 @@ def spec_tree_attention(q, k_pages, v_pages, page_table, prefix_lens, parents, T
     return ws
 
 
+def spec_tree_attention_noalloc(q, k_pages, v_pages, page_table, prefix_lens, parents, T_b, sm_scale, out, lse=None,
+                                status=None):
+    """spec_tree_attention with its split-K workspace in the library's own device scratch (64 MiB per GPU): no
+    allocation, for callers that cannot allocate (graph capture, serving loops). Calls on one GPU must not overlap."""
+    for name, t, nd in (("q", q, 4), ("k_pages", k_pages, 4), ("page_table", page_table, 2)):
+        if not isinstance(t, torch.Tensor) or t.dim() != nd:
+            raise ValueError(f"{name} must be a {nd}-D tensor")
+    B, max_T, Hq, d = q.shape
+    P, page, Hkv = k_pages.shape[:3]
+    max_pages = page_table.shape[1]
+    _check(_spec("q", q, torch.bfloat16), _spec("k_pages", k_pages, torch.bfloat16, (P, page, Hkv, d)),
+           _spec("v_pages", v_pages, torch.bfloat16, (P, page, Hkv, d)),
+           _spec("page_table", page_table, torch.int32, (B, max_pages)),
+           _spec("prefix_lens", prefix_lens, torch.int32, (B,)), _spec("parents", parents, torch.int32, (B, max_T)),
+           *_opt("T_b", T_b, torch.int32, (B,)), _spec("out", out, torch.bfloat16, (B, max_T, Hq, d)),
+           *_opt("lse", lse, torch.float32, (B, max_T, Hq)), *_opt("status", status, torch.int32, (B,)))
+    rc = load().spec_tree_attention_noalloc(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(page_table), _ptr(prefix_lens),
+                                            _ptr(parents), _ptr(T_b), B, max_T, Hq, Hkv, d, page, max_pages, P,
+                                            float(sm_scale), _ptr(out), _ptr(lse), _ptr(status), _stream(q))
+    check(rc, "spec_tree_attention_noalloc")
+
+
 # ------------------------------------------------------------------ verify
 def _verify_specs(rows, rows_name, draft_probs, q_row, tokens, parents, T_b, mode, accept_len, accept_nodes,
                   out_tokens, status, ws):
