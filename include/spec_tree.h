@@ -8,6 +8,7 @@
  *   spec_tree_attention                                            tree attention
  *   spec_tree_verify                                               accepted path + bonus
  *   spec_kv_compact                                                keep accepted KV
+ *   spec_kv_prune                                 release rejected branches' pages
  *
  * Conventions shared by every entry point
  *   - Tensor arguments are DEVICE pointers to caller-owned, contiguous,
@@ -60,6 +61,7 @@ extern "C" {
 #define SPEC_STATUS_ZERO_RESIDUAL 16u  /* sampling node on the path whose residual max(0, p - q) became zero */
 #define SPEC_STATUS_INVALID_PAGE 32u   /* page-table entry outside [0, num_pages): its keys are skipped */
 #define SPEC_STATUS_INVALID_LENGTH 64u /* prefix_lens[b] < 0 or prefix + T_b beyond the page table: clamped */
+#define SPEC_STATUS_INVALID_PATH 128u  /* accept_len / accept_nodes not a path of the tree: page table left as is */
 
 /* verification modes (per sequence, int8) */
 #define SPEC_MODE_GREEDY 0
@@ -318,6 +320,50 @@ int32_t spec_kv_compact(void* k_pages, void* v_pages, const int32_t* page_table,
                         const int32_t* accept_nodes, const int32_t* accept_len, int32_t B, int32_t max_T,
                         int32_t Hkv, int32_t d, int32_t page, int32_t max_pages, int32_t num_pages,
                         int32_t num_layers, int64_t layer_stride_elems, int32_t* new_prefix_lens, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * Page-table pruning of rejected branches - tanhdev section 4 "Production
+ * Failure Modes", Failure Mode 2 "KV Cache Memory Fragmentation" (the tree
+ * cache prunes discarded branches without copying KV); lesty.tech section 6
+ * "Paged Tree KV-Cache Allocation" (rejected candidates' physical blocks go
+ * straight back to the free pool). No KV moves; only page_table changes.
+ *
+ * Sequence b's tree used logical slots L_b .. L_b + T_b - 1 (node i at L_b + i)
+ * and verification accepted the path n_0 = 0 < n_1 < ... < n_a (accept_nodes,
+ * accept_len). Afterwards the path reads, in order, at logical slots
+ * L_b .. L_b + a, and new_prefix_lens[b] = L_b + 1 + a.
+ *   mode SPEC_PRUNE_REMAP (page must be 1, a table of token slots): zero-copy.
+ *     Entry L_b + k takes the old entry of slot L_b + n_k (k = 1..a), entries
+ *     L_b + a + 1 .. L_b + T_b - 1 become -1, and the old entries of the
+ *     T_b - 1 - a rejected nodes are returned in node order. Call it INSTEAD
+ *     of spec_kv_compact.
+ *   mode SPEC_PRUNE_TAIL (any page size): call it AFTER spec_kv_compact with
+ *     the same accept_nodes / accept_len. The pages the tree touched whose
+ *     slots all lie at or past L_b + 1 + a (logical pages ceil((L_b + 1 + a) /
+ *     page) .. floor((L_b + T_b - 1) / page)) are returned in logical order and
+ *     their entries become -1.
+ * page_table      int32 [B, max_pages], rewritten in place
+ * prefix_lens, T_b, accept_len int32 [B]; accept_nodes int32 [B, max_T]
+ * freed           int32 [B, max_T] out: released entries (physical page ids,
+ *                 token slots for REMAP), then -1 up to max_T
+ * freed_count     int32 [B] out
+ * new_prefix_lens int32 [B] out; it may be prefix_lens itself (in place)
+ * status          uint32 [B] out or NULL: SPEC_STATUS_INVALID_PAGE when a
+ *                 touched entry lies outside [0, num_pages) (cleared, never
+ *                 returned); SPEC_STATUS_INVALID_LENGTH (T_b outside
+ *                 [1, max_T], L_b < 0, or the tree past the table) or
+ *                 SPEC_STATUS_INVALID_PATH: that sequence's table is left as
+ *                 is, nothing is returned and new_prefix_lens[b] = max(L_b, 0).
+ * Outputs must not overlap each other or the inputs (apart from the in-place
+ * new_prefix_lens). Host checks: sizes, max_T <= 65, page, mode
+ * (SPEC_E_INVAL / SPEC_E_UNSUPPORTED), null pointers.
+ * ------------------------------------------------------------------------- */
+#define SPEC_PRUNE_TAIL 0
+#define SPEC_PRUNE_REMAP 1
+int32_t spec_kv_prune(int32_t* page_table, const int32_t* prefix_lens, const int32_t* T_b, const int32_t* accept_nodes,
+                      const int32_t* accept_len, int32_t B, int32_t max_T, int32_t page, int32_t max_pages,
+                      int32_t num_pages, int32_t mode, int32_t* freed, int32_t* freed_count, int32_t* new_prefix_lens,
+                      uint32_t* status, void* stream);
 
 #ifdef __cplusplus
 }

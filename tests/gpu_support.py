@@ -7,6 +7,7 @@ import sys
 import numpy as np
 
 import oracle
+from oracle.kvcompact import kv_prune as oracle_kv_prune
 from oracle.tree import build_tree
 from oracle.verify import verify_sequence
 from workloads.synth import bf16_bits_to_f32
@@ -100,3 +101,29 @@ def check_verify(w, host, trees, seqs=None, tokens=None, parents=None, q_row=Non
         assert host["out_tokens"][b, : n + 1].tolist() == out, f"out_tokens b={b}"
         assert (host["accept_nodes"][b, n + 1 :] == -1).all() and (host["out_tokens"][b, n + 1 :] == -1).all()
         assert int(host["status"][b]) == st, f"status b={b}: gpu {host['status'][b]} oracle {st}"
+
+
+def gpu_kv_prune(pt, L, T, nodes, alen, page, num_pages, mode, in_place=False):
+    """spec_kv_prune on device copies (outputs pre-filled with junk); returns host arrays."""
+    import torch
+
+    from tree_attention_verification_03_amd import ops
+
+    dev = torch.device("cuda")
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    B, max_T = nodes.shape
+    tpt, tl = i32(pt), i32(L)
+    junk = lambda *s: torch.full(s, 7, dtype=torch.int32, device=dev)
+    freed, cnt, st = junk(B, max_T), junk(B), junk(B)
+    newl = tl if in_place else junk(B)
+    ops.spec_kv_prune(tpt, tl, i32(T), i32(nodes), i32(alen), page, num_pages, mode, freed, cnt, newl, st)
+    torch.cuda.synchronize()
+    return tuple(x.cpu().numpy() for x in (tpt, freed, cnt, newl, st))
+
+
+def check_kv_prune(pt, L, T, nodes, alen, page, num_pages, mode, in_place=False):
+    got = gpu_kv_prune(pt, L, T, nodes, alen, page, num_pages, mode, in_place)
+    ref = oracle_kv_prune(pt, L, T, nodes, alen, page, num_pages, mode)
+    for name, g, r in zip(("page_table", "freed", "freed_count", "new_prefix_lens", "status"), got, ref):
+        assert np.array_equal(g.astype(np.int64), np.asarray(r, dtype=np.int64)), name
+    return ref

@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_pipeline():
     names = declared_functions()
     for n in ["spec_tree_build_step", "spec_tree_build_step_finish", "spec_tree_build_finish", "spec_tree_mask", "spec_tree_attention",
-              "spec_tree_verify", "spec_kv_compact", "spec_abi_version", "spec_last_error"]:
+              "spec_tree_verify", "spec_kv_compact", "spec_kv_prune", "spec_abi_version", "spec_last_error"]:
         assert n in names
 
 
@@ -125,6 +125,20 @@ def test_verify_build_compact_mask_host_validation(lib):
     assert lib.spec_kv_compact(p, p, p, p, p, p, 2, 9, 2, 128, 16, 4, 4, 1, 0, q, None) == SPEC_E_INVAL
     assert b"overlaps" in lib.spec_last_error()
     assert lib.spec_tree_mask(None, None, 1, 9, None, None, None, None) == SPEC_E_INVAL
+
+
+def test_kv_prune_host_validation(lib):
+    p = ctypes.c_void_p(1 << 20)
+    pr = lambda **kw: lib.spec_kv_prune(p, p, kw.get("T_b", p), p, p, kw.get("B", 2), kw.get("T", 9), kw.get("page", 16),
+                                        8, kw.get("num_pages", 64), kw.get("mode", 0), p, p, p, None, None)
+    assert pr(T=66) == SPEC_E_UNSUPPORTED
+    assert pr(page=12) == SPEC_E_UNSUPPORTED
+    assert pr(B=0) == SPEC_E_INVAL
+    assert pr(num_pages=0) == SPEC_E_INVAL
+    assert pr(mode=2) == SPEC_E_INVAL
+    assert pr(mode=1) == SPEC_E_INVAL  # the zero-copy remap needs one slot per table entry
+    assert b"page" in lib.spec_last_error()
+    assert pr(T_b=None) == SPEC_E_INVAL
 
 
 def test_verify_logits_host_validation(lib):

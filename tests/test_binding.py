@@ -150,3 +150,28 @@ def test_kv_compact_rejects():
         ops.spec_kv_compact(**{**good, "prefix_lens": lens[:B], "new_prefix_lens": lens[1:B + 1]})
     with pytest.raises(ValueError, match="must be on the GPU"):
         ops.spec_kv_compact(**good)
+
+
+def test_kv_prune_rejects():
+    good = dict(page_table=i32(B, MP), prefix_lens=i32(B), T_b=i32(B), accept_nodes=i32(B, T), accept_len=i32(B),
+                page=PG, num_pages=P, mode=ops.PRUNE_TAIL, freed=i32(B, T), freed_count=i32(B),
+                new_prefix_lens=i32(B), status=i32(B))
+    for bad, msg in ((dict(page_table=i64(B, MP)), "page_table must be torch.int32"),
+                     (dict(T_b=i32(B + 1)), "T_b must have shape"),
+                     (dict(freed=i32(B, T - 1)), "freed must have shape"),
+                     (dict(freed_count=f32(B)), "freed_count must be torch.int32"),
+                     (dict(status=i32(B, 2)), "status must have shape"),
+                     (dict(accept_nodes=i32(B, 2 * T)[:, ::2]), "accept_nodes must be contiguous")):
+        with pytest.raises((ValueError, TypeError), match=msg):
+            ops.spec_kv_prune(**{**good, **bad})
+    buf = i32(B * (T + 1))
+    with pytest.raises(ValueError, match="freed must not overlap freed_count"):
+        ops.spec_kv_prune(**{**good, "freed": buf[:B * T].view(B, T), "freed_count": buf[B * T - 1:B * T - 1 + B]})
+    with pytest.raises(ValueError, match="page_table must not overlap accept_nodes"):
+        ops.spec_kv_prune(**{**good, "page_table": buf[:B * MP].view(B, MP), "accept_nodes": buf[:B * T].view(B, T)})
+    # new_prefix_lens may be prefix_lens itself (in place), but not a shifted view of it
+    lens = i32(2 * B)
+    with pytest.raises(ValueError, match="new_prefix_lens must not overlap prefix_lens"):
+        ops.spec_kv_prune(**{**good, "prefix_lens": lens[:B], "new_prefix_lens": lens[1:B + 1]})
+    with pytest.raises(ValueError, match="must be on the GPU"):
+        ops.spec_kv_prune(**{**good, "new_prefix_lens": good["prefix_lens"]})

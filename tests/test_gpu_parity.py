@@ -10,8 +10,10 @@
 import numpy as np
 import pytest
 
+from gpu_support import check_kv_prune
 from gpu_support import (ATTN_MAX_ABS, ATTN_REL_L2, LSE_ABS, check_build, check_verify, compare_attention, log,
                          oracle_trees, parents_array, run_pipeline, to_np)
+from oracle.kvcompact import PRUNE_REMAP, PRUNE_TAIL
 from oracle.kvcompact import kv_compact as oracle_kv_compact
 from oracle.tree import build_tree
 from workloads import get_config, make_workload
@@ -544,6 +546,48 @@ def test_kv_compact_multilayer():
     assert np.array_equal(kt.view(torch.int16).cpu().numpy().view(np.uint16), k_ref)
     assert np.array_equal(vt.view(torch.int16).cpu().numpy().view(np.uint16), v_ref)
     assert newl.cpu().numpy().tolist() == l_ref.tolist()
+
+
+def _random_tree_path(rng, T):
+    parents = random_parents(rng, T, "random")
+    node, path = int(rng.integers(0, T)), []
+    while node > 0:
+        path.append(node)
+        node = int(parents[node])
+    return path[::-1]
+
+
+@pytest.mark.parametrize("mode,page,in_place", [(PRUNE_TAIL, 1, False), (PRUNE_TAIL, 4, False), (PRUNE_TAIL, 16, True),
+                                                (PRUNE_TAIL, 64, False), (PRUNE_REMAP, 1, False),
+                                                (PRUNE_REMAP, 1, True)])
+def test_kv_prune_matches_oracle(mode, page, in_place):
+    """Page table, released entries, counts, new lengths and status bit-exact with the oracle: random trees of
+    1 to 65 nodes and random accepted paths (empty and whole-chain ones among them), plus one sequence each with a
+    non-increasing path, a tree past the table and an entry outside the pool."""
+    rng = np.random.default_rng(100 * page + mode + in_place)
+    B, max_T = 12, 65
+    T = np.array([1, 65, 2, 33] + [int(x) for x in rng.integers(1, 66, size=B - 4)], dtype=np.int64)
+    L = rng.integers(0, 300, size=B)
+    max_pages = -(-(300 + 65) // page) + 1
+    P = B * max_pages + 5
+    pt = rng.permutation(P)[: B * max_pages].reshape(B, max_pages)
+    nodes = np.full((B, max_T), -1, dtype=np.int64)
+    nodes[:, 0] = 0
+    alen = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        path = list(range(1, int(T[b]))) if b == 1 else _random_tree_path(rng, int(T[b]))
+        nodes[b, 1:1 + len(path)] = path
+        alen[b] = len(path)
+    nodes[B - 3, 1:3], alen[B - 3], T[B - 3] = [4, 2], 2, max(T[B - 3], 6)  # not increasing
+    L[B - 2] = max_pages * page - T[B - 2] + 1  # tree past the table
+    L[B - 1], T[B - 1], alen[B - 1] = 60, 40, 1  # slot 99 is a rejected node's, on a page past the new length 62
+    nodes[B - 1, 1:] = -1
+    nodes[B - 1, 1] = 1
+    pt[B - 1, 99 // page] = P + 3  # outside the pool
+    log(f"[prune] mode={mode} page={page} in_place={in_place}")
+    ref = check_kv_prune(pt, L, T, nodes, alen, page, P, mode, in_place)
+    assert ref[4].tolist()[B - 3:] == [128, 64, 32]
+    assert ref[2][0] == 0 and ref[2][1] == 0  # a root-only tree, a whole chain accepted
 
 
 # ---------------------------------------------------------------- HIP graph replay

@@ -42,6 +42,8 @@ SIGNATURES = {
                                         c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "spec_kv_compact": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                 c_i32, c_i64, c_vp, c_vp]),
+    "spec_kv_prune": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp,
+                              c_vp, c_vp]),
 }
 
 _lib = None

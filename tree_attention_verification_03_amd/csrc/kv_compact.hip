@@ -7,6 +7,12 @@
 // L_b + k. One block per (sequence, layer, KV head) loads every source row
 // into LDS before it stores any destination, so overlapping moves are safe.
 //
+// Pruning: tanhdev section 4 "Production Failure Modes", Failure Mode 2 "KV
+// Cache Memory Fragmentation" (discarded branches pruned without copies);
+// lesty.tech section 6 (rejected candidates' blocks go back to the free pool).
+// Only the page table changes: one wave per sequence rewrites its tree region
+// and packs the released entries with a ballot prefix count.
+//
 // Mask: tanhdev section 2 "Dynamic Tree-Attention Verification" and section 5
 // "FlashAttention-3 Tree Kernel Design" (one 64-bit ancestry word per node).
 #include "api_common.h"
@@ -17,6 +23,7 @@ namespace {
 
 constexpr int kCompactThreads = 256;
 constexpr int kMaskThreads = 128;
+constexpr int kPruneThreads = 64;  // one wave: a tree has at most 64 drafts, and its tail at most 64 pages
 
 template <int D>
 __global__ void __launch_bounds__(kCompactThreads) kv_compact_kernel(uint16_t* k, uint16_t* v, const int32_t* page_table,
@@ -75,6 +82,76 @@ __global__ void __launch_bounds__(kCompactThreads) kv_compact_kernel(uint16_t* k
     if (s < 0 || d < 0) continue;
     reinterpret_cast<uint4*>(kl + size_t(d) * row_stride)[c] = stage[0][j - 1][c];
     reinterpret_cast<uint4*>(vl + size_t(d) * row_stride)[c] = stage[1][j - 1][c];
+  }
+}
+
+// REMAP (one slot per entry): lane i handles draft node i + 1; the k-th accepted node's entry moves to slot L + k.
+// TAIL: lane i handles logical page ceil(L' / page) + i, which holds only rejected slots once the accepted KV has
+// been compacted below L' = L + 1 + accept_len.
+__global__ void __launch_bounds__(kPruneThreads) kv_prune_kernel(int32_t* page_table, const int32_t* prefix_lens,
+                                                                  const int32_t* T_b, const int32_t* accept_nodes,
+                                                                  const int32_t* accept_len, int max_T, int page_shift,
+                                                                  int max_pages, int num_pages, int remap, int32_t* freed,
+                                                                  int32_t* freed_count, int32_t* new_prefix_lens,
+                                                                  uint32_t* status) {
+  __shared__ int on_path[kPruneThreads + 1];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int L = prefix_lens[b], T = T_b[b], a = accept_len[b];
+  const size_t nb = size_t(b) * max_T;
+  int32_t* row = page_table + size_t(b) * max_pages;
+  const bool len_ok = T >= 1 && T <= max_T && L >= 0 && int64_t(L) + T <= (int64_t(max_pages) << page_shift);
+  bool path_ok = len_ok && a >= 0 && a <= T - 1;
+  const int j = lane + 1;  // path position of this lane, and its draft node in REMAP
+  int n = 0;
+  if (path_ok && j <= a) n = accept_nodes[nb + j];
+  int prev = __shfl_up(n, 1);
+  if (lane == 0) prev = 0;
+  path_ok = path_ok && __ballot(j <= a && !(prev < n && n < T)) == 0;
+  if (!path_ok) {
+    for (int i = lane; i < max_T; i += kPruneThreads) freed[nb + i] = -1;
+    if (lane == 0) {
+      new_prefix_lens[b] = L < 0 ? 0 : L;
+      freed_count[b] = 0;
+      if (status) status[b] = len_ok ? SPEC_STATUS_INVALID_PATH : SPEC_STATUS_INVALID_LENGTH;
+    }
+    return;
+  }
+  int32_t old = -1;
+  bool put = false, bad = false;
+  if (remap) {
+    on_path[j] = 0;
+    __syncthreads();
+    if (j <= a) on_path[n] = 1;
+    const bool in = j < T;
+    if (in) old = row[L + j];
+    __syncthreads();
+    const int32_t moved = __shfl(old, (j <= a ? n : 1) - 1);  // the entry of accepted node n sits in lane n - 1
+    if (j <= a)
+      row[L + j] = moved;
+    else if (in)
+      row[L + j] = -1;
+    bad = in && (old < 0 || old >= num_pages);
+    put = in && !bad && !on_path[j];
+  } else {
+    const int first = (L + a + (1 << page_shift)) >> page_shift;  // ceil((L + 1 + a) / page)
+    const int last = (L + T - 1) >> page_shift;
+    const int pidx = first + lane;
+    if (pidx <= last) {
+      old = row[pidx];
+      row[pidx] = -1;
+      bad = old < 0 || old >= num_pages;
+      put = !bad;
+    }
+  }
+  const uint64_t mask = __ballot(put);
+  const int cnt = __popcll(mask);
+  if (put) freed[nb + __popcll(mask & ((1ull << lane) - 1))] = old;
+  for (int i = cnt + lane; i < max_T; i += kPruneThreads) freed[nb + i] = -1;
+  const bool any_bad = __ballot(bad) != 0;
+  if (lane == 0) {
+    new_prefix_lens[b] = L + 1 + a;
+    freed_count[b] = cnt;
+    if (status) status[b] = any_bad ? SPEC_STATUS_INVALID_PAGE : 0u;
   }
 }
 
@@ -168,6 +245,27 @@ extern "C" int32_t spec_kv_compact(void* k_pages, void* v_pages, const int32_t* 
                        static_cast<uint16_t*>(v_pages), page_table, prefix_lens, accept_nodes, accept_len, max_T, Hkv, ps,
                        max_pages, num_pages, layer_stride_elems, new_prefix_lens);
   return check_launch("spec_kv_compact");
+}
+
+extern "C" int32_t spec_kv_prune(int32_t* page_table, const int32_t* prefix_lens, const int32_t* T_b,
+                                 const int32_t* accept_nodes, const int32_t* accept_len, int32_t B, int32_t max_T,
+                                 int32_t page, int32_t max_pages, int32_t num_pages, int32_t mode, int32_t* freed,
+                                 int32_t* freed_count, int32_t* new_prefix_lens, uint32_t* status, void* stream) {
+  if (B < 1 || max_T < 1 || max_pages < 1 || num_pages < 1)
+    return fail(SPEC_E_INVAL, "spec_kv_prune: sizes must be positive (B=%d max_T=%d max_pages=%d num_pages=%d)", B, max_T,
+                max_pages, num_pages);
+  if (max_T > 65) return fail(SPEC_E_UNSUPPORTED, "spec_kv_prune: max_T=%d > 65", max_T);
+  if (!is_pow2(page) || page > 1024) return fail(SPEC_E_UNSUPPORTED, "spec_kv_prune: page %d not a power of two <= 1024", page);
+  if (mode != SPEC_PRUNE_TAIL && mode != SPEC_PRUNE_REMAP) return fail(SPEC_E_INVAL, "spec_kv_prune: mode %d", mode);
+  if (mode == SPEC_PRUNE_REMAP && page != 1)
+    return fail(SPEC_E_INVAL, "spec_kv_prune: SPEC_PRUNE_REMAP needs one slot per page-table entry (page %d)", page);
+  if ((long long)max_pages * page > (1LL << 30)) return fail(SPEC_E_UNSUPPORTED, "spec_kv_prune: more than 2^30 slots per sequence");
+  if (!page_table || !prefix_lens || !T_b || !accept_nodes || !accept_len || !freed || !freed_count || !new_prefix_lens)
+    return fail(SPEC_E_INVAL, "spec_kv_prune: null pointer");
+  hipLaunchKernelGGL(kv_prune_kernel, dim3(B), dim3(kPruneThreads), 0, static_cast<hipStream_t>(stream), page_table,
+                     prefix_lens, T_b, accept_nodes, accept_len, max_T, ilog2(page), max_pages, num_pages,
+                     mode == SPEC_PRUNE_REMAP ? 1 : 0, freed, freed_count, new_prefix_lens, status);
+  return check_launch("spec_kv_prune");
 }
 
 extern "C" int32_t spec_tree_mask(const int32_t* parents, const int32_t* T_b, int32_t B, int32_t max_T,

@@ -359,3 +359,37 @@ def spec_kv_compact(k_pages, v_pages, page_table, prefix_lens, accept_nodes, acc
                                 _ptr(accept_len), B, max_T, Hkv, d, page, page_table.shape[1], P, num_layers,
                                 layer_stride_elems, _ptr(new_prefix_lens), _stream(k_pages))
     check(rc, "spec_kv_compact")
+
+
+PRUNE_TAIL = 0  # after spec_kv_compact: release the pages past the new length that the tree touched
+PRUNE_REMAP = 1  # page == 1: zero-copy remap of the accepted path, release the rejected nodes' slots
+
+
+def spec_kv_prune(page_table, prefix_lens, T_b, accept_nodes, accept_len, page: int, num_pages: int, mode: int,
+                  freed, freed_count, new_prefix_lens, status=None):
+    """page_table int32 [B, max_pages] (rewritten in place); prefix_lens, T_b, accept_len int32 [B]; accept_nodes
+    int32 [B, max_T]; outputs freed int32 [B, max_T], freed_count int32 [B], new_prefix_lens int32 [B] (may be
+    prefix_lens itself), status int32 [B] or None (uint32 bits)."""
+    for name, t in (("accept_nodes", accept_nodes), ("page_table", page_table)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D tensor")
+    B, max_T = accept_nodes.shape
+    specs = (_spec("page_table", page_table, torch.int32, (B, None)),
+             _spec("prefix_lens", prefix_lens, torch.int32, (B,)), _spec("T_b", T_b, torch.int32, (B,)),
+             _spec("accept_nodes", accept_nodes, torch.int32, (B, max_T)),
+             _spec("accept_len", accept_len, torch.int32, (B,)), _spec("freed", freed, torch.int32, (B, max_T)),
+             _spec("freed_count", freed_count, torch.int32, (B,)),
+             _spec("new_prefix_lens", new_prefix_lens, torch.int32, (B,)), *_opt("status", status, torch.int32, (B,)))
+    _check_layout(*specs)
+    outs = [("page_table", page_table), ("freed", freed), ("freed_count", freed_count),
+            ("new_prefix_lens", new_prefix_lens)] + ([("status", status)] if status is not None else [])
+    ins = [("prefix_lens", prefix_lens), ("T_b", T_b), ("accept_nodes", accept_nodes), ("accept_len", accept_len)]
+    for i, (na, a) in enumerate(outs):
+        for nb, b in outs[i + 1:] + ins:
+            if _overlap(a, b) and not (na == "new_prefix_lens" and b.data_ptr() == a.data_ptr() and nb == "prefix_lens"):
+                raise ValueError(f"{na} must not overlap {nb}")
+    _check_device(*specs)
+    rc = load().spec_kv_prune(_ptr(page_table), _ptr(prefix_lens), _ptr(T_b), _ptr(accept_nodes), _ptr(accept_len), B,
+                              max_T, page, page_table.shape[1], num_pages, mode, _ptr(freed), _ptr(freed_count),
+                              _ptr(new_prefix_lens), _ptr(status), _stream(page_table))
+    check(rc, "spec_kv_prune")
