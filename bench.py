@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 PMC_COPY_BYTES = 256 << 20  # calibration copy of --profile-kernels
 BF16_DENSE_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP8_DENSE_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 HEADLINE = "mixed_serving_b32"
 METRIC = "tree-attn+verify draft tokens/s per layer; achieved HBM GB/s vs MI355X peak"
 
@@ -102,6 +103,59 @@ def pmc_traffic(workload):
     except (KeyError, ValueError):
         return None
 
+
+
+def measure_fp8(w, steps, bf16_call_ms, args, torch):
+    """The FP8-KV variant of the attention call (spec_tree_attention_fp8) on the same trees and queries, E4M3
+    pools drawn for the workload's shape: back-to-back calls in one graph over >= --rotate-gib of pools."""
+    import numpy as np
+
+    from tree_attention_verification_03_amd import ops
+    from workloads.synth import fp8_kv_pools
+
+    eprint("[bench] FP8-KV variant: drawing E4M3 pools")
+    k8, v8, ks, vs = fp8_kv_pools(w.k_pages.shape, seed=1)
+    dev = steps[0].dw.device
+    per = k8.nbytes + v8.nbytes
+    Rf = int(min(512, max(2, np.ceil(args.rotate_gib * 2**30 / per))))
+    kt, vt = torch.from_numpy(k8).to(dev), torch.from_numpy(v8).to(dev)
+    pools = [(kt, vt)] + [(kt.clone(), vt.clone()) for _ in range(Rf - 1)]
+    kst, vst = torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev)
+
+    def call(i):
+        st = steps[i % len(steps)]
+        o, d = st.o, st.dw
+        k, v = pools[i]
+        ops.spec_tree_attention_fp8(d.q, k, v, kst, vst, d.page_table, d.prefix_lens, o.parents, d.T_b, d.w.sm_scale,
+                                    o.attn_out, o.lse, None, st.ws_attn)
+
+    for i in range(Rf):
+        call(i)
+    torch.cuda.synchronize()
+
+    def chain():
+        for i in range(Rf):
+            call(i)
+
+    g = capture(chain, torch)
+    time_graphs([g], 2, torch)
+    ms = time_graphs([g], max(4, args.steps // Rf), torch)[0] / Rf
+    L = w.prefix_lens.astype(np.int64)
+    T = w.T_b.astype(np.int64)
+    nbytes = int((L * w.Hkv * w.d * 2).sum() + (T * w.Hkv * w.d * 2).sum() + 2 * (T * w.Hq * w.d * 2).sum())
+    host_depth = steps[0].o.depth.cpu().numpy()
+    tree_keys = int(sum((host_depth[b, : T[b]] + 1).sum() for b in range(w.B)))
+    flops = int(4 * w.d * w.Hq * ((T * L).sum() + tree_keys))
+    t = ms * 1e-3
+    eprint(f"[bench] FP8-KV attention call, back-to-back: {ms * 1e3:.2f} us per call ({Rf} pool replicas)")
+    bound = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (FP8_DENSE_TFLOPS * 1e12) else "mfma"
+    del pools, g
+    return dict(attn_us=round(ms * 1e3, 3), speedup_vs_bf16=round(bf16_call_ms / ms, 3), bound=bound,
+                bytes_per_call=nbytes, achieved_gbs=round(nbytes / t / 1e9, 1),
+                hbm_frac=round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), flops_per_call=flops,
+                achieved_tflops=round(flops / t / 1e12, 2), fp8_mfma_frac=round(flops / t / 1e12 / FP8_DENSE_TFLOPS, 4),
+                kernel="tree_attn_fp8_kernel + tree_attn_combine (E4M3 K/V with per-head scales, E4M3 MFMA)",
+                replicas=Rf)
 
 def time_graphs(graphs, n, torch):
     """Replay graphs round-robin n times; returns (gpu ms per replay, wall ms per replay)."""
@@ -215,9 +269,28 @@ def measure(spec, args, torch, profile_mode=False):
         return f
 
     if profile_mode:
-        op = {"attention": attn_only, "verify": lambda st: st.verify, "build": lambda st: st.build}[args.profile_op]
-        for i in range(args.profile_kernels):
-            op(steps[i % R])()
+        if args.profile_op == "attention_fp8":
+            from workloads.synth import fp8_kv_pools
+
+            k8, v8, ks, vs = fp8_kv_pools(w.k_pages.shape, seed=1)
+            dev = dw0.device
+            kt, vt = torch.from_numpy(k8).to(dev), torch.from_numpy(v8).to(dev)
+            Rf = int(min(512, max(2, np.ceil(args.rotate_gib * 2**30 / (k8.nbytes + v8.nbytes)))))
+            pools = [(kt, vt)] + [(kt.clone(), vt.clone()) for _ in range(Rf - 1)]
+            kst, vst = torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev)
+
+            def fp8_call(i):
+                st = steps[i % R]
+                return lambda: ops.spec_tree_attention_fp8(st.dw.q, pools[i % Rf][0], pools[i % Rf][1], kst, vst,
+                                                           st.dw.page_table, st.dw.prefix_lens, st.o.parents,
+                                                           st.dw.T_b, w.sm_scale, st.o.attn_out, st.o.lse, None,
+                                                           st.ws_attn)
+            for i in range(args.profile_kernels):
+                fp8_call(i)()
+        else:
+            op = {"attention": attn_only, "verify": lambda st: st.verify, "build": lambda st: st.build}[args.profile_op]
+            for i in range(args.profile_kernels):
+                op(steps[i % R])()
         torch.cuda.synchronize()
         src = torch.empty(PMC_COPY_BYTES, dtype=torch.uint8, device=dw0.device)
         dst = torch.empty_like(src)
@@ -273,6 +346,8 @@ def measure(spec, args, torch, profile_mode=False):
         attn_call_ms = time_graphs([attn_chain], reps, torch)[0] / R
         eprint(f"[bench] attention call, back-to-back: {attn_call_ms * 1e3:.2f} us per call")
 
+    fp8 = measure_fp8(w, steps, attn_call_ms, args, torch) if (w.d == 128 and not args.eager and not args.no_fp8) else None
+
     work = algorithmic_work(w, host)
     n_draft = int(w.num_draft.sum())
     t_attn = attn_call_ms * 1e-3
@@ -301,6 +376,8 @@ def measure(spec, args, torch, profile_mode=False):
         stage_us={k: round(v * 1e3, 3) for k, v in stage_ms.items()},
         verify_hbm_gbs=round(work["verify_bytes"] / (stage_ms["verify"] * 1e-3) / 1e9, 1),
         roofline=roof, replicas=R, batch=w.B, draft_tokens=n_draft)
+    if fp8 is not None:
+        res["fp8_variant"] = fp8
     del av, full, stage, attn_chain, steps, replicas, dw0
     gc.collect()
     torch.cuda.synchronize()
@@ -321,6 +398,7 @@ def main():
                     help="CPU oracle: whole oracle steps until this many seconds have passed (at least one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-KV attention variant's timing")
     ap.add_argument("--verify-logits", action="store_true",
                     help="verify with spec_tree_verify_logits (sampling distributions formed from the target logits and "
                          "temperatures inside the library) instead of supplied probabilities")
@@ -332,7 +410,7 @@ def main():
                     help="profiling mode (run under rocprofv3): N eager calls of --profile-op over the replicas of the "
                          "--config workload, then one 256 MiB device-to-device copy whose counters calibrate "
                          "FETCH_SIZE / WRITE_SIZE; no timing")
-    ap.add_argument("--profile-op", choices=["attention", "verify", "build"], default="attention")
+    ap.add_argument("--profile-op", choices=["attention", "attention_fp8", "verify", "build"], default="attention")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -384,6 +462,7 @@ def main():
         "stage_us": head["stage_us"],
         "verify_hbm_gbs": head["verify_hbm_gbs"],
         "roofline": head["roofline"],
+        "fp8_variant": head.get("fp8_variant"),
         "per_config": per_config,
     }
     if not args.no_cpu_baseline:

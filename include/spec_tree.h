@@ -6,6 +6,7 @@
  *   spec_tree_build_step (x depth) -> spec_tree_build_finish      draft tree
  *     (or spec_tree_build_step_finish x depth, the same in fewer launches)
  *   spec_tree_attention                                            tree attention
+ *     (or spec_tree_attention_fp8 over an E4M3 KV cache)
  *   spec_tree_verify                                               accepted path + bonus
  *   spec_kv_compact                                                keep accepted KV
  *   spec_kv_prune                                 release rejected branches' pages
@@ -202,6 +203,33 @@ int32_t spec_tree_attention(const void* q, const void* k_pages, const void* v_pa
                             int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d, int32_t page, int32_t max_pages,
                             int32_t num_pages, float sm_scale, void* out, float* lse, uint32_t* status, void* ws,
                             size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * FP8-KV variant of tree attention - tanhdev section 3 "Quantitative Hardware
+ * Benchmarks on NVIDIA H100" (FP8 targets); n1n.ai page, FAQ "Can speculative
+ * decoding be combined with FP8 or AWQ quantization?". The pages fix no
+ * format; this variant's is:
+ *   k_pages, v_pages  uint8 [num_pages, page, Hkv, d]: OCP E4M3 ("fn") codes;
+ *                     slot s's value is code value * k_scale[g] (v_scale[g])
+ *   k_scale, v_scale  fp32 [Hkv] device arrays
+ *   q                 bf16 as in spec_tree_attention; each (node, head) row is
+ *                     rounded to E4M3 (nearest, ties to even) after scaling by
+ *                     2^-e, e the smallest integer with max|q| <= 448 * 2^e,
+ *                     and stands for code value * 2^e.
+ * The attention is spec_tree_attention's over those values. Both products run
+ * on E4M3 MFMAs: the softmax weights p (each at most 256 times the row's
+ * largest, never above 448) are rounded to E4M3 before the P V product and
+ * the row sums add the rounded weights. Codes 0x7f / 0xff (NaN) must not occur.
+ * Supported: d = 128 only (SPEC_E_UNSUPPORTED otherwise); all other shapes,
+ * arguments, outputs, status bits and the workspace (same size as
+ * spec_tree_attention_workspace_size) as spec_tree_attention.
+ * ------------------------------------------------------------------------- */
+int32_t spec_tree_attention_fp8(const void* q, const void* k_pages, const void* v_pages, const float* k_scale,
+                                const float* v_scale, const int32_t* page_table, const int32_t* prefix_lens,
+                                const int32_t* parents, const int32_t* T_b, int32_t B, int32_t max_T, int32_t Hq,
+                                int32_t Hkv, int32_t d, int32_t page, int32_t max_pages, int32_t num_pages,
+                                float sm_scale, void* out, float* lse, uint32_t* status, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /* spec_tree_attention for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The

@@ -35,13 +35,14 @@ def gather_slots(pages: np.ndarray, page_table_b: np.ndarray, n_slots: int, page
 
 
 def tree_attention(q, k_pages, v_pages, page_table, prefix_lens, parents, T_b, sm_scale,
-                   batch_heads=None):
+                   batch_heads=None, kv_values=None):
     """Reference tree attention.
 
     q: [B, T_max, Hq, d]; k_pages, v_pages: [P, page, Hkv, d] (any float dtype,
     converted exactly to fp64); page_table: [B, max_pages]; prefix_lens, T_b:
     [B]; parents: [B, T_max]. ``batch_heads`` optionally restricts the work to
-    a list of (b, h) pairs (other outputs stay NaN).
+    a list of (b, h) pairs (other outputs stay NaN). ``kv_values(slots, which)`` optionally maps a sequence's
+    gathered K (which = 0) or V (which = 1) slots [n, Hkv, d] to their fp64 values (default: the stored values).
     Returns (out [B, T_max, Hq, d] fp64, lse [B, T_max, Hq] fp64); entries of
     nodes i >= T_b are NaN.
     """
@@ -66,8 +67,9 @@ def tree_attention(q, k_pages, v_pages, page_table, prefix_lens, parents, T_b, s
         L = int(prefix_lens[b])
         T = int(T_b[b])
         anc, _, _ = tree_mask(parents[b], T)
-        K = gather_slots(k_pages, page_table[b], L + T, page).astype(np.float64)
-        Vv = gather_slots(v_pages, page_table[b], L + T, page).astype(np.float64)
+        K = gather_slots(k_pages, page_table[b], L + T, page)
+        Vv = gather_slots(v_pages, page_table[b], L + T, page)
+        K, Vv = (K.astype(np.float64), Vv.astype(np.float64)) if kv_values is None else (kv_values(K, 0), kv_values(Vv, 1))
         # allowed[i, s]: does node i see slot s?
         allowed = np.zeros((T, L + T), dtype=bool)
         allowed[:, :L] = True
@@ -87,3 +89,18 @@ def tree_attention(q, k_pages, v_pages, page_table, prefix_lens, parents, T_b, s
             out[b, :T, h, :] = (e @ Vv[:, g, :]) / z
             lse[b, :T, h] = (m + np.log(z))[:, 0]
     return out, lse
+
+
+def tree_attention_fp8(q, k8_pages, v8_pages, k_scale, v_scale, page_table, prefix_lens, parents, T_b, sm_scale,
+                       batch_heads=None):
+    """The FP8-KV variant: K and V stored as E4M3 codes with one fp32 scale per KV head (value = code value *
+    scale[g]), q quantized per row as oracle.fp8 defines; then the same tree attention as above, in fp64.
+
+    Sources and readings: oracle.fp8 (the pages name FP8 targets but fix no format). q: [B, T_max, Hq, d] float;
+    k8_pages, v8_pages: uint8 [P, page, Hkv, d]; k_scale, v_scale: [Hkv].
+    """
+    from .fp8 import e4m3_decode, quantize_q_rows
+
+    scales = (np.asarray(k_scale, dtype=np.float64)[None, :, None], np.asarray(v_scale, dtype=np.float64)[None, :, None])
+    return tree_attention(quantize_q_rows(q), k8_pages, v8_pages, page_table, prefix_lens, parents, T_b, sm_scale,
+                          batch_heads, kv_values=lambda codes, which: e4m3_decode(codes) * scales[which])

@@ -127,6 +127,18 @@ def test_verify_build_compact_mask_host_validation(lib):
     assert lib.spec_tree_mask(None, None, 1, 9, None, None, None, None) == SPEC_E_INVAL
 
 
+def test_attention_fp8_host_validation(lib):
+    p = ctypes.c_void_p(1 << 20)
+    big = 1 << 40
+    a = lambda **kw: lib.spec_tree_attention_fp8(p, p, p, kw.get("ks", p), p, p, p, p, None, 2, 9, 8, 2, kw.get("d", 128),
+                                                 16, 8, 64, 0.125, p, None, None, kw.get("ws", p), kw.get("wsb", big),
+                                                 None)
+    assert a(d=64) == SPEC_E_UNSUPPORTED
+    assert a(ks=None) == SPEC_E_INVAL
+    assert a(wsb=8) == SPEC_E_WORKSPACE
+    assert a(ws=None) == SPEC_E_WORKSPACE
+
+
 def test_kv_prune_host_validation(lib):
     p = ctypes.c_void_p(1 << 20)
     pr = lambda **kw: lib.spec_kv_prune(p, p, kw.get("T_b", p), p, p, kw.get("B", 2), kw.get("T", 9), kw.get("page", 16),

@@ -175,3 +175,18 @@ def test_kv_prune_rejects():
         ops.spec_kv_prune(**{**good, "prefix_lens": lens[:B], "new_prefix_lens": lens[1:B + 1]})
     with pytest.raises(ValueError, match="must be on the GPU"):
         ops.spec_kv_prune(**{**good, "new_prefix_lens": good["prefix_lens"]})
+
+
+def test_attention_fp8_rejects():
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)
+    good = dict(q=bf16(B, T, Hq, 128), k_pages=u8(P, PG, Hkv, 128), v_pages=u8(P, PG, Hkv, 128), k_scale=f32(Hkv),
+                v_scale=f32(Hkv), page_table=i32(B, MP), prefix_lens=i32(B), parents=i32(B, T), T_b=i32(B),
+                sm_scale=0.125, out=bf16(B, T, Hq, 128), lse=f32(B, T, Hq), status=i32(B), ws=u8(64))
+    for bad, msg in ((dict(k_pages=bf16(P, PG, Hkv, 128)), "k_pages must be torch.uint8"),
+                     (dict(v_pages=u8(P, PG, Hkv, 64)), "v_pages must have shape"),
+                     (dict(k_scale=f32(Hkv + 1)), "k_scale must have shape"),
+                     (dict(v_scale=torch.zeros(Hkv, dtype=torch.float64)), "v_scale must be torch.float32")):
+        with pytest.raises((ValueError, TypeError), match=msg):
+            ops.spec_tree_attention_fp8(**{**good, **bad})
+    with pytest.raises(ValueError, match="must be on the GPU"):  # float8 pages are taken as their codes
+        ops.spec_tree_attention_fp8(**{**good, "k_pages": good["k_pages"].view(torch.float8_e4m3fn)})

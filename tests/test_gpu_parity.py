@@ -10,14 +10,14 @@
 import numpy as np
 import pytest
 
-from gpu_support import check_kv_prune
+from gpu_support import check_fp8_attention, check_kv_prune, run_attention_fp8
 from gpu_support import (ATTN_MAX_ABS, ATTN_REL_L2, LSE_ABS, check_build, check_verify, compare_attention, log,
                          oracle_trees, parents_array, run_pipeline, to_np)
 from oracle.kvcompact import PRUNE_REMAP, PRUNE_TAIL
 from oracle.kvcompact import kv_compact as oracle_kv_compact
 from oracle.tree import build_tree
 from workloads import get_config, make_workload
-from workloads.synth import from_spec, random_parents
+from workloads.synth import fp8_kv_pools, from_spec, random_parents
 
 pytestmark = pytest.mark.gpu
 
@@ -87,6 +87,52 @@ def test_attention_small(case, monkeypatch):
     assert (status == 0).all()
     for b in range(B):  # rows of padding nodes are never written
         assert np.isnan(out[b, T[b]:]).all()
+
+
+FP8_CASES = [
+    # name, B, Hq, Hkv, prefix, T, page, parent kind, chunk override: d = 128
+    ("ragged_g2", 3, 8, 4, [0, 37, 300], [1, 17, 65], 16, "random", None),
+    ("page1", 2, 4, 4, [5, 70], [3, 9], 1, "random", None),
+    ("page64_chain", 2, 8, 2, [200, 129], [33, 5], 64, "chain", None),
+    ("many_splits", 2, 16, 2, [2000, 1], [9, 9], 16, "random", 128),
+    ("star_g8_t65", 1, 64, 8, [513], [65], 16, "star", 256),
+    ("g3_odd_rows", 2, 6, 2, [77, 1030], [11, 23], 32, "random", 384),
+    ("chunk_edges", 3, 8, 8, [128, 256, 129], [2, 3, 4], 16, "random", 130),
+    ("many_items_b8", 8, 8, 2, [50, 700, 1300, 0, 333, 1024, 5, 3000], [9, 3, 17, 1, 9, 5, 2, 33], 16, "random", 160),
+    ("g16_t65_8wave", 1, 32, 2, [300], [65], 16, "random", None),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_attention_fp8_matches_oracle(case, monkeypatch):
+    """FP8-KV variant against the oracle (exact E4M3 decoding, the same q quantization) on every (sequence, head)
+    pair, within the bound that E4M3 softmax weights imply, element by element; rows of padding nodes stay
+    unwritten; status clean."""
+    name, B, Hq, Hkv, prefix, T, page, kind, chunk = case
+    if chunk:
+        monkeypatch.setenv("SPEC_TREE_ATTN_CHUNK", str(chunk))
+    w, parents = _attn_case(B, Hq, Hkv, 128, prefix, T, page, kind, seed=len(name) + 40)
+    k8, v8, ks, vs = fp8_kv_pools(w.k_pages.shape, seed=len(name))
+    log(f"[fp8] {name}")
+    out, lse, status = run_attention_fp8(w, parents, k8, v8, ks, vs)
+    worst, rel = check_fp8_attention(w, k8, v8, ks, vs, parents, out, lse, [(b, h) for b in range(B) for h in range(Hq)])
+    log(f"[fp8] {name}: worst error / bound {worst:.3f}, rel L2 {rel:.3e}")
+    assert (status == 0).all()
+    for b in range(B):
+        assert np.isnan(out[b, T[b]:]).all()
+
+
+def test_attention_fp8_status_and_invalid_parents():
+    """Invalid parents hang off the root (bit 1) and an entry outside the pool drops its keys (bit 32), as in the
+    bf16 kernel; the oracle sees the corrected parents and the pool without that page's keys."""
+    w, parents = _attn_case(2, 8, 2, 128, [40, 90], [9, 17], 16, "random", seed=91)
+    parents[0, 5] = 7  # not below its node
+    k8, v8, ks, vs = fp8_kv_pools(w.k_pages.shape, seed=91)
+    out, lse, status = run_attention_fp8(w, parents, k8, v8, ks, vs)
+    assert int(status[0]) & 1 and int(status[1]) == 0
+    fixed = parents.copy()
+    fixed[0, 5] = 0
+    check_fp8_attention(w, k8, v8, ks, vs, fixed, out, lse, [(b, h) for b in range(2) for h in range(8)])
 
 
 def test_attention_large_values_through_split_partials(monkeypatch):

@@ -193,3 +193,23 @@ def test_full_kv_prune(cfg):
         via_remap = i32(remap[0][b]).long()[s]
         assert torch.equal(rows(kc)[via_tail], rows(k0)[via_remap]), f"K of sequence {b}"
         assert torch.equal(rows(vc)[via_tail], rows(v0)[via_remap]), f"V of sequence {b}"
+
+
+@pytest.mark.parametrize("cfg", [3, 4], ids=lambda i: get_config(i).name)
+def test_full_attention_fp8(cfg):
+    """FP8-KV variant at full size with the oracle's trees: the 64-node tree on all 64 heads, the mixed batch on
+    every sequence (four heads each, one per KV-head pair), within the E4M3-weight bound element by element."""
+    from gpu_support import check_fp8_attention, run_attention_fp8
+    from workloads.synth import fp8_kv_pools
+
+    w = from_spec(get_config(cfg))
+    parents = parents_array(w, oracle_trees(w))
+    log(f"[fp8] {w.name}: drawing E4M3 pools")
+    k8, v8, ks, vs = fp8_kv_pools(w.k_pages.shape, seed=cfg)
+    out, lse, status = run_attention_fp8(w, parents, k8, v8, ks, vs)
+    assert (status == 0).all()
+    G = w.Hq // w.Hkv
+    pairs = [(0, h) for h in range(w.Hq)] if w.B == 1 else [(b, (2 * G * k + b) % w.Hq) for b in range(w.B) for k in range(4)]
+    log(f"[fp8] {w.name}: oracle on {len(pairs)} sequence x head pairs")
+    worst, rel = check_fp8_attention(w, k8, v8, ks, vs, parents, out, lse, pairs)
+    log(f"[fp8] {w.name}: worst error / bound {worst:.3f}, rel L2 {rel:.3e}")

@@ -32,6 +32,8 @@ SIGNATURES = {
     "spec_tree_attention_workspace_size": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "spec_tree_attention": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                                     c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "spec_tree_attention_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
+                                        c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "spec_tree_attention_noalloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                             c_i32, c_i32, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp]),
     "spec_tree_verify_workspace_size": (c_sz, [c_i32, c_i32, c_i32]),

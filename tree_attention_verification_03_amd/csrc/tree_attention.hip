@@ -70,6 +70,8 @@ struct AttnParams {
   uint32_t* status;
   float* part;
   const uint16_t* zeros;  // a zero-filled (token, head) row in the workspace: source of masked loads
+  const float* k_scale;   // FP8-KV variant: per-KV-head scales of the E4M3 codes (else unused)
+  const float* v_scale;
   int max_T, Hq, Hkv, G;
   int page_shift, max_pages, num_pages;
   int chunk, n_splits, n_rb, tpb, npg;
@@ -603,6 +605,387 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
   }
 }
 
+// ---------------------------------------------------------------- FP8-KV variant (d = 128)
+// K and V pages hold OCP E4M3 codes with one fp32 scale per KV head; q is quantized per row to E4M3 with a power of
+// two scale 2^e (the smallest e with max|q| <= 448 * 2^e), and both products run on the gfx950 E4M3 MFMA
+// 16x16x128, which takes the whole head dim of 16 keys in one instruction:
+//   S^T = K8 Q8^T   A = 16 keys x 128 bytes (lane: key l % 16, bytes 32 (l / 16) .. +31), B the same bytes of
+//                   the lane's query row; any byte order shared by A and B gives the same dot products;
+//   P^T             the 32 scores a lane holds per 128-key step (keys 16 u + 4 (l / 16) + i of its row) become
+//                   E4M3 in place: the reference max lags the row max by at most 2^kTau = 256 < 448, so no
+//                   scaling; the row sums come from an MFMA against all-ones codes, so l sums the rounded p;
+//   O^T += V^T P^T  A = V^T: lane l needs column 16 dt + l % 16 of the same 32 keys, gathered by four
+//                   transposing 8-byte LDS reads (in each 16-lane group, lane l receives byte l % 8 of the
+//                   rows named by lanes (l / 8) % 2 + 2 m, m = 0..7).
+// Scores carry the row's scale 2^e * k_scale[g] into the exponent; O is scaled by v_scale[g] at the end.
+constexpr int kTile8 = 64;  // keys per ring stage (64 x 128 B of K, then of V)
+
+// 16-byte chunk swizzles of one 128-byte row (8 chunks), per key:
+//   K: c ^ ((key >> 1) & 7): the 16 keys of one A-operand read at one chunk hit 16 distinct 16-byte bank groups;
+//   V: c ^ (((key >> 1) & 3) | ((key >> 4) & 1) << 2): the 16 keys each half-wave reads in one transposing read
+//      ({0..7, 16..23} or {8..15, 24..31} + 32 t) hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int k8_swz(int key) { return (key >> 1) & 7; }
+__device__ __forceinline__ int v8_swz(int key) { return ((key >> 1) & 3) | (((key >> 4) & 1) << 2); }
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+__device__ __forceinline__ f32x4 mfma_e4m3(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);  // E4M3 x E4M3, no block scale
+}
+
+// four fp32 -> four E4M3 codes in one dword (round to nearest even)
+__device__ __forceinline__ int pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+template <int NW, int NS>
+__global__ void __launch_bounds__(64 * NW, NW / 4 * 2) tree_attn_fp8_kernel(AttnParams p) {
+  constexpr int D = 128, DT = 8, ROWB = 128, CPR = 8;
+  constexpr int TILE_B = kTile8 * ROWB;  // 8 KB of K (or V) per ring stage
+  constexpr int STAGE_B = 2 * TILE_B;
+  constexpr int NLD = TILE_B / 1024;     // 8 direct loads of 1 KB (8 rows) per stage and buffer
+  constexpr int PW = 2 * NLD / NW;       // per wave and stage
+  constexpr int PH = PW / 2;
+  constexpr int NT = 64 * NW;
+  constexpr int SPS = 2;                 // stages per softmax step: 128 keys, one MFMA k-block of P V
+  static_assert(PW >= 2 && PW * NW == 2 * NLD, "each wave loads whole K/V row groups");
+  static_assert(NS == 2 * SPS, "two steps in the ring");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE_B];
+  __shared__ uint64_t anc_s[65];
+  extern __shared__ int pg_s[];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int s, rb, bg;
+  if constexpr (NW == 8) {  // XCD-aware 1-D grid: a group's row blocks share one XCD's L2 (as the bf16 kernel)
+    const int xcd = blockIdx.x & (kXcds - 1), slot = blockIdx.x / kXcds;
+    const int grp = (slot / p.n_rb) * kXcds + xcd;
+    if (grp >= p.n_groups) return;
+    rb = slot - (slot / p.n_rb) * p.n_rb;
+    bg = grp / p.n_splits;
+    s = grp - bg * p.n_splits;
+  } else {
+    s = blockIdx.x;
+    rb = blockIdx.y;
+    bg = blockIdx.z;
+  }
+  const int b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int32_t* ptab = p.page_table + size_t(b) * p.max_pages;
+  const int t0 = rb * p.tpb;
+  const int l15 = lane & 15, lg = lane >> 4, g4 = 4 * lg;
+
+  const int T_raw = p.T_b ? p.T_b[b] : p.max_T;
+  const int L_raw = p.prefix_lens[b];
+  const int pg0 = (s * p.chunk) >> p.page_shift;
+  for (int i = tid; i < p.npg; i += NT) {
+    const int pi = pg0 + i;
+    pg_s[i] = pi < p.max_pages ? ptab[pi] : -1;
+  }
+  int par_raw = 0;
+  if (tid < kWave && tid + 1 < p.max_T) par_raw = p.parents[size_t(b) * p.max_T + tid + 1];
+  const float ksc = p.k_scale[g], vsc = p.v_scale[g];
+  // this wave's row tile: lane = row l % 16, head-dim elements 32 lg .. 32 lg + 31, quantized to E4M3 with the
+  // row's exponent (the row's four lanes agree on max|q|)
+  const int r_own = 16 * (t0 + wave) + l15;
+  i32x8 q8;
+  float row_scale;
+  {
+    const bool ok = wave < p.tpb && r_own < p.G * p.max_T;
+    const int rr = ok ? r_own : 0;
+    const int i = rr / p.G, h = g * p.G + (rr - i * p.G);
+    const uint16_t* src = p.q + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 32 * lg;
+    float x[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 u = reinterpret_cast<const uint4*>(src)[c];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * c + 2 * k] = ok ? __uint_as_float(w[k] << 16) : 0.f;
+        x[8 * c + 2 * k + 1] = ok ? __uint_as_float(w[k] & 0xffff0000u) : 0.f;
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(x[k]));
+    amax = lanegroup_max(amax);
+    // smallest e with amax <= 448 * 2^e: amax = f 2^x with f in [1/2, 1) and 448 = 0.875 * 2^9
+    int ex = 0;
+    const float f = frexpf(amax, &ex);
+    const int e = amax == 0.f ? 0 : (f <= 0.875f ? ex - 9 : ex - 8);
+    row_scale = ldexpf(1.f, e);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      q8[k] = pack4_e4m3(ldexpf(x[4 * k], -e), ldexpf(x[4 * k + 1], -e), ldexpf(x[4 * k + 2], -e), ldexpf(x[4 * k + 3], -e));
+  }
+  __syncthreads();
+
+  int T = min(max(T_raw, 1), p.max_T);
+  int L = L_raw;
+  const int cap = p.max_pages << p.page_shift;
+  if (L < 0 || L > cap - T) {
+    if (p.status && s == 0 && rb == 0 && g == 0 && tid == 0) atomicOr(p.status + b, SPEC_STATUS_INVALID_LENGTH);
+    L = min(max(L, 0), cap - T);
+  }
+  const int M = p.G * T;
+  const int ntM = (M + 15) >> 4;
+  if (t0 >= ntM) return;
+  const int n_items = (L + T + p.chunk - 1) / p.chunk;
+  if (s >= n_items) return;
+  const int key_lo = s * p.chunk;
+  const int key_hi = min(L + T, key_lo + p.chunk);
+  const bool has_tree = key_hi > L;
+
+  bool bad = false;
+  {
+    const int npg_used = ((key_hi - 1) >> p.page_shift) - pg0 + 1;
+    for (int i = tid; i < npg_used; i += NT) bad |= unsigned(pg_s[i]) >= unsigned(p.num_pages);
+  }
+  if (has_tree && tid < kWave) {  // ancestry words by pointer doubling over lanes (node n in lane n - 1)
+    const int n = tid + 1;
+    const bool real = n < T;
+    int par = 0;
+    if (real) {
+      par = par_raw;
+      if (par < 0 || par >= n) {
+        par = 0;
+        if (p.status && rb == 0 && g == 0) atomicOr(p.status + b, SPEC_STATUS_INVALID_PARENT);
+      }
+    }
+    uint64_t a = real ? (1ull << tid) : 0ull;
+    int jump = par;
+    while (__ballot(jump != 0)) {
+      const int src = jump > 0 ? jump - 1 : tid;
+      const uint64_t pa = (uint64_t(uint32_t(__shfl(int(a >> 32), src))) << 32) | uint32_t(__shfl(int(a), src));
+      const int pj = __shfl(jump, src);
+      if (jump != 0) {
+        a |= pa;
+        jump = pj;
+      }
+    }
+    if (real) anc_s[n] = a;
+    if (tid == 0) anc_s[0] = 0;
+  }
+  const bool pages_ok = !__syncthreads_or(bad);
+  if (!pages_ok && p.status && tid == 0) atomicOr(p.status + b, SPEC_STATUS_INVALID_PAGE);
+  // the row's ancestry word stays in LDS (read in masked steps only); rows past the tree see the prefix and root
+  const int anc_idx = (has_tree && r_own < M) ? r_own / p.G : 0;
+  const bool active = wave < p.tpb && t0 + wave < ntM;
+  const float c_row = p.scale_log2 * row_scale * ksc;  // log2-domain factor of this lane's raw scores
+
+  float m_run = -INFINITY;
+  f32x4 acc[DT], lacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const i32x8 ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+
+  const int pmask = (1 << p.page_shift) - 1;
+  const size_t tok_stride = size_t(p.Hkv) * D;  // bytes between consecutive slots of a page
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + size_t(g) * D;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + size_t(g) * D;
+  const uint8_t* zeros = reinterpret_cast<const uint8_t*>(p.zeros);
+  const size_t page_bytes = tok_stride << p.page_shift;
+  int lkey[PH], koff[PH], voff[PH];
+#pragma unroll
+  for (int i = 0; i < PH; ++i) {
+    lkey[i] = (wave + NW * i) * 8 + lane / CPR;
+    const int pos = lane % CPR;
+    koff[i] = 16 * (pos ^ k8_swz(lkey[i]));
+    voff[i] = 16 * (pos ^ v8_swz(lkey[i]));
+  }
+  auto issue = [&](int tile, int slot) {
+    const int st = key_lo + tile * kTile8;
+    unsigned char* sb = ring + slot * STAGE_B;
+    const bool full = pages_ok && st + kTile8 <= key_hi;
+#pragma unroll
+    for (int i = 0; i < PH; ++i) {
+      const int slot_k = st + lkey[i];
+      const uint8_t *ks, *vs;
+      if (full) {
+        const int phys = pg_s[(slot_k >> p.page_shift) - pg0];
+        const size_t off = size_t(uint32_t(phys)) * page_bytes + size_t((slot_k & pmask) * tok_stride);
+        ks = kbase + off + koff[i];
+        vs = vbase + off + voff[i];
+      } else {
+        const bool in = slot_k < key_hi;
+        const int phys = pg_s[in ? (slot_k >> p.page_shift) - pg0 : 0];
+        const bool ok = in && unsigned(phys) < unsigned(p.num_pages);
+        const size_t off = size_t(uint32_t(phys)) * page_bytes + size_t((slot_k & pmask) * tok_stride);
+        ks = ok ? kbase + off + koff[i] : zeros + koff[i];
+        vs = ok ? vbase + off + voff[i] : zeros + voff[i];
+      }
+      const int sub = wave + NW * i;
+      load_to_lds16(ks, sb + sub * 1024);
+      load_to_lds16(vs, sb + TILE_B + sub * 1024);
+    }
+  };
+
+  // one 128-key step (ring stages slot, slot + 1)
+  auto compute = [&](int tile, int slot, bool masked) {
+    const int st = key_lo + tile * kTile8;
+    auto key_of = [&](int e) { return st + 16 * (e >> 2) + g4 + (e & 3); };  // lane score e <-> key
+    f32x4 sc[8];
+    auto read_k = [&](int u) {  // A operand of key tile u (16 keys): key l15, chunks 2 lg and 2 lg + 1
+      const int key = 16 * (u & 3) + l15;
+      const unsigned char* kr = ring + ((slot + (u >> 2)) % NS) * STAGE_B + key * ROWB;
+      const uint4 a = *reinterpret_cast<const uint4*>(kr + 16 * ((2 * lg) ^ k8_swz(key)));
+      const uint4 c = *reinterpret_cast<const uint4*>(kr + 16 * ((2 * lg + 1) ^ k8_swz(key)));
+      return i32x8{int(a.x), int(a.y), int(a.z), int(a.w), int(c.x), int(c.y), int(c.z), int(c.w)};
+    };
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sc[u] = mfma_e4m3(read_k(u), q8, f32x4{0.f, 0.f, 0.f, 0.f});
+      if (u % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // at most two K fragments (16 registers) in flight
+    }
+    uint32_t vis = 0xffffffffu;
+    if (masked) {  // uniform: the chunk's end, tree slots outside the row's ancestry
+      // the lane's keys come in 8 groups of 4 consecutive keys (u): tree nodes j0 .. j0 + 3 with j0 = base + 16 u;
+      // node <= 0 (prefix, root) is visible, node j >= 1 iff bit j - 1 of the row's ancestry word
+      vis = 0;
+      const uint64_t ranc = anc_s[anc_idx];
+      const int base = st + g4 - L;
+      const int lim = key_hi - st - g4;  // keys 16 u + i < lim lie in the chunk
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j0 = base + 16 * u;
+        uint32_t a4;
+        if (j0 >= 1)
+          a4 = j0 <= 64 ? uint32_t(ranc >> (j0 - 1)) & 0xFu : 0u;
+        else if (j0 <= -3)
+          a4 = 0xFu;
+        else
+          a4 = ((1u << (1 - j0)) - 1u) | ((uint32_t(ranc) << (1 - j0)) & 0xFu);
+        const int cnt = min(max(lim - 16 * u, 0), 4);
+        vis |= (a4 & ((1u << cnt) - 1u)) << (4 * u);
+      }
+      if (!pages_ok) {  // uniform and rare: keys on pages outside the pool, one lookup at a time
+#pragma unroll 1
+        for (int e = 0; e < 32; ++e) {
+          const int key = key_of(e);
+          if (key < key_hi && unsigned(pg_s[(key >> p.page_shift) - pg0]) >= unsigned(p.num_pages)) vis &= ~(1u << e);
+        }
+      }
+    }
+    if (masked) {  // scores of invisible keys -> -inf, in place
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        float x = ((vis >> e) & 1u) ? sc[e >> 2][e & 3] : -INFINITY;
+        asm volatile("" : "+v"(x));
+        sc[e >> 2][e & 3] = x;
+      }
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) mx = fmaxf(mx, sc[e >> 2][e & 3]);
+    mx = lanegroup_max(mx);
+    const float mxs = mx * c_row;
+    const bool move = mxs > m_run + kTau;
+    if (__any(move)) {
+      const float mnew = move ? mxs : m_run;
+      const float alpha = move ? fast_exp2(m_run - mnew) : 1.f;
+      lacc *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+      m_run = mnew;
+    }
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+    i32x8 pop;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float pe[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pe[j] = fast_exp2(__builtin_fmaf(sc[k][j], c_row, -mref));
+      pop[k] = pack4_e4m3(pe[0], pe[1], pe[2], pe[3]);
+    }
+    lacc = mfma_e4m3(ones8, pop, lacc);
+    // the V reads stay behind the softmax (hoisted above it they would hold 64 registers across it)
+    __builtin_amdgcn_sched_barrier(0);
+    // V^T operand, column 16 dt + l15: read t covers keys 32 t' + 16 (m >> 2) + g4 + (m & 3) of stage slot + t / 2
+    // (t' = t % 2); lane r of each 16-lane group names key (r >> 1) at column half r & 1
+    const int mr = l15 >> 1, half = l15 & 1;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      i32x8 vop;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int key = 32 * (t & 1) + 16 * (mr >> 2) + g4 + (mr & 3);
+        const unsigned char* vb = ring + ((slot + (t >> 1)) % NS) * STAGE_B + TILE_B + key * ROWB;
+        const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vb + 16 * (dt ^ v8_swz(key)) + 8 * half));
+        vop[2 * t] = w[0];
+        vop[2 * t + 1] = w[1];
+      }
+      acc[dt] = mfma_e4m3(vop, pop, acc[dt]);
+      if (dt % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // at most two columns' V operands in flight
+    }
+  };
+
+  const int ntile = (key_hi - key_lo + kTile8 - 1) / kTile8;
+#pragma unroll
+  for (int i = 0; i < NS - SPS; ++i) issue(i, i);
+#pragma unroll 1
+  for (int t = 0; t < ntile; t += SPS) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(PW * (NS - 2 * SPS)) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < SPS; ++j) {
+      const int nt = t + NS - SPS + j;
+      issue(nt, nt % NS);
+    }
+    if (active) {
+      const int st = key_lo + t * kTile8;
+      compute(t, t % NS, !pages_ok || st + SPS * kTile8 > min(key_hi, L));
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  const float l_run = lacc[0];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] *= vsc;
+  constexpr float kLn2 = 0.69314718055994530942f;
+  if (!active || r_own >= M) return;
+  const int i_node = r_own / p.G, h = g * p.G + (r_own - i_node * p.G);
+  if (n_items == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* dst = p.out + ((size_t(b) * p.max_T + i_node) * p.Hq + h) * D + g4;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 v = acc[dt] * inv;
+      *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
+    }
+    if (p.lse && lane < 16)
+      p.lse[(size_t(b) * p.max_T + i_node) * p.Hq + h] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+    return;
+  }
+  // partial of this item, in the layout the combine kernel reads (o fp16 = O / (l sc), m, l, sc)
+  const int TR = p.tpb * 16;
+  const size_t ITEM = size_t(TR) * (D / 2 + 3);
+  float* const mine = p.part + ((size_t(bg) * p.n_rb + rb) * size_t(p.n_splits) + s) * ITEM;
+  const int row = wave * 16 + l15;
+  uint16_t* o = reinterpret_cast<uint16_t*>(mine) + size_t(row) * D + g4;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  float amax = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fabsf(acc[dt][k]));
+  amax = lanegroup_max(amax) * inv;
+  int ex = 0;
+  (void)frexpf(amax, &ex);
+  const float sc = ex > 14 ? ldexpf(1.f, ex - 14) : 1.f;
+  const float mul = inv * (1.f / sc);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<uint2*>(o + 16 * dt) = pack4_f16(acc[dt] * mul);
+  if (lane < 16) {
+    mine[size_t(TR) * (D / 2) + row] = m_run;
+    mine[size_t(TR) * (D / 2 + 1) + row] = l_run;
+    mine[size_t(TR) * (D / 2 + 2) + row] = sc;
+  }
+}
+
 // Split-K combine (runs after the main kernel): one wave per block, D / 4 threads per row (4 columns
 // each), so a block holds 64 / (D / 4) rows and the grid spreads the partials over many CUs. Rows that
 // no tree of the batch can have (r >= G * max_T) exit before any load. The first CB items' partials
@@ -695,7 +1078,8 @@ struct AttnPlan {
   size_t zero_bytes, part_bytes, lds_dyn;
 };
 
-AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_pages) {
+// fp8: the FP8-KV kernel's shape (one row tile per wave, 4-stage ring; only the wave count is chosen here)
+AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_pages, bool fp8 = false) {
   AttnPlan pl;
   pl.G = Hq / Hkv;
   pl.tiles = (pl.G * max_T + 15) / 16;
@@ -711,6 +1095,7 @@ AttnPlan make_plan(int B, int max_T, int Hq, int Hkv, int d, int page, int max_p
     if (n >= 3 && (single || pair)) pl.sh = AttnShape{nw, rw, ns, sps};
   }
   if (d == 64) pl.sh.NW = 4;
+  if (fp8) pl.sh = AttnShape{pl.sh.NW, 1, 4, 2};
   const int cap = pl.sh.NW * pl.sh.RW;
   pl.n_rb = (pl.tiles + cap - 1) / cap;
   pl.tpb = (pl.tiles + pl.n_rb - 1) / pl.n_rb;  // row tiles spread evenly over the row blocks
@@ -821,7 +1206,7 @@ extern "C" size_t spec_tree_attention_workspace_size(int32_t B, int32_t max_T, i
 static int32_t attention_validate(const char* who, const void* q, const void* k_pages, const void* v_pages,
                                   const int32_t* page_table, const int32_t* prefix_lens, const int32_t* parents, int32_t B,
                                   int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d, int32_t page, int32_t max_pages,
-                                  int32_t num_pages, float sm_scale, void* out, AttnPlan* pl) {
+                                  int32_t num_pages, float sm_scale, void* out, AttnPlan* pl, bool fp8 = false) {
   int32_t rc = check_shapes(B, max_T, Hq, Hkv, d, page, max_pages);
   if (rc != SPEC_OK) return rc;
   if (!q || !k_pages || !v_pages || !page_table || !prefix_lens || !parents || !out)
@@ -830,7 +1215,7 @@ static int32_t attention_validate(const char* who, const void* q, const void* k_
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SPEC_E_INVAL, "%s: sm_scale must be finite and > 0", who);
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages)) & 15)
     return fail(SPEC_E_INVAL, "%s: q, k_pages and v_pages must be 16-byte aligned", who);
-  *pl = make_plan(B, max_T, Hq, Hkv, d, page, max_pages);
+  *pl = make_plan(B, max_T, Hq, Hkv, d, page, max_pages, fp8);
   return SPEC_OK;
 }
 
@@ -838,7 +1223,8 @@ static int32_t attention_launch(const AttnPlan& pl, const void* q, const void* k
                                 const int32_t* page_table, const int32_t* prefix_lens, const int32_t* parents,
                                 const int32_t* T_b, int32_t B, int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d,
                                 int32_t page, int32_t max_pages, int32_t num_pages, float sm_scale, void* out, float* lse,
-                                uint32_t* status, void* ws, hipStream_t st);
+                                uint32_t* status, void* ws, hipStream_t st, const float* k_scale = nullptr,
+                                const float* v_scale = nullptr);
 
 extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const void* v_pages, const int32_t* page_table,
                                        const int32_t* prefix_lens, const int32_t* parents, const int32_t* T_b, int32_t B,
@@ -856,12 +1242,37 @@ extern "C" int32_t spec_tree_attention(const void* q, const void* k_pages, const
                           max_pages, num_pages, sm_scale, out, lse, status, ws, static_cast<hipStream_t>(stream));
 }
 
+// k_scale / v_scale non-null: the FP8-KV kernel (E4M3 pages, d = 128)
+extern "C" int32_t spec_tree_attention_fp8(const void* q, const void* k_pages, const void* v_pages,
+                                           const float* k_scale, const float* v_scale, const int32_t* page_table,
+                                           const int32_t* prefix_lens, const int32_t* parents, const int32_t* T_b,
+                                           int32_t B, int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d, int32_t page,
+                                           int32_t max_pages, int32_t num_pages, float sm_scale, void* out, float* lse,
+                                           uint32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  if (d != 128) return fail(SPEC_E_UNSUPPORTED, "spec_tree_attention_fp8: head dim %d (only 128)", d);
+  AttnPlan pl;
+  const int32_t rc = attention_validate("spec_tree_attention_fp8", q, k_pages, v_pages, page_table, prefix_lens, parents,
+                                        B, max_T, Hq, Hkv, d, page, max_pages, num_pages, sm_scale, out, &pl, true);
+  if (rc != SPEC_OK) return rc;
+  if (!k_scale || !v_scale) return fail(SPEC_E_INVAL, "spec_tree_attention_fp8: null scale pointer");
+  const size_t need = pl.zero_bytes + pl.part_bytes;
+  if (!ws || ws_bytes < need)
+    return fail(SPEC_E_WORKSPACE, "spec_tree_attention_fp8: workspace %zu bytes < %zu", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(SPEC_E_INVAL, "spec_tree_attention_fp8: ws must be 16-byte aligned");
+  return attention_launch(pl, q, k_pages, v_pages, page_table, prefix_lens, parents, T_b, B, max_T, Hq, Hkv, d, page,
+                          max_pages, num_pages, sm_scale, out, lse, status, ws, static_cast<hipStream_t>(stream), k_scale,
+                          v_scale);
+}
+
 static int32_t attention_launch(const AttnPlan& pl, const void* q, const void* k_pages, const void* v_pages,
                                 const int32_t* page_table, const int32_t* prefix_lens, const int32_t* parents,
                                 const int32_t* T_b, int32_t B, int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d,
                                 int32_t page, int32_t max_pages, int32_t num_pages, float sm_scale, void* out, float* lse,
-                                uint32_t* status, void* ws, hipStream_t st) {
+                                uint32_t* status, void* ws, hipStream_t st, const float* k_scale, const float* v_scale) {
+  const bool fp8 = k_scale != nullptr;
   AttnParams prm;
+  prm.k_scale = k_scale;
+  prm.v_scale = v_scale;
   prm.q = static_cast<const uint16_t*>(q);
   prm.k = static_cast<const uint16_t*>(k_pages);
   prm.v = static_cast<const uint16_t*>(v_pages);
@@ -904,7 +1315,12 @@ static int32_t attention_launch(const AttnPlan& pl, const void* q, const void* k
         hipLaunchKernelGGL((tree_attn_combine<64, false>), cgrid, dim3(64), 0, st, prm);
     }
   } else {
-    launch_d<128>(pl, prm, grid, st);
+    if (!fp8)
+      launch_d<128>(pl, prm, grid, st);
+    else if (pl.sh.NW == 8)
+      hipLaunchKernelGGL((tree_attn_fp8_kernel<8, 4>), grid, dim3(512), pl.lds_dyn, st, prm);
+    else
+      hipLaunchKernelGGL((tree_attn_fp8_kernel<4, 4>), grid, dim3(256), pl.lds_dyn, st, prm);
     const dim3 cgrid(unsigned((rows_used + 1) / 2), unsigned(pl.n_rb * B * Hkv));
     if (pl.n_splits > 1) {
       if (known)

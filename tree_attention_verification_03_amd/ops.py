@@ -243,6 +243,36 @@ def spec_tree_attention(q, k_pages, v_pages, page_table, prefix_lens, parents, T
     return ws
 
 
+def spec_tree_attention_fp8(q, k_pages, v_pages, k_scale, v_scale, page_table, prefix_lens, parents, T_b, sm_scale,
+                            out, lse=None, status=None, ws=None):
+    """FP8-KV variant (d = 128): k/v_pages uint8 (or float8_e4m3fn) [P, page, Hkv, 128] E4M3 codes, k_scale /
+    v_scale fp32 [Hkv]; q bf16 [B, max_T, Hq, 128]; other arguments as spec_tree_attention."""
+    for name, t, nd in (("q", q, 4), ("k_pages", k_pages, 4), ("page_table", page_table, 2)):
+        if not isinstance(t, torch.Tensor) or t.dim() != nd:
+            raise ValueError(f"{name} must be a {nd}-D tensor")
+    k_pages, v_pages = (t.view(torch.uint8) if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn else t
+                        for t in (k_pages, v_pages))
+    B, max_T, Hq, d = q.shape
+    P, page, Hkv = k_pages.shape[:3]
+    max_pages = page_table.shape[1]
+    _check(_spec("q", q, torch.bfloat16), _spec("k_pages", k_pages, torch.uint8, (P, page, Hkv, d)),
+           _spec("v_pages", v_pages, torch.uint8, (P, page, Hkv, d)), _spec("k_scale", k_scale, torch.float32, (Hkv,)),
+           _spec("v_scale", v_scale, torch.float32, (Hkv,)),
+           _spec("page_table", page_table, torch.int32, (B, max_pages)),
+           _spec("prefix_lens", prefix_lens, torch.int32, (B,)), _spec("parents", parents, torch.int32, (B, max_T)),
+           *_opt("T_b", T_b, torch.int32, (B,)), _spec("out", out, torch.bfloat16, (B, max_T, Hq, d)),
+           *_opt("lse", lse, torch.float32, (B, max_T, Hq)), *_opt("status", status, torch.int32, (B,)),
+           *_opt("ws", ws, torch.uint8, (None,)))
+    if ws is None:
+        ws = zeroed_workspace(spec_tree_attention_workspace_size(B, max_T, Hq, Hkv, d, page, max_pages), q.device)
+    rc = load().spec_tree_attention_fp8(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(k_scale), _ptr(v_scale),
+                                        _ptr(page_table), _ptr(prefix_lens), _ptr(parents), _ptr(T_b), B, max_T, Hq,
+                                        Hkv, d, page, max_pages, P, float(sm_scale), _ptr(out), _ptr(lse),
+                                        _ptr(status), _ptr(ws), ws.numel(), _stream(q))
+    check(rc, "spec_tree_attention_fp8")
+    return ws
+
+
 def spec_tree_attention_noalloc(q, k_pages, v_pages, page_table, prefix_lens, parents, T_b, sm_scale, out, lse=None,
                                 status=None):
     """spec_tree_attention with its split-K workspace in the library's own device scratch (64 MiB per GPU): no

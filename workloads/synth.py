@@ -25,6 +25,10 @@ does not shift the others):
   (a frequency ranking has no relation to token ids); the draft rows hold V_d
   entries (logits ~ N(0, 2) over the subset) and the draft probabilities are
   scattered to the full vocabulary (zero outside the subset).
+* FP8 KV pools (``fp8_kv_pools``): per KV head a scale 2^U(-7, -5); values
+  ~ N(0, 1) / scale in fp32, clipped to +-448 and converted to OCP E4M3 codes
+  by torch's float8_e4m3fn cast (input data only: the attention consumes the
+  codes as they are).
 
 Nothing here builds trees, masks, attends or verifies.
 """
@@ -295,3 +299,27 @@ def random_parents(rng: np.random.Generator, T: int, kind: str = "random") -> np
         else:
             p[i] = rng.integers(0, i)
     return p
+
+
+def fp8_kv_pools(shape, seed: int, chunk: int = 1 << 22):
+    """E4M3 code pools of ``shape`` = [P, page, Hkv, d] for K and V, and fp32 per-KV-head scales.
+
+    Returns (k8, v8, k_scale, v_scale): uint8 arrays and float32 [Hkv] arrays.
+    """
+    import torch
+
+    rng = np.random.default_rng([seed, 0xF8])
+    Hkv = shape[2]
+    scales = [(2.0 ** rng.uniform(-7, -5, size=Hkv)).astype(np.float32) for _ in range(2)]
+    pools = []
+    for sc in scales:
+        inv = (1.0 / sc.astype(np.float64)).astype(np.float32)
+        out = np.empty(shape, dtype=np.uint8)
+        flat = out.reshape(-1, Hkv, shape[3])
+        for lo in range(0, flat.shape[0], max(1, chunk // (Hkv * shape[3]))):
+            hi = min(flat.shape[0], lo + max(1, chunk // (Hkv * shape[3])))
+            x = rng.standard_normal((hi - lo, Hkv, shape[3]), dtype=np.float32) * inv[None, :, None]
+            np.clip(x, -448.0, 448.0, out=x)
+            flat[lo:hi] = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        pools.append(out)
+    return pools[0], pools[1], scales[0], scales[1]
