@@ -193,6 +193,13 @@ namespace spectree {
 // another XCD. The writer waits for its stores to complete (vmcnt) before it
 // takes a ticket; the block that draws the last ticket reads after it.
 // This avoids agent-scope fences, whose L2 writeback serialises the blocks.
+// The ordering is the hardware's, not the C++/HIP model's (which leaves
+// relaxed accesses unordered): in gfx950 code (the LLVM AMDGPU memory model
+// for GFX942/GFX950) a relaxed agent-scope store or load is a global store or
+// load with the sc1 bit, served at the device coherence point, and
+// s_waitcnt vmcnt(0) returns once the wave's stores are complete there; the
+// reader's loads issue only after its ticket's value has returned.
+// tests/test_handoff_codegen.py checks the built code for these forms.
 template <typename T>
 __device__ __forceinline__ void st_agent(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
