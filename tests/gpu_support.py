@@ -206,3 +206,34 @@ def run_attention_fp8(w, parents, k8, v8, ks, vs, T_b=True):
                                 i32(w.T_b) if T_b else None, w.sm_scale, out, lse, status)
     torch.cuda.synchronize()
     return to_np(out), to_np(lse), to_np(status)
+
+
+def plant_path(rng, w, trees, target, draft):
+    """Make a random root->leaf path likely to be accepted (inputs only)."""
+    for b, t in enumerate(trees):
+        sampling = int(w.modes[b]) == 1
+        u = 0
+        while True:
+            kids = [i for i in range(1, len(t.tokens)) if t.parents[i] == u]
+            if not kids or rng.random() < 0.15:
+                break
+            c = kids[int(rng.integers(len(kids)))]
+            if sampling:
+                if t.q_row[u] >= 0:
+                    draft[b, t.q_row[u]] = target[b, u]  # q == p: accepted with probability 1
+            else:
+                target[b, u, t.tokens[c]] = target[b, u].max() + 1.0
+            u = c
+
+
+def oracle_accepts(w, trees, target=None):
+    """The oracle's accepted paths: (accept_nodes [B, max_T] padded with -1, accept_len [B])."""
+    target = w.target if target is None else target
+    nodes = np.full((w.B, w.max_T), -1, dtype=np.int64)
+    alen = np.zeros(w.B, dtype=np.int64)
+    for b, t in enumerate(trees):
+        n, path, _, _ = verify_sequence(target[b], w.draft_probs[b], t.q_row, t.tokens, t.parents, int(w.T_b[b]),
+                                        int(w.modes[b]), w.philox_key, w.philox_offset, b)
+        nodes[b, : n + 1] = path
+        alen[b] = n
+    return nodes, alen

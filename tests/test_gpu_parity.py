@@ -10,7 +10,7 @@
 import numpy as np
 import pytest
 
-from gpu_support import check_fp8_attention, check_kv_prune, run_attention_fp8
+from gpu_support import check_fp8_attention, check_kv_prune, plant_path, run_attention_fp8
 from gpu_support import (ATTN_MAX_ABS, ATTN_REL_L2, LSE_ABS, check_build, check_verify, compare_attention, log,
                          oracle_trees, parents_array, run_pipeline, to_np)
 from oracle.kvcompact import PRUNE_REMAP, PRUNE_TAIL
@@ -393,30 +393,12 @@ def _small_verify_workload(seed, verify, V=64, B=6, temperature=1.0):
     return w, trees, pad("tokens"), pad("parents"), pad("q_row")
 
 
-def _plant_path(rng, w, trees, target, draft):
-    """Make a random root->leaf path likely to be accepted (inputs only)."""
-    for b, t in enumerate(trees):
-        sampling = int(w.modes[b]) == 1
-        u = 0
-        while True:
-            kids = [i for i in range(1, len(t.tokens)) if t.parents[i] == u]
-            if not kids or rng.random() < 0.15:
-                break
-            c = kids[int(rng.integers(len(kids)))]
-            if sampling:
-                if t.q_row[u] >= 0:
-                    draft[b, t.q_row[u]] = target[b, u]  # q == p: accepted with probability 1
-            else:
-                target[b, u, t.tokens[c]] = target[b, u].max() + 1.0
-            u = c
-
-
 @pytest.mark.parametrize("seed", range(8))
 @pytest.mark.parametrize("verify", ["greedy", "sample", "alternate"])
 def test_verify_planted(seed, verify):
     w, trees, tok, par, qr = _small_verify_workload(seed, verify, V=[64, 1000, 333, 4096][seed % 4])
     target, draft = w.target.copy(), w.draft_probs.copy()
-    _plant_path(np.random.default_rng(seed), w, trees, target, draft)
+    plant_path(np.random.default_rng(seed), w, trees, target, draft)
     w.target, w.draft_probs = target, draft
     log(f"[verify] planted {verify} seed={seed}")
     host = _verify(w, tok, par, qr)
@@ -432,7 +414,7 @@ def test_verify_planted_residual_passes_only(seed, verify, monkeypatch):
     monkeypatch.setenv("SPEC_TREE_VERIFY_FAST", "0")
     w, trees, tok, par, qr = _small_verify_workload(seed, verify, V=[64, 1000, 333, 4096][seed % 4])
     target, draft = w.target.copy(), w.draft_probs.copy()
-    _plant_path(np.random.default_rng(seed), w, trees, target, draft)
+    plant_path(np.random.default_rng(seed), w, trees, target, draft)
     w.target, w.draft_probs = target, draft
     log(f"[verify] planted {verify} seed={seed}, residual passes only")
     host = _verify(w, tok, par, qr)

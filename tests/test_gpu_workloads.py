@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 from gpu_support import (ATTN_MAX_ABS, ATTN_REL_L2, LSE_ABS, check_build, check_kv_prune, check_verify,
-                         compare_attention, log, oracle_trees, parents_array, run_pipeline, to_np)
+                         compare_attention, log, oracle_accepts, oracle_trees, parents_array, run_pipeline,
+                         to_np)
 from oracle.kvcompact import PRUNE_REMAP, PRUNE_TAIL
 from oracle.kvcompact import kv_compact as oracle_kv_compact
 from workloads import get_config
@@ -94,8 +95,9 @@ def test_full_pipeline_with_planted_acceptance_and_compaction():
     check_build(w, host, trees)
     check_verify(w, host, trees)
     assert host["accept_len"][0] > 0
-    k_ref, v_ref, l_ref = oracle_kv_compact(k_before[None], v_before[None], w.page_table, w.prefix_lens,
-                                            host["accept_nodes"], host["accept_len"], w.page)
+    nodes, alen = oracle_accepts(w, trees)
+    k_ref, v_ref, l_ref = oracle_kv_compact(k_before[None], v_before[None], w.page_table, w.prefix_lens, nodes, alen,
+                                            w.page)
     assert np.array_equal(dw.k_pages.view(torch.int16).cpu().numpy().view(np.uint16), k_ref[0])
     assert np.array_equal(dw.v_pages.view(torch.int16).cpu().numpy().view(np.uint16), v_ref[0])
     assert host["new_prefix_lens"].tolist() == l_ref.tolist()
