@@ -51,6 +51,7 @@ constexpr int kMaxKids = 64;  // children of one node (T <= 65)
 constexpr int kQ = 32;
 constexpr int kKS = 16;
 constexpr int kMaxSampleMap = 2048;  // sampling sequences a block lists in LDS
+constexpr int kRs = 8;               // u64 words of a node's published resampling state
 
 // Residual mass from a window of ratio bins. Over a node's row, the mass after j rejections,
 // W(G) = sum_v max(0, P[v] S_Q - G Q[v]) with G = gamma_j, only counts elements whose ratio P/Q exceeds
@@ -73,7 +74,8 @@ struct VerifyWs {
   uint64_t* keys;      // [B*max_T] greedy argmax keys (0 = empty)
   uint32_t* rowflag;   // [B*max_T] NaN seen in the greedy row
   int32_t* acc_child;  // [B*max_T] sampling: accepted child node or -1
-  int32_t* bonus;      // [B*max_T] sampling: bonus token when the walk stops here
+  uint64_t* rstate;    // [B*max_T][kRs] sampling: a node without an accepted child: W (u128), gamma, S_Q, K, the
+                       // argmax key of fx(p), plain | mass source << 8 (its per-slice masses: ssum or smass)
   uint32_t* nflag;     // [B*max_T] sampling node flags
   uint32_t* tickets;   // [B] greedy: rows done; sampling: nodes done
   uint32_t* rtick;     // [B*max_T] greedy: slice blocks of the row done
@@ -102,7 +104,7 @@ VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
   w.keys = reinterpret_cast<uint64_t*>(take(8 * n * kKS));
   w.rowflag = reinterpret_cast<uint32_t*>(take(4 * n));
   w.acc_child = reinterpret_cast<int32_t*>(take(4 * n));
-  w.bonus = reinterpret_cast<int32_t*>(take(4 * n));
+  w.rstate = reinterpret_cast<uint64_t*>(take(8 * n * kRs));
   w.nflag = reinterpret_cast<uint32_t*>(take(4 * n));
   w.tickets = reinterpret_cast<uint32_t*>(take(4 * size_t(B) * kQ));
   w.rtick = reinterpret_cast<uint32_t*>(take(4 * n * kQ));
@@ -134,6 +136,7 @@ struct VerifyArgs {
   const int8_t* mode;
   uint64_t key0, key1, offset;
   int B, max_T, R, V, n_slices, slice, nsl, n_greedy_blocks, n_sample_blocks;
+  int sample_first;  // sampling slice blocks take the grid's first ids (else the greedy blocks do)
   int row_tickets;  // greedy: count slice blocks per row first (sequences with many slice blocks)
   int fast;         // sampling: residual masses from the window records when they allow it
   int32_t* accept_len;
@@ -298,6 +301,23 @@ __device__ __forceinline__ u128 residual(uint32_t P, uint32_t Q, uint64_t S_Q, u
   return a > c ? a - c : u128(0);
 }
 
+// does element (P, Q) have a positive residual, P S_Q > gamma Q (always, for a plain resample from p)? The
+// products' fp32 estimates are within 2^-22 of the exact values, so they decide unless within 1e-6 of each other
+__device__ __forceinline__ bool res_pos(uint32_t P, uint32_t Q, uint64_t S_Q, uint64_t gamma, bool plain_p) {
+  if (plain_p) return P != 0u;
+  const float a = float(P) * float(S_Q), c = float(gamma) * float(Q);
+  if (a > c * 1.000001f) return true;
+  if (a < c * 0.999999f) return false;
+  return mul64x32(S_Q, P) > mul64x32(gamma, Q);
+}
+
+// sum of the residuals of a set of positive-residual elements from their sums of P and Q (exact:
+// sum (P S_Q - gamma Q) = S_Q sum P - gamma sum Q over elements that are each positive)
+__device__ __forceinline__ u128 res_sum(uint64_t sp, uint64_t sq, uint64_t S_Q, uint64_t gamma, bool plain_p) {
+  if (plain_p) return u128(sp);
+  return u128(S_Q) * sp - u128(gamma) * sq;
+}
+
 __device__ __forceinline__ u128 shfl_xor_u128(u128 x, int o) {
   const uint64_t lo = __shfl_xor(uint64_t(x), o, kWave);
   const uint64_t hi = __shfl_xor(uint64_t(x >> 64), o, kWave);
@@ -446,8 +466,9 @@ __device__ __forceinline__ void block_sum3(uint64_t& x0, uint64_t& x1, uint64_t&
     }
 }
 
-__device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArgs& a, int b, int u, int acc, int bonus, uint32_t flags,
-                              bool trivial);
+template <bool VEC, bool LG>
+__device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArgs& a, int b, int u, int acc, uint32_t flags,
+                                              bool trivial);
 
 // window bin of an element (see kWinBins): 0..kWinBins-1 for 1/2 <= P/Q < 8 (floor(8 P / Q) - 4), kWinHi
 // for P/Q >= 8 or Q = 0, -1 for P = 0 or P/Q < 1/2. e = 8 P / Q from a hardware reciprocal is within 3e-5 of
@@ -681,18 +702,28 @@ __device__ __forceinline__ void row_mass(const VerifyWs& w, const VerifyArgs& a,
   u128 total = 0;
   for (int sl = 0; sl < nsl; ++sl) {
     const int lo = sl * kSampleSlice, hi = min(V, lo + kSampleSlice);
-    u128 acc = 0;
-    slice_for<VEC>(prow, qrow, lo, hi, [&] { return pr; },
-                   [&](int, float x, float y) { acc += residual(fx(x), fx(y), S_Q, gamma, false); });
-    acc = wave_sum_u128(acc);
-    if (lane == 0) part[sl & 1][wave] = acc;
+    uint64_t sp = 0, sq = 0;  // sums of P and Q over the elements with a positive residual (res_sum)
+    slice_for<VEC>(prow, qrow, lo, hi, [&] { return pr; }, [&](int, float x, float y) {
+      const uint32_t P = fx(x), Q = fx(y);
+      const bool pos = res_pos(P, Q, S_Q, gamma, false);
+      sp += pos ? P : 0u;
+      sq += pos ? Q : 0u;
+    });
+    sp = wave_sum_u64(sp);
+    sq = wave_sum_u64(sq);
+    if (lane == 0) part[sl & 1][wave] = (u128(sq) << 64) | sp;
     __syncthreads();
     if (tid == 0) {
-      const u128 m = part[sl & 1][0] + part[sl & 1][1] + part[sl & 1][2] + part[sl & 1][3];
+      uint64_t SPs = 0, SQs = 0;
+      for (int i = 0; i < kWaves; ++i) {
+        SPs += uint64_t(part[sl & 1][i]);
+        SQs += uint64_t(part[sl & 1][i] >> 64);
+      }
+      const u128 m = res_sum(SPs, SQs, S_Q, gamma, false);
       if (sl < kThreads) ssl[sl] = m;
-      uint64_t* sm = w.smass + (node * nsl + sl) * 2;
-      sm[0] = uint64_t(m);
-      sm[1] = uint64_t(m >> 64);
+      uint64_t* sm = w.smass + (node * nsl + sl) * 2;  // read by the block that walks the tree
+      st_agent(sm, uint64_t(m));
+      st_agent(sm + 1, uint64_t(m >> 64));
       total += m;
     }
   }
@@ -707,15 +738,13 @@ __device__ __forceinline__ void decide_node(const VerifyWs& w, const VerifyArgs&
   __shared__ uint64_t km_s[kMaxKids];   // node c's acceptance integer m at km_s[c - 1]
   __shared__ int act_s;  // accepted child; -1: a rejection needs the next residual mass; -2: resample
   __shared__ int fast_s, fastok_s, ki_s, tested_s, test_s, src_s;
-  __shared__ u128 W_s, wtot_s[kWaves], part_s[2][kWaves];
+  __shared__ u128 W_s, part_s[2][kWaves];
   __shared__ uint64_t SP_s, SQ_s, gamma_s, AM_s, K_s;
   __shared__ uint32_t flags_s;
-  __shared__ int plain_s, bonus_s;
+  __shared__ int plain_s;
   __shared__ u128 ssl_s[kThreads];  // per-slice masses of the current W (the first kThreads slices)
   __shared__ u128 wred_s[kWaves];
   __shared__ uint64_t red_s[kWaves][3];
-  __shared__ int found_s;
-  __shared__ u128 run_s, tau_s;
   __shared__ WinLds win_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, max_T = a.max_T, V = a.V;
   const size_t node = size_t(b) * max_T + u;
@@ -872,92 +901,212 @@ __device__ __forceinline__ void decide_node(const VerifyWs& w, const VerifyArgs&
   }
   __syncthreads();
   if (act_s >= 0) {
-    sample_finish(w, a, b, u, act_s, -1, flags_s, false);
+    sample_finish<VEC, LG>(w, a, b, u, act_s, flags_s, false);
     return;
   }
-  // ---- no draft accepted: resample from the residual (or from p if nothing was tested); ssl_s holds the
-  // masses of the first kThreads slices (pass 0's sums of fx(p), the window's, or this block's row pass)
-  const u128 W = W_s;
-  const bool plain = plain_s;
-  if (W == 0) {
-    if (tid == 0) bonus_s = int(0xffffffffu - uint32_t(AM_s));  // smallest-index argmax of p
-  } else {
+  // ---- no draft accepted: the bonus is drawn only if the walk stops at this node, by the block that walks the
+  // tree (resample_stop); publish what it needs: the final residual mass W, gamma, S_Q, the node's uniform K, the
+  // argmax of fx(p), whether anything was tested, and where the per-slice masses are (pass 0's sums of fx(p) in
+  // ssum, or smass: this block's row pass wrote it; window masses are written there now)
+  if (src_s == 1 && tid < a.nsl) {
+    uint64_t* sm = w.smass + (node * a.nsl + tid) * 2;
+    st_agent(sm, uint64_t(ssl_s[tid]));
+    st_agent(sm + 1, uint64_t(ssl_s[tid] >> 64));
+  }
+  if (tid == 0) {
+    uint64_t* rs = w.rstate + node * kRs;
+    const u128 W = W_s;
+    st_agent(rs, uint64_t(W));
+    st_agent(rs + 1, uint64_t(W >> 64));
+    st_agent(rs + 2, gamma_s);
+    st_agent(rs + 3, SQ_s);
+    st_agent(rs + 4, K_s);
+    st_agent(rs + 5, AM_s);
+    st_agent(rs + 6, uint64_t(plain_s ? 1u : 0u) | (uint64_t(src_s == 0 ? 0u : 2u) << 8));
+  }
+  wait_global_stores();
+  __syncthreads();  // every thread's stores are complete before the ticket
+  sample_finish<VEC, LG>(w, a, b, u, -1, flags_s, false);
+}
+
+// The bonus of a sampling sequence whose accepted chain stops at node u, drawn by the block that walks the tree
+// from the state u's deciding block published: from the residual after u's rejections (or from p if u tested
+// nothing) with u's resampling uniform K, i.e. the smallest v with 2^32 prefix(v) > K W (prefix of the residual
+// masses in index order); the slice from the per-slice masses, then one pass over that slice. Every thread calls
+// it; the token is returned to every thread.
+template <bool VEC, bool LG>
+__device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs& a, int b, int u) {
+  __shared__ u128 W_s, tau_s, run_s, grem_s, wtot_s[kWaves], ssl_s[kThreads];
+  __shared__ uint64_t gsp_s[kWaves][kSampleSlice / (4 * kThreads)], gsq_s[kWaves][kSampleSlice / (4 * kThreads)];
+  __shared__ uint64_t gamma_s, SQ_s, AM_s;
+  __shared__ int plain_s, src_s, found_s, grp_s, bonus_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, V = a.V;
+  const size_t node = size_t(b) * a.max_T + u;
+  if (tid == 0) {
+    const uint64_t* rs = w.rstate + node * kRs;
+    const u128 W = u128(ld_agent(rs)) | (u128(ld_agent(rs + 1)) << 64);
+    const uint64_t K = ld_agent(rs + 4);
+    const uint64_t f = ld_agent(rs + 6);
+    W_s = W;
+    gamma_s = ld_agent(rs + 2);
+    SQ_s = ld_agent(rs + 3);
+    AM_s = ld_agent(rs + 5);
+    plain_s = int(f & 1u);
+    src_s = int(f >> 8);
     // threshold: smallest v with 2^32 * prefix(v) > K W  <=>  prefix(v) > floor(K W / 2^32)
-    if (tid == 0) {
-      const U192 kw = mul_u128_u64(W, K_s);
-      tau_s = (u128(kw.hi) << 96) | (u128(kw.mid) << 32) | u128(kw.lo >> 32);
-      run_s = 0;
-      found_s = -1;
-      bonus_s = -1;
-    }
-    // the slice holding the threshold: slice sums kThreads at a time (the first chunk is in LDS
-    // already), one round trip per further chunk
-    for (int c0 = 0; c0 < a.nsl; c0 += kThreads) {
-      __syncthreads();
-      if (found_s >= 0) break;
-      const int sl = c0 + tid;
-      if (c0 > 0 && sl < a.nsl) {  // past the first kThreads slices (never with window masses)
-        const size_t r = node * a.nsl + sl;
-        ssl_s[tid] = src_s == 0 ? u128(w.ssum[r]) : (u128(w.smass[r * 2]) | (u128(w.smass[r * 2 + 1]) << 64));
-      }
-      __syncthreads();
-      if (tid == 0) {
-        u128 run = run_s;
-        const int n = min(kThreads, a.nsl - c0);
-        for (int i = 0; i < n; ++i) {
-          if (run + ssl_s[i] > tau_s) {
-            found_s = c0 + i;
-            break;
-          }
-          run += ssl_s[i];
-        }
-        if (found_s < 0 && c0 + n >= a.nsl) found_s = a.nsl - 1;  // unreachable with exact sums
-        run_s = run;
-      }
+    const U192 kw = mul_u128_u64(W, K);
+    tau_s = (u128(kw.hi) << 96) | (u128(kw.mid) << 32) | u128(kw.lo >> 32);
+    run_s = 0;
+    found_s = -1;
+    bonus_s = -1;
+  }
+  __syncthreads();
+  const u128 W = W_s;
+  if (W == 0) return int(0xffffffffu - uint32_t(AM_s));  // zero residual: smallest-index argmax of p
+  const bool plain = plain_s;
+  const float* prow = sample_row(a, node);
+  const ProbRow<LG> pr = prob_row<LG>(a, node);
+  const int qr = a.q_row ? a.q_row[node] : -1;
+  const float* qrow = (!plain && a.draft != nullptr && qr >= 0 && qr < a.R) ? a.draft + (size_t(b) * a.R + qr) * V : nullptr;
+  // the slice holding the threshold: per-slice masses kThreads at a time, one round trip per chunk
+  for (int c0 = 0; c0 < a.nsl; c0 += kThreads) {
+    __syncthreads();
+    if (found_s >= 0) break;
+    const int sl = c0 + tid;
+    if (sl < a.nsl) {
+      const size_t r = node * a.nsl + sl;
+      ssl_s[tid] = src_s == 0 ? u128(w.ssum[r]) : (u128(ld_agent(w.smass + r * 2)) | (u128(ld_agent(w.smass + r * 2 + 1)) << 64));
     }
     __syncthreads();
-    // the block searches the chosen slice in one pass: each thread sums a contiguous range of E elements, a
-    // block scan gives every range's prefix, and the one thread whose range holds the crossing reads its
-    // range again and walks it element by element
-    const uint64_t S_Q = SQ_s, gamma = gamma_s;
-    constexpr int E = kSampleSlice / kThreads;
-    const int e0 = found_s * kSampleSlice + tid * E, whi = min(V, found_s * kSampleSlice + kSampleSlice);
-    const u128 rem = tau_s - run_s;  // remaining threshold inside the slice
-    auto range_for = [&](auto&& f) {  // f(i, P, Q) over this thread's range in index order
-      if (VEC && e0 + E <= whi) {
-#pragma unroll
-        for (int i = 0; i < E; i += 4) {
-          const float4 x = *reinterpret_cast<const float4*>(prow + e0 + i);
-          const float4 y = qrow ? *reinterpret_cast<const float4*>(qrow + e0 + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-          f(i, fx(pr(x.x)), fx(y.x));
-          f(i + 1, fx(pr(x.y)), fx(y.y));
-          f(i + 2, fx(pr(x.z)), fx(y.z));
-          f(i + 3, fx(pr(x.w)), fx(y.w));
+    if (tid == 0) {
+      u128 run = run_s;
+      const int n = min(kThreads, a.nsl - c0);
+      for (int i = 0; i < n; ++i) {
+        if (run + ssl_s[i] > tau_s) {
+          found_s = c0 + i;
+          break;
         }
-      } else {
-        for (int i = 0; i < E; ++i) {
-          const int v = e0 + i;
-          if (v < whi) f(i, fx(pr(prow[v])), qrow ? fx(qrow[v]) : 0u);  // past the slice: adds nothing
-        }
+        run += ssl_s[i];
       }
-    };
-    u128 tsum = 0;
-    range_for([&](int, uint32_t P, uint32_t Q) { tsum += residual(P, Q, S_Q, gamma, plain); });
-    const u128 ex = block_exclusive_scan_u128(tsum, wtot_s);
-    if (tsum > 0 && ex <= rem && rem < ex + tsum) {
-      u128 run = ex;
-      int hit = -1;
-      range_for([&](int i, uint32_t P, uint32_t Q) {
-        run += residual(P, Q, S_Q, gamma, plain);
-        if (run > rem && hit < 0) hit = e0 + i;
-      });
-      bonus_s = hit;
+      if (found_s < 0 && c0 + n >= a.nsl) found_s = a.nsl - 1;  // unreachable with exact sums
+      run_s = run;
     }
   }
   __syncthreads();
-  int bn = bonus_s;
-  if (bn < 0) bn = int(0xffffffffu - uint32_t(AM_s));  // unreachable with exact sums; keeps the output defined
-  sample_finish(w, a, b, u, -1, bn, flags_s, false);
+  // the block searches the chosen slice: coalesced loads (thread t holds elements lo + 4 t + 1024 i + k,
+  // k < 4, of the slice's 8 groups of 1024), the groups' sums by wave reductions locate the group holding
+  // the threshold, one block scan over that group's 256 chunks of 4 elements locates the chunk, and its
+  // thread walks the 4 elements it holds
+  const uint64_t S_Q = SQ_s, gamma = gamma_s;
+  constexpr int NG = kSampleSlice / (4 * kThreads);
+  const int lo = found_s * kSampleSlice, whi = min(V, lo + kSampleSlice);
+  const u128 rem = tau_s - run_s;  // remaining threshold inside the slice
+  // every load issued before any is used: addresses clamped into the row, elements past the slice masked
+  float4 x[NG], y[NG];
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int v = lo + 4 * tid + 4 * kThreads * i;
+    if (VEC) {
+      const int vc = v + 4 <= whi ? v : lo;
+      x[i] = *reinterpret_cast<const float4*>(prow + vc);
+      y[i] = qrow ? *reinterpret_cast<const float4*>(qrow + vc) : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      float e[4], f[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int vk = v + k < whi ? v + k : lo;
+        e[k] = prow[vk];
+        f[k] = qrow ? qrow[vk] : 0.f;
+      }
+      x[i] = make_float4(e[0], e[1], e[2], e[3]);
+      y[i] = make_float4(f[0], f[1], f[2], f[3]);
+    }
+  }
+  // element k of group i in fixed point (past the slice: P = Q = 0, no residual), formed where it is used
+  auto PQ = [&](int i, int k, uint32_t& P, uint32_t& Q) {
+    const int v = lo + 4 * tid + 4 * kThreads * i + k;
+    const float xe = k == 0 ? x[i].x : (k == 1 ? x[i].y : (k == 2 ? x[i].z : x[i].w));
+    const float ye = k == 0 ? y[i].x : (k == 1 ? y[i].y : (k == 2 ? y[i].z : y[i].w));
+    P = v < whi ? fx(pr(xe)) : 0u;
+    Q = v < whi ? fx(ye) : 0u;
+  };
+  // per group: this thread's sums of P and Q over its positive-residual elements, then the wave's
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    uint64_t sp = 0, sq = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t P, Q;
+      PQ(i, k, P, Q);
+      const bool pos = res_pos(P, Q, S_Q, gamma, plain);
+      sp += pos ? P : 0u;
+      sq += pos ? Q : 0u;
+    }
+    sp = wave_sum_u64(sp);
+    sq = wave_sum_u64(sq);
+    if (lane == 0) {
+      gsp_s[wave][i] = sp;
+      gsq_s[wave][i] = sq;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    u128 run = 0;
+    int g = NG - 1;
+    for (int i = 0; i < NG; ++i) {
+      uint64_t sp = 0, sq = 0;
+      for (int q = 0; q < kWaves; ++q) {
+        sp += gsp_s[q][i];
+        sq += gsq_s[q][i];
+      }
+      const u128 t = res_sum(sp, sq, S_Q, gamma, plain);
+      if (run + t > rem) {
+        g = i;
+        break;
+      }
+      run += t;
+    }
+    grp_s = g;
+    grem_s = rem - run;
+  }
+  __syncthreads();
+  const int g = grp_s;
+  const u128 grem = grem_s;
+  u128 mine = 0;  // this thread's chunk of group g
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    if (i != g) continue;
+    uint64_t sp = 0, sq = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t P, Q;
+      PQ(i, k, P, Q);
+      const bool pos = res_pos(P, Q, S_Q, gamma, plain);
+      sp += pos ? P : 0u;
+      sq += pos ? Q : 0u;
+    }
+    mine = res_sum(sp, sq, S_Q, gamma, plain);
+  }
+  const u128 ex = block_exclusive_scan_u128(mine, wtot_s);
+  if (mine > 0 && ex <= grem && grem < ex + mine) {
+    u128 run = ex;
+    int hit = -1;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      if (i != g) continue;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t P, Q;
+        PQ(i, k, P, Q);
+        run += residual(P, Q, S_Q, gamma, plain);
+        if (run > grem && hit < 0) hit = lo + 4 * tid + 4 * kThreads * i + k;
+      }
+    }
+    bonus_s = hit;
+  }
+  __syncthreads();
+  const int bn = bonus_s;
+  return bn >= 0 ? bn : int(0xffffffffu - uint32_t(AM_s));  // unreachable with exact sums; keeps the output defined
 }
 
 // ------------------------------------------------------------------ walk
@@ -971,7 +1120,8 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
 // validity (AND) and depth (sum) along the path come from pointer doubling over lanes, the deepest
 // valid node (ties -> smaller index) from a wave maximum, and the path from its ancestry bits.
 // Sampling: the accepted child chain from the root, chased in registers.
-__device__ __forceinline__ void walk(const VerifyWs& w, const VerifyArgs& a, int b) {
+__device__ __forceinline__ void walk(const VerifyWs& w, const VerifyArgs& a, int b, int* stop_out = nullptr,
+                                     int* nacc_out = nullptr) {
   __shared__ int path_s[65], tok_s[65];
   if (threadIdx.x >= kWave) return;
   const int lane = threadIdx.x, max_T = a.max_T, V = a.V;
@@ -1041,28 +1191,30 @@ __device__ __forceinline__ void walk(const VerifyWs& w, const VerifyArgs& a, int
     bonus = e > 0 ? __shfl(am, e - 1) : am0;
   } else {
     const uint32_t nf0 = ld_agent(w.nflag + base);
-    const int ch0 = ld_agent(w.acc_child + base), bo0 = ld_agent(w.bonus + base);
+    const int ch0 = ld_agent(w.acc_child + base);
     uint32_t nf = 0;
-    int ch = -1, bo = 0;
+    int ch = -1;
     if (real) {
       nf = ld_agent(w.nflag + base + n);
       ch = ld_agent(w.acc_child + base + n);
-      bo = ld_agent(w.bonus + base + n);
     }
     f |= nf & SPEC_STATUS_NAN_INPUT;
     constexpr uint32_t kPathFlags = SPEC_STATUS_ZERO_Q | SPEC_STATUS_ZERO_RESIDUAL;
     rootf = nf0 & (SPEC_STATUS_NAN_INPUT | kPathFlags);
     int u = 0, c = ch0, cnt = 0;
-    bonus = bo0;
     while (c > u && c < T && cnt < kWave) {  // uniform: every value comes from a readlane
       u = c;
       ++cnt;
       if (lane == 0) path_s[cnt] = u;
       rootf |= __builtin_amdgcn_readlane(nf, u - 1) & kPathFlags;
-      bonus = __builtin_amdgcn_readlane(bo, u - 1);
       c = __builtin_amdgcn_readlane(ch, u - 1);
     }
     nacc = cnt;
+    bonus = -1;  // drawn at the stop node u by the caller (resample_stop), which writes it
+    if (lane == 0) {
+      *stop_out = u;
+      *nacc_out = cnt;
+    }
   }
   const uint32_t st = wave_or_u32(f) | rootf;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // path_s / tok_s written by other lanes
@@ -1074,20 +1226,21 @@ __device__ __forceinline__ void walk(const VerifyWs& w, const VerifyArgs& a, int
   }
   for (int k = lane; k < max_T; k += kWave) {
     a.accept_nodes[base + k] = k <= nacc ? path_s[k] : -1;
-    a.out_tokens[base + k] = k < nacc ? tok_s[path_s[k + 1]] : (k == nacc ? bonus : -1);
+    if (k != nacc || greedy) a.out_tokens[base + k] = k < nacc ? tok_s[path_s[k + 1]] : (k == nacc ? bonus : -1);
   }
 }
 
 // a node's outcome is final: publish it and count it for its sequence; the block finishing a sequence's last
-// node walks the tree. Rows past T_b are counted without outcome (trivial).
-__device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArgs& a, int b, int u, int acc, int bonus, uint32_t flags,
-                              bool trivial) {
-  __shared__ int last_s;
+// node walks the tree and then draws the bonus of the node where the accepted chain stops. Rows past T_b are
+// counted without outcome (trivial).
+template <bool VEC, bool LG>
+__device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArgs& a, int b, int u, int acc, uint32_t flags,
+                                              bool trivial) {
+  __shared__ int last_s, stop_s, nacc_s;
   const size_t node = size_t(b) * a.max_T + u;
   if (threadIdx.x == 0) {
     if (!trivial) {
       st_agent(w.acc_child + node, acc);
-      st_agent(w.bonus + node, bonus);
       st_agent(w.nflag + node, flags);
     }
     wait_global_stores();
@@ -1096,7 +1249,10 @@ __device__ __forceinline__ void sample_finish(const VerifyWs& w, const VerifyArg
   __syncthreads();
   if (!last_s) return;
   if (threadIdx.x == 0) ticket_reset(&w.tickets[size_t(b) * kQ]);
-  walk(w, a, b);
+  walk(w, a, b, &stop_s, &nacc_s);
+  __syncthreads();
+  const int bonus = resample_stop<VEC, LG>(w, a, b, stop_s);
+  if (threadIdx.x == 0) a.out_tokens[size_t(b) * a.max_T + nacc_s] = bonus;
 }
 
 // The sampling sequences in index order into smap (when there are at most kMaxSampleMap); returns their count
@@ -1133,7 +1289,8 @@ __device__ __forceinline__ void sample_slices(const VerifyWs& w, const VerifyArg
   if (nseq == 0) return;
   const bool mapped = nseq <= kMaxSampleMap;
   const long long items = (long long)(mapped ? nseq : a.B) * a.max_T * a.nsl;
-  for (long long it = int(blockIdx.x) - a.n_greedy_blocks; it < items; it += a.n_sample_blocks) {
+  const int sb = a.sample_first ? int(blockIdx.x) : int(blockIdx.x) - a.n_greedy_blocks;
+  for (long long it = sb; it < items; it += a.n_sample_blocks) {
     const int sl = int(it % a.nsl);
     const long long nd = it / a.nsl;
     const int u = int(nd % a.max_T), si = int(nd / a.max_T);
@@ -1144,14 +1301,19 @@ __device__ __forceinline__ void sample_slices(const VerifyWs& w, const VerifyArg
   }
 }
 
+// sampling slice blocks and greedy slice blocks; the sampling ones take the first ids when the call carries
+// draft rows (their blocks run longest), else the last (a batch without draft rows is usually all greedy, and
+// its sampling blocks only find that out)
 template <bool VEC, bool LG>
 __global__ void __launch_bounds__(kThreads) verify_rows_kernel(VerifyWs w, VerifyArgs a) {
   __shared__ int last_s;
-  if (int(blockIdx.x) >= a.n_greedy_blocks) {
+  const bool sampling_block = a.sample_first ? int(blockIdx.x) < a.n_sample_blocks : int(blockIdx.x) >= a.n_greedy_blocks;
+  if (sampling_block) {
     sample_slices<VEC, LG>(w, a);
     return;
   }
-  const int x = blockIdx.x % a.n_slices, row = blockIdx.x / a.n_slices;
+  const int gb = a.sample_first ? int(blockIdx.x) - a.n_sample_blocks : int(blockIdx.x);
+  const int x = gb % a.n_slices, row = gb / a.n_slices;
   const int b = row / a.max_T, u = row - b * a.max_T;
   if (a.mode[b] == SPEC_MODE_SAMPLE) return;
   if (u < seq_T(a.T_b, b, a.max_T)) {
@@ -1201,7 +1363,7 @@ __global__ void __launch_bounds__(kThreads) verify_decide_kernel(VerifyWs w, Ver
   if (a.mode[b] != SPEC_MODE_SAMPLE) return;
   const int T = seq_T(a.T_b, b, a.max_T);
   if (u >= T) {
-    sample_finish(w, a, b, u, -1, -1, 0u, true);
+    sample_finish<VEC, LG>(w, a, b, u, -1, 0u, true);
     return;
   }
   decide_node<VEC, LG>(w, a, b, u, T);
@@ -1349,7 +1511,13 @@ static int32_t verify_impl(const char* who, const float* target, float2* sm_part
   a.nsl = int(nsl);
   a.n_greedy_blocks = int(rows) * a.n_slices;
   a.row_tickets = (long long)a.n_slices * max_T > 256;
-  a.n_sample_blocks = int(std::min<long long>(kMaxSampleBlocks, rows * nsl));
+  long long max_sblocks = kMaxSampleBlocks;
+  if (const char* env = getenv("SPEC_TREE_VERIFY_SBLOCKS")) {  // sampling slice blocks per launch, for sweeps
+    const long long v = atoll(env);
+    if (v >= 256 && v <= (1LL << 20)) max_sblocks = v;
+  }
+  a.n_sample_blocks = int(std::min<long long>(max_sblocks, rows * nsl));
+  a.sample_first = draft_probs != nullptr;
   a.fast = verify_fast_enabled();
   a.accept_len = accept_len;
   a.accept_nodes = accept_nodes;
