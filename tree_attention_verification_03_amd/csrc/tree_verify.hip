@@ -52,6 +52,7 @@ constexpr int kQ = 32;
 constexpr int kKS = 16;
 constexpr int kMaxSampleMap = 2048;  // sampling sequences a block lists in LDS
 constexpr int kRs = 8;               // u64 words of a node's published resampling state
+constexpr int kKidsSeqs = 256;       // sampling sequences whose child masks a slice block keeps in LDS
 
 // Residual mass from a window of ratio bins. Over a node's row, the mass after j rejections,
 // W(G) = sum_v max(0, P[v] S_Q - G Q[v]) with G = gamma_j, only counts elements whose ratio P/Q exceeds
@@ -495,7 +496,7 @@ __device__ __forceinline__ int win_bin(uint32_t P, uint32_t Q) {
 // ballot offset, then counted and summed per bin, then placed by per-bin cursors: the order inside a bin is
 // arbitrary, and nothing depends on it.
 template <bool VEC, bool LG>
-__device__ __forceinline__ void sample_slice(const VerifyWs& w, const VerifyArgs& a, int b, int u, int s) {
+__device__ __forceinline__ void sample_slice(const VerifyWs& w, const VerifyArgs& a, int b, int u, int s, bool kids) {
   __shared__ uint64_t red[kWaves][3];
   __shared__ uint64_t amr[kWaves];
   __shared__ uint32_t wc_s[kWinSlots], wcur_s[kWinSlots], wn_s[kWaves];
@@ -506,7 +507,7 @@ __device__ __forceinline__ void sample_slice(const VerifyWs& w, const VerifyArgs
   const size_t node = size_t(b) * a.max_T + u;
   const size_t rec = node * a.nsl + s;
   const float* prow = sample_row(a, node);
-  const float* qrow = node_qrow_any(a, b, u);
+  const float* qrow = kids ? node_qrow_any(a, b, u) : nullptr;  // a node without children never reads its q row
   const int lo = s * kSampleSlice, hi = min(a.V, lo + kSampleSlice);
   const bool win = a.fast && qrow != nullptr && w.wcnt != nullptr;
   if (win && tid < kWinSlots) {
@@ -1285,9 +1286,29 @@ template <bool VEC, bool LG>
 __device__ __forceinline__ void sample_slices(const VerifyWs& w, const VerifyArgs& a) {
   __shared__ int smap[kMaxSampleMap];
   __shared__ int wcnt[kWaves];
+  __shared__ unsigned long long kids_s[kKidsSeqs][2];  // bit u: node u of listed sampling sequence i has a child
   const int nseq = sampling_map(a, smap, wcnt);
   if (nseq == 0) return;
   const bool mapped = nseq <= kMaxSampleMap;
+  // which nodes have children (only their q rows and window records are ever read): one pass over the listed
+  // sequences' parents (an invalid parent counts as the root, as in the decisions); more sequences than the
+  // mask holds: every node counts as having children
+  const int tid = threadIdx.x;
+  const bool kmap = mapped && nseq <= kKidsSeqs;
+  if (kmap) {
+    for (int i = tid; i < 2 * nseq; i += kThreads) kids_s[i >> 1][i & 1] = 0ull;
+    __syncthreads();
+    for (int i = tid; i < nseq * a.max_T; i += kThreads) {
+      const int si = i / a.max_T, c = i - si * a.max_T;
+      const int b = smap[si];
+      if (c >= 1 && c < seq_T(a.T_b, b, a.max_T)) {
+        int pc = a.parents[size_t(b) * a.max_T + c];
+        if (pc < 0 || pc >= c) pc = 0;
+        atomicOr(&kids_s[si][pc >> 6], 1ull << (pc & 63));
+      }
+    }
+    __syncthreads();
+  }
   const long long items = (long long)(mapped ? nseq : a.B) * a.max_T * a.nsl;
   const int sb = a.sample_first ? int(blockIdx.x) : int(blockIdx.x) - a.n_greedy_blocks;
   for (long long it = sb; it < items; it += a.n_sample_blocks) {
@@ -1296,7 +1317,8 @@ __device__ __forceinline__ void sample_slices(const VerifyWs& w, const VerifyArg
     const int u = int(nd % a.max_T), si = int(nd / a.max_T);
     const int b = mapped ? smap[si] : si;
     if (a.mode[b] != SPEC_MODE_SAMPLE || u >= seq_T(a.T_b, b, a.max_T)) continue;
-    sample_slice<VEC, LG>(w, a, b, u, sl);
+    const bool kids = !kmap || ((kids_s[si][u >> 6] >> (u & 63)) & 1ull);
+    sample_slice<VEC, LG>(w, a, b, u, sl, kids);
     __syncthreads();  // the slice's LDS is free for the next item
   }
 }
