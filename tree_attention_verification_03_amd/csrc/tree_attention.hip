@@ -430,6 +430,10 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) vbuf[dt] = read_v(0, dt);
     }
+    // kernels without them keep one V operand in flight: the first now, each next one before the MFMA
+    // that consumes the current one
+    bf16x8 vnext;
+    if constexpr (!kPrefetchV) vnext = read_v(0, 0);
     // usable keys among the lane's NE (bit e <-> key_of(e))
     uint32_t kvis = (1u << NE) - 1u;
     if (masked) {  // uniform
@@ -501,7 +505,16 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
     for (int ss = 0; ss < SPS; ++ss) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 vop = kPrefetchV ? vbuf[dt] : read_v(ss, dt);
+        bf16x8 vop;
+        if constexpr (kPrefetchV) {
+          vop = vbuf[dt];
+        } else {
+          vop = vnext;
+          if (dt + 1 < DT)
+            vnext = read_v(ss, dt + 1);
+          else if (ss + 1 < SPS)
+            vnext = read_v(ss + 1, 0);
+        }
 #pragma unroll
         for (int rw = 0; rw < RW; ++rw)
           acc[rw][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rw][ss], acc[rw][dt], 0, 0, 0);

@@ -282,10 +282,11 @@ __device__ __forceinline__ void greedy_slice(const VerifyWs& w, const VerifyArgs
 
 // ------------------------------------------------------------------ sampling
 __device__ __forceinline__ uint32_t fx(float x) {
-  // 2^-32 fixed point: 0 for NaN / x <= 0, 2^32-1 for x >= 1, floor(x * 2^32) otherwise
-  if (!(x > 0.f)) return 0u;
-  if (x >= 1.f) return 0xffffffffu;
-  return uint32_t(x * 4294967296.0f);  // exact power-of-two scaling, truncation = floor
+  // 2^-32 fixed point: 0 for NaN / x <= 0, 2^32-1 for x >= 1, floor(x * 2^32) otherwise. Branch-free: the operand
+  // is clamped into [0, 1 - 2^-24] (NaN -> 0; the identity on (0, 1)), scaled exactly by 2^32 and truncated
+  const float c = fminf(fmaxf(x, 0.f), 0.99999994f);
+  const uint32_t f = uint32_t(c * 4294967296.0f);
+  return x >= 1.f ? 0xffffffffu : f;
 }
 
 __device__ __forceinline__ u128 mul64x32(uint64_t a, uint32_t b) {
@@ -302,10 +303,12 @@ __device__ __forceinline__ u128 residual(uint32_t P, uint32_t Q, uint64_t S_Q, u
   return a > c ? a - c : u128(0);
 }
 
-// does element (P, Q) have a positive residual, P S_Q > gamma Q (always, for a plain resample from p)? The
-// products' fp32 estimates are within 2^-22 of the exact values, so they decide unless within 1e-6 of each other
+// does element (P, Q) have a positive residual, P S_Q > gamma Q (always, for a plain resample from p)? P = 0
+// never does; otherwise the products' fp32 estimates are within 2^-22 of the exact values, so they decide unless
+// within 1e-6 of each other
 __device__ __forceinline__ bool res_pos(uint32_t P, uint32_t Q, uint64_t S_Q, uint64_t gamma, bool plain_p) {
-  if (plain_p) return P != 0u;
+  if (P == 0u) return false;
+  if (plain_p) return true;
   const float a = float(P) * float(S_Q), c = float(gamma) * float(Q);
   if (a > c * 1.000001f) return true;
   if (a < c * 0.999999f) return false;
@@ -943,6 +946,14 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
   __shared__ int plain_s, src_s, found_s, grp_s, bonus_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, V = a.V;
   const size_t node = size_t(b) * a.max_T + u;
+  // the first kThreads slices' masses from both possible sources, in the state's round trip (the state says which)
+  uint64_t m0 = 0, m1 = 0, m2 = 0;
+  if (tid < a.nsl) {
+    const size_t r = node * a.nsl + tid;
+    m0 = w.ssum[r];
+    m1 = ld_agent(w.smass + r * 2);
+    m2 = ld_agent(w.smass + r * 2 + 1);
+  }
   if (tid == 0) {
     const uint64_t* rs = w.rstate + node * kRs;
     const u128 W = u128(ld_agent(rs)) | (u128(ld_agent(rs + 1)) << 64);
@@ -964,7 +975,7 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
   __syncthreads();
   const u128 W = W_s;
   if (W == 0) return int(0xffffffffu - uint32_t(AM_s));  // zero residual: smallest-index argmax of p
-  const bool plain = plain_s;
+  const bool plain = __builtin_amdgcn_readfirstlane(plain_s) != 0;
   const float* prow = sample_row(a, node);
   const ProbRow<LG> pr = prob_row<LG>(a, node);
   const int qr = a.q_row ? a.q_row[node] : -1;
@@ -976,7 +987,10 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
     const int sl = c0 + tid;
     if (sl < a.nsl) {
       const size_t r = node * a.nsl + sl;
-      ssl_s[tid] = src_s == 0 ? u128(w.ssum[r]) : (u128(ld_agent(w.smass + r * 2)) | (u128(ld_agent(w.smass + r * 2 + 1)) << 64));
+      if (c0 == 0)
+        ssl_s[tid] = src_s == 0 ? u128(m0) : (u128(m1) | (u128(m2) << 64));
+      else
+        ssl_s[tid] = src_s == 0 ? u128(w.ssum[r]) : (u128(ld_agent(w.smass + r * 2)) | (u128(ld_agent(w.smass + r * 2 + 1)) << 64));
     }
     __syncthreads();
     if (tid == 0) {
@@ -1023,26 +1037,45 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
       y[i] = make_float4(f[0], f[1], f[2], f[3]);
     }
   }
-  // element k of group i in fixed point (past the slice: P = Q = 0, no residual), formed where it is used
-  auto PQ = [&](int i, int k, uint32_t& P, uint32_t& Q) {
-    const int v = lo + 4 * tid + 4 * kThreads * i + k;
-    const float xe = k == 0 ? x[i].x : (k == 1 ? x[i].y : (k == 2 ? x[i].z : x[i].w));
-    const float ye = k == 0 ? y[i].x : (k == 1 ? y[i].y : (k == 2 ? y[i].z : y[i].w));
-    P = v < whi ? fx(pr(xe)) : 0u;
-    Q = v < whi ? fx(ye) : 0u;
-  };
-  // per group: this thread's sums of P and Q over its positive-residual elements, then the wave's
-#pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    uint64_t sp = 0, sq = 0;
+  // this thread's 4 elements of group i in fixed point (past the slice: P = Q = 0, no residual) and its sums of P
+  // and Q over those with a positive residual. P = 0 is never positive and the fp32 test decides the rest
+  // branch-free; an element it cannot decide (products within 1e-6 of each other, rare) is left out of the sums
+  // and returned as bit k
+  const float fS = float(S_Q), fG = float(gamma);
+  auto fast = [&](float4 xv, float4 yv, int i, uint64_t& sp, uint64_t& sq) __attribute__((always_inline)) -> uint32_t {
+    const float xs[4] = {xv.x, xv.y, xv.z, xv.w}, ys[4] = {yv.x, yv.y, yv.z, yv.w};
+    uint32_t und = 0;
+    sp = 0;
+    sq = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      uint32_t P, Q;
-      PQ(i, k, P, Q);
-      const bool pos = res_pos(P, Q, S_Q, gamma, plain);
+      const bool in = lo + 4 * tid + 4 * kThreads * i + k < whi;
+      const uint32_t P = fx(in ? pr(xs[k]) : 0.f), Q = fx(in ? ys[k] : 0.f);  // fx(0) = 0
+      const float fa = float(P) * fS, fc = float(Q) * fG;
+      const bool pos = plain ? P != 0u : fa > fc * 1.000001f;
       sp += pos ? P : 0u;
       sq += pos ? Q : 0u;
+      und |= (P != 0u && !pos && !(fa < fc * 0.999999f)) ? 1u << k : 0u;  // plain: pos == (P != 0)
     }
+    return und;
+  };
+  // the undecided elements of group i (bits), reloaded from the row: each joins the sums when P S_Q > gamma Q
+  auto settle = [&](uint32_t bits, int i, uint64_t& sp, uint64_t& sq) __attribute__((always_inline)) {
+    for (; bits != 0u; bits &= bits - 1u) {
+      const int v = lo + 4 * tid + 4 * kThreads * i + __builtin_ctz(bits);
+      const uint32_t P = fx(pr(prow[v])), Q = qrow ? fx(qrow[v]) : 0u;
+      if (mul64x32(S_Q, P) > mul64x32(gamma, Q)) {
+        sp += P;
+        sq += Q;
+      }
+    }
+  };
+  // per group: the wave's sums; undecided elements (bit 4 i + k of amb) are added in a second, rare pass
+  uint32_t amb = 0;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    uint64_t sp, sq;
+    amb |= fast(x[i], y[i], i, sp, sq) << (4 * i);
     sp = wave_sum_u64(sp);
     sq = wave_sum_u64(sq);
     if (lane == 0) {
@@ -1050,7 +1083,19 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
       gsq_s[wave][i] = sq;
     }
   }
-  __syncthreads();
+  if (__syncthreads_or(amb != 0u)) {
+    for (int i = 0; i < NG; ++i) {
+      uint64_t sp = 0, sq = 0;
+      settle((amb >> (4 * i)) & 0xfu, i, sp, sq);
+      sp = wave_sum_u64(sp);
+      sq = wave_sum_u64(sq);
+      if (lane == 0) {
+        gsp_s[wave][i] += sp;
+        gsq_s[wave][i] += sq;
+      }
+    }
+    __syncthreads();
+  }
   if (tid == 0) {
     u128 run = 0;
     int g = NG - 1;
@@ -1071,37 +1116,43 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
     grem_s = rem - run;
   }
   __syncthreads();
-  const int g = grp_s;
+  const int g = __builtin_amdgcn_readfirstlane(grp_s);
   const u128 grem = grem_s;
-  u128 mine = 0;  // this thread's chunk of group g
+  // group g's 4 elements of this thread, loaded again (just read, so from cache): holding all groups' registers
+  // until g is known would cost the kernel an occupancy step
+  float4 xg, yg;
+  {
+    const int v = lo + 4 * tid + 4 * kThreads * g;
+    if (VEC) {
+      const int vc = v + 4 <= whi ? v : lo;
+      xg = *reinterpret_cast<const float4*>(prow + vc);
+      yg = qrow ? *reinterpret_cast<const float4*>(qrow + vc) : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      float e[4], f[4];
 #pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    if (i != g) continue;
-    uint64_t sp = 0, sq = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t P, Q;
-      PQ(i, k, P, Q);
-      const bool pos = res_pos(P, Q, S_Q, gamma, plain);
-      sp += pos ? P : 0u;
-      sq += pos ? Q : 0u;
+      for (int k = 0; k < 4; ++k) {
+        const int vk = v + k < whi ? v + k : lo;
+        e[k] = prow[vk];
+        f[k] = qrow ? qrow[vk] : 0.f;
+      }
+      xg = make_float4(e[0], e[1], e[2], e[3]);
+      yg = make_float4(f[0], f[1], f[2], f[3]);
     }
-    mine = res_sum(sp, sq, S_Q, gamma, plain);
   }
+  uint64_t sp, sq;
+  settle(fast(xg, yg, g, sp, sq), g, sp, sq);
+  const u128 mine = res_sum(sp, sq, S_Q, gamma, plain);  // this thread's chunk of group g
   const u128 ex = block_exclusive_scan_u128(mine, wtot_s);
   if (mine > 0 && ex <= grem && grem < ex + mine) {
+    const float xs[4] = {xg.x, xg.y, xg.z, xg.w}, ys[4] = {yg.x, yg.y, yg.z, yg.w};
     u128 run = ex;
     int hit = -1;
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      if (i != g) continue;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t P, Q;
-        PQ(i, k, P, Q);
-        run += residual(P, Q, S_Q, gamma, plain);
-        if (run > grem && hit < 0) hit = lo + 4 * tid + 4 * kThreads * i + k;
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int v = lo + 4 * tid + 4 * kThreads * g + k;
+      const uint32_t P = fx(v < whi ? pr(xs[k]) : 0.f), Q = fx(v < whi ? ys[k] : 0.f);
+      run += residual(P, Q, S_Q, gamma, plain);
+      if (run > grem && hit < 0) hit = v;
     }
     bonus_s = hit;
   }
