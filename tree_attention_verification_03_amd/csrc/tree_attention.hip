@@ -107,9 +107,16 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char* addr) {
 // is synchronised explicitly instead (s_waitcnt vmcnt(n) + barrier), and no load the compiler issues
 // is in flight while the ring runs. M0 carries the LDS base (uniform by contract: read from lane 0);
 // nothing else in this file uses M0.
-__device__ __forceinline__ void load_to_lds16(const void* src, unsigned char* lds_dst) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_void*)lds_dst)));
+__device__ __forceinline__ void load_to_lds16(const void* src, uint32_t lds_off) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_off);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m) : "memory");
+}
+
+// LDS byte address of a __shared__ array (taken once: a generic pointer cast back to LDS costs a null
+// check per use)
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* shared_array) {
+  return uint32_t(reinterpret_cast<uintptr_t>((lds_void*)shared_array));
 }
 
 // max over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes holding one query row of an S^T tile), with
@@ -200,6 +207,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
   constexpr bool kPrefetchV = NW / 4 * blocks_per_cu(D, NS) <= 2;
   static_assert(NT >= 65, "the tree prologue uses one thread per node");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE_B];
+  const uint32_t ring_lds = lds_addr(ring);
   __shared__ uint64_t anc_s[65];
   extern __shared__ int pg_s[];  // page-table entries covering this item's keys (p.npg of them)
 
@@ -332,47 +340,53 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * blocks_per_cu(D, NS)) tree_a
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
   const int pmask = (1 << p.page_shift) - 1;
-  const size_t tok_stride = size_t(p.Hkv) * D;
-  const uint16_t* kbase = p.k + size_t(g) * D;
-  const uint16_t* vbase = p.v + size_t(g) * D;
+  // load addresses in bytes: a page's offset is one 32 x 32 -> 64-bit multiply-add, everything inside a
+  // page stays in 32 bits (the host checks that a page spans less than 2^31 bytes)
+  const uint32_t tok_b = uint32_t(p.Hkv) * (2 * D);  // bytes between consecutive slots of a page
+  const uint32_t page_b = tok_b << p.page_shift;
+  const uint64_t kbase = reinterpret_cast<uint64_t>(p.k) + uint64_t(g) * (2 * D);
+  const uint64_t vbase = reinterpret_cast<uint64_t>(p.v) + uint64_t(g) * (2 * D);
 
   // this wave's share of a stage: key rows sub_i * RPI + lane / CPR (sub_i = wave + NW i), one 16-byte chunk
   // per lane, loaded once for K and once for V (swizzled on the global side: LDS gets lane-order bytes)
-  const size_t page_elems = tok_stride << p.page_shift;
-  int lkey[PH], koff[PH], voff[PH];
+  int lkey[PH];
+  uint32_t koff[PH], voff[PH];  // byte offsets of the lane's chunk inside its (slot, head) row
 #pragma unroll
   for (int i = 0; i < PH; ++i) {
     lkey[i] = (wave + NW * i) * RPI + lane / CPR;
     const int pos = lane % CPR;
-    koff[i] = 8 * (pos ^ k_swz<D>(lkey[i]));
-    voff[i] = 8 * (pos ^ v_swz<D>(lkey[i]));
+    koff[i] = 16u * uint32_t(pos ^ k_swz<D>(lkey[i]));
+    voff[i] = 16u * uint32_t(pos ^ v_swz<D>(lkey[i]));
   }
+  const uint64_t zbase = reinterpret_cast<uint64_t>(p.zeros);
   // issue the direct loads of this wave's share of key tile `tile` into ring stage `slot`; slots past
   // the chunk and slots on invalid pages read the zero row (their keys are masked in compute)
   auto issue = [&](int tile, int slot) {
     const int st = key_lo + tile * kTile;
-    unsigned char* sb = ring + slot * STAGE_B;
+    const uint32_t sb = ring_lds + slot * STAGE_B;
     const bool full = pages_ok && st + kTile <= key_hi;  // uniform
 #pragma unroll
     for (int i = 0; i < PH; ++i) {
       const int slot_k = st + lkey[i];
-      const uint16_t *ks, *vs;
+      uint64_t ks, vs;
       if (full) {
-        const int phys = pg_s[(slot_k >> p.page_shift) - pg0];
-        const size_t off = size_t(uint32_t(phys)) * page_elems + size_t((slot_k & pmask) * tok_stride);
-        ks = kbase + off + koff[i];
-        vs = vbase + off + voff[i];
+        const uint32_t phys = uint32_t(pg_s[(slot_k >> p.page_shift) - pg0]);
+        const uint64_t pgo = uint64_t(phys) * page_b;
+        const uint32_t in_pg = uint32_t(slot_k & pmask) * tok_b;
+        ks = kbase + pgo + (in_pg + koff[i]);
+        vs = vbase + pgo + (in_pg + voff[i]);
       } else {
         const bool in = slot_k < key_hi;
-        const int phys = pg_s[in ? (slot_k >> p.page_shift) - pg0 : 0];
-        const bool ok = in && unsigned(phys) < unsigned(p.num_pages);
-        const size_t off = size_t(uint32_t(phys)) * page_elems + size_t((slot_k & pmask) * tok_stride);
-        ks = ok ? kbase + off + koff[i] : p.zeros + koff[i];
-        vs = ok ? vbase + off + voff[i] : p.zeros + voff[i];
+        const uint32_t phys = uint32_t(pg_s[in ? (slot_k >> p.page_shift) - pg0 : 0]);
+        const bool ok = in && phys < unsigned(p.num_pages);
+        const uint64_t pgo = uint64_t(phys) * page_b;
+        const uint32_t in_pg = uint32_t(slot_k & pmask) * tok_b;
+        ks = ok ? kbase + pgo + (in_pg + koff[i]) : zbase + koff[i];
+        vs = ok ? vbase + pgo + (in_pg + voff[i]) : zbase + voff[i];
       }
       const int sub = wave + NW * i;
-      load_to_lds16(ks, sb + sub * 1024);
-      load_to_lds16(vs, sb + TILE_B + sub * 1024);
+      load_to_lds16(reinterpret_cast<const void*>(ks), sb + sub * 1024);
+      load_to_lds16(reinterpret_cast<const void*>(vs), sb + TILE_B + sub * 1024);
     }
   };
 
@@ -667,6 +681,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * 2) tree_attn_fp8_kernel(Attn
   static_assert(PW >= 2 && PW * NW == 2 * NLD, "each wave loads whole K/V row groups");
   static_assert(NS == 2 * SPS, "two steps in the ring");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * STAGE_B];
+  const uint32_t ring_lds = lds_addr(ring);
   __shared__ uint64_t anc_s[65];
   extern __shared__ int pg_s[];
 
@@ -811,7 +826,7 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * 2) tree_attn_fp8_kernel(Attn
   }
   auto issue = [&](int tile, int slot) {
     const int st = key_lo + tile * kTile8;
-    unsigned char* sb = ring + slot * STAGE_B;
+    const uint32_t sb = ring_lds + slot * STAGE_B;
     const bool full = pages_ok && st + kTile8 <= key_hi;
 #pragma unroll
     for (int i = 0; i < PH; ++i) {
@@ -1200,6 +1215,8 @@ int32_t check_shapes(int32_t B, int32_t max_T, int32_t Hq, int32_t Hkv, int32_t 
   if ((long long)max_pages * page < max_T)
     return fail(SPEC_E_INVAL, "spec_tree_attention: page table holds %lld slots < max_T=%d", (long long)max_pages * page, max_T);
   if ((long long)max_pages * page > (1LL << 30)) return fail(SPEC_E_UNSUPPORTED, "spec_tree_attention: more than 2^30 slots per sequence");
+  if ((long long)Hkv * d * 2 * page >= (1LL << 31))
+    return fail(SPEC_E_UNSUPPORTED, "spec_tree_attention: a page of Hkv=%d heads x %d slots spans 2^31 bytes or more", Hkv, page);
   return SPEC_OK;
 }
 
