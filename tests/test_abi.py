@@ -74,6 +74,9 @@ def test_attention_host_validation(lib):
     assert _attn(lib, ws_bytes=16) == SPEC_E_WORKSPACE
     assert _attn(lib, ptr=(1 << 20) + 2) == SPEC_E_INVAL  # misaligned
     assert _attn(lib, scale=float("nan")) == SPEC_E_INVAL
+    # in-page load offsets are 32-bit: a page of 32768 heads x 1024 slots x 256 bytes is refused
+    assert _attn(lib, Hq=32768, Hkv=32768, page=1024) == SPEC_E_UNSUPPORTED
+    assert b"2^31" in lib.spec_last_error()
     assert lib.spec_tree_attention(None, None, None, None, None, None, None, 1, 9, 8, 2, 128, 16, 64, 64, 0.1, None,
                                    None, None, None, 0, None) == SPEC_E_INVAL
 
