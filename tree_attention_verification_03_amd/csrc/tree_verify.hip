@@ -322,6 +322,36 @@ __device__ __forceinline__ u128 res_sum(uint64_t sp, uint64_t sq, uint64_t S_Q, 
   return u128(S_Q) * sp - u128(gamma) * sq;
 }
 
+// x + y after a row swap of the pair: the 32-lane swap exchanges the upper half of x with the lower half of y,
+// so lanes 0-31 get x summed with its xor-32 partner and lanes 32-63 get y summed likewise (the 16-lane swap:
+// even 16-lane rows x, odd rows y, over the xor-16 partners)
+template <bool HALVES>
+__device__ __forceinline__ uint64_t swap_add_u64(uint64_t x, uint64_t y) {
+  const uint32_t xl = uint32_t(x), xh = uint32_t(x >> 32), yl = uint32_t(y), yh = uint32_t(y >> 32);
+  const auto l = HALVES ? __builtin_amdgcn_permlane32_swap(xl, yl, false, false) : __builtin_amdgcn_permlane16_swap(xl, yl, false, false);
+  const auto h = HALVES ? __builtin_amdgcn_permlane32_swap(xh, yh, false, false) : __builtin_amdgcn_permlane16_swap(xh, yh, false, false);
+  return ((uint64_t(uint32_t(h[0])) << 32) | uint32_t(l[0])) + ((uint64_t(uint32_t(h[1])) << 32) | uint32_t(l[1]));
+}
+
+// the wave sums of 8 u64 values at once: lane l returns the sum of v[l / 8] over the wave. A transposing
+// butterfly halves the values held per lane at each step (32-lane halves, 16-lane rows, 8-lane halves of a row
+// by rotation: each step pairs lanes that differ in the bit that selects which value they keep), then sums the
+// 8 lanes left (half-row mirror, quad): about a third of the instructions of 8 separate sums
+__device__ __forceinline__ uint64_t wave_sum8_u64(const uint64_t (&v)[8]) {
+  constexpr int kRor8 = 0x128;  // row_ror:8 (xor 8 inside a 16-lane row)
+  const int lane = threadIdx.x & 63;
+  uint64_t w[4], u[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = swap_add_u64<true>(v[j], v[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) u[j] = swap_add_u64<false>(w[j], w[j + 2]);
+  const bool b3 = (lane & 8) != 0;
+  uint64_t x = (b3 ? u[1] : u[0]) + dpp_u64<kRor8>(b3 ? u[0] : u[1]);
+  x += dpp_u64<dpp::kHalfMirror>(x);
+  x += dpp_u64<dpp::kXor1>(x);
+  return x + dpp_u64<dpp::kXor2>(x);
+}
+
 __device__ __forceinline__ u128 shfl_xor_u128(u128 x, int o) {
   const uint64_t lo = __shfl_xor(uint64_t(x), o, kWave);
   const uint64_t hi = __shfl_xor(uint64_t(x >> 64), o, kWave);
@@ -1070,17 +1100,22 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
       }
     }
   };
-  // per group: the wave's sums; undecided elements (bit 4 i + k of amb) are added in a second, rare pass
+  // per group: the wave's sums, four groups' P and Q sums per transposed reduction; undecided elements (bit
+  // 4 i + k of amb) are added in a second, rare pass
+  static_assert(NG % 4 == 0, "groups in fours");
   uint32_t amb = 0;
 #pragma unroll
-  for (int i = 0; i < NG; ++i) {
-    uint64_t sp, sq;
-    amb |= fast(x[i], y[i], i, sp, sq) << (4 * i);
-    sp = wave_sum_u64(sp);
-    sq = wave_sum_u64(sq);
-    if (lane == 0) {
-      gsp_s[wave][i] = sp;
-      gsq_s[wave][i] = sq;
+  for (int h = 0; h < NG; h += 4) {
+    uint64_t gs[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amb |= fast(x[h + i], y[h + i], h + i, gs[i], gs[4 + i]) << (4 * (h + i));
+    const uint64_t tot = wave_sum8_u64(gs);
+    const int j = lane >> 3;  // value j: the sum of P (j < 4) or of Q of group h + j % 4
+    if ((lane & 7) == 0) {
+      if (j < 4)
+        gsp_s[wave][h + j] = tot;
+      else
+        gsq_s[wave][h + j - 4] = tot;
     }
   }
   if (__syncthreads_or(amb != 0u)) {
@@ -1096,24 +1131,28 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
     }
     __syncthreads();
   }
-  if (tid == 0) {
-    u128 run = 0;
-    int g = NG - 1;
-    for (int i = 0; i < NG; ++i) {
+  if (wave == 0) {  // group i's residual mass in lane i, an inclusive scan over the NG lanes, the first to pass rem
+    u128 t = 0;
+    if (lane < NG) {
       uint64_t sp = 0, sq = 0;
       for (int q = 0; q < kWaves; ++q) {
-        sp += gsp_s[q][i];
-        sq += gsq_s[q][i];
+        sp += gsp_s[q][lane];
+        sq += gsq_s[q][lane];
       }
-      const u128 t = res_sum(sp, sq, S_Q, gamma, plain);
-      if (run + t > rem) {
-        g = i;
-        break;
-      }
-      run += t;
+      t = res_sum(sp, sq, S_Q, gamma, plain);
     }
-    grp_s = g;
-    grem_s = rem - run;
+    u128 incl = t;
+#pragma unroll
+    for (int o = 1; o < NG; o <<= 1) {
+      const u128 up = shfl_up_u128(incl, o);
+      if (lane >= o) incl += up;
+    }
+    const uint64_t over = __ballot(lane < NG && incl > rem);
+    const int g = over ? __builtin_ctzll(over) : NG - 1;  // NG - 1: unreachable with exact sums
+    if (lane == g) {
+      grp_s = g;
+      grem_s = rem - (incl - t);
+    }
   }
   __syncthreads();
   const int g = __builtin_amdgcn_readfirstlane(grp_s);
