@@ -194,7 +194,9 @@ int32_t spec_tree_mask(const int32_t* parents, const int32_t* T_b, int32_t B, in
  * status   uint32 [B] or NULL: INVALID_PARENT / INVALID_PAGE / INVALID_LENGTH (OR-ed in)
  * sm_scale softmax scale (typically 1/sqrt(d)).
  * Supported: d in {64, 128}; page a power of two in [1, 1024]; 1 <= max_T <= 65;
- * Hq % Hkv == 0 and G <= 16. bf16 inputs, fp32 accumulation and softmax.
+ * Hq % Hkv == 0 and G <= 16; a page (page x Hkv x d x 2 bytes) under 2^31 bytes.
+ * q, k_pages, v_pages and out 16-byte aligned (else SPEC_E_INVAL). bf16 inputs,
+ * fp32 accumulation and softmax.
  * ------------------------------------------------------------------------- */
 size_t spec_tree_attention_workspace_size(int32_t B, int32_t max_T, int32_t Hq, int32_t Hkv, int32_t d,
                                           int32_t page, int32_t max_pages);

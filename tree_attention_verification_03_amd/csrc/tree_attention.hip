@@ -43,6 +43,8 @@ constexpr int kXcds = 8;  // MI355X: 8 XCDs, each with its own L2
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -153,10 +155,10 @@ constexpr int blocks_per_cu(int D, int NS) { return NS * 128 * D + 4096 <= 160 *
 // the item's normalised output (stored fp16 times a power-of-two row scale). A thread owns 4 columns (o).
 struct RowMerge {
   float mx = -INFINITY, ls = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  f32x8 o = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // fold the first `navail` of a batch of CB items (the rest are unused loads and may hold anything)
   template <int CB>
-  __device__ __forceinline__ void fold(const float (&mi)[CB], const float (&li)[CB], const f32x4 (&ai)[CB], int navail) {
+  __device__ __forceinline__ void fold(const float (&mi)[CB], const float (&li)[CB], const f32x8 (&ai)[CB], int navail) {
     float mb = mx;
 #pragma unroll
     for (int u = 0; u < CB; ++u)
@@ -175,14 +177,14 @@ struct RowMerge {
     }
     mx = mb;
   }
-  // out / lse of packed row r (node r / G, head g G + r % G) of sequence b, KV head g; columns 4c..4c+3
+  // out / lse of packed row r (node r / G, head g G + r % G) of sequence b, KV head g; columns 8c..8c+7
   template <int D>
   __device__ __forceinline__ void write(const AttnParams& p, int b, int g, int r, int c) const {
     const int i = r / p.G, h = g * p.G + (r - i * p.G);
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
-    const f32x4 v = o * inv;
-    *reinterpret_cast<uint2*>(p.out + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 4 * c) =
-        make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
+    const f32x8 v = o * inv;
+    *reinterpret_cast<uint4*>(p.out + ((size_t(b) * p.max_T + i) * p.Hq + h) * D + 8 * c) =
+        make_uint4(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]), pack2_bf16(v[6], v[7]));
     constexpr float kLn2 = 0.69314718055994530942f;
     if (p.lse && c == 0) p.lse[(size_t(b) * p.max_T + i) * p.Hq + h] = ls > 0.f ? (mx + __log2f(ls)) * kLn2 : -INFINITY;
   }
@@ -1025,10 +1027,13 @@ __global__ void __launch_bounds__(64 * NW, NW / 4 * 2) tree_attn_fp8_kernel(Attn
 // KNOWN: the lengths are loaded first and only the sequence's own items are read (one more round trip,
 // used for batches of many sequences, whose lengths may differ: a short sequence then reads its one or
 // two items instead of every slot of the longest).
+// rows of partials per 64-thread combine block (D / 8 threads per row, 8 columns each)
+constexpr int combine_rpb(int D) { return 64 / (D / 8); }
+
 template <int D, bool KNOWN>
 __global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
-  constexpr int TPR = D / 4;     // threads per row
-  constexpr int RPB = 64 / TPR;  // rows per block
+  constexpr int TPR = D / 8;     // threads per row (8 columns each)
+  constexpr int RPB = combine_rpb(D);
   constexpr int CB = 16;         // items per batch at most
   const int tid = threadIdx.x;
   const int rsub = tid / TPR, c = tid - rsub * TPR;
@@ -1053,7 +1058,7 @@ __global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
 #pragma unroll 1
     for (int ib = 0; ib < n_items; ib += CBV) {
       float mi[CBV], li[CBV];
-      f32x4 ai[CBV];
+      f32x8 ai[CBV];
 #pragma unroll
       for (int u = 0; u < CBV; ++u) {
         const int item = KNOWN ? min(ib + u, n_items - 1) : min(ib + u, p.n_splits - 1);
@@ -1061,8 +1066,8 @@ __global__ void __launch_bounds__(64) tree_attn_combine(AttnParams p) {
         mi[u] = base[size_t(TR) * (D / 2) + row];
         li[u] = base[size_t(TR) * (D / 2 + 1) + row];
         const float scu = base[size_t(TR) * (D / 2 + 2) + row];
-        const uint2 h = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + size_t(row) * D + 4 * c);
-        ai[u] = __builtin_convertvector(__builtin_bit_cast(f16x4, h), f32x4) * scu;
+        const uint4 h = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + size_t(row) * D + 8 * c);
+        ai[u] = __builtin_convertvector(__builtin_bit_cast(f16x8, h), f32x8) * scu;
       }
       if (!KNOWN && ib == 0) {
         const int T = min(max(T_raw, 1), p.max_T);
@@ -1243,8 +1248,9 @@ static int32_t attention_validate(const char* who, const void* q, const void* k_
     return fail(SPEC_E_INVAL, "%s: null tensor pointer", who);
   if (num_pages < 1) return fail(SPEC_E_INVAL, "%s: num_pages=%d", who, num_pages);
   if (!(sm_scale > 0.f) || !std::isfinite(sm_scale)) return fail(SPEC_E_INVAL, "%s: sm_scale must be finite and > 0", who);
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages)) & 15)
-    return fail(SPEC_E_INVAL, "%s: q, k_pages and v_pages must be 16-byte aligned", who);
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pages) | reinterpret_cast<uintptr_t>(v_pages) |
+       reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(SPEC_E_INVAL, "%s: q, k_pages, v_pages and out must be 16-byte aligned", who);
   *pl = make_plan(B, max_T, Hq, Hkv, d, page, max_pages, fp8);
   return SPEC_OK;
 }
@@ -1337,7 +1343,7 @@ static int32_t attention_launch(const AttnPlan& pl, const void* q, const void* k
   const bool known = B >= 8 && pl.n_splits >= 8;
   if (d == 64) {
     launch_d<64>(pl, prm, grid, st);
-    const dim3 cgrid(unsigned((rows_used + 3) / 4), unsigned(pl.n_rb * B * Hkv));
+    const dim3 cgrid(unsigned((rows_used + combine_rpb(64) - 1) / combine_rpb(64)), unsigned(pl.n_rb * B * Hkv));
     if (pl.n_splits > 1) {
       if (known)
         hipLaunchKernelGGL((tree_attn_combine<64, true>), cgrid, dim3(64), 0, st, prm);
@@ -1351,7 +1357,7 @@ static int32_t attention_launch(const AttnPlan& pl, const void* q, const void* k
       hipLaunchKernelGGL((tree_attn_fp8_kernel<8, 4>), grid, dim3(512), pl.lds_dyn, st, prm);
     else
       hipLaunchKernelGGL((tree_attn_fp8_kernel<4, 4>), grid, dim3(256), pl.lds_dyn, st, prm);
-    const dim3 cgrid(unsigned((rows_used + 1) / 2), unsigned(pl.n_rb * B * Hkv));
+    const dim3 cgrid(unsigned((rows_used + combine_rpb(128) - 1) / combine_rpb(128)), unsigned(pl.n_rb * B * Hkv));
     if (pl.n_splits > 1) {
       if (known)
         hipLaunchKernelGGL((tree_attn_combine<128, true>), cgrid, dim3(64), 0, st, prm);
