@@ -496,6 +496,31 @@ def test_verify_degenerate_rows():
     assert host["status"][0] & 4 and host["status"][2] & 2 and host["status"][6] & 1
 
 
+def test_verify_nan_in_draft_rows():
+    """A NaN in the q row of a sampling node with children sets NAN_INPUT; in the q row of a childless node it
+    is never read (that node decides nothing) and sets nothing."""
+    w, trees, tok, par, qr = _small_verify_workload(5, "sample", V=1000, B=6)
+    draft = w.draft_probs.copy()
+    flagged, quiet = 0, 0
+    for b in range(w.B):
+        T = int(w.T_b[b])
+        kids = {int(x) for x in par[b, 1:T]}
+        rows_kids = {int(qr[b, u]) for u in range(T) if u in kids and qr[b, u] >= 0}
+        rows_lone = {int(qr[b, u]) for u in range(T) if u not in kids and qr[b, u] >= 0} - rows_kids
+        if rows_lone:
+            draft[b, min(rows_lone), 3] = np.nan
+            quiet += 1
+        elif b % 2 == 0 and rows_kids:
+            draft[b, min(rows_kids), 3] = np.nan
+            flagged += 1
+    assert flagged and quiet
+    w.draft_probs = draft
+    log("[verify] NaN in draft rows")
+    host = _verify(w, tok, par, qr)
+    check_verify(w, host, trees, tokens=tok, parents=par, q_row=qr)
+    assert sum(int(host["status"][b]) & 4 != 0 for b in range(w.B)) == flagged
+
+
 def test_verify_root_only_trees():
     w = make_workload(name="verify", B=4, Hq=2, Hkv=1, d=64, prefix=16, topk=1, depth=1, num_draft=[0, 0, 1, 0],
                       V=128256, verify="alternate", seed=11)

@@ -282,11 +282,13 @@ __device__ __forceinline__ void greedy_slice(const VerifyWs& w, const VerifyArgs
 
 // ------------------------------------------------------------------ sampling
 __device__ __forceinline__ uint32_t fx(float x) {
-  // 2^-32 fixed point: 0 for NaN / x <= 0, 2^32-1 for x >= 1, floor(x * 2^32) otherwise. Branch-free: the operand
-  // is clamped into [0, 1 - 2^-24] (NaN -> 0; the identity on (0, 1)), scaled exactly by 2^32 and truncated
-  const float c = fminf(fmaxf(x, 0.f), 0.99999994f);
-  const uint32_t f = uint32_t(c * 4294967296.0f);
-  return x >= 1.f ? 0xffffffffu : f;
+  // 2^-32 fixed point: 0 for NaN / x <= 0, 2^32-1 for x >= 1, floor(x * 2^32) otherwise. x * 2^32 is exact (a
+  // power-of-two scaling) and the hardware conversion truncates and clamps (NaN and negatives to 0, 2^32 and
+  // above to 2^32 - 1): two instructions. C++ leaves an out-of-range conversion undefined, hence the
+  // instruction itself
+  uint32_t r;
+  asm("v_cvt_u32_f32 %0, %1" : "=v"(r) : "v"(x * 4294967296.0f));
+  return r;
 }
 
 __device__ __forceinline__ u128 mul64x32(uint64_t a, uint32_t b) {
@@ -554,34 +556,46 @@ __device__ __forceinline__ void sample_slice(const VerifyWs& w, const VerifyArgs
   uint8_t* const sbin_w = sbin_s + (tid >> 6) * kCapW;
   uint32_t run = 0;  // the wave's window elements so far (wave-uniform)
   uint64_t sp = 0, sq = 0, am = 0, hp = 0, hq = 0;
-  uint32_t nan = 0;
-  slice_for<VEC>(prow, qrow, lo, hi, [&] { return prob_row<LG>(a, node); }, [&](int v, float x, float y) {
-    nan |= (x != x ? 1u : 0u) | (y != y ? 2u : 0u);
-    const uint32_t P = fx(x), Q = fx(y);
-    sp += P;
-    sq += Q;
-    const uint64_t k = (uint64_t(P) << 32) | uint64_t(0xffffffffu - uint32_t(v));
-    am = k > am ? k : am;
-    if (win) {
-      const int bin = win_bin(P, Q);
-      if (bin == kWinHi) {
-        hp += P;
-        hq += Q;
+  uint64_t nanp = 0, nanq = 0;  // lanes that met a NaN in p / q (wave-uniform ballots)
+  const auto pre = [&] { return prob_row<LG>(a, node); };
+  if (qrow) {
+    slice_for<VEC>(prow, qrow, lo, hi, pre, [&](int v, float x, float y) {
+      nanp |= __ballot(x != x);
+      nanq |= __ballot(y != y);
+      const uint32_t P = fx(x), Q = fx(y);
+      sp += P;
+      sq += Q;
+      const uint64_t k = (uint64_t(P) << 32) | uint64_t(0xffffffffu - uint32_t(v));
+      am = k > am ? k : am;
+      if (win) {
+        const int bin = win_bin(P, Q);
+        if (bin == kWinHi) {
+          hp += P;
+          hq += Q;
+        }
+        const bool in = bin >= 0 && bin < kWinBins;
+        const uint64_t m = __ballot(in);
+        const uint32_t pos = run + uint32_t(__popcll(m & ((1ull << lane) - 1)));
+        if (in && pos < kCapW) {
+          stage_w[pos] = (uint64_t(P) << 32) | Q;
+          sbin_w[pos] = uint8_t(bin);
+        }
+        run += uint32_t(__popcll(m));
       }
-      const bool in = bin >= 0 && bin < kWinBins;
-      const uint64_t m = __ballot(in);
-      const uint32_t pos = run + uint32_t(__popcll(m & ((1ull << lane) - 1)));
-      if (in && pos < kCapW) {
-        stage_w[pos] = (uint64_t(P) << 32) | Q;
-        sbin_w[pos] = uint8_t(bin);
-      }
-      run += uint32_t(__popcll(m));
-    }
-  });
+    });
+  } else {  // no q row (a childless node, or none given): p's sums, argmax and NaN bit only
+    slice_for<VEC>(prow, nullptr, lo, hi, pre, [&](int v, float x, float) {
+      nanp |= __ballot(x != x);
+      const uint32_t P = fx(x);
+      sp += P;
+      const uint64_t k = (uint64_t(P) << 32) | uint64_t(0xffffffffu - uint32_t(v));
+      am = k > am ? k : am;
+    });
+  }
   if (win && lane == 0) wn_s[tid >> 6] = run;
   am = wave_max_u64(am);
   // NaN bits travel through the block sum as counts (lane 0 of each wave): p in bits 0-3, q in bits 4-7
-  const uint32_t nw = wave_or_u32(nan);
+  const uint32_t nw = (nanp ? 1u : 0u) | (nanq ? 2u : 0u);
   uint64_t nn = lane == 0 ? uint64_t(nw & 1u) + ((nw & 2u) ? 16u : 0u) : 0u;
   if (lane == 0) amr[tid >> 6] = am;
   if (win) {
