@@ -28,7 +28,13 @@
  *     matching *_workspace_size() returns for the same arguments. A workspace
  *     must be zero-filled before its FIRST use; every call leaves the parts
  *     that must start at zero at zero again, so it can be reused without
- *     clearing. Calls that share one workspace must not overlap in time.
+ *     clearing by calls with the same shape arguments (tree build: B,
+ *     max_topk, max_depth; verification: B, max_T, V). A build or
+ *     verification workspace passed to a call of another shape must be
+ *     zero-filled again first: the parts that must start at zero move with
+ *     the shape. Attention workspaces keep those parts at fixed offsets and
+ *     can be reused by calls of any shape. Calls that share one workspace
+ *     must not overlap in time.
  *
  * Notation: B sequences; node 0 of a tree is the root (the last emitted token,
  * whose KV the target writes in the same forward pass) and nodes 1..N are
