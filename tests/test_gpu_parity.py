@@ -73,6 +73,40 @@ def _run_attention(w, parents):
     return to_np(out), to_np(lse), to_np(status)
 
 
+def test_attention_workspace_reused_across_shapes(monkeypatch):
+    """One workspace, zero-filled once, serves attention calls of different shapes in turn (split-K on): its
+    zero row sits at a fixed offset and nothing else in it has to start at zero, so every call's outputs are
+    bit-identical to those of the same call with a fresh workspace."""
+    from tree_attention_verification_03_amd import ops
+    from tree_attention_verification_03_amd.pipeline import DeviceWorkload
+
+    monkeypatch.setenv("SPEC_TREE_ATTN_CHUNK", "128")
+    shapes = [(2, 8, 2, 128, [700, 1500], [9, 33], 16, "random", 31), (3, 16, 4, 128, [2100, 64, 999], [17, 5, 65],
+                                                                          16, "chain", 32)]
+    cases = []
+    for B, Hq, Hkv, d, prefix, T, page, kind, seed in shapes:
+        w, parents = _attn_case(B, Hq, Hkv, d, prefix, T, page, kind, seed)
+        fresh = _run_attention(w, parents)
+        cases.append((w, parents, fresh))
+    dev = torch.device("cuda:0")
+    size = max(ops.spec_tree_attention_workspace_size(w.B, w.max_T, w.Hq, w.Hkv, w.d, w.page, w.max_pages)
+               for w, _, _ in cases)
+    ws = torch.zeros(size, dtype=torch.uint8, device=dev)
+    for i in (0, 1, 0, 1):
+        w, parents, fresh = cases[i]
+        dw = DeviceWorkload(w)
+        out = torch.full((w.B, w.max_T, w.Hq, w.d), float("nan"), dtype=torch.bfloat16, device=dev)
+        lse = torch.zeros(w.B, w.max_T, w.Hq, dtype=torch.float32, device=dev)
+        status = torch.zeros(w.B, dtype=torch.int32, device=dev)
+        log(f"[attn] shared workspace, shape {i}")
+        ops.spec_tree_attention(dw.q, dw.k_pages, dw.v_pages, dw.page_table, dw.prefix_lens,
+                                torch.from_numpy(parents).to(dev), dw.T_b, w.sm_scale, out, lse, status, ws=ws)
+        torch.cuda.synchronize()
+        got = (to_np(out), to_np(lse), to_np(status))
+        for a, b in zip(got, fresh):
+            assert np.array_equal(np.nan_to_num(a.astype(np.float32), nan=7.0), np.nan_to_num(b.astype(np.float32), nan=7.0))
+
+
 @pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
 def test_attention_small(case, monkeypatch):
     name, B, Hq, Hkv, d, prefix, T, page, kind, chunk = case
