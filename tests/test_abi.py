@@ -73,6 +73,11 @@ def test_attention_host_validation(lib):
     assert _attn(lib, page=12) == SPEC_E_UNSUPPORTED
     assert _attn(lib, ws_bytes=16) == SPEC_E_WORKSPACE
     assert _attn(lib, ptr=(1 << 20) + 2) == SPEC_E_INVAL  # misaligned
+    # out alone 8-byte aligned: the merge writes 16-byte rows
+    p16, p8 = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 8)
+    assert lib.spec_tree_attention(p16, p16, p16, p16, p16, p16, None, 1, 9, 8, 2, 128, 16, 64, 64, 0.1, p8, None, None,
+                                   p16, 1 << 30, None) == SPEC_E_INVAL
+    assert b"out" in lib.spec_last_error()
     assert _attn(lib, scale=float("nan")) == SPEC_E_INVAL
     # in-page load offsets are 32-bit: a page of 32768 heads x 1024 slots x 256 bytes is refused
     assert _attn(lib, Hq=32768, Hkv=32768, page=1024) == SPEC_E_UNSUPPORTED
