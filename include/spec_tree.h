@@ -24,17 +24,19 @@
  *   - Problems in the DATA (which the host cannot see) never abort: they are
  *     reported in per-sequence `status` words (SPEC_STATUS_* bits) and have
  *     the defined fallbacks documented below.
- *   - Workspaces: caller-allocated device memory of at least the size the
- *     matching *_workspace_size() returns for the same arguments. A workspace
- *     must be zero-filled before its FIRST use; every call leaves the parts
- *     that must start at zero at zero again, so it can be reused without
- *     clearing by calls with the same shape arguments (tree build: B,
- *     max_topk, max_depth; verification: B, max_T, V). A build or
- *     verification workspace passed to a call of another shape must be
- *     zero-filled again first: the parts that must start at zero move with
- *     the shape. Attention workspaces keep those parts at fixed offsets and
- *     can be reused by calls of any shape. Calls that share one workspace
- *     must not overlap in time.
+ *   - Workspaces: caller-allocated device memory (ws, ws_bytes) of at least
+ *     the size the matching *_workspace_size() returns for the same
+ *     arguments. A workspace must be zero-filled before its FIRST use; every
+ *     call leaves the parts that must start at zero at zero again. Those
+ *     parts and the rest sit at opposite ends of ws_bytes (tree build: the
+ *     pool at the start, tickets at the end; verification: keys, flags and
+ *     tickets at the start, the rest at the end; attention: fixed offsets),
+ *     so one zero-filled workspace serves calls of several shapes without
+ *     clearing when ws_bytes is at least the *_workspace_size() of each
+ *     call's V (verification) taken with the largest B, max_T, max_topk and
+ *     max_depth of the calls. The steps and finish of one tree build pass
+ *     the same ws and ws_bytes. Calls that share one workspace must not
+ *     overlap in time.
  *
  * Notation: B sequences; node 0 of a tree is the root (the last emitted token,
  * whose KV the target writes in the same forward pass) and nodes 1..N are
@@ -327,7 +329,7 @@ int32_t spec_tree_verify(const float* target, const float* draft_probs, const in
  * probabilities NaN.
  * Other arguments, outputs and errors as spec_tree_verify. The workspace
  * (spec_tree_verify_logits_workspace_size) also holds the slices' partials:
- * 8 bytes per 8192 logits beyond the verify workspace. Requires
+ * 8 bytes per 8192 logits beyond the verify workspace, at its end. Requires
  * B * max_T <= 65535.
  * ------------------------------------------------------------------------- */
 size_t spec_tree_verify_logits_workspace_size(int32_t B, int32_t max_T, int32_t V);

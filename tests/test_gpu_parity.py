@@ -714,7 +714,7 @@ def test_graph_replay_matches_eager(from_logits, draft_vocab):
 
 
 # ---------------------------------------------------------------- verification from logits
-def _verify_logits(w, tokens, parents, q_row, logits, draft, temperature):
+def _verify_logits(w, tokens, parents, q_row, logits, draft, temperature, ws=None):
     from tree_attention_verification_03_amd import ops
 
     dev = torch.device("cuda")
@@ -729,7 +729,7 @@ def _verify_logits(w, tokens, parents, q_row, logits, draft, temperature):
     mode = torch.from_numpy(w.modes.astype(np.int8)).to(dev)
     ops.spec_tree_verify_logits(lg, temp, dr, i32(q_row), i32(tokens), i32(parents), i32(w.T_b), mode, w.philox_key,
                                 w.philox_offset, outs["accept_len"], outs["accept_nodes"], outs["out_tokens"],
-                                outs["status"])
+                                outs["status"], ws)
     torch.cuda.synchronize()
     return {k: to_np(v) for k, v in outs.items()}
 
@@ -779,6 +779,65 @@ def test_verify_logits_planted(seed, verify, fast, monkeypatch):
     again = _verify_logits(w, tok, par, qr, logits, draft, w.temperature)
     for k in host:
         assert np.array_equal(host[k], again[k]), f"repeat differs: {k}"
+
+
+def test_verify_and_build_workspaces_reused_across_shapes():
+    """One verification workspace and one build workspace, each zero-filled once, serve calls of several shapes
+    in turn: greedy and sampling sequences, rows with window records (V <= 131072) and without, and the logits
+    entry point. The parts that must start at zero sit at one end of the buffer and the rest of every call's
+    data at the other, so each verification's outputs are bit-identical to the same call's with a fresh workspace
+    and each build's tree is the oracle's."""
+    from tree_attention_verification_03_amd import ops
+    from tree_attention_verification_03_amd.pipeline import DeviceWorkload, SpecTreeStep
+
+    dev = torch.device("cuda:0")
+    cases = []  # (workload, tokens, parents, q_row, logits inputs or None, fresh outputs)
+    for seed, verify, V, B, logits in ((1, "alternate", 1000, 6, False), (2, "sample", 140000, 3, False),
+                                       (3, "alternate", 4096, 8, True), (4, "greedy", 333, 2, False)):
+        w, trees, tok, par, qr = _small_verify_workload(seed, verify, V=V, B=B, temperature=0.8)
+        if logits:
+            lin = (w.target_logits.copy(), w.draft_probs.copy(), w.temperature)
+            fresh = _verify_logits(w, tok, par, qr, *lin)
+            _check_logits(w, fresh, tok, par, qr, *lin)
+        else:
+            lin = None
+            fresh = _verify(w, tok, par, qr)
+            check_verify(w, fresh, trees, tokens=tok, parents=par, q_row=qr)
+        cases.append((w, tok, par, qr, lin, fresh))
+    Bm, Tm = max(c[0].B for c in cases), max(c[0].max_T for c in cases)
+    size = max((ops.spec_tree_verify_logits_workspace_size if c[4] else ops.spec_tree_verify_workspace_size)(
+        Bm, Tm, c[0].V) for c in cases)
+    ws = torch.zeros(size, dtype=torch.uint8, device=dev)
+    for i in (0, 1, 2, 3, 1, 0, 3, 2, 0):
+        w, tok, par, qr, lin, fresh = cases[i]
+        log(f"[verify] shared workspace, case {i}")
+        got = _verify_logits(w, tok, par, qr, *lin, ws=ws) if lin else _verify(w, tok, par, qr, ws=ws)
+        for k in fresh:
+            assert np.array_equal(got[k], fresh[k]), f"case {i}: {k} differs from a fresh workspace"
+
+    builds = []
+    for seed, B, mt, md, V in ((11, 3, 8, 6, 1000), (12, 7, 4, 3, 4099), (13, 2, 6, 5, 50)):
+        rng = np.random.default_rng(seed)
+        topk = [min(int(k), V) for k in rng.integers(1, mt + 1, size=B)]
+        depth = rng.integers(1, md + 1, size=B).tolist()
+        nd = [int(rng.integers(1, min(k + (D - 1) * k * k, 64) + 1)) for k, D in zip(topk, depth)]
+        w = make_workload(name="build", B=B, Hq=2, Hkv=1, d=64, prefix=16, topk=topk, depth=depth, num_draft=nd,
+                          V=V, seed=seed, max_topk=mt, max_depth=md)
+        step = SpecTreeStep(DeviceWorkload(w), fused_finish=seed != 12)
+        builds.append((w, step, oracle_trees(w)))
+    size = ops.spec_tree_build_workspace_size(max(b[0].B for b in builds), max(b[0].max_topk for b in builds),
+                                              max(b[0].max_depth for b in builds))
+    ws = torch.zeros(size, dtype=torch.uint8, device=dev)
+    keys = ("tokens", "parents", "depth", "anc", "q_row", "frontier")
+    for i in (0, 1, 2, 1, 0, 2):
+        w, step, trees = builds[i]
+        for k in keys:
+            getattr(step.o, k).fill_(-5)
+        step.ws_build = ws
+        log(f"[build] shared workspace, case {i}")
+        step.build()
+        torch.cuda.synchronize()
+        check_build(w, {k: to_np(getattr(step.o, k)) for k in keys}, trees)
 
 
 # rows of more than 64 softmax slices (V > 524288): each lane of a wave merges several slice partials

@@ -55,7 +55,12 @@ size_t pool_cap(int max_topk, int max_depth) {
   return size_t(max_topk) + size_t(max_depth - 1) * max_topk * max_topk;
 }
 
-BuildWs carve(void* ws, int B, int max_topk, int max_depth, size_t* total) {
+// The pool, frontier and candidates, which carry a build from step to step, sit at the start of the
+// workspace; the tickets, the only part that must start at zero, sit at the end of its ws_bytes. A workspace
+// zero-filled once therefore serves builds of several shapes without clearing: no build's pool lands on
+// another shape's tickets as long as ws_bytes covers the largest pool plus the largest tickets. With ws null
+// (or ws_bytes below *total) only *total is meaningful.
+BuildWs carve(void* ws, size_t ws_bytes, int B, int max_topk, int max_depth, size_t* total) {
   const size_t P = pool_cap(max_topk, max_depth);
   char* c = static_cast<char*>(ws);
   size_t off = 0;
@@ -72,9 +77,10 @@ BuildWs carve(void* ws, int B, int max_topk, int max_depth, size_t* total) {
   w.fslot = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * P));
   w.frontier = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * B * max_topk));
   w.fscore = reinterpret_cast<double*>(take(sizeof(double) * B * max_topk));
-  w.ticket = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * B * kTicketStride));
   w.cand = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * B * max_topk * kCand));
-  *total = off;
+  const size_t tickets = align_up(sizeof(uint32_t) * B * kTicketStride, 256);
+  *total = off + tickets;
+  w.ticket = c && ws_bytes >= *total ? reinterpret_cast<uint32_t*>(c + ((ws_bytes - tickets) & ~size_t(255))) : nullptr;
   return w;
 }
 
@@ -701,7 +707,7 @@ using namespace spectree;
 extern "C" size_t spec_tree_build_workspace_size(int32_t B, int32_t max_topk, int32_t max_depth) {
   if (check_build("spec_tree_build_workspace_size", B, max_topk, max_depth) != SPEC_OK) return 0;
   size_t total = 0;
-  carve(nullptr, B, max_topk, max_depth, &total);
+  carve(nullptr, 0, B, max_topk, max_depth, &total);
   return total;
 }
 
@@ -720,7 +726,7 @@ int32_t launch_step(const char* who, void* ws, size_t ws_bytes, int32_t step, co
   if (B > 1 && seq_stride < min_stride)
     return fail(SPEC_E_INVAL, "%s: seq_stride=%lld < %lld", who, (long long)seq_stride, (long long)min_stride);
   size_t need = 0;
-  BuildWs w = carve(ws, B, max_topk, max_depth, &need);
+  BuildWs w = carve(ws, ws_bytes, B, max_topk, max_depth, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
   const int P = int(pool_cap(max_topk, max_depth));
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -844,7 +850,7 @@ extern "C" int32_t spec_tree_build_finish(void* ws, size_t ws_bytes, const int32
   if (!root_tokens || !topk || !depth || !num_draft || !tokens || !parents || !depth_out || !anc_mask || !q_row)
     return fail(SPEC_E_INVAL, "spec_tree_build_finish: null pointer");
   size_t need = 0;
-  BuildWs w = carve(ws, B, max_topk, max_depth, &need);
+  BuildWs w = carve(ws, ws_bytes, B, max_topk, max_depth, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_finish: workspace %zu < %zu bytes", ws_bytes, need);
   const int P = int(pool_cap(max_topk, max_depth));
   const FinishArgs fa{root_tokens, num_draft, max_T, tokens, parents, depth_out, anc_mask, q_row};

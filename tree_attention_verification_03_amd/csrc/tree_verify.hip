@@ -91,7 +91,37 @@ struct VerifyWs {
 
 int sample_slices(int V) { return (V + kSampleSlice - 1) / kSampleSlice; }
 
-VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
+// the parts that need not start at zero, laid out from c (null: sizes only); returns their size
+size_t carve_data(char* c, size_t n, size_t nsl, VerifyWs& w) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = c ? c + off : nullptr;
+    off = align_up(off + bytes, 256);
+    return r;
+  };
+  w.acc_child = reinterpret_cast<int32_t*>(take(4 * n));
+  w.rstate = reinterpret_cast<uint64_t*>(take(8 * n * kRs));
+  w.nflag = reinterpret_cast<uint32_t*>(take(4 * n));
+  w.ssum = reinterpret_cast<uint64_t*>(take(8 * n * nsl));
+  w.psum = reinterpret_cast<uint64_t*>(take(24 * n * nsl));
+  w.smass = reinterpret_cast<uint64_t*>(take(16 * n * nsl));
+  w.wcnt = nullptr;
+  w.wsum = nullptr;
+  w.wel = nullptr;
+  if (nsl <= size_t(kFastMaxSl)) {
+    w.wcnt = reinterpret_cast<uint32_t*>(take(4 * n * nsl * kWinSlots));
+    w.wsum = reinterpret_cast<uint64_t*>(take(16 * n * nsl * kWinSlots));
+    w.wel = reinterpret_cast<uint64_t*>(take(8 * n * nsl * kWinCap));
+  }
+  return off;
+}
+
+// The parts that must start at zero (keys, row flags, tickets) sit at the start of the workspace, at offsets
+// set by B and max_T alone; the rest sits at the end of its ws_bytes. A workspace zero-filled once therefore
+// serves calls of several shapes without clearing: no call's data lands on another shape's zero parts as
+// long as ws_bytes covers the largest zero parts plus every call's data. With ws null (or ws_bytes below
+// *total) only *total is meaningful.
+VerifyWs carve(void* ws, size_t ws_bytes, int B, int max_T, int V, size_t* total) {
   const size_t n = size_t(B) * max_T;
   const size_t nsl = size_t(sample_slices(V));
   char* c = static_cast<char*>(ws);
@@ -104,23 +134,11 @@ VerifyWs carve(void* ws, int B, int max_T, int V, size_t* total) {
   VerifyWs w;
   w.keys = reinterpret_cast<uint64_t*>(take(8 * n * kKS));
   w.rowflag = reinterpret_cast<uint32_t*>(take(4 * n));
-  w.acc_child = reinterpret_cast<int32_t*>(take(4 * n));
-  w.rstate = reinterpret_cast<uint64_t*>(take(8 * n * kRs));
-  w.nflag = reinterpret_cast<uint32_t*>(take(4 * n));
   w.tickets = reinterpret_cast<uint32_t*>(take(4 * size_t(B) * kQ));
   w.rtick = reinterpret_cast<uint32_t*>(take(4 * n * kQ));
-  w.ssum = reinterpret_cast<uint64_t*>(take(8 * n * nsl));
-  w.psum = reinterpret_cast<uint64_t*>(take(24 * n * nsl));
-  w.smass = reinterpret_cast<uint64_t*>(take(16 * n * nsl));
-  w.wcnt = nullptr;
-  w.wsum = nullptr;
-  w.wel = nullptr;
-  if (nsl <= size_t(kFastMaxSl)) {
-    w.wcnt = reinterpret_cast<uint32_t*>(take(4 * n * nsl * kWinSlots));
-    w.wsum = reinterpret_cast<uint64_t*>(take(16 * n * nsl * kWinSlots));
-    w.wel = reinterpret_cast<uint64_t*>(take(8 * n * nsl * kWinCap));
-  }
-  *total = off;
+  const size_t data = carve_data(nullptr, n, nsl, w);
+  *total = off + data;
+  if (c && ws_bytes >= *total) carve_data(c + ((ws_bytes - data) & ~size_t(255)), n, nsl, w);
   return w;
 }
 
@@ -1579,7 +1597,7 @@ using namespace spectree;
 extern "C" size_t spec_tree_verify_workspace_size(int32_t B, int32_t max_T, int32_t V) {
   if (B < 1 || max_T < 1 || max_T > 65 || V < 1) return 0;
   size_t total = 0;
-  carve(nullptr, B, max_T, V, &total);
+  carve(nullptr, 0, B, max_T, V, &total);
   return total;
 }
 
@@ -1607,7 +1625,7 @@ static int32_t verify_impl(const char* who, const float* target, float2* sm_part
   const long long nsl = sample_slices(V);
   if (rows * nsl >= (1LL << 31)) return fail(SPEC_E_UNSUPPORTED, "%s: B*max_T*ceil(V/%d) too large", who, kSampleSlice);
   size_t need = 0;
-  VerifyWs w = carve(ws, B, max_T, V, &need);
+  VerifyWs w = carve(ws, ws_bytes, B, max_T, V, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
   // greedy slices of kGreedySlice elements (one round trip of loads per block), doubled or tripled when
   // the rows would otherwise need more blocks than a launch keeps resident (2 per CU at this kernel's
@@ -1691,17 +1709,16 @@ extern "C" int32_t spec_tree_verify(const float* target, const float* draft_prob
                      ws_bytes, stream);
 }
 
-// the logits entry point's workspace: the verify workspace, then the slices' softmax partials
-static size_t logits_part_offset(int32_t B, int32_t max_T, int32_t V) {
-  size_t total = 0;
-  carve(nullptr, B, max_T, V, &total);
-  return align_up(total, 256);
+// the logits entry point's workspace: the verify workspace, then the slices' softmax partials at its very
+// end (they need not start at zero); the verify part is everything below them
+static size_t logits_part_bytes(int32_t B, int32_t max_T, int32_t V) {
+  const size_t nsl = (size_t(V) + kSmSlice - 1) / kSmSlice;
+  return align_up(size_t(B) * max_T * nsl * sizeof(float2), 256);
 }
 
 extern "C" size_t spec_tree_verify_logits_workspace_size(int32_t B, int32_t max_T, int32_t V) {
-  if (B < 1 || max_T < 1 || max_T > 65 || V < 1) return 0;
-  const size_t nsl = (size_t(V) + kSmSlice - 1) / kSmSlice;
-  return logits_part_offset(B, max_T, V) + align_up(size_t(B) * max_T * nsl * sizeof(float2), 256);
+  const size_t verify = spec_tree_verify_workspace_size(B, max_T, V);
+  return verify ? verify + logits_part_bytes(B, max_T, V) : 0;
 }
 
 extern "C" int32_t spec_tree_verify_logits(const float* logits, const float* temperature, const float* draft_probs,
@@ -1718,7 +1735,7 @@ extern "C" int32_t spec_tree_verify_logits(const float* logits, const float* tem
   if ((long long)B * max_T > 65535) return fail(SPEC_E_UNSUPPORTED, "%s: B*max_T=%lld > 65535", who, (long long)B * max_T);
   const size_t need = spec_tree_verify_logits_workspace_size(B, max_T, V);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
-  const size_t off = logits_part_offset(B, max_T, V);
+  const size_t off = (ws_bytes - logits_part_bytes(B, max_T, V)) & ~size_t(255);
   float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + off);
   return verify_impl(who, logits, part, temperature, draft_probs, q_row, tokens, parents, T_b, mode, philox_key0, philox_key1,
                      philox_offset, B, max_T, R, V, accept_len, accept_nodes, out_tokens, status, ws, off, stream);
