@@ -24,9 +24,9 @@
  *   - Problems in the DATA (which the host cannot see) never abort: they are
  *     reported in per-sequence `status` words (SPEC_STATUS_* bits) and have
  *     the defined fallbacks documented below.
- *   - Workspaces: caller-allocated device memory (ws, ws_bytes) of at least
- *     the size the matching *_workspace_size() returns for the same
- *     arguments. A workspace must be zero-filled before its FIRST use; every
+ *   - Workspaces: caller-allocated device memory (ws, ws_bytes), 16-byte
+ *     aligned (else SPEC_E_INVAL), of at least the size the matching
+ *     *_workspace_size() returns for the same arguments. A workspace must be zero-filled before its FIRST use; every
  *     call leaves the parts that must start at zero at zero again. Those
  *     parts and the rest sit at opposite ends of ws_bytes (tree build: the
  *     pool at the start, tickets at the end; verification: keys, flags and

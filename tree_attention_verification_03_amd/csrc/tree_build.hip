@@ -728,6 +728,7 @@ int32_t launch_step(const char* who, void* ws, size_t ws_bytes, int32_t step, co
   size_t need = 0;
   BuildWs w = carve(ws, ws_bytes, B, max_topk, max_depth, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(SPEC_E_INVAL, "%s: ws must be 16-byte aligned", who);
   const int P = int(pool_cap(max_topk, max_depth));
   hipStream_t st = static_cast<hipStream_t>(stream);
   // about 256 blocks per launch, within: slices of at least 8 elements per thread and of at most
@@ -852,6 +853,7 @@ extern "C" int32_t spec_tree_build_finish(void* ws, size_t ws_bytes, const int32
   size_t need = 0;
   BuildWs w = carve(ws, ws_bytes, B, max_topk, max_depth, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "spec_tree_build_finish: workspace %zu < %zu bytes", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(SPEC_E_INVAL, "spec_tree_build_finish: ws must be 16-byte aligned");
   const int P = int(pool_cap(max_topk, max_depth));
   const FinishArgs fa{root_tokens, num_draft, max_T, tokens, parents, depth_out, anc_mask, q_row};
   hipLaunchKernelGGL(build_finish_kernel, dim3(B), dim3(kFinishThreads), 0, static_cast<hipStream_t>(stream), w, P,

@@ -1627,6 +1627,7 @@ static int32_t verify_impl(const char* who, const float* target, float2* sm_part
   size_t need = 0;
   VerifyWs w = carve(ws, ws_bytes, B, max_T, V, &need);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(SPEC_E_INVAL, "%s: ws must be 16-byte aligned", who);
   // greedy slices of kGreedySlice elements (one round trip of loads per block), doubled or tripled when
   // the rows would otherwise need more blocks than a launch keeps resident (2 per CU at this kernel's
   // register count): a 65-node tree at V = 128256 takes 390 blocks of 24 K instead of 1040 of 8 K
@@ -1735,6 +1736,7 @@ extern "C" int32_t spec_tree_verify_logits(const float* logits, const float* tem
   if ((long long)B * max_T > 65535) return fail(SPEC_E_UNSUPPORTED, "%s: B*max_T=%lld > 65535", who, (long long)B * max_T);
   const size_t need = spec_tree_verify_logits_workspace_size(B, max_T, V);
   if (!ws || ws_bytes < need) return fail(SPEC_E_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(SPEC_E_INVAL, "%s: ws must be 16-byte aligned", who);
   const size_t off = (ws_bytes - logits_part_bytes(B, max_T, V)) & ~size_t(255);
   float2* part = reinterpret_cast<float2*>(static_cast<char*>(ws) + off);
   return verify_impl(who, logits, part, temperature, draft_probs, q_row, tokens, parents, T_b, mode, philox_key0, philox_key1,
