@@ -19,8 +19,8 @@
 //                  block of a greedy sequence (ticket) walks its tree. Sampling
 //                  slice blocks take every (node, slice) of the sampling
 //                  sequences by a fixed stride and publish the slice's exact
-//                  integer sums of fx(p) and fx(q), the argmax of fx(p), and
-//                  its ratio-bin window record (below).
+//                  integer sums of fx(p) and fx(q) and its ratio-bin window
+//                  record (below).
 //   decide kernel  one block per sampling node: it tests the node's children in
 //                  index order against the residual, each rejection's residual
 //                  mass from the window records, or (outside the window) from
@@ -75,13 +75,13 @@ struct VerifyWs {
   uint64_t* keys;      // [B*max_T] greedy argmax keys (0 = empty)
   uint32_t* rowflag;   // [B*max_T] NaN seen in the greedy row
   int32_t* acc_child;  // [B*max_T] sampling: accepted child node or -1
-  uint64_t* rstate;    // [B*max_T][kRs] sampling: a node without an accepted child: W (u128), gamma, S_Q, K, the
-                       // argmax key of fx(p), plain | mass source << 8 (its per-slice masses: ssum or smass)
+  uint64_t* rstate;    // [B*max_T][kRs] sampling: a node without an accepted child: W (u128), gamma, S_Q, K,
+                       // plain | mass source << 8 (its per-slice masses: ssum or smass)
   uint32_t* nflag;     // [B*max_T] sampling node flags
   uint32_t* tickets;   // [B] greedy: rows done; sampling: nodes done
   uint32_t* rtick;     // [B*max_T] greedy: slice blocks of the row done
   uint64_t* ssum;      // [B*max_T][nsl] slice sums of fx(p)
-  uint64_t* psum;      // [B*max_T][nsl][3] slice sum of fx(q), argmax key of fx(p), NaN / window bits
+  uint64_t* psum;      // [B*max_T][nsl][2] slice sum of fx(q), NaN / window bits
   uint64_t* smass;     // [B*max_T][nsl][2] a decision's own row pass: per-slice residual masses (u128)
   // window records (null when a row has more than kFastMaxSl slices)
   uint32_t* wcnt;      // [B*max_T*nsl][kWinSlots] elements per window bin; slot kWinHi: all window elements
@@ -103,7 +103,7 @@ size_t carve_data(char* c, size_t n, size_t nsl, VerifyWs& w) {
   w.rstate = reinterpret_cast<uint64_t*>(take(8 * n * kRs));
   w.nflag = reinterpret_cast<uint32_t*>(take(4 * n));
   w.ssum = reinterpret_cast<uint64_t*>(take(8 * n * nsl));
-  w.psum = reinterpret_cast<uint64_t*>(take(24 * n * nsl));
+  w.psum = reinterpret_cast<uint64_t*>(take(16 * n * nsl));
   w.smass = reinterpret_cast<uint64_t*>(take(16 * n * nsl));
   w.wcnt = nullptr;
   w.wsum = nullptr;
@@ -543,7 +543,7 @@ __device__ __forceinline__ int win_bin(uint32_t P, uint32_t Q) {
   return n >= 64 ? kWinHi : (n < 4 ? -1 : n - 4);
 }
 
-// slice s of a sampling node: sums of fx(p) and fx(q), argmax key of fx(p), NaN bits, published per slice
+// slice s of a sampling node: sums of fx(p) and fx(q) and NaN bits, published per slice
 // (the node's decision block reduces them); for a node with a q row also the slice's window record and its window
 // elements grouped by bin. Window elements are first staged in LDS, each wave in its own region at a running
 // ballot offset, then counted and summed per bin, then placed by per-bin cursors: the order inside a bin is
@@ -551,7 +551,6 @@ __device__ __forceinline__ int win_bin(uint32_t P, uint32_t Q) {
 template <bool VEC, bool LG>
 __device__ __forceinline__ void sample_slice(const VerifyWs& w, const VerifyArgs& a, int b, int u, int s, bool kids) {
   __shared__ uint64_t red[kWaves][3];
-  __shared__ uint64_t amr[kWaves];
   __shared__ uint32_t wc_s[kWinSlots], wcur_s[kWinSlots], wn_s[kWaves];
   __shared__ unsigned long long wp_s[kWinSlots], wq_s[kWinSlots];
   __shared__ uint64_t stage_s[kWinCap];
@@ -573,7 +572,7 @@ __device__ __forceinline__ void sample_slice(const VerifyWs& w, const VerifyArgs
   uint64_t* const stage_w = stage_s + (tid >> 6) * kCapW;
   uint8_t* const sbin_w = sbin_s + (tid >> 6) * kCapW;
   uint32_t run = 0;  // the wave's window elements so far (wave-uniform)
-  uint64_t sp = 0, sq = 0, am = 0, hp = 0, hq = 0;
+  uint64_t sp = 0, sq = 0, hp = 0, hq = 0;
   uint64_t nanp = 0, nanq = 0;  // lanes that met a NaN in p / q (wave-uniform ballots)
   const auto pre = [&] { return prob_row<LG>(a, node); };
   if (qrow) {
@@ -583,8 +582,6 @@ __device__ __forceinline__ void sample_slice(const VerifyWs& w, const VerifyArgs
       const uint32_t P = fx(x), Q = fx(y);
       sp += P;
       sq += Q;
-      const uint64_t k = (uint64_t(P) << 32) | uint64_t(0xffffffffu - uint32_t(v));
-      am = k > am ? k : am;
       if (win) {
         const int bin = win_bin(P, Q);
         if (bin == kWinHi) {
@@ -601,21 +598,16 @@ __device__ __forceinline__ void sample_slice(const VerifyWs& w, const VerifyArgs
         run += uint32_t(__popcll(m));
       }
     });
-  } else {  // no q row (a childless node, or none given): p's sums, argmax and NaN bit only
-    slice_for<VEC>(prow, nullptr, lo, hi, pre, [&](int v, float x, float) {
+  } else {  // no q row (a childless node, or none given): p's sum and NaN bit only
+    slice_for<VEC>(prow, nullptr, lo, hi, pre, [&](int, float x, float) {
       nanp |= __ballot(x != x);
-      const uint32_t P = fx(x);
-      sp += P;
-      const uint64_t k = (uint64_t(P) << 32) | uint64_t(0xffffffffu - uint32_t(v));
-      am = k > am ? k : am;
+      sp += fx(x);
     });
   }
   if (win && lane == 0) wn_s[tid >> 6] = run;
-  am = wave_max_u64(am);
   // NaN bits travel through the block sum as counts (lane 0 of each wave): p in bits 0-3, q in bits 4-7
   const uint32_t nw = (nanp ? 1u : 0u) | (nanq ? 2u : 0u);
   uint64_t nn = lane == 0 ? uint64_t(nw & 1u) + ((nw & 2u) ? 16u : 0u) : 0u;
-  if (lane == 0) amr[tid >> 6] = am;
   if (win) {
     hp = wave_sum_u64(hp);
     hq = wave_sum_u64(hq);
@@ -668,12 +660,10 @@ __device__ __forceinline__ void sample_slice(const VerifyWs& w, const VerifyArgs
     }
   }
   if (tid == 0) {
-    for (int i = 1; i < kWaves; ++i) am = amr[i] > am ? amr[i] : am;
-    uint64_t* ps = w.psum + rec * 3;
+    uint64_t* ps = w.psum + rec * 2;
     w.ssum[rec] = sp;
     ps[0] = sq;
-    ps[1] = am;
-    ps[2] = uint64_t(((nn & 15u) ? 1u : 0u) | ((nn >> 4) ? 2u : 0u)) | wflag;
+    ps[1] = uint64_t(((nn & 15u) ? 1u : 0u) | ((nn >> 4) ? 2u : 0u)) | wflag;
   }
 }
 
@@ -805,12 +795,12 @@ __device__ __forceinline__ void decide_node(const VerifyWs& w, const VerifyArgs&
   __shared__ int act_s;  // accepted child; -1: a rejection needs the next residual mass; -2: resample
   __shared__ int fast_s, fastok_s, ki_s, tested_s, test_s, src_s;
   __shared__ u128 W_s, part_s[2][kWaves];
-  __shared__ uint64_t SP_s, SQ_s, gamma_s, AM_s, K_s;
+  __shared__ uint64_t SP_s, SQ_s, gamma_s, K_s;
   __shared__ uint32_t flags_s;
   __shared__ int plain_s;
   __shared__ u128 ssl_s[kThreads];  // per-slice masses of the current W (the first kThreads slices)
   __shared__ u128 wred_s[kWaves];
-  __shared__ uint64_t red_s[kWaves][3];
+  __shared__ uint64_t red_s[kWaves][2];
   __shared__ WinLds win_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, max_T = a.max_T, V = a.V;
   const size_t node = size_t(b) * max_T + u;
@@ -823,16 +813,15 @@ __device__ __forceinline__ void decide_node(const VerifyWs& w, const VerifyArgs&
   const int qr = a.q_row ? a.q_row[node] : -1;
   const bool may_win = a.fast && w.wcnt != nullptr && qr >= 0 && qr < a.R && a.draft != nullptr;
   if (may_win) win_load(w, a, node, win_s);
-  uint64_t sp = 0, sq = 0, am = 0, nanb = 0;
+  uint64_t sp = 0, sq = 0, nanb = 0;
   for (int sl = tid; sl < a.nsl; sl += kThreads) {
     const size_t r = node * a.nsl + sl;
     const uint64_t v = w.ssum[r];
-    const uint64_t* p3 = w.psum + r * 3;
+    const uint64_t* p2 = w.psum + r * 2;
     if (sl < kThreads) ssl_s[sl] = u128(v);
     sp += v;
-    sq += p3[0];
-    am = p3[1] > am ? p3[1] : am;
-    nanb |= p3[2];
+    sq += p2[0];
+    nanb |= p2[1];
   }
   int c_kid = 0, c_tok = -1;  // wave 0, lane l: the tree's node l + 1 if it is a child of u, its token
   if (wave == 0) {
@@ -855,13 +844,11 @@ __device__ __forceinline__ void decide_node(const VerifyWs& w, const VerifyArgs&
   // ---- reductions (sum, sum, max, or) and the child list in index order
   sp = wave_sum_u64(sp);
   sq = wave_sum_u64(sq);
-  am = wave_max_u64(am);
   nanb = wave_or_u32(uint32_t(nanb));
   if (lane == 0) {
     wred_s[wave] = u128(sp);
     red_s[wave][0] = sq;
-    red_s[wave][1] = am;
-    red_s[wave][2] = nanb;
+    red_s[wave][1] = nanb;
   }
   int kslot = -1;  // this lane's position in the child list
   if (wave == 0) {
@@ -887,8 +874,7 @@ __device__ __forceinline__ void decide_node(const VerifyWs& w, const VerifyArgs&
     for (int i = 1; i < kWaves; ++i) {
       S_P += uint64_t(wred_s[i]);
       sq += red_s[i][0];
-      am = red_s[i][1] > am ? red_s[i][1] : am;
-      nanb |= red_s[i][2];
+      nanb |= red_s[i][1];
     }
     const uint64_t S_Q = qrow ? sq : 0;
     const bool test = nkid > 0 && qrow != nullptr && S_Q > 0;
@@ -896,7 +882,6 @@ __device__ __forceinline__ void decide_node(const VerifyWs& w, const VerifyArgs&
     if (nkid > 0 && !test) flags |= SPEC_STATUS_ZERO_Q;
     SP_s = S_P;
     SQ_s = S_Q;
-    AM_s = am;
     W_s = u128(S_P) * S_Q;
     gamma_s = 0;
     flags_s = flags;
@@ -971,8 +956,8 @@ __device__ __forceinline__ void decide_node(const VerifyWs& w, const VerifyArgs&
     return;
   }
   // ---- no draft accepted: the bonus is drawn only if the walk stops at this node, by the block that walks the
-  // tree (resample_stop); publish what it needs: the final residual mass W, gamma, S_Q, the node's uniform K, the
-  // argmax of fx(p), whether anything was tested, and where the per-slice masses are (pass 0's sums of fx(p) in
+  // tree (resample_stop); publish what it needs: the final residual mass W, gamma, S_Q, the node's uniform K,
+  // whether anything was tested, and where the per-slice masses are (pass 0's sums of fx(p) in
   // ssum, or smass: this block's row pass wrote it; window masses are written there now)
   if (src_s == 1 && tid < a.nsl) {
     uint64_t* sm = w.smass + (node * a.nsl + tid) * 2;
@@ -987,12 +972,33 @@ __device__ __forceinline__ void decide_node(const VerifyWs& w, const VerifyArgs&
     st_agent(rs + 2, gamma_s);
     st_agent(rs + 3, SQ_s);
     st_agent(rs + 4, K_s);
-    st_agent(rs + 5, AM_s);
-    st_agent(rs + 6, uint64_t(plain_s ? 1u : 0u) | (uint64_t(src_s == 0 ? 0u : 2u) << 8));
+    st_agent(rs + 5, uint64_t(plain_s ? 1u : 0u) | (uint64_t(src_s == 0 ? 0u : 2u) << 8));
   }
   wait_global_stores();
   __syncthreads();  // every thread's stores are complete before the ticket
   sample_finish<VEC, LG>(w, a, b, u, -1, flags_s, false);
+}
+
+// The smallest index among the largest fx(p) of a node's row (key fx(p) << 32 | ~index, maximum over the row), in
+// one pass of the block over the row: the bonus when the residual is zero, the only time it is needed. Every
+// thread calls it; the index is returned to every thread.
+template <bool VEC, bool LG>
+__device__ __forceinline__ int row_argmax(const VerifyArgs& a, size_t node) {
+  __shared__ uint64_t am_s[kWaves];
+  const float* prow = sample_row(a, node);
+  const auto pre = [&] { return prob_row<LG>(a, node); };
+  uint64_t am = 0;
+  for (int lo = 0; lo < a.V; lo += kSampleSlice)
+    slice_for<VEC>(prow, nullptr, lo, min(a.V, lo + kSampleSlice), pre, [&](int v, float x, float) {
+      const uint64_t k = (uint64_t(fx(x)) << 32) | uint64_t(0xffffffffu - uint32_t(v));
+      am = k > am ? k : am;
+    });
+  am = wave_max_u64(am);
+  __syncthreads();  // every earlier use of am_s is done
+  if ((threadIdx.x & (kWave - 1)) == 0) am_s[threadIdx.x / kWave] = am;
+  __syncthreads();
+  for (int i = 0; i < kWaves; ++i) am = am_s[i] > am ? am_s[i] : am;
+  return int(0xffffffffu - uint32_t(am));
 }
 
 // The bonus of a sampling sequence whose accepted chain stops at node u, drawn by the block that walks the tree
@@ -1004,7 +1010,7 @@ template <bool VEC, bool LG>
 __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs& a, int b, int u) {
   __shared__ u128 W_s, tau_s, run_s, grem_s, wtot_s[kWaves], ssl_s[kThreads];
   __shared__ uint64_t gsp_s[kWaves][kSampleSlice / (4 * kThreads)], gsq_s[kWaves][kSampleSlice / (4 * kThreads)];
-  __shared__ uint64_t gamma_s, SQ_s, AM_s;
+  __shared__ uint64_t gamma_s, SQ_s;
   __shared__ int plain_s, src_s, found_s, grp_s, bonus_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, V = a.V;
   const size_t node = size_t(b) * a.max_T + u;
@@ -1020,11 +1026,10 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
     const uint64_t* rs = w.rstate + node * kRs;
     const u128 W = u128(ld_agent(rs)) | (u128(ld_agent(rs + 1)) << 64);
     const uint64_t K = ld_agent(rs + 4);
-    const uint64_t f = ld_agent(rs + 6);
+    const uint64_t f = ld_agent(rs + 5);
     W_s = W;
     gamma_s = ld_agent(rs + 2);
     SQ_s = ld_agent(rs + 3);
-    AM_s = ld_agent(rs + 5);
     plain_s = int(f & 1u);
     src_s = int(f >> 8);
     // threshold: smallest v with 2^32 * prefix(v) > K W  <=>  prefix(v) > floor(K W / 2^32)
@@ -1036,7 +1041,7 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
   }
   __syncthreads();
   const u128 W = W_s;
-  if (W == 0) return int(0xffffffffu - uint32_t(AM_s));  // zero residual: smallest-index argmax of p
+  if (W == 0) return row_argmax<VEC, LG>(a, node);  // zero residual: smallest-index argmax of p
   const bool plain = __builtin_amdgcn_readfirstlane(plain_s) != 0;
   const float* prow = sample_row(a, node);
   const ProbRow<LG> pr = prob_row<LG>(a, node);
@@ -1229,7 +1234,7 @@ __device__ __forceinline__ int resample_stop(const VerifyWs& w, const VerifyArgs
   }
   __syncthreads();
   const int bn = bonus_s;
-  return bn >= 0 ? bn : int(0xffffffffu - uint32_t(AM_s));  // unreachable with exact sums; keeps the output defined
+  return bn >= 0 ? bn : row_argmax<VEC, LG>(a, node);  // unreachable with exact sums; keeps the output defined
 }
 
 // ------------------------------------------------------------------ walk
