@@ -59,6 +59,29 @@ def test_workspace_sizes(lib):
     assert lib.spec_tree_build_workspace_size(1, 9, 3) == 0
 
 
+def test_workspace_sizes_grow_with_the_shape(lib):
+    """One workspace serves calls of several shapes when it is sized for the largest B, max_T, max_topk and
+    max_depth (verification: for each call's own V): that rests on the size functions never shrinking as those
+    grow. V is not among them for verification: rows of more than 16 slices keep no window records."""
+    vs = lib.spec_tree_verify_workspace_size
+    vl = lib.spec_tree_verify_logits_workspace_size
+    for V in (1000, 32000, 131072, 131073, 600001):
+        for f in (vs, vl):
+            for B in (1, 3, 8):
+                for T in (1, 9, 33, 65):
+                    here = f(B, T, V)
+                    assert here > 0
+                    assert f(B + 1, T, V) >= here and (T == 65 or f(B, T + 1, V) >= here)
+    assert vs(8, 33, 131073) < vs(8, 33, 131072)  # the window records end at 16 slices
+    bs = lib.spec_tree_build_workspace_size
+    for B in (1, 5):
+        for k in range(1, 8):
+            for D in range(1, 7):
+                here = bs(B, k, D)
+                assert here > 0
+                assert bs(B + 1, k, D) >= here and bs(B, k + 1, D) >= here and bs(B, k, D + 1) >= here
+
+
 def _attn(lib, d=128, max_T=9, Hq=8, Hkv=2, page=16, ws_bytes=1 << 30, ptr=1 << 20, scale=0.1):
     p = ctypes.c_void_p(ptr)
     return lib.spec_tree_attention(p, p, p, p, p, p, None, 1, max_T, Hq, Hkv, d, page, 64, 64, scale, p, None, None, p,
