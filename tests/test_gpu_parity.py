@@ -530,6 +530,32 @@ def test_verify_degenerate_rows():
     assert host["status"][0] & 4 and host["status"][2] & 2 and host["status"][6] & 1
 
 
+@pytest.mark.parametrize("V", [4099, 128256], ids=["V4099", "V128256"])
+def test_verify_zero_residual_bonus_is_the_argmax(V):
+    """Each sampling root's p equals its q row, and both are zero at its children's tokens: every child is
+    rejected and leaves an exactly zero residual max(0, p - q), so the bonus is the smallest-index argmax of
+    fx(p), which the walking block finds in a pass over the root's row (a random row: an interior index)."""
+    w, trees, tok, par, qr = _small_verify_workload(7, "sample", V=V, B=12)
+    target, draft = w.target.copy(), w.draft_probs.copy()
+    for b in range(w.B):
+        if qr[b, 0] < 0:
+            continue
+        row = draft[b, qr[b, 0], :].copy()
+        for c in range(1, int(w.T_b[b])):
+            if par[b, c] == 0 and 0 <= tok[b, c] < V:
+                row[tok[b, c]] = 0.0
+        draft[b, qr[b, 0], :] = row
+        target[b, 0, :] = row
+    w.target, w.draft_probs = target, draft
+    log(f"[verify] zero residual, V={V}")
+    host = _verify(w, tok, par, qr)
+    check_verify(w, host, trees, tokens=tok, parents=par, q_row=qr)
+    zero = [b for b in range(w.B) if host["status"][b] & 16]
+    assert len(zero) >= w.B // 2, f"zero residual on {len(zero)} sequences only"
+    for b in zero:
+        assert host["accept_len"][b] == 0 and host["out_tokens"][b, 0] > 0  # an interior argmax
+
+
 def test_verify_nan_in_draft_rows():
     """A NaN in the q row of a sampling node with children sets NAN_INPUT; in the q row of a childless node it
     is never read (that node decides nothing) and sets nothing."""
